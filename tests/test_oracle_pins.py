@@ -1,0 +1,377 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test names what it pins and why that is independent of the oracle's own
+arithmetic (closed forms, invariants, exact high-precision arithmetic, library
+routines, brute force).  CPU only.
+"""
+from decimal import Decimal, getcontext
+from fractions import Fraction
+import math
+import os
+
+import numpy as np
+import pytest
+
+from int4_quantized_attention_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TINY = synth.CONFIGS["tiny"]
+
+
+def _f32_next_above(x: Decimal) -> np.float32:
+    """Smallest binary32 strictly above the decimal x (exact decimal compare)."""
+    f = np.float32(float(x))
+    while not Decimal(float(f)) > x:
+        f = np.nextafter(f, np.float32(np.inf))
+    while Decimal(float(np.nextafter(f, np.float32(-np.inf)))) > x:
+        f = np.nextafter(f, np.float32(-np.inf))
+    return f
+
+
+# --- P code (Key design 2) -------------------------------------------------------
+
+def test_p_thresholds_match_50_digit_decimal(orc):
+    """The 15 level thresholds equal log2(k - 1/2) computed with 50-digit decimal
+    arithmetic (independent of the oracle's x87 log2l)."""
+    getcontext().prec = 50
+    ln2 = Decimal(2).ln()
+    want = [np.nextafter(np.float32(-1.0), np.float32(0.0))]
+    for k in range(2, 16):
+        want.append(_f32_next_above((Decimal(k) - Decimal("0.5")).ln() / ln2))
+    got = orc.p_thresholds()
+    assert np.array_equal(np.array(want, np.float32).view(np.uint32), got.view(np.uint32))
+
+
+def test_p_level_bruteforce_all_floats(orc):
+    """Every binary32 y with |y| in [2^-10, 4]: the threshold-decided level equals
+    round-half-even(exp2(y)) from libm's binary64 exp2 (brute force)."""
+    bad, first = orc.p_level_bruteforce(2.0 ** -10, 4.0)
+    assert bad == 0, "first mismatch at y=%r" % first
+    # |y| < 2^-10: 2^y is within 0.07% of 1, so the level is 1; far below -1 it is
+    # 0; at and above log2(15.5) it saturates at 15.
+    small = np.float32(np.linspace(-2.0 ** -10, 2.0 ** -10, 10001))
+    assert np.all(orc.p_levels(small) == 1)
+    assert np.all(orc.p_levels(np.float32([-1.0, -1.5, -30.0, -1e30])) == 0)
+    assert np.all(orc.p_levels(np.float32([np.log2(15.5) + 1e-6, 7.0, 1e30])) == 15)
+
+
+def test_p_code_golden_endpoints(orc):
+    """Worked values of the fixed-scale/zero-point map (golden fixture)."""
+    rows = []
+    with open(os.path.join(GOLDEN, "p_rectify_endpoints.txt")) as fh:
+        for line in fh:
+            line = line.split("#")[0].strip()
+            if line:
+                expr, code = line.split(";")
+                rows.append((sum(Fraction(t) for t in expr.strip().split("+")), int(code)))
+    getcontext().prec = 50
+    ln2 = Decimal(2).ln()
+    for P, code in rows:
+        x = 15 * P
+        # exact tie 15 P = 1/2 is reached by y' = -1 exactly
+        y = np.float32(-1.0) if x == Fraction(1, 2) else np.float32(
+            float((Decimal(x.numerator) / Decimal(x.denominator)).ln() / ln2))
+        assert int(orc.p_levels(np.array([y]))[0]) - 8 == code, (P, code)
+
+
+def test_p_levels_monotone_and_complete(orc):
+    y = np.float32(np.linspace(-3.0, 4.2, 200001))
+    r = orc.p_levels(y).astype(int)
+    assert np.all(np.diff(r) >= 0)
+    assert set(r.tolist()) == set(range(16))
+
+
+# --- RoPE and rotation (Key design 1) --------------------------------------------
+
+def _one_head(cfg, x):
+    N = synth.n_tokens(cfg)
+    return x.reshape(1, 1, N, cfg["D"])
+
+
+def _shape1(cfg):
+    s = dict(cfg)
+    s["B"], s["H"] = 1, 1
+    return s
+
+
+def test_rope_relative_position_property(orc):
+    """<RoPE(q, p), RoPE(k, p')> depends only on p - p' per axis (textbook RoPE)."""
+    cfg = _shape1(synth.custom(1, 1, 5, 6, 7, 64, 24, 20, 20, 16, 16))
+    N, D = synth.n_tokens(cfg), 64
+    tab = orc.rope_table(cfg, orc.ROT_NONE, f64=True)
+    rng = np.random.default_rng(7)
+    qv, kv = rng.standard_normal(D), rng.standard_normal(D)
+    tok = lambda f, y, x: (f * cfg["Hs"] + y) * cfg["Ws"] + x
+    X = np.zeros((N, D))
+    X[:] = qv
+    Rq = orc.rope_rotate(cfg, orc.ROT_NONE, tab, _one_head(cfg, X))[0, 0]
+    X[:] = kv
+    Rk = orc.rope_rotate(cfg, orc.ROT_NONE, tab, _one_head(cfg, X))[0, 0]
+    for (p1, p2, dd) in [((0, 0, 0), (1, 2, 3), (2, 1, 1)), ((1, 3, 2), (0, 0, 6), (3, 2, 0)),
+                         ((4, 5, 6), (4, 5, 6), (-4, -5, -6))]:
+        a = Rq[tok(*p1)] @ Rk[tok(*p2)]
+        sh = lambda p: tuple(p[i] + dd[i] for i in range(3))
+        b = Rq[tok(*sh(p1))] @ Rk[tok(*sh(p2))]
+        assert abs(a - b) <= 1e-12 * (abs(a) + 1)
+    # position (0,0,0) is the identity; norms are preserved everywhere
+    assert np.allclose(Rq[0], qv, atol=0, rtol=0)
+    assert np.allclose(np.linalg.norm(Rq, axis=1), np.linalg.norm(qv), rtol=1e-14)
+    # a half-turn sanity value: theta_{j,0} = 1, so frame position 1 rotates the
+    # first frame pair by exactly 1 radian
+    c, s = math.cos(1.0), math.sin(1.0)
+    want = np.array([qv[0] * c - qv[1] * s, qv[0] * s + qv[1] * c])
+    assert np.allclose(Rq[tok(1, 0, 0)][:2], want, rtol=1e-15, atol=1e-15)
+
+
+@pytest.mark.parametrize("rot", [1, 2])
+def test_rotation_is_orthogonal_block_2x2(orc, rot):
+    """At position 0 RoPE is the identity, so the pipeline applies R itself:
+    R R^T = I (the pages require R in O(D)), and R only mixes 2x2 channel pairs --
+    (2i, 2i+1) for Interleaved, (o+i, o+Dj/2+i) -> (o+2i, o+2i+1) for Half."""
+    D, Df, Dh, Dw = 64, 24, 20, 20
+    cfg = synth.custom(1, D, 1, 1, 1, D, Df, Dh, Dw, 1, 1)  # one token per head
+    tab = orc.rope_table(cfg, rot, f64=True)
+    E = np.eye(D).reshape(1, D, 1, D)
+    R = orc.rope_rotate(cfg, rot, tab, E)[0, :, 0, :].T  # column j = R e_j
+    assert np.max(np.abs(R @ R.T - np.eye(D))) <= 1e-15
+    assert np.max(np.abs(R - np.eye(D))) > 0.1
+    nz = np.abs(R) > 1e-12
+    assert np.all(nz.sum(axis=0) == 2) and np.all(nz.sum(axis=1) == 2)
+    for o, dj in [(0, Df), (Df, Dh), (Df + Dh, Dw)]:
+        for i in range(dj // 2):
+            if rot == 1:
+                src, dst = [o + 2 * i, o + 2 * i + 1], [o + 2 * i, o + 2 * i + 1]
+            else:
+                src, dst = [o + i, o + dj // 2 + i], [o + 2 * i, o + 2 * i + 1]
+            assert np.allclose(np.abs(R[np.ix_(dst, src)]), 1 / np.sqrt(2), rtol=1e-15)
+
+
+@pytest.mark.parametrize("rot", [1, 2])
+def test_qk_invariance_under_rotation(orc, rot):
+    """Q K^T = (Q R)(K R)^T for orthogonal R (pages: Key design 1), in binary64."""
+    cfg = dict(TINY)
+    q, k, _ = synth.make_inputs(cfg)
+    q, k = q.astype(np.float64), k.astype(np.float64)
+    t0 = orc.rope_table(cfg, 0, f64=True)
+    tr = orc.rope_table(cfg, rot, f64=True)
+    for h in range(cfg["H"]):
+        a = orc.rope_rotate(cfg, 0, t0, q)[0, h] @ orc.rope_rotate(cfg, 0, t0, k)[0, h].T
+        b = orc.rope_rotate(cfg, rot, tr, q)[0, h] @ orc.rope_rotate(cfg, rot, tr, k)[0, h].T
+        assert np.max(np.abs(a - b)) <= 1e-13 * np.max(np.abs(a))
+
+
+def test_interleaved_fused_equals_rotate_after_rope(orc):
+    """Fused table (alpha, beta) == H2 applied after plain RoPE (M' = R M)."""
+    cfg = dict(TINY)
+    q, _, _ = synth.make_inputs(cfg)
+    t0 = orc.rope_table(cfg, 0, f64=True)
+    t1 = orc.rope_table(cfg, 1, f64=True)
+    x = q.astype(np.float64)
+    plain = orc.rope_rotate(cfg, 0, t0, x)
+    fused = orc.rope_rotate(cfg, 1, t1, x)
+    seq = np.empty_like(plain)
+    seq[..., 0::2] = (plain[..., 0::2] + plain[..., 1::2]) / np.sqrt(2)
+    seq[..., 1::2] = (plain[..., 0::2] - plain[..., 1::2]) / np.sqrt(2)
+    assert np.max(np.abs(fused - seq)) <= 1e-14 * np.max(np.abs(seq))
+    # binary32 spec path: same up to a few ulp (not bit-identical by design)
+    f32 = orc.rope_rotate(cfg, 1, orc.rope_table(cfg, 1), q.astype(np.float32))
+    rel = np.abs(f32 - seq) / (np.abs(seq) + 1e-30)
+    assert np.median(rel) < 1e-6 and np.max(np.abs(f32 - seq)) < 1e-5 * np.max(np.abs(seq))
+
+
+def test_rope_table_closed_form(orc):
+    """Table entries equal cos/sin(pos * 10000^(-2i/Dj)) (plain) and the H2-folded
+    (cos+sin)/sqrt2, (cos-sin)/sqrt2 (Interleaved), rounded to binary32."""
+    cfg = dict(TINY)
+    t0, t1 = orc.rope_table(cfg, 0), orc.rope_table(cfg, 1)
+    # width axis (third block): Ws=4 positions x Dw/2=10 pairs
+    off = 2 * (cfg["F"] * 12 + cfg["Hs"] * 10)
+    p, i = 3, 7
+    ang = p * 10000.0 ** (-2.0 * i / 20)
+    e = off + 2 * (p * 10 + i)
+    assert t0[e] == np.float32(math.cos(ang)) and t0[e + 1] == np.float32(math.sin(ang))
+    assert abs(t1[e] - (math.cos(ang) + math.sin(ang)) / math.sqrt(2)) <= 6e-8
+    assert abs(t1[e + 1] - (math.cos(ang) - math.sin(ang)) / math.sqrt(2)) <= 6e-8
+
+
+# --- quantisation ---------------------------------------------------------------
+
+@pytest.mark.parametrize("rot", [1, 2])
+def test_quantize_invariants(orc, rot):
+    cfg = dict(TINY)
+    q, k, v = synth.make_inputs(cfg)
+    tab = orc.rope_table(cfg, rot)
+    z = orc.quantize(cfg, rot, tab, q, k, v, smooth_k=True, diag=True)
+    N, D, qb = synth.n_tokens(cfg), cfg["D"], cfg["qk_blk"]
+    # q_rot is the rotation of q (binary32 pipeline)
+    assert np.array_equal(z["q_rot"], orc.rope_rotate(cfg, rot, tab, q))
+    # smoothing: mu is the per-channel mean of the rotated K (binary64 mean)
+    mu = z["k_rot"].astype(np.float64).mean(axis=2)
+    assert np.max(np.abs(z["k_mu"] - mu)) <= 1e-6 * np.max(np.abs(mu)) + 1e-12
+    ks_in = (z["k_rot"] - z["k_mu"][:, :, None, :]).astype(np.float32)
+    for name, x, c, sc in [("q", z["q_rot"], z["qc"], z["qs"]), ("k", ks_in, z["kc"], z["ks"])]:
+        for b in range(sc.shape[2]):
+            blk = x[0, :, b * qb:(b + 1) * qb]
+            cb = c[0, :, b * qb:(b + 1) * qb].astype(np.float64)
+            s = sc[0, :, b]
+            amax = np.abs(blk).reshape(cfg["H"], -1).max(axis=1)
+            assert np.allclose(s, amax / 7, rtol=1e-7)
+            err = np.abs(blk - s[:, None, None] * cb)
+            assert np.all(err <= s[:, None, None] / 2 * (1 + 2 ** -20)), name
+            # the block maximum lands on +-7
+            for h in range(cfg["H"]):
+                idx = np.unravel_index(np.argmax(np.abs(blk[h])), blk[h].shape)
+                assert abs(cb[h][idx]) == 7
+    vq = z["vc"].astype(np.float64) * z["vs"][:, :, None, :]
+    assert np.all(np.abs(vq - v) <= z["vs"][:, :, None, :] / 2 * (1 + 2 ** -20))
+    # column sums of the V codes per kv block (brute force)
+    kb = cfg["kv_blk"]
+    for sblk in range(z["vcol"].shape[2]):
+        assert np.array_equal(z["vcol"][:, :, sblk], z["vc"][:, :, sblk * kb:(sblk + 1) * kb].sum(axis=2))
+    assert z["qc"].min() >= -7 and z["qc"].max() <= 7
+
+
+def test_quantize_zero_block_and_v_scale(orc):
+    cfg = dict(TINY)
+    q, k, v = synth.make_inputs(cfg)
+    q[0, 0, :16] = 0
+    v[0, 1, :, 5] = 0
+    z = orc.quantize(cfg, 1, orc.rope_table(cfg, 1), q, k, v)
+    assert z["qs"][0, 0, 0] == 0 and np.all(z["qc"][0, 0, :16] == 0)
+    assert z["vs"][0, 1, 5] == 0 and np.all(z["vc"][0, 1, :, 5] == 0)
+
+
+# --- quantised attention --------------------------------------------------------
+
+def _ints(rng, shape):
+    return rng.integers(-7, 8, size=shape).astype(np.int8)
+
+
+def test_attention_integer_accumulators_bruteforce(orc):
+    cfg = dict(TINY)
+    rng = np.random.default_rng(3)
+    B, H, N, D = 1, 2, 32, 64
+    z = dict(qc=_ints(rng, (B, H, N, D)), kc=_ints(rng, (B, H, N, D)), vc=_ints(rng, (B, H, N, D)),
+             qs=rng.uniform(0.05, 0.5, (B, H, 2)).astype(np.float32),
+             ks=rng.uniform(0.05, 0.5, (B, H, 2)).astype(np.float32),
+             vs=rng.uniform(0.1, 1, (B, H, D)).astype(np.float32))
+    r = orc.attention(cfg, z, dumps=True)
+    qc, kc, vc = (z[n].astype(np.int64) for n in ("qc", "kc", "vc"))
+    want = np.einsum("bhid,bhjd->bhij", qc, kc).reshape(B * H * N, N)
+    assert np.array_equal(r["a_qk"], want)
+    # per-step P.V accumulators: sum_j (code_j + 8) * vc_jd over the step (brute force)
+    lev = r["pcode"].astype(np.int64) + 8
+    for row in range(B * H * N):
+        bh = row // N
+        for st in range(2):
+            sl = slice(16 * st, 16 * st + 16)
+            assert np.array_equal(r["a_pv"][row, st], lev[row, sl] @ vc.reshape(B * H, N, D)[bh, sl])
+    assert r["pcode"].min() >= -8 and r["pcode"].max() <= 7
+
+
+def _dequant_v(z):
+    return z["vc"].astype(np.float64) * z["vs"][:, :, None, :].astype(np.float64)
+
+
+def test_attention_single_token_returns_value(orc):
+    """N = 1: P = 1 -> code 7, so the output is the dequantised V row (closed form)."""
+    cfg = synth.custom(1, 3, 1, 1, 1, 64, 24, 20, 20, 16, 16)
+    q, k, v = synth.make_inputs(cfg)
+    z = orc.quantize(cfg, 2, orc.rope_table(cfg, 2), q, k, v)
+    r = orc.attention(cfg, z, dumps=True)
+    assert np.all(r["pcode"] == 7)
+    assert np.allclose(r["out"], _dequant_v(z).reshape(3, 64), rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("kv", [16, 32])
+def test_attention_zero_query_is_mean_of_values(orc, kv):
+    """Q = 0: every score is 0, every P is 1 (code 7): output = mean of dequantised V."""
+    cfg = dict(TINY, kv_blk=kv)
+    q, k, v = synth.make_inputs(cfg)
+    q[:] = 0
+    z = orc.quantize(cfg, 1, orc.rope_table(cfg, 1), q, k, v)
+    r = orc.attention(cfg, z, dumps=True)
+    assert np.all(r["pcode"] == 7)
+    want = np.repeat(_dequant_v(z).mean(axis=2), 32, axis=1).reshape(-1, 64)
+    assert np.allclose(r["out"], want, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("kv", [16, 32, 64])
+def test_attention_within_rounding_bound_of_exact_softmax(orc, kv):
+    """Lossless Q/K/V codes: the only approximation left is rounding 15 P to an
+    integer level (error <= 1/2 per key, with running-max rescales <= 1), so the
+    output is within 1/2 sum_j |v_j| / l of textbook softmax attention on the
+    dequantised scores (numpy softmax, binary64)."""
+    rng = np.random.default_rng(11)
+    B, H, F, Hs, Ws, D = 1, 2, 2, 4, 8, 64
+    cfg = synth.custom(B, H, F, Hs, Ws, D, 24, 20, 20, 16, kv)
+    N = F * Hs * Ws
+    z = dict(qc=_ints(rng, (B, H, N, D)), kc=_ints(rng, (B, H, N, D)), vc=_ints(rng, (B, H, N, D)),
+             qs=rng.uniform(0.02, 0.1, (B, H, N // 16)).astype(np.float32),
+             ks=rng.uniform(0.02, 0.1, (B, H, N // 16)).astype(np.float32),
+             vs=rng.uniform(0.5, 1, (B, H, D)).astype(np.float32))
+    r = orc.attention(cfg, z, dumps=True)
+    V = _dequant_v(z).reshape(B * H, N, D)
+    sq = np.repeat(z["qs"].astype(np.float64), 16, axis=2).reshape(B * H, N)
+    sk = np.repeat(z["ks"].astype(np.float64), 16, axis=2).reshape(B * H, N)
+    A = np.einsum("hid,hjd->hij", z["qc"].reshape(B * H, N, D).astype(np.float64),
+                  z["kc"].reshape(B * H, N, D).astype(np.float64))
+    S = A * sq[:, :, None] * sk[:, None, :] / math.sqrt(D)
+    P = np.exp(S - S.max(axis=2, keepdims=True))
+    exact = np.einsum("hij,hjd->hid", P / P.sum(axis=2, keepdims=True), V).reshape(-1, D)
+    bound = 0.5 * np.abs(V).sum(axis=1)[:, None, :].repeat(N, axis=1).reshape(-1, D) / r["l"][:, None]
+    assert np.all(np.abs(r["out"] - exact) <= bound * (1 + 1e-5) + 1e-9)
+    cos = np.sum(r["out"] * exact) / np.linalg.norm(r["out"]) / np.linalg.norm(exact)
+    assert cos > 0.95
+
+
+def test_attention_key_permutation_within_step_and_v_scaling(orc):
+    """Invariants: permuting keys inside one online-softmax step leaves the output
+    unchanged; scaling V by 2 doubles it exactly."""
+    cfg = dict(TINY)
+    q, k, v = synth.make_inputs(cfg)
+    tab = orc.rope_table(cfg, 1)
+    z = orc.quantize(cfg, 1, tab, q, k, v)
+    base = orc.attention(cfg, z)["out"]
+    perm = np.concatenate([np.random.default_rng(1).permutation(16), 16 + np.arange(16)])
+    z2 = dict(z)
+    for n in ("kc", "vc"):
+        z2[n] = z[n][:, :, perm]
+    assert np.allclose(orc.attention(cfg, z2)["out"], base, rtol=1e-12, atol=1e-14)
+    z3 = orc.quantize(cfg, 1, tab, q, k, 2 * v)
+    assert np.array_equal(orc.attention(cfg, z3)["out"], 2 * base)
+
+
+def test_fallback_oracle_close_to_exact(orc):
+    """The fallback oracle is exact attention on binary16-rounded RoPE'd Q, K:
+    within binary16 rounding of the binary64 reference."""
+    cfg = dict(TINY)
+    q, k, v = synth.make_inputs(cfg)
+    q, k = q / 8, k / 8
+    fb = orc.fallback_attention(cfg, orc.rope_table(cfg, 0), q, k, v)
+    ex = orc.exact_attention(cfg, q, k, v)
+    assert np.max(np.abs(fb - ex)) < 5e-3 * np.max(np.abs(ex))
+
+
+def test_f16_rounding_matches_numpy(orc):
+    """binary16 round-half-even used by the fallback oracle == numpy's cast."""
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(200000).astype(np.float32) * s
+                        for s in (1e-8, 1e-6, 1e-4, 1, 100, 6e4)] +
+                       [np.float32([0.0, -0.0, 65504, 65520, 1e9, -1e9, 2 ** -24, 2 ** -25, 3 * 2 ** -26])])
+    assert np.array_equal(orc.f32_to_f16_bits(x), x.astype(np.float16).view(np.uint16))
+
+
+def test_report_cosine_vs_exact_tiny(orc, capsys):
+    """Reported (no threshold -- the pages give none): cosine / rel-L2 of the
+    quantised output against exact attention on the tiny config."""
+    cfg = dict(TINY)
+    q, k, v = synth.make_inputs(cfg)
+    ex = orc.exact_attention(cfg, q, k, v)
+    for rot in (0, 1, 2):
+        z = orc.quantize(cfg, rot, orc.rope_table(cfg, rot), q, k, v)
+        o = orc.attention(cfg, z)["out"]
+        cos = float(np.sum(o * ex) / np.linalg.norm(o) / np.linalg.norm(ex))
+        rel = float(np.linalg.norm(o - ex) / np.linalg.norm(ex))
+        print("tiny rot=%d cosine=%.4f relL2=%.4f" % (rot, cos, rel))
+        assert cos > 0.5
