@@ -1,0 +1,180 @@
+/* rotattn.h -- C ABI of the MI355X (gfx950) RotateAttention hot path.
+ *
+ * RotateAttention (arXiv 2607.02584): mixed-precision INT4 FlashAttention for
+ * DiT video models with 3D RoPE.  The problem statement (papernotes.org note,
+ * "Key design 1"): Q, K, V of shape [B, H, N = F*Hs*Ws, D] with the head
+ * dimension split into frame / height / width RoPE segments, D = Df + Dh + Dw.
+ *
+ * Three calls, in the order the pages' framework flowchart runs them:
+ *   rotattn_quantize_qk    3D RoPE -> RoPE-aware orthogonal rotation -> K smoothing
+ *                          -> symmetric per-block INT4 codes (Q, K); per-channel
+ *                          INT4 codes of V.
+ *   rotattn_int4_attention INT4 Q K^T, online softmax, range-rectified P codes
+ *                          round(15 P) - 8 in [-8, 7], INT4 P V, normalisation.
+ *   rotattn_fp16_fallback  FP16 FlashAttention for the heads/steps routed to full
+ *                          precision ("Key design 3", selective FP16 fallback).
+ *
+ * Conventions shared by every call
+ *   - Plain C, no HIP or torch types.  `stream` is a hipStream_t passed as void*
+ *     (NULL = the default stream).  All work is enqueued asynchronously on it.
+ *   - Ownership: the caller allocates and owns every buffer.  The library never
+ *     allocates, frees or synchronises.  Device pointers must be on the current
+ *     device; host pointers are read before the call returns.
+ *   - Errors: arguments are validated on the host before any launch; a bad
+ *     argument returns a status without touching the GPU.  A launch failure
+ *     returns ROTATTN_E_HIP.  Nothing is thrown across the ABI.
+ *   - Thread safety: no mutable global state; calls are reentrant.
+ *   - Layouts are C-contiguous.  Token n of a head sits at RoPE position
+ *     (f, y, x) with n = (f*Hs + y)*Ws + x.  Code tensors are padded to
+ *     Np = rotattn_padded_tokens() tokens; padding codes and scales are zero.
+ *   - Supported: D in {64, 128}; Df, Dh, Dw even and summing to D;
+ *     qk_blk in {16, 32, 64, 128}; kv_blk in {16, 32, 64, 128} with
+ *     qk_blk <= max(kv_blk, 32) ... see rotattn_check_shape(); N >= 1.
+ */
+#ifndef ROTATTN_H_
+#define ROTATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ROTATTN_OK = 0,
+  ROTATTN_E_NULL = 1,        /* a required pointer is NULL                      */
+  ROTATTN_E_SHAPE = 2,       /* inconsistent shape (D != Df+Dh+Dw, N < 1, ...)   */
+  ROTATTN_E_UNSUPPORTED = 3, /* valid but not implemented (D, block sizes...)    */
+  ROTATTN_E_WORKSPACE = 4,   /* workspace too small                              */
+  ROTATTN_E_HIP = 5,         /* a HIP launch failed                              */
+  ROTATTN_E_ARG = 6          /* other bad argument (head id out of range, ...)   */
+} rotattn_status;
+
+typedef enum {
+  ROTATTN_ROT_NONE = 0,        /* RoPE only                                       */
+  ROTATTN_ROT_INTERLEAVED = 1, /* H2 on channel pairs (2i, 2i+1), pre-multiplied   */
+                               /* into the RoPE 2x2 blocks (M' = R M)             */
+  ROTATTN_ROT_HALF = 2         /* per segment: pair channel i with i + Dj/2, H2,  */
+                               /* results at (2i, 2i+1)  (Q Pi R)                 */
+} rotattn_rot;
+
+typedef enum { ROTATTN_F32 = 0, ROTATTN_F16 = 1, ROTATTN_BF16 = 2 } rotattn_dtype;
+
+/* Problem shape.  N = F*Hs*Ws.  qk_blk: tokens per Q/K scale (one scale covers
+ * qk_blk tokens x all D channels).  kv_blk: keys per online-softmax step; the P
+ * codes depend on it (the running maximum is updated once per step). */
+typedef struct {
+  int32_t B, H, F, Hs, Ws, D, Df, Dh, Dw, qk_blk, kv_blk;
+} rotattn_shape;
+
+/* Validate a shape for all three calls (no GPU work). */
+rotattn_status rotattn_check_shape(const rotattn_shape* s);
+
+/* Tokens per head in every code tensor: N rounded up to a multiple of 256. */
+int64_t rotattn_padded_tokens(const rotattn_shape* s);
+
+/* ---- RoPE tables (host, init-time) --------------------------------------------
+ * 3D RoPE (Key design 1): axis j in {frame, height, width} owns Dj channels; pair
+ * i in [0, Dj/2) of the axis rotates by pos * base^(-2i/Dj).  Layout: frame
+ * block [F][Df/2][2], then height [Hs][Dh/2][2], then width [Ws][Dw/2][2].
+ * rot = INTERLEAVED stores the fused (alpha, beta) = ((c+s)/sqrt2, (c-s)/sqrt2),
+ * i.e. H2 x Rot folded into the RoPE constants ("zero inference overhead");
+ * otherwise (cos, sin).  Computed in binary64 (cos, sin of pos*theta), rounded
+ * once to binary32.  host_out must hold rotattn_rope_table_floats() floats; the
+ * caller copies it to the device for the calls below. */
+size_t rotattn_rope_table_floats(const rotattn_shape* s);
+rotattn_status rotattn_build_rope_table(const rotattn_shape* s, rotattn_rot rot, double base,
+                                        float* host_out);
+
+/* ---- rotattn_quantize_qk --------------------------------------------------------
+ * Fused RoPE -> rotation -> smoothing -> INT4 (papernotes note: framework
+ * flowchart and Key design 1; SageAttention-style K smoothing).
+ *   q, k, v       device [B,H,N,D] of in_dtype.
+ *   rope_table    device, from rotattn_build_rope_table(s, rot, ...).
+ *   smooth_k      1: subtract from K its per-(b,h) channel mean over all N tokens
+ *                 (after RoPE and rotation; softmax-invariant); 0: no smoothing.
+ * Outputs (device; code nibbles are two's complement, element 2i in the low
+ * nibble of byte i, element 2i+1 in the high nibble):
+ *   q_codes, k_codes  u8 [B,H,Np,D/2]   symmetric codes in [-7, 7]
+ *   q_scale, k_scale  f32 [B,H,Np/qk_blk]  amax/7 of each qk_blk-token block
+ *   v_codes           u8 [B,H,D,Np/2]   V transposed (token pairs per byte),
+ *                                       codes in [-7, 7]
+ *   v_scale           f32 [B,H,D]       per-channel amax/7 over all N tokens
+ *   v_colsum          i32 [B,H,ceil(N/kv_blk),D] or NULL: per kv block sums of V
+ *                                       codes (the zero-point term of P~ V)
+ * Binary32 op order (bit-reproducible): RoPE u = fma(a,c,-(b*s)), v = fma(a,s,b*c);
+ * fused Interleaved o0 = fma(a,al,b*be), o1 = fma(a,be,-(b*al)); Half
+ * o0 = (x1+x2)*r, o1 = (x1-x2)*r with r = (float)(1/sqrt2); K mean = binary64 sum
+ * of in-order 64-token partial sums, in block order, / N, rounded to binary32;
+ * code = clamp(rint(x * (7/amax)), -7, 7), scale = amax/7 (IEEE division);
+ * amax == 0 gives scale 0 and codes 0.
+ * workspace: device, >= rotattn_quantize_qk_workspace(s) bytes. */
+size_t rotattn_quantize_qk_workspace(const rotattn_shape* s);
+rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
+                                   const void* q, const void* k, const void* v,
+                                   const float* rope_table, int32_t smooth_k,
+                                   uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+                                   uint8_t* v_codes, float* v_scale, int32_t* v_colsum,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- rotattn_int4_attention -----------------------------------------------------
+ * INT4 FlashAttention forward (framework flowchart; Key design 2).  For each query
+ * row i and online-softmax step s of kv_blk keys:
+ *   a_ij = sum_d qc_id kc_jd (exact integer)
+ *   c_ij = fl(fl(sq_i sk_j) C0), C0 = fl(log2(e)/sqrt(D)); t_ij = fl(a_ij c_ij)
+ *   m_s  = max(m_{s-1}, max_j t_ij)
+ *   y_ij = fma(a_ij, c_ij, fl(L15 - m_s)),  L15 = fl(log2 15)
+ *   r_ij = round-half-even(2^y_ij) clamped to [0, 15], decided exactly;
+ *          P code P~ = r - 8 in [-8, 7]  (fixed scale 15, zero point -8)
+ *   l    = 2^(m_{s-1}-m_s) l + sum_j 2^y_ij       (unquantised P)
+ *   O_d  = 2^(m_{s-1}-m_s) O_d + sv_d sum_j (P~_ij + 8) vc_jd
+ *   out  = O / l.
+ * The rotation mode is not needed: an orthogonal R cancels in Q K^T.
+ *   heads/n_heads  host list of flat head ids b*H + h to compute; NULL = all.
+ *   out_dtype      F32 or F16; out device [B,H,N,D]; rows of heads not listed are
+ *                  left untouched.
+ *   dbg            NULL in production.  Otherwise a debug run for rows
+ *                  [row0, row0+n_rows) of head `bh` only, writing (device):
+ *                  a_qk [n_rows][N] i32, p_codes [n_rows][N] i8 (P~),
+ *                  a_pv [n_rows][S][D] i32 with S = ceil(N/kv_blk) (per-step
+ *                  sum_j (P~+8) vc), m [n_rows] f32, l [n_rows] f32.  The output
+ *                  rows are written as well. */
+typedef struct {
+  int32_t bh, row0, n_rows;
+  int32_t* a_qk;
+  int8_t* p_codes;
+  int32_t* a_pv;
+  float* m;
+  float* l;
+} rotattn_debug;
+
+rotattn_status rotattn_int4_attention(const rotattn_shape* s,
+                                      const uint8_t* q_codes, const float* q_scale,
+                                      const uint8_t* k_codes, const float* k_scale,
+                                      const uint8_t* v_codes, const float* v_scale,
+                                      const int32_t* heads, int32_t n_heads,
+                                      rotattn_dtype out_dtype, void* out,
+                                      const rotattn_debug* dbg, void* stream);
+
+/* ---- rotattn_fp16_fallback ------------------------------------------------------
+ * Full-precision fallback for sensitive heads / denoising steps (Key design 3):
+ * out = softmax(RoPE(Q) RoPE(K)^T / sqrt(D)) V with binary16 MFMA operands and
+ * binary32 softmax and accumulation.  RoPE'd Q, K are rounded to binary16.
+ *   in_dtype   F16 (the only one implemented).
+ *   rope_table plain (cos, sin) table: rotattn_build_rope_table(s, NONE, ...).
+ *   heads      as above.  workspace >= rotattn_fp16_fallback_workspace(s). */
+size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s);
+rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dtype,
+                                     const void* q, const void* k, const void* v,
+                                     const float* rope_table,
+                                     const int32_t* heads, int32_t n_heads,
+                                     rotattn_dtype out_dtype, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+const char* rotattn_status_str(rotattn_status st);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ROTATTN_H_ */

@@ -1,0 +1,283 @@
+// Host side of the rotattn C ABI: validation, workspace layout, RoPE tables,
+// P-level thresholds and kernel launches.  See include/rotattn.h.
+#include "../../include/rotattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <limits>
+
+#include "kernels.h"
+
+namespace {
+
+using ra::Shape;
+
+Shape to_shape(const rotattn_shape* s) {
+  return Shape{s->B, s->H, s->F, s->Hs, s->Ws, s->D, s->Df, s->Dh, s->Dw, s->qk_blk, s->kv_blk};
+}
+int64_t tokens(const rotattn_shape* s) { return (int64_t)s->F * s->Hs * s->Ws; }
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// P level thresholds, found independently of any other code base: T[k-1] is the
+// smallest binary32 y with 2^y rounding (half to even) to a level >= k.  For k = 1
+// the boundary 2^y = 1/2 is a tie that rounds down, so T[0] is the float after -1;
+// for k >= 2 the boundary k - 1/2 is never a power of two and T[k-1] is the
+// smallest float whose extended-precision exp2 exceeds k - 1/2.
+struct Levels {
+  float T[16];
+  Levels() {
+    T[0] = std::nextafter(-1.0f, 0.0f);
+    for (int k = 2; k <= 15; ++k) {
+      const long double bound = (long double)k - 0.5L;
+      float y = (float)std::log2((double)bound);
+      while (exp2l((long double)y) <= bound) y = std::nextafter(y, std::numeric_limits<float>::infinity());
+      for (;;) {
+        const float below = std::nextafter(y, -std::numeric_limits<float>::infinity());
+        if (exp2l((long double)below) > bound) y = below;
+        else break;
+      }
+      T[k - 1] = y;
+    }
+    T[15] = std::numeric_limits<float>::infinity();
+  }
+};
+const Levels& levels() {
+  static const Levels lv;
+  return lv;
+}
+
+rotattn_status launch_status(hipError_t e) { return e == hipSuccess ? ROTATTN_OK : ROTATTN_E_HIP; }
+
+void grid_map(int64_t nqt, int nheads, int& total, int& per_xcd) {
+  total = (int)(nqt * nheads);
+  per_xcd = (total + 7) / 8;
+}
+
+}  // namespace
+
+extern "C" {
+
+rotattn_status rotattn_check_shape(const rotattn_shape* s) {
+  if (!s) return ROTATTN_E_NULL;
+  if (s->B < 1 || s->H < 1 || s->F < 1 || s->Hs < 1 || s->Ws < 1) return ROTATTN_E_SHAPE;
+  if (s->Df < 2 || s->Dh < 2 || s->Dw < 2 || (s->Df | s->Dh | s->Dw) & 1) return ROTATTN_E_SHAPE;
+  if (s->Df + s->Dh + s->Dw != s->D) return ROTATTN_E_SHAPE;
+  if (s->D != 64 && s->D != 128) return ROTATTN_E_UNSUPPORTED;
+  if (!pow2_in(s->qk_blk, 16, 128) || !pow2_in(s->kv_blk, 16, 128)) return ROTATTN_E_UNSUPPORTED;
+  const int64_t N = tokens(s);
+  if (N > (int64_t)1 << 28) return ROTATTN_E_UNSUPPORTED;
+  if ((int64_t)s->B * s->H > 65535) return ROTATTN_E_UNSUPPORTED;
+  return ROTATTN_OK;
+}
+
+int64_t rotattn_padded_tokens(const rotattn_shape* s) {
+  if (!s) return 0;
+  const int64_t N = tokens(s);
+  return (N + ra::kTokenPad - 1) / ra::kTokenPad * ra::kTokenPad;
+}
+
+size_t rotattn_rope_table_floats(const rotattn_shape* s) {
+  if (!s) return 0;
+  return (size_t)2 * ((size_t)s->F * (s->Df / 2) + (size_t)s->Hs * (s->Dh / 2) + (size_t)s->Ws * (s->Dw / 2));
+}
+
+rotattn_status rotattn_build_rope_table(const rotattn_shape* s, rotattn_rot rot, double base, float* host_out) {
+  if (!s || !host_out) return ROTATTN_E_NULL;
+  const rotattn_status st = rotattn_check_shape(s);
+  if (st != ROTATTN_OK) return st;
+  if (rot < ROTATTN_ROT_NONE || rot > ROTATTN_ROT_HALF || !(base > 1.0)) return ROTATTN_E_ARG;
+  const int npos[3] = {s->F, s->Hs, s->Ws};
+  const int dj[3] = {s->Df, s->Dh, s->Dw};
+  const double half_sqrt2 = 0.70710678118654752440;  // nearest binary64 to 1/sqrt(2)
+  float* out = host_out;
+  for (int ax = 0; ax < 3; ++ax) {
+    for (int p = 0; p < npos[ax]; ++p) {
+      for (int i = 0; i < dj[ax] / 2; ++i) {
+        const double theta = std::pow(base, -(2.0 * i) / (double)dj[ax]);
+        const double ang = (double)p * theta;
+        const double c = std::cos(ang), sn = std::sin(ang);
+        if (rot == ROTATTN_ROT_INTERLEAVED) {
+          out[0] = (float)((c + sn) * half_sqrt2);
+          out[1] = (float)((c - sn) * half_sqrt2);
+        } else {
+          out[0] = (float)c;
+          out[1] = (float)sn;
+        }
+        out += 2;
+      }
+    }
+  }
+  return ROTATTN_OK;
+}
+
+static size_t q_ws_parts(const rotattn_shape* s, size_t* off_mu, size_t* off_amax) {
+  const int64_t N = tokens(s);
+  const int64_t BH = (int64_t)s->B * s->H;
+  const int64_t nblk = (N + 63) / 64;
+  const size_t kpart = align256((size_t)BH * nblk * s->D * sizeof(double));
+  const size_t mu = align256((size_t)BH * s->D * sizeof(float));
+  const size_t amax = align256((size_t)BH * s->D * sizeof(uint32_t));
+  if (off_mu) *off_mu = kpart;
+  if (off_amax) *off_amax = kpart + mu;
+  return kpart + mu + amax;
+}
+
+size_t rotattn_quantize_qk_workspace(const rotattn_shape* s) {
+  if (!s || rotattn_check_shape(s) != ROTATTN_OK) return 0;
+  return q_ws_parts(s, nullptr, nullptr);
+}
+
+rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
+                                   const void* q, const void* k, const void* v,
+                                   const float* rope_table, int32_t smooth_k,
+                                   uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+                                   uint8_t* v_codes, float* v_scale, int32_t* v_colsum,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  const rotattn_status st = rotattn_check_shape(s);
+  if (st != ROTATTN_OK) return st;
+  if (!q || !k || !v || !rope_table || !q_codes || !q_scale || !k_codes || !k_scale || !v_codes ||
+      !v_scale || !workspace)
+    return ROTATTN_E_NULL;
+  if (rot < ROTATTN_ROT_NONE || rot > ROTATTN_ROT_HALF) return ROTATTN_E_ARG;
+  if (in_dtype < ROTATTN_F32 || in_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
+  size_t off_mu, off_amax;
+  if (workspace_bytes < q_ws_parts(s, &off_mu, &off_amax)) return ROTATTN_E_WORKSPACE;
+  ra::QuantArgs a;
+  a.s = to_shape(s);
+  a.Np = rotattn_padded_tokens(s);
+  a.rot = (int)rot;
+  a.smooth = smooth_k ? 1 : 0;
+  a.q = q; a.k = k; a.v = v;
+  a.table = rope_table;
+  a.qc = q_codes; a.qs = q_scale; a.kc = k_codes; a.ks = k_scale;
+  a.vc = v_codes; a.vs = v_scale; a.vcol = v_colsum;
+  a.kpart = (double*)workspace;
+  a.kmu = (float*)((char*)workspace + off_mu);
+  a.vamax = (uint32_t*)((char*)workspace + off_amax);
+  return launch_status(ra::launch_quantize(a, (int)in_dtype, (hipStream_t)stream));
+}
+
+rotattn_status rotattn_int4_attention(const rotattn_shape* s,
+                                      const uint8_t* q_codes, const float* q_scale,
+                                      const uint8_t* k_codes, const float* k_scale,
+                                      const uint8_t* v_codes, const float* v_scale,
+                                      const int32_t* heads, int32_t n_heads,
+                                      rotattn_dtype out_dtype, void* out,
+                                      const rotattn_debug* dbg, void* stream) {
+  const rotattn_status st = rotattn_check_shape(s);
+  if (st != ROTATTN_OK) return st;
+  if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !out) return ROTATTN_E_NULL;
+  if (out_dtype != ROTATTN_F32 && out_dtype != ROTATTN_F16) return ROTATTN_E_ARG;
+  const int BH = s->B * s->H;
+  if (heads) {
+    if (n_heads < 0) return ROTATTN_E_ARG;
+    for (int i = 0; i < n_heads; ++i)
+      if (heads[i] < 0 || heads[i] >= BH) return ROTATTN_E_ARG;
+  }
+  const int64_t N = tokens(s);
+  ra::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.qc = q_codes; a.qs = q_scale; a.kc = k_codes; a.ks = k_scale; a.vc = v_codes; a.vs = v_scale;
+  a.out = out;
+  a.out_f16 = out_dtype == ROTATTN_F16;
+  a.N = N;
+  a.Np = rotattn_padded_tokens(s);
+  a.qk_blk = s->qk_blk;
+  a.nqt = (int)((N + 127) / 128);
+  a.C0 = (float)(1.4426950408889634074 / std::sqrt((double)s->D));
+  a.L15 = (float)std::log2(15.0);
+  std::memcpy(a.T, levels().T, sizeof(a.T));
+  hipStream_t hs = (hipStream_t)stream;
+  if (dbg) {
+    if (!dbg->a_qk || !dbg->p_codes || !dbg->a_pv || !dbg->m || !dbg->l) return ROTATTN_E_NULL;
+    if (dbg->bh < 0 || dbg->bh >= BH || dbg->row0 < 0 || dbg->n_rows < 1 || (int64_t)dbg->row0 + dbg->n_rows > N)
+      return ROTATTN_E_ARG;
+    a.dbg_row0 = dbg->row0; a.dbg_n = dbg->n_rows;
+    a.dbg_aqk = dbg->a_qk; a.dbg_p = dbg->p_codes; a.dbg_apv = dbg->a_pv; a.dbg_m = dbg->m; a.dbg_l = dbg->l;
+    a.nheads = 1;
+    a.heads[0] = dbg->bh;
+    a.total = a.nqt;
+    a.per_xcd = 0;
+    return launch_status(ra::launch_attention(a, s->D, s->kv_blk, true, hs));
+  }
+  const int nh = heads ? n_heads : BH;
+  for (int h0 = 0; h0 < nh; h0 += ra::kMaxHeads) {
+    const int cnt = nh - h0 < ra::kMaxHeads ? nh - h0 : ra::kMaxHeads;
+    a.nheads = cnt;
+    for (int i = 0; i < cnt; ++i) a.heads[i] = heads ? heads[h0 + i] : h0 + i;
+    grid_map(a.nqt, cnt, a.total, a.per_xcd);
+    const hipError_t e = ra::launch_attention(a, s->D, s->kv_blk, false, hs);
+    if (e != hipSuccess) return ROTATTN_E_HIP;
+  }
+  return ROTATTN_OK;
+}
+
+size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s) {
+  if (!s || rotattn_check_shape(s) != ROTATTN_OK) return 0;
+  const size_t per = (size_t)s->B * s->H * rotattn_padded_tokens(s) * s->D * sizeof(uint16_t);
+  return 3 * align256(per);
+}
+
+rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dtype,
+                                     const void* q, const void* k, const void* v,
+                                     const float* rope_table,
+                                     const int32_t* heads, int32_t n_heads,
+                                     rotattn_dtype out_dtype, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  const rotattn_status st = rotattn_check_shape(s);
+  if (st != ROTATTN_OK) return st;
+  if (!q || !k || !v || !rope_table || !out || !workspace) return ROTATTN_E_NULL;
+  if (in_dtype != ROTATTN_F16) return ROTATTN_E_UNSUPPORTED;
+  if (out_dtype != ROTATTN_F32 && out_dtype != ROTATTN_F16) return ROTATTN_E_ARG;
+  if (workspace_bytes < rotattn_fp16_fallback_workspace(s)) return ROTATTN_E_WORKSPACE;
+  const int BH = s->B * s->H;
+  if (heads) {
+    if (n_heads < 0) return ROTATTN_E_ARG;
+    for (int i = 0; i < n_heads; ++i)
+      if (heads[i] < 0 || heads[i] >= BH) return ROTATTN_E_ARG;
+  }
+  ra::FbArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.s = to_shape(s);
+  a.N = tokens(s);
+  a.Np = rotattn_padded_tokens(s);
+  a.q = q; a.k = k; a.v = v;
+  a.table = rope_table;
+  const size_t per = align256((size_t)BH * a.Np * s->D * sizeof(uint16_t));
+  a.qr = (_Float16*)workspace;
+  a.kr = (_Float16*)((char*)workspace + per);
+  a.vt = (_Float16*)((char*)workspace + 2 * per);
+  a.out = out;
+  a.out_f16 = out_dtype == ROTATTN_F16;
+  a.nqt = (int)((a.N + 127) / 128);
+  a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)s->D));
+  hipStream_t hs = (hipStream_t)stream;
+  if (ra::launch_fallback_prep(a, hs) != hipSuccess) return ROTATTN_E_HIP;
+  const int nh = heads ? n_heads : BH;
+  for (int h0 = 0; h0 < nh; h0 += ra::kMaxHeads) {
+    const int cnt = nh - h0 < ra::kMaxHeads ? nh - h0 : ra::kMaxHeads;
+    a.nheads = cnt;
+    for (int i = 0; i < cnt; ++i) a.heads[i] = heads ? heads[h0 + i] : h0 + i;
+    grid_map(a.nqt, cnt, a.total, a.per_xcd);
+    if (ra::launch_fallback(a, hs) != hipSuccess) return ROTATTN_E_HIP;
+  }
+  return ROTATTN_OK;
+}
+
+const char* rotattn_status_str(rotattn_status st) {
+  switch (st) {
+    case ROTATTN_OK: return "ok";
+    case ROTATTN_E_NULL: return "a required pointer is NULL";
+    case ROTATTN_E_SHAPE: return "inconsistent shape";
+    case ROTATTN_E_UNSUPPORTED: return "shape or option not supported";
+    case ROTATTN_E_WORKSPACE: return "workspace too small";
+    case ROTATTN_E_HIP: return "HIP launch failed";
+    case ROTATTN_E_ARG: return "bad argument";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Kernel argument blocks and launchers (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+struct Shape {
+  int B, H, F, Hs, Ws, D, Df, Dh, Dw, qk_blk, kv_blk;
+};
+
+constexpr int kTokenPad = 256;   // code tensors hold Np = N rounded up to this
+constexpr int kMaxHeads = 512;   // heads per attention launch (more -> several launches)
+
+struct QuantArgs {
+  Shape s;
+  int64_t Np;
+  int rot, smooth;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* table;
+  uint8_t* qc;
+  float* qs;
+  uint8_t* kc;
+  float* ks;
+  uint8_t* vc;
+  float* vs;
+  int32_t* vcol;
+  // workspace
+  double* kpart;
+  float* kmu;
+  uint32_t* vamax;
+};
+
+struct AttnArgs {
+  const uint8_t* qc;
+  const float* qs;
+  const uint8_t* kc;
+  const float* ks;
+  const uint8_t* vc;
+  const float* vs;
+  void* out;
+  int out_f16;
+  int64_t N, Np;
+  int qk_blk;
+  int nqt, total, per_xcd;
+  float C0, L15;
+  float T[16];  // P level thresholds (15 used)
+  // debug (rows [dbg_row0, dbg_row0 + dbg_n) of the single listed head)
+  int dbg_row0, dbg_n;
+  int32_t* dbg_aqk;
+  int8_t* dbg_p;
+  int32_t* dbg_apv;
+  float* dbg_m;
+  float* dbg_l;
+  int nheads;
+  int heads[kMaxHeads];
+};
+
+struct FbArgs {
+  Shape s;
+  int64_t N, Np;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* table;
+  _Float16* qr;   // workspace: RoPE'd Q  [B*H][Np][D] f16
+  _Float16* kr;   // workspace: RoPE'd K  [B*H][Np][D] f16
+  _Float16* vt;   // workspace: V^T       [B*H][D][Np] f16 (32-key groups permuted)
+  void* out;
+  int out_f16;
+  int nqt, total, per_xcd;
+  float scale_log2;  // log2(e) / sqrt(D)
+  int nheads;
+  int heads[kMaxHeads];
+};
+
+hipError_t launch_quantize(const QuantArgs& a, int dtype, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, int D, int kv_blk, bool dbg, hipStream_t st);
+hipError_t launch_fallback_prep(const FbArgs& a, hipStream_t st);
+hipError_t launch_fallback(const FbArgs& a, hipStream_t st);
+
+}  // namespace ra

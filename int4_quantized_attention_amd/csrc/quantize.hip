@@ -1,0 +1,298 @@
+// K1: fused 3D RoPE -> RoPE-aware rotation -> K smoothing -> INT4 quantisation.
+//
+// RotateAttention (arXiv 2607.02584), papernotes.org note: "Overall framework"
+// (smoothing, RoPE-aware rotation, INT4 Q/K) and "Key design 1" (3D RoPE split
+// D = Df + Dh + Dw; Interleaved rotation fused into the RoPE 2x2 blocks; Half
+// rotation Q Pi R pairing channel i with i + Dj/2 inside each segment).
+//
+// Memory-bound.  Every launch stages a 128-token tile of the input in LDS (one
+// coalesced 16-byte global load per 8 elements), computes the rotated values in
+// registers and writes packed nibbles with 16-byte stores.  K and V need global
+// statistics (the channel mean of K, the channel amax of V), so they are read twice.
+#include "common.h"
+#include "kernels.h"
+#include "rope.h"
+
+namespace ra {
+
+// ---------------------------------------------------------------------------------
+// K statistics: ordered binary64 partial sums of rotated K over 64-token blocks.
+// grid (ceil(N/64), B*H); 256 threads.  partial [B*H][nblk][D] f64.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  const Shape s = a.s;
+  const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
+  const int bh = blockIdx.y, blk = blockIdx.x;
+  const int64_t n0 = (int64_t)blk * kMeanTile;
+  const void* base = (const char*)a.k + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
+  stage_tile<D, DT>(base, n0, N, kMeanTile, lds);
+  __syncthreads();
+  // rotated values into a float tile after the input tile
+  const size_t in_bytes = (size_t)kMeanTile * (DT == 0 ? (D + 1) * 4 : (D + 2) * 2);
+  float* rot = (float*)(lds + ((in_bytes + 15) & ~(size_t)15));
+  for (int e = threadIdx.x; e < kMeanTile * D; e += blockDim.x) {
+    const int r = e / D, c = e % D;
+    float val = 0.f;
+    if (n0 + r < N) {
+      int f, y, x;
+      token_pos(n0 + r, s, f, y, x);
+      val = rope_rot<D, DT>(lds, r, c, s, a.rot, a.table, f, y, x);
+    }
+    rot[r * (D + 1) + c] = val;
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    double part = 0.0;
+    const int cnt = (int)min((int64_t)kMeanTile, N - n0);
+    for (int r = 0; r < cnt; ++r) part += (double)rot[r * (D + 1) + c];
+    const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
+    a.kpart[((int64_t)bh * nblk + blk) * D + c] = part;
+  }
+}
+
+// Channel mean of K: binary64 sum of the partials in block order, / N, to binary32.
+__global__ void k1_kmean(QuantArgs a) {
+  const int D = a.s.D;
+  const int64_t N = (int64_t)a.s.F * a.s.Hs * a.s.Ws;
+  const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.s.B * a.s.H * D) return;
+  const int64_t bh = idx / D, c = idx % D;
+  double total = 0.0;
+  for (int64_t b = 0; b < nblk; ++b) total += a.kpart[(bh * nblk + b) * D + c];
+  a.kmu[idx] = (float)(total / (double)N);
+}
+
+__global__ void k1_zero_u32(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// V channel amax over all tokens: tile of 128 tokens, atomic max on the float
+// bits (non-negative floats order like unsigned integers).
+template <int D, int DT>
+__global__ __launch_bounds__(256) void k1_vamax(QuantArgs a) {
+  const Shape s = a.s;
+  const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
+  const int bh = blockIdx.y;
+  const int64_t n0 = (int64_t)blockIdx.x * kTile;
+  const void* base = (const char*)a.v + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
+  constexpr int G = 256 / D;
+  const int c = threadIdx.x % D, g = threadIdx.x / D;
+  float m = 0.f;
+  for (int r = g; r < kTile; r += G) {
+    const int64_t n = n0 + r;
+    if (n < N) m = fmaxf(m, fabsf(load_elem<DT>(base, n * D + c)));
+  }
+  __shared__ float red[256];
+  red[threadIdx.x] = m;
+  __syncthreads();
+  if (g == 0) {
+    for (int k = 1; k < G; ++k) m = fmaxf(m, red[k * D + c]);
+    atomicMax(a.vamax + (int64_t)bh * D + c, __float_as_uint(m));
+  }
+}
+
+// Q / K quantisation: grid (Np/128, B*H, 2 (0 = Q, 1 = K)); 256 threads, two
+// threads per token, each owning D/2 consecutive output channels.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  __shared__ float wred[4];
+  const Shape s = a.s;
+  const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
+  const int64_t Np = a.Np;
+  const int bh = blockIdx.y;
+  const bool isK = blockIdx.z == 1;
+  const int64_t n0 = (int64_t)blockIdx.x * kTile;
+  const void* src = isK ? a.k : a.q;
+  const void* base = (const char*)src + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
+  stage_tile<D, DT>(base, n0, N, kTile, lds);
+  __syncthreads();
+
+  constexpr int CPT = D / 2;
+  const int lt = threadIdx.x >> 1, part = threadIdx.x & 1;
+  const int64_t n = n0 + lt;
+  const bool valid = n < N;
+  int f, y, x;
+  token_pos(n, s, f, y, x);
+  float v[CPT];
+  if (valid) {
+    // padding tokens (n >= N) have no grid position: never index the table for them
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = part * CPT + i;
+      float t = rope_rot<D, DT>(lds, lt, c, s, a.rot, a.table, f, y, x);
+      if (isK && a.smooth) t = t - a.kmu[(int64_t)bh * D + c];
+      v[i] = t;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) v[i] = 0.f;
+  }
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) am = fmaxf(am, fabsf(v[i]));
+  // reduce over the 2*qk_blk threads of one scale block
+  const int grp = 2 * s.qk_blk;
+  if (grp <= 64) {
+    am = wave_max(am, grp);
+  } else {
+    am = wave_max(am, 64);
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) wred[wid] = am;
+    __syncthreads();
+    const int wpg = grp / 64;  // waves per group
+    const int g0 = (wid / wpg) * wpg;
+    am = wred[g0];
+    for (int k = 1; k < wpg; ++k) am = fmaxf(am, wred[g0 + k]);
+  }
+  const float inv = am == 0.f ? 0.f : 7.0f / am;
+  uint32_t packed[CPT / 8];
+#pragma unroll
+  for (int w = 0; w < CPT / 8; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int code = am == 0.f ? 0 : quant_code(v[w * 8 + e], inv);
+      word |= ((uint32_t)code & 0xFu) << (4 * e);
+    }
+    packed[w] = word;
+  }
+  uint8_t* codes = isK ? a.kc : a.qc;
+  uint4* dst = (uint4*)(codes + ((int64_t)bh * Np + n) * (D / 2) + part * (CPT / 2));
+#pragma unroll
+  for (int w = 0; w < CPT / 8; w += 4) dst[w / 4] = make_uint4(packed[w], packed[w + 1], packed[w + 2], packed[w + 3]);
+  if (part == 0 && (lt % s.qk_blk) == 0) {
+    float* sc = isK ? a.ks : a.qs;
+    sc[(int64_t)bh * (Np / s.qk_blk) + n / s.qk_blk] = am == 0.f ? 0.f : am / 7.0f;
+  }
+}
+
+// V quantisation into the transposed layout [B,H,D,Np/2] plus per-kv-block
+// column sums.  grid (Np/128, B*H); thread -> (channel c, token group g).
+template <int D, int DT>
+__global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  const Shape s = a.s;
+  const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
+  const int64_t Np = a.Np;
+  const int bh = blockIdx.y;
+  const int64_t n0 = (int64_t)blockIdx.x * kTile;
+  const void* base = (const char*)a.v + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
+  stage_tile<D, DT>(base, n0, N, kTile, lds);
+  __syncthreads();
+  constexpr int G = 256 / D, TPG = kTile / G;  // groups, tokens per group
+  const int c = threadIdx.x % D, g = threadIdx.x / D;
+  const float amax = __uint_as_float(a.vamax[(int64_t)bh * D + c]);
+  const float inv = amax == 0.f ? 0.f : 7.0f / amax;
+  if (blockIdx.x == 0 && g == 0) a.vs[(int64_t)bh * D + c] = amax == 0.f ? 0.f : amax / 7.0f;
+  int codes[TPG];
+#pragma unroll
+  for (int i = 0; i < TPG; ++i) {
+    const int r = g * TPG + i;
+    const bool valid = n0 + r < N;
+    codes[i] = (valid && amax != 0.f) ? quant_code(lds_elem<D, DT>(lds, r, c), inv) : 0;
+  }
+  uint32_t words[TPG / 8];
+#pragma unroll
+  for (int w = 0; w < TPG / 8; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) word |= ((uint32_t)codes[w * 8 + e] & 0xFu) << (4 * e);
+    words[w] = word;
+  }
+  uint4* dst = (uint4*)(a.vc + ((int64_t)bh * D + c) * (Np / 2) + (n0 + g * TPG) / 2);
+#pragma unroll
+  for (int w = 0; w < TPG / 8; w += 4) dst[w / 4] = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
+  if (a.vcol) {
+    // column sums per kv block; 16-token chunk sums first (static indices keep
+    // everything in registers), then blocks of kv_blk tokens.
+    __shared__ int part[256];
+    const int kvb = s.kv_blk;
+    const int64_t nkb = (N + kvb - 1) / kvb;
+    int chunk[TPG / 16];
+#pragma unroll
+    for (int ch = 0; ch < TPG / 16; ++ch) {
+      int acc = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc += codes[ch * 16 + i];
+      chunk[ch] = acc;
+    }
+    if (kvb <= TPG) {
+      int acc = 0;
+#pragma unroll
+      for (int ch = 0; ch < TPG / 16; ++ch) {
+        acc += chunk[ch];
+        if (((ch + 1) * 16) % kvb == 0) {
+          const int64_t sblk = (n0 + g * TPG + (ch + 1) * 16 - kvb) / kvb;
+          if (sblk < nkb) a.vcol[((int64_t)bh * nkb + sblk) * D + c] = acc;
+          acc = 0;
+        }
+      }
+    } else {
+      int acc = 0;
+#pragma unroll
+      for (int ch = 0; ch < TPG / 16; ++ch) acc += chunk[ch];
+      part[threadIdx.x] = acc;
+      __syncthreads();
+      const int gpb = kvb / TPG;  // groups per block
+      if (g % gpb == 0) {
+        for (int k = 1; k < gpb; ++k) acc += part[(g + k) * D + c];
+        const int64_t sblk = (n0 + g * TPG) / kvb;
+        if (sblk < nkb) a.vcol[((int64_t)bh * nkb + sblk) * D + c] = acc;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+template <int D, int DT>
+hipError_t launch_quantize_t(const QuantArgs& a, hipStream_t st) {
+  const int64_t N = (int64_t)a.s.F * a.s.Hs * a.s.Ws;
+  const int BH = a.s.B * a.s.H;
+  const size_t in_tile = (size_t)kTile * (DT == 0 ? (D + 1) * 4 : (D + 2) * 2);
+  const size_t mean_in = (size_t)kMeanTile * (DT == 0 ? (D + 1) * 4 : (D + 2) * 2);
+  const size_t mean_lds = ((mean_in + 15) & ~(size_t)15) + (size_t)kMeanTile * (D + 1) * 4;
+  const int64_t nvamax = (int64_t)BH * D;
+  if (DT == 0) {
+    // fp32 tiles exceed the default 64 KiB of dynamic LDS; gfx950 has 160 KiB
+    static const hipError_t attr = [&] {
+      hipError_t e = hipFuncSetAttribute((const void*)k1_quant_qk<D, DT>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)in_tile);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)k1_quant_v<D, DT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)in_tile);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)k1_kstats<D, DT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)mean_lds);
+      return e;
+    }();
+    if (attr != hipSuccess) return attr;
+  }
+  k1_zero_u32<<<(unsigned)((nvamax + 255) / 256), 256, 0, st>>>(a.vamax, nvamax);
+  k1_vamax<D, DT><<<dim3((unsigned)(a.Np / kTile), BH), 256, 0, st>>>(a);
+  if (a.smooth) {
+    const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
+    k1_kstats<D, DT><<<dim3((unsigned)nblk, BH), 256, mean_lds, st>>>(a);
+    k1_kmean<<<(unsigned)((nvamax + 255) / 256), 256, 0, st>>>(a);
+  }
+  k1_quant_qk<D, DT><<<dim3((unsigned)(a.Np / kTile), BH, 2), 256, in_tile, st>>>(a);
+  k1_quant_v<D, DT><<<dim3((unsigned)(a.Np / kTile), BH), 256, in_tile, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs& a, int dtype, hipStream_t st) {
+  if (a.s.D == 128) {
+    if (dtype == 0) return launch_quantize_t<128, 0>(a, st);
+    if (dtype == 1) return launch_quantize_t<128, 1>(a, st);
+    return launch_quantize_t<128, 2>(a, st);
+  }
+  if (dtype == 0) return launch_quantize_t<64, 0>(a, st);
+  if (dtype == 1) return launch_quantize_t<64, 1>(a, st);
+  return launch_quantize_t<64, 2>(a, st);
+}
+
+}  // namespace ra

@@ -1,0 +1,198 @@
+"""ctypes binding of librotattn (the C ABI in include/rotattn.h).
+
+Argument marshalling only: every step of the hot path runs in the library's HIP
+kernels.  torch provides device memory and the current stream.  There is no CPU
+fallback: if the library is not built, importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librotattn.so")
+
+ROT_NONE, ROT_INTERLEAVED, ROT_HALF = 0, 1, 2
+F32, F16, BF16 = 0, 1, 2
+_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+ROT_BY_NAME = {"none": ROT_NONE, "interleaved": ROT_INTERLEAVED, "half": ROT_HALF}
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "H", "F", "Hs", "Ws", "D", "Df", "Dh", "Dw", "qk_blk", "kv_blk")]
+
+    @classmethod
+    def of(cls, cfg) -> "Shape":
+        return cls(*[int(cfg[n]) for n, _ in cls._fields_])
+
+    @property
+    def N(self) -> int:
+        return self.F * self.Hs * self.Ws
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("bh", ctypes.c_int32), ("row0", ctypes.c_int32), ("n_rows", ctypes.c_int32),
+                ("a_qk", ctypes.c_void_p), ("p_codes", ctypes.c_void_p), ("a_pv", ctypes.c_void_p),
+                ("m", ctypes.c_void_p), ("l", ctypes.c_void_p)]
+
+
+class RotattnError(RuntimeError):
+    pass
+
+
+_lib = None
+_VP, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+_SIGS = {
+    "rotattn_check_shape": (_I32, [_VP]),
+    "rotattn_padded_tokens": (ctypes.c_int64, [_VP]),
+    "rotattn_rope_table_floats": (_SZ, [_VP]),
+    "rotattn_build_rope_table": (_I32, [_VP, _I32, ctypes.c_double, _VP]),
+    "rotattn_quantize_qk_workspace": (_SZ, [_VP]),
+    "rotattn_quantize_qk": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
+                                   _VP, _VP, _VP, _SZ, _VP]),
+    "rotattn_int4_attention": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP]),
+    "rotattn_fp16_fallback_workspace": (_SZ, [_VP]),
+    "rotattn_fp16_fallback": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ, _VP]),
+    "rotattn_status_str": (ctypes.c_char_p, [_I32]),
+}
+
+
+def lib():
+    """Load librotattn.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RotattnError("librotattn.so is not built (run __graft_entry__.build() or "
+                               "python -m int4_quantized_attention_amd.build_lib)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise RotattnError("%s: %s (status %d)" % (what, lib().rotattn_status_str(st).decode(), st))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise RotattnError("expected a contiguous device tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _heads(heads: Optional[Sequence[int]]):
+    if heads is None:
+        return None, 0
+    arr = (ctypes.c_int32 * len(heads))(*[int(h) for h in heads])
+    return arr, len(heads)
+
+
+# ---- thin wrappers with the C names ---------------------------------------------
+
+def rotattn_check_shape(shape: Shape) -> int:
+    return lib().rotattn_check_shape(ctypes.byref(shape))
+
+
+def rotattn_padded_tokens(shape: Shape) -> int:
+    return int(lib().rotattn_padded_tokens(ctypes.byref(shape)))
+
+
+def rotattn_build_rope_table(shape: Shape, rot: int, base: float = 10000.0) -> torch.Tensor:
+    """Host RoPE table (float32 CPU tensor); copy it to the device for the calls."""
+    n = lib().rotattn_rope_table_floats(ctypes.byref(shape))
+    out = torch.empty(n, dtype=torch.float32)
+    _check(lib().rotattn_build_rope_table(ctypes.byref(shape), rot, base, ctypes.c_void_p(out.data_ptr())),
+           "rotattn_build_rope_table")
+    return out
+
+
+def rotattn_quantize_qk_workspace(shape: Shape) -> int:
+    return int(lib().rotattn_quantize_qk_workspace(ctypes.byref(shape)))
+
+
+def rotattn_fp16_fallback_workspace(shape: Shape) -> int:
+    return int(lib().rotattn_fp16_fallback_workspace(ctypes.byref(shape)))
+
+
+def alloc_codes(shape: Shape, device="cuda", colsum: bool = True) -> dict:
+    """Output buffers of rotattn_quantize_qk (torch device tensors)."""
+    Np = rotattn_padded_tokens(shape)
+    B, H, D = shape.B, shape.H, shape.D
+    nkb = -(-shape.N // shape.kv_blk)
+    u8, f32 = torch.uint8, torch.float32
+    z = dict(q_codes=torch.empty((B, H, Np, D // 2), dtype=u8, device=device),
+             q_scale=torch.empty((B, H, Np // shape.qk_blk), dtype=f32, device=device),
+             k_codes=torch.empty((B, H, Np, D // 2), dtype=u8, device=device),
+             k_scale=torch.empty((B, H, Np // shape.qk_blk), dtype=f32, device=device),
+             v_codes=torch.empty((B, H, D, Np // 2), dtype=u8, device=device),
+             v_scale=torch.empty((B, H, D), dtype=f32, device=device),
+             v_colsum=torch.empty((B, H, nkb, D), dtype=torch.int32, device=device) if colsum else None)
+    z["workspace"] = torch.empty(rotattn_quantize_qk_workspace(shape), dtype=torch.uint8, device=device)
+    return z
+
+
+def rotattn_quantize_qk(shape: Shape, rot: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        rope_table: torch.Tensor, smooth_k: bool, z: dict) -> dict:
+    """z: buffers from alloc_codes (filled in place, returned)."""
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise RotattnError("q, k, v must share one of float32 / float16 / bfloat16")
+    ws = z["workspace"]
+    _check(lib().rotattn_quantize_qk(
+        ctypes.byref(shape), rot, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table),
+        1 if smooth_k else 0, _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
+        _ptr(z["v_codes"]), _ptr(z["v_scale"]), _ptr(z.get("v_colsum")), _ptr(ws), ws.numel(), _stream()),
+        "rotattn_quantize_qk")
+    return z
+
+
+def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Optional[Sequence[int]] = None,
+                           debug: Optional[dict] = None) -> torch.Tensor:
+    """out: device [B,H,N,D] float32 or float16.  debug: dict(bh, row0, n_rows) ->
+    filled with device tensors a_qk, p_codes, a_pv, m, l."""
+    if out.dtype not in (torch.float32, torch.float16):
+        raise RotattnError("out must be float32 or float16")
+    harr, nh = _heads(heads)
+    dbg = None
+    if debug is not None:
+        n, N = int(debug["n_rows"]), shape.N
+        S = -(-N // shape.kv_blk)
+        dev = out.device
+        debug.update(a_qk=torch.zeros((n, N), dtype=torch.int32, device=dev),
+                     p_codes=torch.zeros((n, N), dtype=torch.int8, device=dev),
+                     a_pv=torch.zeros((n, S, shape.D), dtype=torch.int32, device=dev),
+                     m=torch.zeros(n, dtype=torch.float32, device=dev),
+                     l=torch.zeros(n, dtype=torch.float32, device=dev))
+        dbg = Debug(int(debug["bh"]), int(debug["row0"]), n, debug["a_qk"].data_ptr(),
+                    debug["p_codes"].data_ptr(), debug["a_pv"].data_ptr(), debug["m"].data_ptr(),
+                    debug["l"].data_ptr())
+    _check(lib().rotattn_int4_attention(
+        ctypes.byref(shape), _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
+        _ptr(z["v_codes"]), _ptr(z["v_scale"]), harr, nh, F16 if out.dtype == torch.float16 else F32,
+        _ptr(out), ctypes.byref(dbg) if dbg is not None else None, _stream()), "rotattn_int4_attention")
+    return out
+
+
+def rotattn_fp16_fallback(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          rope_table: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                          heads: Optional[Sequence[int]] = None) -> torch.Tensor:
+    if q.dtype != torch.float16:
+        raise RotattnError("the fallback takes float16 q, k, v")
+    harr, nh = _heads(heads)
+    _check(lib().rotattn_fp16_fallback(
+        ctypes.byref(shape), F16, _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table), harr, nh,
+        F16 if out.dtype == torch.float16 else F32, _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
+        "rotattn_fp16_fallback")
+    return out

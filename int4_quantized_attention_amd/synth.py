@@ -94,21 +94,27 @@ def make_head(cfg, b: int, h: int, seed: int = 0):
     return q, k, v
 
 
-def make_inputs(cfg, seed: int = 0, heads=None):
+def make_inputs(cfg, seed: int = 0, heads=None, threads: int = 16):
     """Full [B, H, N, D] tensors in the config's storage dtype (numpy).
-    heads: optional list of flat head ids b*H + h to fill (others left zero)."""
+    heads: optional list of flat head ids b*H + h to fill (others left zero).
+    Heads are drawn in parallel threads; each head has its own stream, so the
+    result does not depend on the thread count."""
+    from concurrent.futures import ThreadPoolExecutor
     B, H, D = int(cfg["B"]), int(cfg["H"]), int(cfg["D"])
     N = n_tokens(cfg)
     dt = np.float16 if cfg["dtype"] == "float16" else np.float32
     Q = np.zeros((B, H, N, D), dt)
     K = np.zeros((B, H, N, D), dt)
     V = np.zeros((B, H, N, D), dt)
-    for b in range(B):
-        for h in range(H):
-            if heads is not None and b * H + h not in heads:
-                continue
-            q, k, v = make_head(cfg, b, h, seed)
-            Q[b, h], K[b, h], V[b, h] = q.astype(dt), k.astype(dt), v.astype(dt)
+    todo = [(b, h) for b in range(B) for h in range(H) if heads is None or b * H + h in heads]
+
+    def one(bh):
+        b, h = bh
+        q, k, v = make_head(cfg, b, h, seed)
+        Q[b, h], K[b, h], V[b, h] = q.astype(dt), k.astype(dt), v.astype(dt)
+
+    with ThreadPoolExecutor(max(1, min(threads, len(todo)))) as ex:
+        list(ex.map(one, todo))
     return Q, K, V
 
 

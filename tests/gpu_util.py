@@ -1,0 +1,85 @@
+"""Helpers of the GPU tests: run the library on torch device tensors, unpack its
+code layouts, and compare with the oracle.  (Layout helpers only; no arithmetic
+of the method.)"""
+import numpy as np
+import torch
+
+from int4_quantized_attention_amd import rotattn as ra
+from int4_quantized_attention_amd import synth
+
+_TDT = {"float16": torch.float16, "float32": torch.float32, "bfloat16": torch.bfloat16}
+
+
+def to_dev(x: np.ndarray, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def gpu_quantize(cfg, rot: int, Q, K, V, smooth=True, in_dtype=None):
+    shape = ra.Shape.of(cfg)
+    tdt = in_dtype or _TDT[cfg["dtype"]]
+    q, k, v = (to_dev(x, tdt) for x in (Q, K, V))
+    tab = ra.rotattn_build_rope_table(shape, rot).cuda()
+    z = ra.alloc_codes(shape)
+    ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, smooth, z)
+    torch.cuda.synchronize()
+    return shape, z
+
+
+def unpack_rows(codes_u8: torch.Tensor) -> np.ndarray:
+    """[..., n/2] bytes -> [..., n] signed nibbles (element 2i low nibble)."""
+    b = codes_u8.cpu().numpy().astype(np.int16)
+    lo, hi = b & 0xF, (b >> 4) & 0xF
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int16)
+    out[..., 0::2], out[..., 1::2] = lo, hi
+    out = np.where(out >= 8, out - 16, out)
+    return out.astype(np.int8)
+
+
+def compare_codes(cfg, z, ref, heads=None):
+    """Bit-exact comparison of the library's code tensors with the oracle's
+    (restricted to flat head ids `heads` of the library's tensors, which the
+    oracle computed as its heads 0..len-1)."""
+    B, H, D = cfg["B"], cfg["H"], cfg["D"]
+    N = synth.n_tokens(cfg)
+    qb, kb = cfg["qk_blk"], cfg["kv_blk"]
+    nqb, nkb = -(-N // qb), -(-N // kb)
+    sel = list(range(B * H)) if heads is None else list(heads)
+    f = lambda t: t.reshape((B * H,) + tuple(t.shape[2:]))[sel]
+    qc, kc = unpack_rows(f(z["q_codes"])), unpack_rows(f(z["k_codes"]))
+    vc = unpack_rows(f(z["v_codes"]))  # [h, D, Np]
+    r = lambda a: a.reshape((-1,) + a.shape[2:])
+    assert np.array_equal(qc[:, :N], r(ref["qc"])), "q codes"
+    assert np.all(qc[:, N:] == 0), "q padding"
+    assert np.array_equal(kc[:, :N], r(ref["kc"])), "k codes"
+    assert np.all(kc[:, N:] == 0), "k padding"
+    assert np.array_equal(vc[:, :, :N].transpose(0, 2, 1), r(ref["vc"])), "v codes"
+    assert np.all(vc[:, :, N:] == 0), "v padding"
+    qs, ks = f(z["q_scale"]).cpu().numpy(), f(z["k_scale"]).cpu().numpy()
+    assert np.array_equal(qs[:, :nqb].view(np.uint32), r(ref["qs"]).view(np.uint32)), "q scales"
+    assert np.array_equal(ks[:, :nqb].view(np.uint32), r(ref["ks"]).view(np.uint32)), "k scales"
+    assert np.all(qs[:, nqb:] == 0) and np.all(ks[:, nqb:] == 0)
+    vs = f(z["v_scale"]).cpu().numpy()
+    assert np.array_equal(vs.view(np.uint32), r(ref["vs"]).view(np.uint32)), "v scales"
+    if z.get("v_colsum") is not None:
+        assert np.array_equal(f(z["v_colsum"]).cpu().numpy()[:, :nkb], r(ref["vcol"])), "v colsums"
+
+
+def assert_close(out: np.ndarray, ref: np.ndarray, max_abs=2e-3, rel_l2=1e-3, what="O"):
+    out = out.astype(np.float64)
+    err = np.abs(out - ref)
+    rl2 = np.linalg.norm(out - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert np.isfinite(out).all(), what + " has non-finite values"
+    assert err.max() <= max_abs, "%s max-abs err %.3g > %.3g" % (what, err.max(), max_abs)
+    assert rl2 <= rel_l2, "%s rel-L2 err %.3g > %.3g" % (what, rl2, rel_l2)
+    return float(err.max()), float(rl2)
+
+
+def rows_sample(N: int, n_rand: int = 32, seed: int = 0):
+    """First tile, the ragged last tile and some random rows of one head."""
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(N, 40))) | set(range(max(0, N - 40), N))
+    rows |= set(rng.integers(0, N, n_rand).tolist())
+    return np.array(sorted(rows), np.int64)

@@ -1,0 +1,95 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every symbol
+the header declares, validates arguments before any launch, and its host-built
+RoPE tables equal the oracle's bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from int4_quantized_attention_amd import rotattn as ra
+from int4_quantized_attention_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rotattn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ra.LIB_PATH):
+        from int4_quantized_attention_amd import build_lib
+        build_lib.build()
+    return ra.lib()
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(rotattn_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _shape(**kw):
+    cfg = dict(synth.CONFIGS["tiny"])
+    cfg.update(kw)
+    return ra.Shape.of(cfg)
+
+
+def test_check_shape_statuses(L):
+    assert ra.rotattn_check_shape(_shape()) == 0
+    assert ra.rotattn_check_shape(_shape(Df=26)) == 2          # D != Df+Dh+Dw
+    assert ra.rotattn_check_shape(_shape(Df=23, Dh=21)) == 2   # odd segments
+    assert ra.rotattn_check_shape(_shape(D=96, Df=32, Dh=32, Dw=32)) == 3
+    assert ra.rotattn_check_shape(_shape(qk_blk=8)) == 3
+    assert ra.rotattn_check_shape(_shape(kv_blk=256)) == 3
+    assert ra.rotattn_check_shape(_shape(F=0)) == 2
+    assert L.rotattn_check_shape(None) == 1
+
+
+def test_padded_tokens_and_workspace(L):
+    s = ra.Shape.of(synth.CONFIGS["wan720p"])
+    assert ra.rotattn_padded_tokens(s) == 75776
+    assert ra.rotattn_quantize_qk_workspace(s) > 0
+    assert ra.rotattn_fp16_fallback_workspace(s) >= 3 * 40 * 75776 * 128 * 2
+
+
+def test_null_and_bad_args_return_before_launch(L):
+    s = _shape()
+    nul = None
+    st = L.rotattn_quantize_qk(ctypes.byref(s), 1, 0, nul, nul, nul, nul, 1, nul, nul, nul, nul, nul,
+                               nul, nul, nul, 0, nul)
+    assert st == 1
+    st = L.rotattn_int4_attention(ctypes.byref(s), nul, nul, nul, nul, nul, nul, nul, 0, 0, nul, nul, nul)
+    assert st == 1
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    bad_heads = (ctypes.c_int32 * 1)(5)  # B*H = 2
+    st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, bad_heads, 1, 0,
+                                  fake, nul, nul)
+    assert st == 6
+    st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 2,
+                                  fake, nul, nul)
+    assert st == 6  # bf16 output is not offered
+    st = L.rotattn_quantize_qk(ctypes.byref(s), 1, 0, fake, fake, fake, fake, 1, fake, fake, fake, fake,
+                               fake, fake, nul, fake, 16, nul)
+    assert st == 4  # workspace too small
+    st = L.rotattn_fp16_fallback(ctypes.byref(s), 0, fake, fake, fake, fake, nul, 0, 0, fake, fake,
+                                 1 << 30, nul)
+    assert st == 3  # only float16 inputs
+    assert L.rotattn_status_str(0) == b"ok"
+
+
+@pytest.mark.parametrize("cfgname", ["tiny", "wan480p", "hunyuan720p"])
+@pytest.mark.parametrize("rot", [0, 1, 2])
+def test_rope_table_matches_oracle(L, orc, cfgname, rot):
+    cfg = synth.CONFIGS[cfgname]
+    mine = ra.rotattn_build_rope_table(ra.Shape.of(cfg), rot).numpy()
+    ref = orc.rope_table(cfg, rot)
+    assert mine.shape == ref.shape
+    assert np.array_equal(mine.view(np.uint32), ref.view(np.uint32))

@@ -1,0 +1,128 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same
+seeded inputs.  Integer work (INT4 codes, scales' bits, P codes, integer
+accumulators, the running maximum) is bit-exact; the output O is within max-abs
+2e-3 and rel-L2 1e-3 of the oracle's binary64 result."""
+import numpy as np
+import pytest
+import torch
+
+from int4_quantized_attention_amd import rotattn as ra
+from int4_quantized_attention_amd import synth
+
+from gpu_util import assert_close, compare_codes, gpu_quantize, rows_sample, to_dev
+
+pytestmark = pytest.mark.gpu
+
+ROTS = {"interleaved": 1, "half": 2, "none": 0}
+
+
+def _oracle_head_cfg(cfg):
+    c = dict(cfg)
+    c["B"], c["H"] = 1, 1
+    return c
+
+
+def _run_case(orc, cfg, rot, smooth=True, debug_rows=None, out_dtype=torch.float32, in_dtype=None):
+    Q, K, V = synth.make_inputs(cfg)
+    shape, z = gpu_quantize(cfg, rot, Q, K, V, smooth, in_dtype)
+    ref = orc.quantize(cfg, rot, orc.rope_table(cfg, rot), Q, K, V, smooth_k=smooth)
+    compare_codes(cfg, z, ref)
+    N, D = synth.n_tokens(cfg), cfg["D"]
+    out = torch.full((cfg["B"], cfg["H"], N, D), float("nan"), dtype=out_dtype, device="cuda")
+    ra.rotattn_int4_attention(shape, z, out)
+    torch.cuda.synchronize()
+    o = orc.attention(cfg, ref)
+    tol = (2e-3, 1e-3) if out_dtype == torch.float32 else (4e-3, 1.5e-3)
+    assert_close(out.float().cpu().numpy().reshape(-1, D), o["out"], *tol)
+    if debug_rows:
+        BH = cfg["B"] * cfg["H"]
+        for bh in range(BH):
+            for (r0, n) in debug_rows:
+                n = min(n, N - r0)
+                dbg = dict(bh=bh, row0=r0, n_rows=n)
+                out2 = torch.zeros_like(out)
+                ra.rotattn_int4_attention(shape, z, out2, debug=dbg)
+                torch.cuda.synchronize()
+                rows = np.arange(bh * N + r0, bh * N + r0 + n)
+                od = orc.attention(cfg, ref, rows=rows, dumps=True)
+                assert np.array_equal(dbg["a_qk"].cpu().numpy(), od["a_qk"]), "a_qk"
+                assert np.array_equal(dbg["p_codes"].cpu().numpy(), od["pcode"]), "P codes"
+                assert np.array_equal(dbg["a_pv"].cpu().numpy(), od["a_pv"]), "a_pv"
+                assert np.array_equal(dbg["m"].cpu().numpy().view(np.uint32), od["m"].view(np.uint32)), "m"
+                assert np.allclose(dbg["l"].cpu().numpy(), od["l"], rtol=1e-5), "l"
+                assert_close(out2.float().cpu().numpy()[bh // cfg["H"], bh % cfg["H"], r0:r0 + n], od["out"])
+    return z, ref
+
+
+@pytest.mark.parametrize("rot", ["interleaved", "half", "none"])
+def test_tiny_full_parity(orc, rot):
+    cfg = dict(synth.CONFIGS["tiny"])
+    _run_case(orc, cfg, ROTS[rot], debug_rows=[(0, 32)])
+
+
+MEDIUM = [
+    # (id, config overrides)
+    ("wan_half_kv64", dict(rot="half")),
+    ("wan_inter_kv16_qk16", dict(rot="interleaved", qk_blk=16, kv_blk=16)),
+    ("wan_half_kv32_qk32", dict(rot="half", qk_blk=32, kv_blk=32)),
+    ("wan_half_kv128_qk128", dict(rot="half", qk_blk=128, kv_blk=128)),
+    ("wan_half_kv128_qk16", dict(rot="half", qk_blk=16, kv_blk=128)),
+    ("hunyuan_inter_B2", dict(rot="interleaved", recipe="hunyuan", Df=16, Dh=56, Dw=56, B=2)),
+    ("peaked_none_nosmooth", dict(rot="none", recipe="peaked")),
+]
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=[c[0] for c in MEDIUM])
+def test_medium_ragged_parity(orc, case):
+    name, over = case
+    cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
+    cfg.update(over)
+    smooth = "nosmooth" not in name
+    _run_case(orc, cfg, ROTS[cfg["rot"]], smooth=smooth, debug_rows=[(0, 40), (1133, 40)])
+
+
+def test_d64_and_float32_and_bf16_inputs(orc):
+    cfg = synth.custom(1, 2, 5, 7, 9, 64, 24, 20, 20, 32, 64, dtype="float32", recipe="tiny")
+    _run_case(orc, cfg, 2)
+    # bf16 storage: the oracle sees the same bf16 values as floats
+    cfg2 = dict(cfg)
+    Q, K, V = synth.make_inputs(cfg2)
+    tb = lambda x: torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    Qb, Kb, Vb = tb(Q), tb(K), tb(V)
+    shape, z = gpu_quantize(cfg2, 1, Qb, Kb, Vb, True, in_dtype=torch.bfloat16)
+    ref = orc.quantize(cfg2, 1, orc.rope_table(cfg2, 1), Qb, Kb, Vb)
+    compare_codes(cfg2, z, ref)
+
+
+def test_fp16_output(orc):
+    cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
+    _run_case(orc, cfg, 2, out_dtype=torch.float16)
+
+
+def test_edge_single_token_and_zero_query(orc):
+    cfg = synth.custom(2, 3, 1, 1, 1, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
+    _run_case(orc, cfg, 2, debug_rows=[(0, 1)])
+    cfg = synth.custom(1, 2, 2, 5, 7, 128, 44, 42, 42, 16, 16, dtype="float16", recipe="wan")
+    Q, K, V = synth.make_inputs(cfg)
+    Q[:] = 0
+    K[0, 1, :20] = 0  # an all-zero K scale block
+    shape, z = gpu_quantize(cfg, 1, Q, K, V)
+    ref = orc.quantize(cfg, 1, orc.rope_table(cfg, 1), Q, K, V)
+    compare_codes(cfg, z, ref)
+    out = torch.empty((1, 2, 70, 128), dtype=torch.float32, device="cuda")
+    ra.rotattn_int4_attention(shape, z, out)
+    assert_close(out.cpu().numpy().reshape(-1, 128), orc.attention(cfg, ref)["out"])
+
+
+def test_head_subset_leaves_other_heads(orc):
+    cfg = synth.custom(1, 4, 3, 10, 11, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
+    Q, K, V = synth.make_inputs(cfg)
+    shape, z = gpu_quantize(cfg, 2, Q, K, V)
+    ref = orc.quantize(cfg, 2, orc.rope_table(cfg, 2), Q, K, V)
+    out = torch.full((1, 4, 330, 128), 7.0, dtype=torch.float32, device="cuda")
+    ra.rotattn_int4_attention(shape, z, out, heads=[3, 1])
+    o = out.cpu().numpy()
+    full = orc.attention(cfg, ref)["out"].reshape(1, 4, 330, 128)
+    assert np.all(o[0, 0] == 7.0) and np.all(o[0, 2] == 7.0)
+    assert_close(o[0, 1], full[0, 1])
+    assert_close(o[0, 3], full[0, 3])
