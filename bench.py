@@ -1,0 +1,165 @@
+"""Benchmark of the RotateAttention INT4 hot path on one MI355X.
+
+One step = the whole INT4 path over one batch of synthetic input already in HBM:
+rotattn_quantize_qk (fused RoPE -> Half rotation -> K smoothing -> INT4 codes)
+then rotattn_int4_attention, on the Wan-14B-720p-like layer (B=1, H=40, grid
+21x45x80 -> N=75600, D=128 split 44/42/42).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+CONFIG = "wan720p"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-fallback", action="store_true", help="skip timing the FP16 fallback")
+    ap.add_argument("--config", default=CONFIG)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU (the path shards by head with no "
+              "communication; see the design notes); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from int4_quantized_attention_amd import rotattn as ra
+    from int4_quantized_attention_amd import synth
+
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.config]
+    B, H, D = cfg["B"], cfg["H"], cfg["D"]
+    N = synth.n_tokens(cfg)
+    rot = ra.ROT_BY_NAME[cfg["rot"]]
+    shape = ra.Shape.of(cfg)
+    ops = 4.0 * N * N * D * H * B
+
+    Q, K, V = synth.make_inputs(cfg)
+    q, k, v = (torch.from_numpy(x).cuda() for x in (Q, K, V))
+    del Q, K, V
+    tab = ra.rotattn_build_rope_table(shape, rot).cuda()
+    z = ra.alloc_codes(shape)
+    out = torch.empty((B, H, N, D), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, True, z)
+        if ev is not None:
+            ev[1].record(stream)
+        ra.rotattn_int4_attention(shape, z, out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_step = wall * 1e3 / args.steps
+
+    # K1 algorithmic bytes: read Q, K, V (fp16) once, write three INT4 code tensors
+    # and the scales: 3*2 + 3*0.5 bytes per element.
+    k1_bytes = (3 * 2.0 + 3 * 0.5) * N * D * H * B
+    k2_tops = ops / (k2_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": "effective attention TOPS (4*N^2*D*H/s) at Wan-720p-like shape; % int8 MFMA peak",
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": "Wan-14B-720p-like attention layer: B=%d H=%d grid %dx%dx%d N=%d D=%d "
+                               "(%d/%d/%d), %s rotation, qk_blk=%d kv_blk=%d, fp16 in/out"
+                               % (B, H, cfg["F"], cfg["Hs"], cfg["Ws"], N, D, cfg["Df"], cfg["Dh"], cfg["Dw"],
+                                  cfg["rot"], cfg["qk_blk"], cfg["kv_blk"]),
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "k2_attention (rotattn_int4_attention)",
+                     "achieved": round(k2_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(k2_tops / PEAK_INT8_TOPS, 4), "traffic": None},
+        "kernels_ms": {"quantize_qk": round(k1_ms, 4), "int4_attention": round(k2_ms, 4)},
+        "quantize_qk_GBps": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
+        "attention_only_TOPS": round(k2_tops, 1),
+    }
+
+    if not args.no_fallback:
+        ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
+        tab0 = ra.rotattn_build_rope_table(shape, 0).cuda()
+        ra.rotattn_fp16_fallback(shape, q, k, v, tab0, out, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 2
+        e0.record(stream)
+        for _ in range(reps):
+            ra.rotattn_fp16_fallback(shape, q, k, v, tab0, out, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fb_ms = e0.elapsed_time(e1) / reps
+        fb_tops = ops / (fb_ms * 1e-3) / 1e12
+        result["fallback"] = {"ms": round(fb_ms, 3), "TFLOPS": round(fb_tops, 1),
+                              "frac_f16_peak": round(fb_tops / PEAK_F16_TFLOPS, 4),
+                              "int4_attention_speedup": round(fb_ms / k2_ms, 3)}
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg, rot)
+    print(json.dumps(result))
+
+
+def cpu_baseline(cfg, rot, rows_target=16384):
+    """The oracle on the host cores: quantisation of one head, then quantised
+    attention for a bounded sample of that head's query rows; scaled to TOPS."""
+    import numpy as np
+    from int4_quantized_attention_amd import synth
+    from oracle import oracle as orc
+    orc.build()
+    N, D = synth.n_tokens(cfg), cfg["D"]
+    c1 = dict(cfg)
+    c1["B"], c1["H"] = 1, 1
+    q, k, v = synth.make_head(cfg, 0, 0)
+    f = lambda x: x.astype(np.float16)[None, None]
+    t0 = time.perf_counter()
+    z = orc.quantize(c1, rot, orc.rope_table(c1, rot), f(q), f(k), f(v))
+    tq = time.perf_counter() - t0
+    rows = np.linspace(0, N - 1, rows_target).astype(np.int64)
+    t0 = time.perf_counter()
+    orc.attention(c1, z, rows=rows)
+    ta = time.perf_counter() - t0
+    ops = 4.0 * N * D * rows.size
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(ops / ta / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": "head 0 of the same workload: quantisation of all %d tokens (%.2f s) and "
+                      "attention for %d of its query rows over all keys (%.2f s)" % (N, tq, rows.size, ta)}
+
+
+if __name__ == "__main__":
+    main()

@@ -21,6 +21,9 @@
 //    (rare) other elements are decided exactly against the 15 thresholds.
 //  * The int32 P V accumulator runs across online-softmax steps and is folded
 //    into the fp32 output only when a row maximum moves.
+//  * Software pipeline, one barrier per key group: the Q K^T MFMAs of group g+1
+//    are issued before the softmax of group g (MFMA and VALU overlap); K and V
+//    tiles are double-buffered in LDS and their global loads run one group ahead.
 //  * Workgroup ids are remapped so that all query tiles of a head run on the same
 //    XCD and share its L2 for the K/V stream.
 #include "common.h"
@@ -39,42 +42,320 @@ RA_DEV uint32_t pack_b2(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_amdgcn_perm(y, x, 0x05040100u);
 }
 
-RA_DEV float partner(float v) {
-  // value of lane l ^ 32
-  return __shfl_xor(v, 32, 64);
+// The fields the device helpers need, copied out of the kernel argument block
+// (which also holds the head list and stays in the kernarg segment).
+struct Ctx {
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const float* ks;
+  int64_t Np;
+  int N, qk_blk;
+  float C0, L15;
+  int dbg_row0, dbg_n;
+  int32_t* dbg_aqk;
+  int8_t* dbg_p;
+  int32_t* dbg_apv;
+};
+
+// value held by lane l ^ 32
+RA_DEV float partner(float v) { return __shfl_xor(v, 32, 64); }
+
+template <int D, int KVB>
+struct Geo {
+  static constexpr int TG = KVB < 32 ? 32 : KVB;  // keys per group (staged together)
+  static constexpr int NT = TG / 32;              // 32-key MFMA tiles per group
+  static constexpr int NDB = D / 32;              // 32-row d blocks of O^T
+  static constexpr int KC = D / 32;               // 32-deep chunks of Q K^T
+  static constexpr int KROW = D + 16;             // LDS K row stride (bytes)
+  static constexpr int VROW = TG + 16;            // LDS V^T row stride (bytes)
+  static constexpr int KBUF = TG * KROW;
+  static constexpr int VBUF = D * VROW;
+  static constexpr int LDS = 2 * KBUF + 2 * VBUF;   // + 17 floats of level thresholds after it
+  static constexpr int KU = TG * D / 16;          // 8-byte global units of a K group
+  static constexpr int VU = D * TG / 16;          // 8-byte global units of a V group
+  static constexpr int KUT = (KU + 255) / 256;    // per thread
+  static constexpr int VUT = (VU + 255) / 256;
+};
+
+// Per-lane running state of one query row (the lane pair l, l^32 shares a row).
+template <int NDB>
+struct RowState {
+  f32x16 Of[NDB];
+  i32x16 acc[NDB];
+  float m, l, Rf;
+  int Rint;
+};
+
+template <int D, int KVB>
+RA_DEV void load_k(const Ctx& a, int bh, int g, uint2 (&r)[Geo<D, KVB>::KUT]) {
+  using G = Geo<D, KVB>;
+  const uint2* src = (const uint2*)(a.kc + ((int64_t)bh * a.Np + (int64_t)g * G::TG) * (D / 2));
+#pragma unroll
+  for (int i = 0; i < G::KUT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (G::KU % 256 == 0 || u < G::KU) r[i] = src[u];
+  }
+}
+template <int D, int KVB>
+RA_DEV void load_v(const Ctx& a, int bh, int g, uint2 (&r)[Geo<D, KVB>::VUT]) {
+  using G = Geo<D, KVB>;
+#pragma unroll
+  for (int i = 0; i < G::VUT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (G::VU % 256 == 0 || u < G::VU) {
+      const int d = u / (G::TG / 16), c = u % (G::TG / 16);
+      r[i] = ((const uint2*)(a.vc + ((int64_t)bh * D + d) * (a.Np / 2) + (int64_t)g * (G::TG / 2)))[c];
+    }
+  }
+}
+// K rows are permuted inside each 32-key tile so that the S^T accumulator of lane
+// half h holds keys 16h..16h+15 of the tile in register order.
+template <int D, int KVB>
+RA_DEV void store_k(uint8_t* Kl, const uint2 (&r)[Geo<D, KVB>::KUT]) {
+  using G = Geo<D, KVB>;
+#pragma unroll
+  for (int i = 0; i < G::KUT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (G::KU % 256 == 0 || u < G::KU) {
+      const int kk = u / (D / 16), c = u % (D / 16);
+      uint32_t lo0, hi0, lo1, hi1;
+      widen_biased(r[i].x, lo0, hi0);
+      widen_biased(r[i].y, lo1, hi1);
+      const int rr = kk & 31, hh = rr >> 4, v = rr & 15;
+      const int row = (kk & ~31) + (v & 3) + 8 * (v >> 2) + 4 * hh;
+      *(uint4*)(Kl + row * G::KROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
+    }
+  }
+}
+template <int D, int KVB>
+RA_DEV void store_v(uint8_t* Vl, const uint2 (&r)[Geo<D, KVB>::VUT]) {
+  using G = Geo<D, KVB>;
+#pragma unroll
+  for (int i = 0; i < G::VUT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (G::VU % 256 == 0 || u < G::VU) {
+      const int d = u / (G::TG / 16), c = u % (G::TG / 16);
+      uint32_t lo0, hi0, lo1, hi1;
+      widen_biased(r[i].x, lo0, hi0);
+      widen_biased(r[i].y, lo1, hi1);
+      *(uint4*)(Vl + d * G::VROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
+    }
+  }
+}
+
+template <int D, int KVB>
+RA_DEV void qk_tiles(const uint8_t* Kl, const i32x4 (&qop)[Geo<D, KVB>::KC], const i32x16& cbias,
+                     i32x16 (&st)[Geo<D, KVB>::NT]) {
+  using G = Geo<D, KVB>;
+  const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int t = 0; t < G::NT; ++t) {
+#pragma unroll
+    for (int kc = 0; kc < G::KC; ++kc) {
+      const i32x4 kop = *(const i32x4*)(Kl + (t * 32 + col) * G::KROW + kc * 32 + 16 * h);
+      st[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop[kc], kc == 0 ? cbias : st[t], 0, 0, 0);
+    }
+  }
+}
+
+// Online-softmax step(s) of one key group: running max, lazy flush, P levels,
+// P^T operand, P V MFMAs.  TAIL: the group holds keys >= N.
+template <int D, int KVB, bool DBG, bool TAIL>
+RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
+                       const i32x16 (&st)[Geo<D, KVB>::NT], float sq, int bh, RowState<D / 32>& S,
+                       bool dbg_row, int dr) {
+  using G = Geo<D, KVB>;
+  const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
+  const int N = (int)a.N;
+  const int j0 = g * G::TG;
+  const int nsteps = (N + KVB - 1) / KVB;
+  float ct[G::NT];
+#pragma unroll
+  for (int t = 0; t < G::NT; ++t) {
+    const int key0 = j0 + t * 32 + 16 * h;
+    const float sk = a.ks[(int64_t)bh * (a.Np / a.qk_blk) + key0 / a.qk_blk];
+    const float ss = sq * sk;
+    ct[t] = ss * a.C0;
+  }
+  constexpr int NSTEP = KVB < 32 ? 2 : 1;
+#pragma unroll
+  for (int sidx = 0; sidx < NSTEP; ++sidx) {
+    const int step = (KVB < 32) ? g * 2 + sidx : g;
+    if (step >= nsteps) break;
+    const bool act = (KVB >= 32) || (h == sidx);
+    // ---- running maximum ---------------------------------------------------------
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < G::NT; ++t) {
+      int im = INT32_MIN;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        bool ok = act;
+        if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+        im = max(im, ok ? st[t][v] : INT32_MIN);
+      }
+      if (im != INT32_MIN) {
+        const float tm = (float)im * ct[t];
+        mloc = fmaxf(mloc, tm);
+      }
+    }
+    const float mnew = fmaxf(S.m, fmaxf(mloc, partner(mloc)));
+    const float alpha = exp2_hw(S.m - mnew);
+    if (DBG || __any(mnew > S.m)) {
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          S.Of[db][v] = (S.Of[db][v] + (float)S.acc[db][v]) * alpha;
+          S.acc[db][v] = 0;
+        }
+      }
+      S.Rf = (S.Rf + (float)S.Rint) * alpha;
+      S.Rint = 0;
+    }
+    S.l = S.l * alpha;
+    S.m = mnew;
+    const float nm = a.L15 - mnew;
+    const bool guard = mnew >= 262144.0f;
+    // ---- P levels ------------------------------------------------------------------
+    uint32_t tt[G::NT][16];
+    u16x2 wmin = {0xFFFF, 0xFFFF};
+#pragma unroll
+    for (int t = 0; t < G::NT; ++t) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        bool ok = act;
+        if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+        const float y = __builtin_fmaf((float)st[t][v], ct[t], nm);
+        float p = exp2_hw(y);
+        if (TAIL || KVB < 32) p = ok ? p : 0.f;
+        S.l += p;
+        tt[t][v] = __float_as_uint(p + kMagic);
+        wmin = __builtin_elementwise_min(wmin, __builtin_bit_cast(u16x2, tt[t][v]));
+      }
+    }
+    if (__any((wmin.x <= 6) || guard)) {
+      // A margin is too small somewhere in the wave (rare).  The hardware-exp level
+      // r^ is within one of the exact level, which is fixed by the two thresholds
+      // around r^ (an LDS table with +inf above the last one).
+#pragma unroll
+      for (int t = 0; t < G::NT; ++t) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float y = __builtin_fmaf((float)st[t][v], ct[t], nm);
+          const int rh = min((int)((tt[t][v] >> 16) & 0xFFu), 16);
+          const float lo = Tl[max(rh - 1, 0)], hi = Tl[rh];
+          int r = rh - ((rh > 0 && y < lo) ? 1 : 0) + ((y >= hi) ? 1 : 0);
+          if (TAIL || KVB < 32) {
+            bool ok = act;
+            if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+            r = ok ? r : 0;
+          }
+          tt[t][v] = (tt[t][v] & 0xFF00FFFFu) | ((uint32_t)r << 16);
+        }
+      }
+    }
+    // ---- P^T operand, level sums, P V ---------------------------------------------
+#pragma unroll
+    for (int t = 0; t < G::NT; ++t) {
+      const uint32_t* T = tt[t];
+      i32x4 pb;
+      pb[0] = (int)pack_b2(T[0], T[2], T[4], T[6]);
+      pb[1] = (int)pack_b2(T[1], T[3], T[5], T[7]);
+      pb[2] = (int)pack_b2(T[8], T[10], T[12], T[14]);
+      pb[3] = (int)pack_b2(T[9], T[11], T[13], T[15]);
+      S.Rint = __builtin_amdgcn_sdot4(pb[0], 0x01010101, S.Rint, false);
+      S.Rint = __builtin_amdgcn_sdot4(pb[1], 0x01010101, S.Rint, false);
+      S.Rint = __builtin_amdgcn_sdot4(pb[2], 0x01010101, S.Rint, false);
+      S.Rint = __builtin_amdgcn_sdot4(pb[3], 0x01010101, S.Rint, false);
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+        const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + t * 32 + 16 * h);
+        S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, S.acc[db], 0, 0, 0);
+      }
+      if (DBG && dbg_row && act) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = j0 + t * 32 + 16 * h + v;
+          if (key < N) {
+            a.dbg_aqk[(int64_t)dr * N + key] = st[t][v];
+            a.dbg_p[(int64_t)dr * N + key] = (int8_t)((int)((T[v] >> 16) & 0xFFu) - 8);
+          }
+        }
+      }
+    }
+    if (DBG) {
+      // per-step accumulator: sum_j (P~ + 8) vc = acc - 8 * (sum of levels of the row)
+      const float rsum = (float)S.Rint + partner((float)S.Rint);
+      if (dbg_row) {
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int d = db * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
+            a.dbg_apv[((int64_t)dr * nsteps + step) * D + d] = S.acc[db][v] - 8 * (int)rsum;
+          }
+        }
+      }
+    }
+  }
+}
+
+// One pipeline stage: Q K^T of group g+1 (into st_next), softmax + P V of group g
+// (from st_cur), widening of the prefetched K(g+2) / V(g+1) into the free LDS
+// buffers, global loads of K(g+3) / V(g+2), one barrier.
+template <int D, int KVB, bool DBG, bool TAIL>
+RA_DEV void group_iter(const Ctx& a, int g, int ngroups, uint8_t* lds,
+                       i32x16 (&st_cur)[Geo<D, KVB>::NT], i32x16 (&st_next)[Geo<D, KVB>::NT],
+                       uint2 (&rk)[Geo<D, KVB>::KUT], uint2 (&rv)[Geo<D, KVB>::VUT],
+                       const i32x4 (&qop)[Geo<D, KVB>::KC], const i32x16& cbias, float sq, int bh,
+                       RowState<D / 32>& S, bool dbg_row, int dr) {
+  using G = Geo<D, KVB>;
+  uint8_t* const kb_even = lds;
+  uint8_t* const kb_odd = lds + G::KBUF;
+  uint8_t* const vb_even = lds + 2 * G::KBUF;
+  uint8_t* const vb_odd = lds + 2 * G::KBUF + G::VBUF;
+  const bool odd = g & 1;
+  if (g + 1 < ngroups) qk_tiles<D, KVB>(odd ? kb_even : kb_odd, qop, cbias, st_next);
+  softmax_pv<D, KVB, DBG, TAIL>(a, g, odd ? vb_odd : vb_even, (const float*)(lds + G::LDS), st_cur, sq, bh, S,
+                                dbg_row, dr);
+  if (g + 1 < ngroups) store_v<D, KVB>(odd ? vb_even : vb_odd, rv);
+  if (g + 2 < ngroups) store_k<D, KVB>(odd ? kb_odd : kb_even, rk);
+  if (g + 3 < ngroups) load_k<D, KVB>(a, bh, g + 3, rk);
+  if (g + 2 < ngroups) load_v<D, KVB>(a, bh, g + 2, rv);
+  __syncthreads();
 }
 
 template <int D, int KVB, bool DBG>
-__global__ __launch_bounds__(256) void k2_attention(const AttnArgs a) {
-  constexpr int TG = KVB < 32 ? 32 : KVB;  // keys staged per group
-  constexpr int NT = TG / 32;              // 32-key tiles per group
-  constexpr int NDB = D / 32;              // 32-row d blocks of O^T
-  constexpr int KC = D / 32;               // 32-deep k chunks of Q K^T
-  constexpr int KROW = D + 16;             // LDS K row stride (bytes)
-  constexpr int VROW = TG + 16;            // LDS V^T row stride (bytes)
-  __shared__ __align__(16) uint8_t Kl[TG * KROW];
-  __shared__ __align__(16) uint8_t Vl[D * VROW];
+__global__ __launch_bounds__(256) void k2_attention(const AttnArgs args) {
+  using G = Geo<D, KVB>;
+  extern __shared__ __align__(16) uint8_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
   int L;
   if (DBG) {
-    L = a.dbg_row0 / kBM + blockIdx.x;
+    L = args.dbg_row0 / kBM + blockIdx.x;
   } else {
-    L = (int)(blockIdx.x % 8) * a.per_xcd + (int)(blockIdx.x / 8);
-    if (L >= a.total) return;
+    L = (int)(blockIdx.x % 8) * args.per_xcd + (int)(blockIdx.x / 8);
+    if (L >= args.total) return;
   }
-  const int hidx = L / a.nqt, qt = L % a.nqt;
-  const int bh = a.heads[hidx];
-  const int64_t N = a.N, Np = a.Np;
+  const int hidx = L / args.nqt, qt = L % args.nqt;
+  const int bh = args.heads[hidx];
+  Ctx a;
+  a.kc = args.kc; a.vc = args.vc; a.ks = args.ks; a.Np = args.Np;
+  a.N = (int)args.N; a.qk_blk = args.qk_blk; a.C0 = args.C0; a.L15 = args.L15;
+  a.dbg_row0 = args.dbg_row0; a.dbg_n = args.dbg_n;
+  a.dbg_aqk = args.dbg_aqk; a.dbg_p = args.dbg_p; a.dbg_apv = args.dbg_apv;
+  const int N = a.N;
   const int qi = qt * kBM + w * 32 + col;
 
   // ---- Q operand (signed int8), row sum, bias for the offset-binary K ---------
-  i32x4 qop[KC];
+  i32x4 qop[G::KC];
   int qsum = 0;
   {
-    const uint2* qp = (const uint2*)(a.qc + ((int64_t)bh * Np + qi) * (D / 2));
+    const uint2* qp = (const uint2*)(args.qc + ((int64_t)bh * a.Np + qi) * (D / 2));
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
+    for (int kc = 0; kc < G::KC; ++kc) {
       const uint2 x = qp[kc * 2 + h];
       uint32_t lo0, hi0, lo1, hi1;
       widen_signed(x.x, lo0, hi0);
@@ -90,206 +371,66 @@ __global__ __launch_bounds__(256) void k2_attention(const AttnArgs a) {
   i32x16 cbias;
 #pragma unroll
   for (int v = 0; v < 16; ++v) cbias[v] = -8 * qsum;
-  const float sq = a.qs[(int64_t)bh * (Np / a.qk_blk) + qi / a.qk_blk];
-  const float C0 = a.C0, L15 = a.L15;
+  const float sq = args.qs[(int64_t)bh * (a.Np / a.qk_blk) + qi / a.qk_blk];
 
-  float m = -INFINITY, l = 0.f, Rf = 0.f;
-  int Rint = 0;
-  f32x16 Of[NDB];
-  i32x16 acc[NDB];
+  RowState<G::NDB> S;
+  S.m = -INFINITY;
+  S.l = 0.f;
+  S.Rf = 0.f;
+  S.Rint = 0;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { Of[db][v] = 0.f; acc[db][v] = 0; }
+    for (int v = 0; v < 16; ++v) { S.Of[db][v] = 0.f; S.acc[db][v] = 0; }
   }
   const bool dbg_row = DBG && qi >= a.dbg_row0 && qi < a.dbg_row0 + a.dbg_n && qi < N;
   const int dr = qi - a.dbg_row0;
-  const int64_t nsteps = (N + KVB - 1) / KVB;
+  const int ngroups = (N + G::TG - 1) / G::TG;
 
-  const int64_t ngroups = (N + TG - 1) / TG;
-  for (int64_t g = 0; g < ngroups; ++g) {
-    const int64_t j0 = g * TG;
-    __syncthreads();
-    // ---- stage K (rows permuted so that S^T lane h holds keys 16h..16h+15) ---
-    for (int it = tid; it < TG * (D / 16); it += 256) {
-      const int kk = it / (D / 16), c = it % (D / 16);
-      const uint2 x = ((const uint2*)(a.kc + ((int64_t)bh * Np + j0 + kk) * (D / 2)))[c];
-      uint32_t lo0, hi0, lo1, hi1;
-      widen_biased(x.x, lo0, hi0);
-      widen_biased(x.y, lo1, hi1);
-      const int r = kk & 31, hh = r >> 4, v = r & 15;
-      const int row = (kk & ~31) + (v & 3) + 8 * (v >> 2) + 4 * hh;
-      *(uint4*)(Kl + row * KROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
-    }
-    // ---- stage V^T ---------------------------------------------------------------
-    for (int it = tid; it < D * (TG / 16); it += 256) {
-      const int d = it / (TG / 16), c = it % (TG / 16);
-      const uint2 x = ((const uint2*)(a.vc + ((int64_t)bh * D + d) * (Np / 2) + j0 / 2))[c];
-      uint32_t lo0, hi0, lo1, hi1;
-      widen_biased(x.x, lo0, hi0);
-      widen_biased(x.y, lo1, hi1);
-      *(uint4*)(Vl + d * VROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
-    }
-    __syncthreads();
+  if (tid < 17) ((float*)(lds + G::LDS))[tid] = tid < 15 ? args.T[tid] : INFINITY;
 
-    // ---- S^T tiles ---------------------------------------------------------------
-    i32x16 st[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const i32x4 kop = *(const i32x4*)(Kl + (t * 32 + col) * KROW + kc * 32 + 16 * h);
-        st[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop[kc], kc == 0 ? cbias : st[t], 0, 0, 0);
-      }
-    }
-    float ct[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int64_t key0 = j0 + t * 32 + 16 * h;
-      const float sk = a.ks[(int64_t)bh * (Np / a.qk_blk) + key0 / a.qk_blk];
-      const float ss = sq * sk;
-      ct[t] = ss * C0;
-    }
-
-    constexpr int NSTEP = KVB < 32 ? 2 : 1;  // online-softmax steps in this group
-#pragma unroll
-    for (int sidx = 0; sidx < NSTEP; ++sidx) {
-      const int64_t step = (KVB < 32) ? g * 2 + sidx : g;
-      if (step >= nsteps) break;
-      const bool act = (KVB >= 32) || (h == sidx);
-      const bool tail = (j0 + TG > N);
-      // ---- row maximum over the step ---------------------------------------------
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        int im = INT32_MIN;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t key = j0 + t * 32 + 16 * h + v;
-          const bool ok = act && (!tail || key < N);
-          im = max(im, ok ? st[t][v] : INT32_MIN);
-        }
-        if (im != INT32_MIN) {
-          const float tm = (float)im * ct[t];
-          mloc = fmaxf(mloc, tm);
-        }
-      }
-      const float mstep = fmaxf(mloc, partner(mloc));
-      const float mnew = fmaxf(m, mstep);
-      const float alpha = exp2_hw(m - mnew);
-      const bool changed = mnew > m;
-      if (DBG || __any(changed)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            Of[db][v] = (Of[db][v] + (float)acc[db][v]) * alpha;
-            acc[db][v] = 0;
-          }
-        }
-        Rf = (Rf + (float)Rint) * alpha;
-        Rint = 0;
-      }
-      l = l * alpha;
-      m = mnew;
-      const float nm = L15 - mnew;
-      const bool guard = mnew >= 262144.0f;
-
-      // ---- P levels --------------------------------------------------------------
-      uint32_t tt[NT][16];
-      u16x2 wmin = {0xFFFF, 0xFFFF};
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t key = j0 + t * 32 + 16 * h + v;
-          const bool ok = act && (!tail || key < N);
-          const float af = (float)st[t][v];
-          const float y = __builtin_fmaf(af, ct[t], nm);
-          const float p = ok ? exp2_hw(y) : 0.f;
-          l += p;
-          const float tv = p + kMagic;
-          tt[t][v] = __float_as_uint(tv);
-          wmin = __builtin_elementwise_min(wmin, __builtin_bit_cast(u16x2, tt[t][v]));
-        }
-      }
-      if (__any((wmin.x <= 6) || guard)) {
-        // exact decision for the elements whose margin is too small
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int64_t key = j0 + t * 32 + 16 * h + v;
-            const bool ok = act && (!tail || key < N);
-            const bool flag = ok && (((tt[t][v] & 0xFFFFu) <= 6u) || guard);
-            if (__any(flag)) {
-              if (flag) {
-                const float y = __builtin_fmaf((float)st[t][v], ct[t], nm);
-                int r = 0;
-#pragma unroll
-                for (int k = 0; k < 15; ++k) r += (y >= a.T[k]) ? 1 : 0;
-                tt[t][v] = (tt[t][v] & 0xFF00FFFFu) | ((uint32_t)r << 16);
-              }
-            }
-          }
-        }
-      }
-      // ---- pack P^T operand, level sums, P V --------------------------------------
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint32_t* T = tt[t];
-        i32x4 pb;
-        pb[0] = (int)pack_b2(T[0], T[2], T[4], T[6]);
-        pb[1] = (int)pack_b2(T[1], T[3], T[5], T[7]);
-        pb[2] = (int)pack_b2(T[8], T[10], T[12], T[14]);
-        pb[3] = (int)pack_b2(T[9], T[11], T[13], T[15]);
-        Rint = __builtin_amdgcn_sdot4(pb[0], 0x01010101, Rint, false);
-        Rint = __builtin_amdgcn_sdot4(pb[1], 0x01010101, Rint, false);
-        Rint = __builtin_amdgcn_sdot4(pb[2], 0x01010101, Rint, false);
-        Rint = __builtin_amdgcn_sdot4(pb[3], 0x01010101, Rint, false);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * VROW + t * 32 + 16 * h);
-          acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, acc[db], 0, 0, 0);
-        }
-        if (DBG && dbg_row && act) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int64_t key = j0 + t * 32 + 16 * h + v;
-            if (key < N) {
-              a.dbg_aqk[(int64_t)dr * N + key] = st[t][v];
-              a.dbg_p[(int64_t)dr * N + key] = (int8_t)((int)((T[v] >> 16) & 0xFFu) - 8);
-            }
-          }
-        }
-      }
-      if (DBG) {
-        // per-step accumulator: sum_j (P~ + 8) vc = acc - 8 * (sum of levels of the row)
-        const float rsum = (float)Rint + partner((float)Rint);
-        if (dbg_row) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int d = db * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
-              a.dbg_apv[((int64_t)dr * nsteps + step) * D + d] = acc[db][v] - 8 * (int)rsum;
-            }
-          }
-        }
-      }
-    }
+  // ---- prologue: K(0), V(0), K(1) in LDS; loads of K(2), V(1) in flight; S(0) ----
+  uint2 rk[G::KUT], rv[G::VUT];
+  load_k<D, KVB>(a, bh, 0, rk);
+  load_v<D, KVB>(a, bh, 0, rv);
+  store_k<D, KVB>(lds, rk);
+  store_v<D, KVB>(lds + 2 * G::KBUF, rv);
+  if (ngroups > 1) {
+    load_k<D, KVB>(a, bh, 1, rk);
+    store_k<D, KVB>(lds + G::KBUF, rk);
   }
+  if (ngroups > 2) load_k<D, KVB>(a, bh, 2, rk);
+  if (ngroups > 1) load_v<D, KVB>(a, bh, 1, rv);
+  __syncthreads();
+  i32x16 stA[G::NT], stB[G::NT];
+  qk_tiles<D, KVB>(lds, qop, cbias, stA);
+  __syncthreads();  // every wave has read K(0) before K(2) overwrites its buffer
+
+  // two groups per trip so that the S^T double buffer needs no register copies
+  int g = 0;
+  for (; g + 2 < ngroups; g += 2) {
+    group_iter<D, KVB, DBG, false>(a, g, ngroups, lds, stA, stB, rk, rv, qop, cbias, sq, bh, S, dbg_row, dr);
+    group_iter<D, KVB, DBG, false>(a, g + 1, ngroups, lds, stB, stA, rk, rv, qop, cbias, sq, bh, S, dbg_row, dr);
+  }
+  if (g + 1 < ngroups) {
+    group_iter<D, KVB, DBG, false>(a, g, ngroups, lds, stA, stB, rk, rv, qop, cbias, sq, bh, S, dbg_row, dr);
+    ++g;
+#pragma unroll
+    for (int t = 0; t < G::NT; ++t) stA[t] = stB[t];
+  }
+  group_iter<D, KVB, DBG, true>(a, g, ngroups, lds, stA, stB, rk, rv, qop, cbias, sq, bh, S, dbg_row, dr);
+
   // ---- epilogue ---------------------------------------------------------------------
-  const float lq = l + partner(l);
-  const float Rq = (Rf + (float)Rint) + partner(Rf + (float)Rint);
+  const float lq = S.l + partner(S.l);
+  const float Rq = (S.Rf + (float)S.Rint) + partner(S.Rf + (float)S.Rint);
   if (DBG && dbg_row && h == 0) {
-    a.dbg_m[dr] = m;
-    a.dbg_l[dr] = lq;
+    args.dbg_m[dr] = S.m;
+    args.dbg_l[dr] = lq;
   }
   if (qi < N) {
     const float inv = 1.0f / lq;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const int d0 = db * 32 + 8 * v4 + 4 * h;
@@ -297,15 +438,15 @@ __global__ __launch_bounds__(256) void k2_attention(const AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = v4 * 4 + e;
-          const float num = (Of[db][v] + (float)acc[db][v]) - 8.0f * Rq;
-          o[e] = num * a.vs[(int64_t)bh * D + d0 + e] * inv;
+          const float num = (S.Of[db][v] + (float)S.acc[db][v]) - 8.0f * Rq;
+          o[e] = num * args.vs[(int64_t)bh * D + d0 + e] * inv;
         }
         const int64_t off = ((int64_t)bh * N + qi) * D + d0;
-        if (a.out_f16) {
+        if (args.out_f16) {
           f16x4 hv = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
-          *(f16x4*)((_Float16*)a.out + off) = hv;
+          *(f16x4*)((_Float16*)args.out + off) = hv;
         } else {
-          *(f32x4*)((float*)a.out + off) = f32x4{o[0], o[1], o[2], o[3]};
+          *(f32x4*)((float*)args.out + off) = f32x4{o[0], o[1], o[2], o[3]};
         }
       }
     }
@@ -314,11 +455,21 @@ __global__ __launch_bounds__(256) void k2_attention(const AttnArgs a) {
 
 template <int D, int KVB>
 hipError_t launch_t(const AttnArgs& a, bool dbg, hipStream_t st) {
+  using G = Geo<D, KVB>;
+  static const hipError_t attr = [] {
+    hipError_t e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS + 128);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS + 128);
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
   if (dbg) {
     const int first = a.dbg_row0 / kBM, last = (a.dbg_row0 + a.dbg_n - 1) / kBM;
-    k2_attention<D, KVB, true><<<last - first + 1, 256, 0, st>>>(a);
+    k2_attention<D, KVB, true><<<last - first + 1, 256, G::LDS + 128, st>>>(a);
   } else {
-    k2_attention<D, KVB, false><<<8 * a.per_xcd, 256, 0, st>>>(a);
+    k2_attention<D, KVB, false><<<8 * a.per_xcd, 256, G::LDS + 128, st>>>(a);
   }
   return hipGetLastError();
 }
