@@ -29,6 +29,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-fallback", action="store_true", help="skip timing the FP16 fallback")
     ap.add_argument("--config", default=CONFIG)
+    ap.add_argument("--kv", type=int, default=0, help="override kv_blk (keys per online-softmax step)")
+    ap.add_argument("--qk", type=int, default=0, help="override qk_blk (tokens per Q/K scale)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on exactly one GPU (the path shards by head with no "
@@ -42,7 +46,19 @@ def main():
     from int4_quantized_attention_amd import synth
 
     torch.cuda.set_device(0)
-    cfg = synth.CONFIGS[args.config]
+    if args.calib_copy:
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": x.numel() * 4, "launches": 3}))
+        return
+    cfg = dict(synth.CONFIGS[args.config])
+    if args.kv:
+        cfg["kv_blk"] = args.kv
+    if args.qk:
+        cfg["qk_blk"] = args.qk
     B, H, D = cfg["B"], cfg["H"], cfg["D"]
     N = synth.n_tokens(cfg)
     rot = ra.ROT_BY_NAME[cfg["rot"]]

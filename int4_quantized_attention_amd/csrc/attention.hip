@@ -10,10 +10,10 @@
 //    v_mfma_i32_32x32x32_i8, so a lane owns one query row and 16 keys of every
 //    32-key tile; its P codes are already laid out as the B operand of the next
 //    MFMA, O^T = V^T P^T, with no LDS round trip.
-//  * K and V stay INT4 in HBM; the workgroup widens each tile once into LDS as
-//    offset-binary bytes (code + 8) with three bit operations per 8 nibbles.  The
-//    +8 on K is removed exactly by starting the Q K^T accumulation at -8 sum_d q_d;
-//    the +8 on V is removed at the end with the per-row sum of the P levels.
+//  * K and V stay INT4 in HBM; the workgroup widens each tile once into LDS with a
+//    few bit operations per 8 nibbles: K sign-extended to int8, V as offset-binary
+//    bytes (code + 8), whose +8 is removed at the end with the per-row sum of the
+//    P levels.
 //  * The P level r = round-half-even(2^y) is taken from the hardware exp2: with
 //    t = 2^y + 128.5 + 4*2^-16 the level is byte 2 of t's bits and the low 16 bits
 //    carry the rounding margin.  v_exp_f32 is within 1.5 * 2^-24 relative of 2^y,
@@ -21,9 +21,9 @@
 //    (rare) other elements are decided exactly against the 15 thresholds.
 //  * The int32 P V accumulator runs across online-softmax steps and is folded
 //    into the fp32 output only when a row maximum moves.
-//  * Software pipeline, one barrier per key group: the Q K^T MFMAs of group g+1
-//    are issued before the softmax of group g (MFMA and VALU overlap); K and V
-//    tiles are double-buffered in LDS and their global loads run one group ahead.
+//  * Two waves per SIMD (<= 256 registers each), so that one wave's MFMAs run
+//    under the other's softmax; one barrier per key group; K and V tiles are
+//    double-buffered in LDS and their global loads run one group ahead.
 //  * Workgroup ids are remapped so that all query tiles of a head run on the same
 //    XCD and share its L2 for the K/V stream.
 #include "common.h"
@@ -108,7 +108,7 @@ RA_DEV void load_v(const Ctx& a, int bh, int g, uint2 (&r)[Geo<D, KVB>::VUT]) {
     }
   }
 }
-// K rows are permuted inside each 32-key tile so that the S^T accumulator of lane
+// K rows (sign-extended) are permuted inside each 32-key tile so that the S^T accumulator of lane
 // half h holds keys 16h..16h+15 of the tile in register order.
 template <int D, int KVB>
 RA_DEV void store_k(uint8_t* Kl, const uint2 (&r)[Geo<D, KVB>::KUT]) {
@@ -119,8 +119,8 @@ RA_DEV void store_k(uint8_t* Kl, const uint2 (&r)[Geo<D, KVB>::KUT]) {
     if (G::KU % 256 == 0 || u < G::KU) {
       const int kk = u / (D / 16), c = u % (D / 16);
       uint32_t lo0, hi0, lo1, hi1;
-      widen_biased(r[i].x, lo0, hi0);
-      widen_biased(r[i].y, lo1, hi1);
+      widen_signed(r[i].x, lo0, hi0);
+      widen_signed(r[i].y, lo1, hi1);
       const int rr = kk & 31, hh = rr >> 4, v = rr & 15;
       const int row = (kk & ~31) + (v & 3) + 8 * (v >> 2) + 4 * hh;
       *(uint4*)(Kl + row * G::KROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
@@ -144,8 +144,7 @@ RA_DEV void store_v(uint8_t* Vl, const uint2 (&r)[Geo<D, KVB>::VUT]) {
 }
 
 template <int D, int KVB>
-RA_DEV void qk_tiles(const uint8_t* Kl, const i32x4 (&qop)[Geo<D, KVB>::KC], const i32x16& cbias,
-                     i32x16 (&st)[Geo<D, KVB>::NT]) {
+RA_DEV void qk_tiles(const uint8_t* Kl, const i32x4 (&qop)[Geo<D, KVB>::KC], i32x16 (&st)[Geo<D, KVB>::NT]) {
   using G = Geo<D, KVB>;
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
 #pragma unroll
@@ -153,7 +152,8 @@ RA_DEV void qk_tiles(const uint8_t* Kl, const i32x4 (&qop)[Geo<D, KVB>::KC], con
 #pragma unroll
     for (int kc = 0; kc < G::KC; ++kc) {
       const i32x4 kop = *(const i32x4*)(Kl + (t * 32 + col) * G::KROW + kc * 32 + 16 * h);
-      st[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop[kc], kc == 0 ? cbias : st[t], 0, 0, 0);
+      const i32x16 zero = {0};
+      st[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop[kc], kc == 0 ? zero : st[t], 0, 0, 0);
     }
   }
 }
@@ -217,11 +217,11 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
     S.m = mnew;
     const float nm = a.L15 - mnew;
     const bool guard = mnew >= 262144.0f;
-    // ---- P levels ------------------------------------------------------------------
-    uint32_t tt[G::NT][16];
-    u16x2 wmin = {0xFFFF, 0xFFFF};
+    // ---- P levels, P^T operand, level sums, P V: one 32-key tile at a time --------
 #pragma unroll
     for (int t = 0; t < G::NT; ++t) {
+      uint32_t tt[16];
+      u16x2 wmin = {0xFFFF, 0xFFFF};
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         bool ok = act;
@@ -230,20 +230,17 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
         float p = exp2_hw(y);
         if (TAIL || KVB < 32) p = ok ? p : 0.f;
         S.l += p;
-        tt[t][v] = __float_as_uint(p + kMagic);
-        wmin = __builtin_elementwise_min(wmin, __builtin_bit_cast(u16x2, tt[t][v]));
+        tt[v] = __float_as_uint(p + kMagic);
+        wmin = __builtin_elementwise_min(wmin, __builtin_bit_cast(u16x2, tt[v]));
       }
-    }
-    if (__any((wmin.x <= 6) || guard)) {
-      // A margin is too small somewhere in the wave (rare).  The hardware-exp level
-      // r^ is within one of the exact level, which is fixed by the two thresholds
-      // around r^ (an LDS table with +inf above the last one).
-#pragma unroll
-      for (int t = 0; t < G::NT; ++t) {
+      if (__any((wmin.x <= 6) || guard)) {
+        // A margin is too small somewhere in the wave (rare).  The hardware-exp
+        // level r^ is within one of the exact level, which is fixed by the two
+        // thresholds around r^ (an LDS table with +inf above the last one).
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float y = __builtin_fmaf((float)st[t][v], ct[t], nm);
-          const int rh = min((int)((tt[t][v] >> 16) & 0xFFu), 16);
+          const int rh = min((int)((tt[v] >> 16) & 0xFFu), 16);
           const float lo = Tl[max(rh - 1, 0)], hi = Tl[rh];
           int r = rh - ((rh > 0 && y < lo) ? 1 : 0) + ((y >= hi) ? 1 : 0);
           if (TAIL || KVB < 32) {
@@ -251,19 +248,14 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
             if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
             r = ok ? r : 0;
           }
-          tt[t][v] = (tt[t][v] & 0xFF00FFFFu) | ((uint32_t)r << 16);
+          tt[v] = (tt[v] & 0xFF00FFFFu) | ((uint32_t)r << 16);
         }
       }
-    }
-    // ---- P^T operand, level sums, P V ---------------------------------------------
-#pragma unroll
-    for (int t = 0; t < G::NT; ++t) {
-      const uint32_t* T = tt[t];
       i32x4 pb;
-      pb[0] = (int)pack_b2(T[0], T[2], T[4], T[6]);
-      pb[1] = (int)pack_b2(T[1], T[3], T[5], T[7]);
-      pb[2] = (int)pack_b2(T[8], T[10], T[12], T[14]);
-      pb[3] = (int)pack_b2(T[9], T[11], T[13], T[15]);
+      pb[0] = (int)pack_b2(tt[0], tt[2], tt[4], tt[6]);
+      pb[1] = (int)pack_b2(tt[1], tt[3], tt[5], tt[7]);
+      pb[2] = (int)pack_b2(tt[8], tt[10], tt[12], tt[14]);
+      pb[3] = (int)pack_b2(tt[9], tt[11], tt[13], tt[15]);
       S.Rint = __builtin_amdgcn_sdot4(pb[0], 0x01010101, S.Rint, false);
       S.Rint = __builtin_amdgcn_sdot4(pb[1], 0x01010101, S.Rint, false);
       S.Rint = __builtin_amdgcn_sdot4(pb[2], 0x01010101, S.Rint, false);
@@ -279,7 +271,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
           const int key = j0 + t * 32 + 16 * h + v;
           if (key < N) {
             a.dbg_aqk[(int64_t)dr * N + key] = st[t][v];
-            a.dbg_p[(int64_t)dr * N + key] = (int8_t)((int)((T[v] >> 16) & 0xFFu) - 8);
+            a.dbg_p[(int64_t)dr * N + key] = (int8_t)((int)((tt[v] >> 16) & 0xFFu) - 8);
           }
         }
       }
@@ -301,33 +293,36 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
   }
 }
 
-// One pipeline stage: Q K^T of group g+1 (into st_next), softmax + P V of group g
-// (from st_cur), widening of the prefetched K(g+2) / V(g+1) into the free LDS
-// buffers, global loads of K(g+3) / V(g+2), one barrier.
+// One key group: Q K^T from LDS buffer g&1, widening of the prefetched K/V of
+// group g+1 into the other buffer, global loads of group g+2, softmax + P V,
+// one barrier.  MFMA/VALU overlap comes from the second wave on each SIMD.
 template <int D, int KVB, bool DBG, bool TAIL>
-RA_DEV void group_iter(const Ctx& a, int g, int ngroups, uint8_t* lds,
-                       i32x16 (&st_cur)[Geo<D, KVB>::NT], i32x16 (&st_next)[Geo<D, KVB>::NT],
-                       uint2 (&rk)[Geo<D, KVB>::KUT], uint2 (&rv)[Geo<D, KVB>::VUT],
-                       const i32x4 (&qop)[Geo<D, KVB>::KC], const i32x16& cbias, float sq, int bh,
-                       RowState<D / 32>& S, bool dbg_row, int dr) {
+RA_DEV void group_iter(const Ctx& a, int g, int ngroups, uint8_t* lds, uint2 (&rk)[Geo<D, KVB>::KUT],
+                       uint2 (&rv)[Geo<D, KVB>::VUT], const i32x4 (&qop)[Geo<D, KVB>::KC],
+                       float sq, int bh, RowState<D / 32>& S, bool dbg_row, int dr) {
   using G = Geo<D, KVB>;
-  uint8_t* const kb_even = lds;
-  uint8_t* const kb_odd = lds + G::KBUF;
-  uint8_t* const vb_even = lds + 2 * G::KBUF;
-  uint8_t* const vb_odd = lds + 2 * G::KBUF + G::VBUF;
   const bool odd = g & 1;
-  if (g + 1 < ngroups) qk_tiles<D, KVB>(odd ? kb_even : kb_odd, qop, cbias, st_next);
-  softmax_pv<D, KVB, DBG, TAIL>(a, g, odd ? vb_odd : vb_even, (const float*)(lds + G::LDS), st_cur, sq, bh, S,
-                                dbg_row, dr);
-  if (g + 1 < ngroups) store_v<D, KVB>(odd ? vb_even : vb_odd, rv);
-  if (g + 2 < ngroups) store_k<D, KVB>(odd ? kb_odd : kb_even, rk);
-  if (g + 3 < ngroups) load_k<D, KVB>(a, bh, g + 3, rk);
-  if (g + 2 < ngroups) load_v<D, KVB>(a, bh, g + 2, rv);
+  uint8_t* const kb_cur = lds + (odd ? G::KBUF : 0);
+  uint8_t* const kb_nxt = lds + (odd ? 0 : G::KBUF);
+  uint8_t* const vb_cur = lds + 2 * G::KBUF + (odd ? G::VBUF : 0);
+  uint8_t* const vb_nxt = lds + 2 * G::KBUF + (odd ? 0 : G::VBUF);
+  i32x16 st[G::NT];
+  qk_tiles<D, KVB>(kb_cur, qop, st);
+  if (g + 1 < ngroups) {
+    store_k<D, KVB>(kb_nxt, rk);
+    store_v<D, KVB>(vb_nxt, rv);
+  }
+  if (g + 2 < ngroups) {
+    load_k<D, KVB>(a, bh, g + 2, rk);
+    load_v<D, KVB>(a, bh, g + 2, rv);
+  }
+  softmax_pv<D, KVB, DBG, TAIL>(a, g, vb_cur, (const float*)(lds + G::LDS), st, sq, bh, S, dbg_row, dr);
   __syncthreads();
 }
 
 template <int D, int KVB, bool DBG>
-__global__ __launch_bounds__(256) void k2_attention(const AttnArgs args) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_attention(
+    const AttnArgs args) {
   using G = Geo<D, KVB>;
   extern __shared__ __align__(16) uint8_t lds[];
 
@@ -349,9 +344,8 @@ __global__ __launch_bounds__(256) void k2_attention(const AttnArgs args) {
   const int N = a.N;
   const int qi = qt * kBM + w * 32 + col;
 
-  // ---- Q operand (signed int8), row sum, bias for the offset-binary K ---------
+  // ---- Q operand (signed int8) ------------------------------------------------
   i32x4 qop[G::KC];
-  int qsum = 0;
   {
     const uint2* qp = (const uint2*)(args.qc + ((int64_t)bh * a.Np + qi) * (D / 2));
 #pragma unroll
@@ -361,16 +355,8 @@ __global__ __launch_bounds__(256) void k2_attention(const AttnArgs args) {
       widen_signed(x.x, lo0, hi0);
       widen_signed(x.y, lo1, hi1);
       qop[kc] = i32x4{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
-      qsum = __builtin_amdgcn_sdot4((int)lo0, 0x01010101, qsum, false);
-      qsum = __builtin_amdgcn_sdot4((int)hi0, 0x01010101, qsum, false);
-      qsum = __builtin_amdgcn_sdot4((int)lo1, 0x01010101, qsum, false);
-      qsum = __builtin_amdgcn_sdot4((int)hi1, 0x01010101, qsum, false);
     }
   }
-  qsum += __shfl_xor(qsum, 32, 64);
-  i32x16 cbias;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) cbias[v] = -8 * qsum;
   const float sq = args.qs[(int64_t)bh * (a.Np / a.qk_blk) + qi / a.qk_blk];
 
   RowState<G::NDB> S;
@@ -389,7 +375,7 @@ __global__ __launch_bounds__(256) void k2_attention(const AttnArgs args) {
 
   if (tid < 17) ((float*)(lds + G::LDS))[tid] = tid < 15 ? args.T[tid] : INFINITY;
 
-  // ---- prologue: K(0), V(0), K(1) in LDS; loads of K(2), V(1) in flight; S(0) ----
+  // ---- prologue: group 0 in LDS, group 1 in flight -------------------------------
   uint2 rk[G::KUT], rv[G::VUT];
   load_k<D, KVB>(a, bh, 0, rk);
   load_v<D, KVB>(a, bh, 0, rv);
@@ -397,28 +383,12 @@ __global__ __launch_bounds__(256) void k2_attention(const AttnArgs args) {
   store_v<D, KVB>(lds + 2 * G::KBUF, rv);
   if (ngroups > 1) {
     load_k<D, KVB>(a, bh, 1, rk);
-    store_k<D, KVB>(lds + G::KBUF, rk);
+    load_v<D, KVB>(a, bh, 1, rv);
   }
-  if (ngroups > 2) load_k<D, KVB>(a, bh, 2, rk);
-  if (ngroups > 1) load_v<D, KVB>(a, bh, 1, rv);
   __syncthreads();
-  i32x16 stA[G::NT], stB[G::NT];
-  qk_tiles<D, KVB>(lds, qop, cbias, stA);
-  __syncthreads();  // every wave has read K(0) before K(2) overwrites its buffer
-
-  // two groups per trip so that the S^T double buffer needs no register copies
-  int g = 0;
-  for (; g + 2 < ngroups; g += 2) {
-    group_iter<D, KVB, DBG, false>(a, g, ngroups, lds, stA, stB, rk, rv, qop, cbias, sq, bh, S, dbg_row, dr);
-    group_iter<D, KVB, DBG, false>(a, g + 1, ngroups, lds, stB, stA, rk, rv, qop, cbias, sq, bh, S, dbg_row, dr);
-  }
-  if (g + 1 < ngroups) {
-    group_iter<D, KVB, DBG, false>(a, g, ngroups, lds, stA, stB, rk, rv, qop, cbias, sq, bh, S, dbg_row, dr);
-    ++g;
-#pragma unroll
-    for (int t = 0; t < G::NT; ++t) stA[t] = stB[t];
-  }
-  group_iter<D, KVB, DBG, true>(a, g, ngroups, lds, stA, stB, rk, rv, qop, cbias, sq, bh, S, dbg_row, dr);
+  for (int g = 0; g + 1 < ngroups; ++g)
+    group_iter<D, KVB, DBG, false>(a, g, ngroups, lds, rk, rv, qop, sq, bh, S, dbg_row, dr);
+  group_iter<D, KVB, DBG, true>(a, ngroups - 1, ngroups, lds, rk, rv, qop, sq, bh, S, dbg_row, dr);
 
   // ---- epilogue ---------------------------------------------------------------------
   const float lq = S.l + partner(S.l);
