@@ -10,17 +10,16 @@
 //    v_mfma_i32_32x32x32_i8, so a lane owns one query row and 16 keys of every
 //    32-key tile; its P codes are already laid out as the B operand of the next
 //    MFMA, O^T = V^T P^T, with no LDS round trip.
-//  * K and V stay INT4 in HBM; the workgroup widens each tile once into LDS with a
-//    few bit operations per 8 nibbles: K sign-extended to int8, V as offset-binary
-//    bytes (code + 8), whose +8 is removed at the end with the per-row sum of the
-//    P levels.
+//  * K and V stay INT4 in HBM; the workgroup sign-extends each tile once into LDS
+//    as int8 with four bit operations per 8 nibbles.
 //  * The P level r = round-half-even(2^y) is taken from the hardware exp2: with
 //    t = 2^y + 128.5 + 4*2^-16 the level is byte 2 of t's bits and the low 16 bits
 //    carry the rounding margin.  v_exp_f32 is within 1.5 * 2^-24 relative of 2^y,
 //    so whenever the margin is above 6/2^16 the level equals the exact one; the
 //    (rare) other elements are decided exactly against the 15 thresholds.
 //  * The int32 P V accumulator runs across online-softmax steps and is folded
-//    into the fp32 output only when a row maximum moves.
+//    into the fp32 output (one fma per element, in a fixed exponent frame) only
+//    when a row maximum moves; the next MFMA then restarts it from zero.
 //  * Two waves per SIMD (<= 256 registers each), so that one wave's MFMAs run
 //    under the other's softmax; one barrier per key group; K and V tiles are
 //    double-buffered in LDS and their global loads run one group ahead.
@@ -78,12 +77,16 @@ struct Geo {
 };
 
 // Per-lane running state of one query row (the lane pair l, l^32 shares a row).
+// Of holds the flushed part of the output numerator in a fixed frame: the sum over
+// flushed steps of 2^(m_s - mref) * acc_s, where acc_s is the integer P V sum of a
+// step with running maximum m_s.  sigma = 2^(m - mref) for the current maximum, so
+// a flush is one fma per element; acc restarts from zero in the next MFMA (fresh).
 template <int NDB>
 struct RowState {
   f32x16 Of[NDB];
   i32x16 acc[NDB];
-  float m, l, Rf;
-  int Rint;
+  float m, l, mref, sigma;
+  bool fresh;
 };
 
 template <int D, int KVB>
@@ -136,8 +139,8 @@ RA_DEV void store_v(uint8_t* Vl, const uint2 (&r)[Geo<D, KVB>::VUT]) {
     if (G::VU % 256 == 0 || u < G::VU) {
       const int d = u / (G::TG / 16), c = u % (G::TG / 16);
       uint32_t lo0, hi0, lo1, hi1;
-      widen_biased(r[i].x, lo0, hi0);
-      widen_biased(r[i].y, lo1, hi1);
+      widen_signed(r[i].x, lo0, hi0);
+      widen_signed(r[i].y, lo1, hi1);
       *(uint4*)(Vl + d * G::VROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
     }
   }
@@ -202,16 +205,26 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
     const float mnew = fmaxf(S.m, fmaxf(mloc, partner(mloc)));
     const float alpha = exp2_hw(S.m - mnew);
     if (DBG || __any(mnew > S.m)) {
+      if (!S.fresh) {
 #pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
+        for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          S.Of[db][v] = (S.Of[db][v] + (float)S.acc[db][v]) * alpha;
-          S.acc[db][v] = 0;
+          for (int v = 0; v < 16; ++v) S.Of[db][v] = __builtin_fmaf((float)S.acc[db][v], S.sigma, S.Of[db][v]);
         }
       }
-      S.Rf = (S.Rf + (float)S.Rint) * alpha;
-      S.Rint = 0;
+      S.fresh = true;
+      if (g == 0 && sidx == 0) S.mref = mnew;
+      if (__any(mnew - S.mref > 64.0f)) {
+        // keep sigma far from overflow: move the frame to the current maximum
+        const float back = exp2_hw(S.mref - mnew);
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) S.Of[db][v] *= back;
+        }
+        S.mref = mnew;
+      }
+      S.sigma = exp2_hw(mnew - S.mref);
     }
     S.l = S.l * alpha;
     S.m = mnew;
@@ -256,14 +269,20 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
       pb[1] = (int)pack_b2(tt[1], tt[3], tt[5], tt[7]);
       pb[2] = (int)pack_b2(tt[8], tt[10], tt[12], tt[14]);
       pb[3] = (int)pack_b2(tt[9], tt[11], tt[13], tt[15]);
-      S.Rint = __builtin_amdgcn_sdot4(pb[0], 0x01010101, S.Rint, false);
-      S.Rint = __builtin_amdgcn_sdot4(pb[1], 0x01010101, S.Rint, false);
-      S.Rint = __builtin_amdgcn_sdot4(pb[2], 0x01010101, S.Rint, false);
-      S.Rint = __builtin_amdgcn_sdot4(pb[3], 0x01010101, S.Rint, false);
+      if (t == 0 && S.fresh) {
+        const i32x16 zero = {0};
 #pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
-        const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + t * 32 + 16 * h);
-        S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, S.acc[db], 0, 0, 0);
+        for (int db = 0; db < G::NDB; ++db) {
+          const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + t * 32 + 16 * h);
+          S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, zero, 0, 0, 0);
+        }
+        S.fresh = false;
+      } else {
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+          const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + t * 32 + 16 * h);
+          S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, S.acc[db], 0, 0, 0);
+        }
       }
       if (DBG && dbg_row && act) {
 #pragma unroll
@@ -276,17 +295,14 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
         }
       }
     }
-    if (DBG) {
-      // per-step accumulator: sum_j (P~ + 8) vc = acc - 8 * (sum of levels of the row)
-      const float rsum = (float)S.Rint + partner((float)S.Rint);
-      if (dbg_row) {
+    if (DBG && dbg_row) {
+      // per-step accumulator sum_j (P~ + 8) vc (the debug run flushes every step)
 #pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
+      for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int d = db * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
-            a.dbg_apv[((int64_t)dr * nsteps + step) * D + d] = S.acc[db][v] - 8 * (int)rsum;
-          }
+        for (int v = 0; v < 16; ++v) {
+          const int d = db * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
+          a.dbg_apv[((int64_t)dr * nsteps + step) * D + d] = S.acc[db][v];
         }
       }
     }
@@ -362,8 +378,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   RowState<G::NDB> S;
   S.m = -INFINITY;
   S.l = 0.f;
-  S.Rf = 0.f;
-  S.Rint = 0;
+  S.mref = 0.f;
+  S.sigma = 1.f;
+  S.fresh = true;
 #pragma unroll
   for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
@@ -392,7 +409,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- epilogue ---------------------------------------------------------------------
   const float lq = S.l + partner(S.l);
-  const float Rq = (S.Rf + (float)S.Rint) + partner(S.Rf + (float)S.Rint);
+  const float inv_sigma = 1.0f / S.sigma;
   if (DBG && dbg_row && h == 0) {
     args.dbg_m[dr] = S.m;
     args.dbg_l[dr] = lq;
@@ -408,7 +425,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = v4 * 4 + e;
-          const float num = (S.Of[db][v] + (float)S.acc[db][v]) - 8.0f * Rq;
+          const float num = __builtin_fmaf(S.Of[db][v], inv_sigma, (float)S.acc[db][v]);
           o[e] = num * args.vs[(int64_t)bh * D + d0 + e] * inv;
         }
         const int64_t off = ((int64_t)bh * N + qi) * D + d0;
