@@ -255,13 +255,13 @@ rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dt
   a.nqt = (int)((a.N + 127) / 128);
   a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)s->D));
   hipStream_t hs = (hipStream_t)stream;
-  if (ra::launch_fallback_prep(a, hs) != hipSuccess) return ROTATTN_E_HIP;
   const int nh = heads ? n_heads : BH;
   for (int h0 = 0; h0 < nh; h0 += ra::kMaxHeads) {
     const int cnt = nh - h0 < ra::kMaxHeads ? nh - h0 : ra::kMaxHeads;
     a.nheads = cnt;
     for (int i = 0; i < cnt; ++i) a.heads[i] = heads ? heads[h0 + i] : h0 + i;
     grid_map(a.nqt, cnt, a.total, a.per_xcd);
+    if (ra::launch_fallback_prep(a, hs) != hipSuccess) return ROTATTN_E_HIP;
     if (ra::launch_fallback(a, hs) != hipSuccess) return ROTATTN_E_HIP;
   }
   return ROTATTN_OK;

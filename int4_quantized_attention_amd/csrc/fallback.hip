@@ -7,9 +7,10 @@
 //
 // Pre-pass (k3_prep): plain 3D RoPE of Q and K in binary32 (same op order as the
 // quantisation kernel) rounded to binary16, and V transposed to [D][Np] binary16.
-// Main kernel (k3_attention): one workgroup = 4 waves x 32 query rows; S^T = K Q^T
-// on v_mfma_f32_32x32x16_f16, online softmax in binary32 with the hardware exp2, P
-// rounded to binary16 and fed straight back as the B operand of O^T = V^T P^T.
+// Main kernel (k3_attention): one workgroup = 4 waves x 32 query rows, two waves per
+// SIMD; S^T = K Q^T on v_mfma_f32_32x32x16_f16, online softmax in binary32 with the
+// hardware exp2, P rounded to binary16 and fed straight back as the B operand of
+// O^T = V^T P^T; K/V tiles double-buffered in LDS with loads one group ahead.
 #include "common.h"
 #include "kernels.h"
 #include "rope.h"
@@ -17,7 +18,7 @@
 namespace ra {
 
 constexpr int kFbTile = 64;
-constexpr int kFbKV = 64;   // keys per online-softmax step
+constexpr int kFbKV = 32;   // keys per online-softmax step
 constexpr int kFbBM = 128;  // query rows per workgroup
 
 // grid (Np/64, B*H, 3): z = 0 Q, 1 K (RoPE -> f16), 2 V (transpose -> f16)
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(256) void k3_prep(FbArgs a) {
   extern __shared__ __align__(16) char lds[];
   const Shape s = a.s;
   const int64_t N = a.N, Np = a.Np;
-  const int bh = blockIdx.y, which = blockIdx.z;
+  const int bh = a.heads[blockIdx.y], which = blockIdx.z;
   const int64_t n0 = (int64_t)blockIdx.x * kFbTile;
   const void* src = which == 0 ? a.q : (which == 1 ? a.k : a.v);
   const void* base = (const char*)src + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
@@ -55,107 +56,187 @@ __global__ __launch_bounds__(256) void k3_prep(FbArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k3_attention(const FbArgs a) {
-  constexpr int NDB = D / 32, KC = D / 16, NT = kFbKV / 32;
-  constexpr int KROW = D + 8;      // halves
-  constexpr int VROW = kFbKV + 8;  // halves
-  __shared__ __align__(16) _Float16 Kl[kFbKV * KROW];
-  __shared__ __align__(16) _Float16 Vl[D * VROW];
+struct FbGeo {
+  static constexpr int TG = kFbKV;             // keys per group
+  static constexpr int NT = TG / 32;           // 32-key tiles per group
+  static constexpr int NDB = D / 32;           // 32-row d blocks of O^T
+  static constexpr int KC = D / 16;            // 16-deep chunks of Q K^T (f16 MFMA)
+  static constexpr int KROW = D + 8;           // halves
+  static constexpr int VROW = TG + 8;          // halves
+  static constexpr int KBUF = TG * KROW;       // halves
+  static constexpr int VBUF = D * VROW;        // halves
+  static constexpr int LDS = 2 * (KBUF + VBUF) * 2;  // bytes
+  static constexpr int KU = TG * D / 8;        // 16-byte global units of a K group
+  static constexpr int VU = D * TG / 8;
+  static constexpr int KUT = (KU + 255) / 256;
+  static constexpr int VUT = (VU + 255) / 256;
+};
+
+// fields the device helpers need, copied out of the kernel argument block
+struct FbCtx {
+  const _Float16* kr;
+  const _Float16* vt;
+  int64_t Np;
+  int N;
+  float scale_log2;
+};
+
+template <int D>
+RA_DEV void fb_load(const FbCtx& a, int bh, int g, i32x4 (&rk)[FbGeo<D>::KUT], i32x4 (&rv)[FbGeo<D>::VUT]) {
+  using G = FbGeo<D>;
+  const i32x4* ks = (const i32x4*)(a.kr + ((int64_t)bh * a.Np + (int64_t)g * G::TG) * D);
+#pragma unroll
+  for (int i = 0; i < G::KUT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (G::KU % 256 == 0 || u < G::KU) rk[i] = ks[u];
+  }
+#pragma unroll
+  for (int i = 0; i < G::VUT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (G::VU % 256 == 0 || u < G::VU) {
+      const int d = u / (G::TG / 8), c = u % (G::TG / 8);
+      rv[i] = ((const i32x4*)(a.vt + ((int64_t)bh * D + d) * a.Np + (int64_t)g * G::TG))[c];
+    }
+  }
+}
+
+// K rows are permuted inside each 32-key tile so that the S^T accumulator of lane
+// half h holds keys 16h..16h+15 of the tile in register order.
+template <int D>
+RA_DEV void fb_store(_Float16* Kl, _Float16* Vl, const i32x4 (&rk)[FbGeo<D>::KUT], const i32x4 (&rv)[FbGeo<D>::VUT]) {
+  using G = FbGeo<D>;
+#pragma unroll
+  for (int i = 0; i < G::KUT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (G::KU % 256 == 0 || u < G::KU) {
+      const int kk = u / (D / 8), c = u % (D / 8);
+      const int r = kk & 31, hh = r >> 4, v = r & 15;
+      const int row = (kk & ~31) + (v & 3) + 8 * (v >> 2) + 4 * hh;
+      *(i32x4*)(Kl + row * G::KROW + 8 * c) = rk[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < G::VUT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (G::VU % 256 == 0 || u < G::VU) {
+      const int d = u / (G::TG / 8), c = u % (G::TG / 8);
+      *(i32x4*)(Vl + d * G::VROW + 8 * c) = rv[i];
+    }
+  }
+}
+
+template <int D, bool TAIL>
+RA_DEV void fb_group(const FbCtx& a, int g, int ngroups, _Float16* lds, i32x4 (&rk)[FbGeo<D>::KUT],
+                     i32x4 (&rv)[FbGeo<D>::VUT], const f16x8 (&qop)[FbGeo<D>::KC], int bh,
+                     f32x16 (&O)[FbGeo<D>::NDB], float& m, float& l) {
+  using G = FbGeo<D>;
+  const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
+  const int N = (int)a.N;
+  const bool odd = g & 1;
+  _Float16* const kb_cur = lds + (odd ? G::KBUF : 0);
+  _Float16* const kb_nxt = lds + (odd ? 0 : G::KBUF);
+  _Float16* const vb_cur = lds + 2 * G::KBUF + (odd ? G::VBUF : 0);
+  _Float16* const vb_nxt = lds + 2 * G::KBUF + (odd ? 0 : G::VBUF);
+  f32x16 st[G::NT];
+#pragma unroll
+  for (int t = 0; t < G::NT; ++t) {
+#pragma unroll
+    for (int kc = 0; kc < G::KC; ++kc) {
+      const f16x8 kop = *(const f16x8*)(kb_cur + (t * 32 + col) * G::KROW + kc * 16 + 8 * h);
+      const f32x16 zero = {0};
+      st[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop[kc], kc == 0 ? zero : st[t], 0, 0, 0);
+    }
+  }
+  if (g + 1 < ngroups) fb_store<D>(kb_nxt, vb_nxt, rk, rv);
+  if (g + 2 < ngroups) fb_load<D>(a, bh, g + 2, rk, rv);
+  const int j0 = g * G::TG;
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < G::NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const bool ok = !TAIL || (j0 + t * 32 + 16 * h + v < N);
+      mloc = fmaxf(mloc, ok ? st[t][v] : -INFINITY);
+    }
+  const float sl2 = a.scale_log2;
+  const float mnew = fmaxf(m, fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * sl2);
+  const float alpha = exp2_hw(m - mnew);
+  if (__any(mnew > m)) {
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) O[db][v] *= alpha;
+  }
+  l *= alpha;
+  m = mnew;
+#pragma unroll
+  for (int t = 0; t < G::NT; ++t) {
+    f16x8 pb[2];
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      float p0 = exp2_hw(__builtin_fmaf(st[t][v], sl2, -mnew));
+      float p1 = exp2_hw(__builtin_fmaf(st[t][v + 1], sl2, -mnew));
+      if (TAIL) {
+        p0 = (j0 + t * 32 + 16 * h + v < N) ? p0 : 0.f;
+        p1 = (j0 + t * 32 + 16 * h + v + 1 < N) ? p1 : 0.f;
+      }
+      l += p0 + p1;
+      pb[v >> 3][v & 7] = (_Float16)p0;
+      pb[v >> 3][(v & 7) + 1] = (_Float16)p1;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+        const f16x8 vop = *(const f16x8*)(vb_cur + (db * 32 + col) * G::VROW + t * 32 + 16 * h + 8 * q);
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pb[q], O[db], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k3_attention(const FbArgs args) {
+  using G = FbGeo<D>;
+  extern __shared__ __align__(16) _Float16 flds[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
-  const int L = (int)(blockIdx.x % 8) * a.per_xcd + (int)(blockIdx.x / 8);
-  if (L >= a.total) return;
-  const int hidx = L / a.nqt, qt = L % a.nqt;
-  const int bh = a.heads[hidx];
-  const int64_t N = a.N, Np = a.Np;
+  const int L = (int)(blockIdx.x % 8) * args.per_xcd + (int)(blockIdx.x / 8);
+  if (L >= args.total) return;
+  const int hidx = L / args.nqt, qt = L % args.nqt;
+  const int bh = args.heads[hidx];
+  FbCtx a;
+  a.kr = args.kr; a.vt = args.vt; a.Np = args.Np; a.N = (int)args.N; a.scale_log2 = args.scale_log2;
+  const int N = a.N;
   const int qi = qt * kFbBM + w * 32 + col;
 
-  f16x8 qop[KC];
+  f16x8 qop[G::KC];
   {
-    const f16x8* qp = (const f16x8*)(a.qr + ((int64_t)bh * Np + qi) * D);
+    const f16x8* qp = (const f16x8*)(args.qr + ((int64_t)bh * a.Np + qi) * D);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) qop[kc] = qp[kc * 2 + h];
+    for (int kc = 0; kc < G::KC; ++kc) qop[kc] = qp[kc * 2 + h];
   }
-  const float sl2 = a.scale_log2;
   float m = -INFINITY, l = 0.f;
-  f32x16 O[NDB];
+  f32x16 O[G::NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
     for (int v = 0; v < 16; ++v) O[db][v] = 0.f;
 
-  const int64_t ngroups = (N + kFbKV - 1) / kFbKV;
-  for (int64_t g = 0; g < ngroups; ++g) {
-    const int64_t j0 = g * kFbKV;
-    __syncthreads();
-    for (int it = tid; it < kFbKV * (D / 8); it += 256) {
-      const int kk = it / (D / 8), c = it % (D / 8);
-      const uint4 x = ((const uint4*)(a.kr + ((int64_t)bh * Np + j0 + kk) * D))[c];
-      const int r = kk & 31, hh = r >> 4, v = r & 15;
-      const int row = (kk & ~31) + (v & 3) + 8 * (v >> 2) + 4 * hh;
-      *(uint4*)(Kl + row * KROW + 8 * c) = x;
-    }
-    for (int it = tid; it < D * (kFbKV / 8); it += 256) {
-      const int d = it / (kFbKV / 8), c = it % (kFbKV / 8);
-      const uint4 x = ((const uint4*)(a.vt + ((int64_t)bh * D + d) * Np + j0))[c];
-      *(uint4*)(Vl + d * VROW + 8 * c) = x;
-    }
-    __syncthreads();
-    f32x16 st[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) st[t][v] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const f16x8 kop = *(const f16x8*)(Kl + (t * 32 + col) * KROW + kc * 16 + 8 * h);
-        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop[kc], st[t], 0, 0, 0);
-      }
-    }
-    const bool tail = j0 + kFbKV > N;
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t key = j0 + t * 32 + 16 * h + v;
-        if (!tail || key < N) mloc = fmaxf(mloc, st[t][v]);
-      }
-    const float mstep = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * sl2;
-    const float mnew = fmaxf(m, mstep);
-    const float alpha = exp2_hw(m - mnew);
-    if (__any(mnew > m)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) O[db][v] *= alpha;
-    }
-    l *= alpha;
-    m = mnew;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f16x8 pb[2];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t key = j0 + t * 32 + 16 * h + v;
-        const float p = (!tail || key < N) ? exp2_hw(__builtin_fmaf(st[t][v], sl2, -mnew)) : 0.f;
-        l += p;
-        pb[v >> 3][v & 7] = (_Float16)p;
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const f16x8 vop = *(const f16x8*)(Vl + (db * 32 + col) * VROW + t * 32 + 16 * h + 8 * q);
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pb[q], O[db], 0, 0, 0);
-        }
-      }
-    }
-  }
+  const int ngroups = (N + G::TG - 1) / G::TG;
+  i32x4 rk[G::KUT], rv[G::VUT];
+  fb_load<D>(a, bh, 0, rk, rv);
+  fb_store<D>(flds, flds + 2 * G::KBUF, rk, rv);
+  if (ngroups > 1) fb_load<D>(a, bh, 1, rk, rv);
+  __syncthreads();
+  for (int g = 0; g + 1 < ngroups; ++g) fb_group<D, false>(a, g, ngroups, flds, rk, rv, qop, bh, O, m, l);
+  fb_group<D, true>(a, ngroups - 1, ngroups, flds, rk, rv, qop, bh, O, m, l);
+
   const float lq = l + __shfl_xor(l, 32, 64);
   if (qi < N) {
     const float inv = 1.0f / lq;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         const int d0 = db * 32 + 8 * v4 + 4 * h;
@@ -163,10 +244,10 @@ __global__ __launch_bounds__(256) void k3_attention(const FbArgs a) {
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = O[db][v4 * 4 + e] * inv;
-        if (a.out_f16) {
-          *(f16x4*)((_Float16*)a.out + off) = f16x4{(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
+        if (args.out_f16) {
+          *(f16x4*)((_Float16*)args.out + off) = f16x4{(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
         } else {
-          *(f32x4*)((float*)a.out + off) = f32x4{o[0], o[1], o[2], o[3]};
+          *(f32x4*)((float*)args.out + off) = f32x4{o[0], o[1], o[2], o[3]};
         }
       }
     }
@@ -174,18 +255,26 @@ __global__ __launch_bounds__(256) void k3_attention(const FbArgs a) {
 }
 
 hipError_t launch_fallback_prep(const FbArgs& a, hipStream_t st) {
-  const int BH = a.s.B * a.s.H;
-  const dim3 grid((unsigned)(a.Np / kFbTile), BH, 3);
+  const dim3 grid((unsigned)(a.Np / kFbTile), a.nheads, 3);
   const size_t lds = (size_t)kFbTile * (a.s.D + 2) * 2;
   if (a.s.D == 128) k3_prep<128, 1><<<grid, 256, lds, st>>>(a);
   else k3_prep<64, 1><<<grid, 256, lds, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_fallback(const FbArgs& a, hipStream_t st) {
-  if (a.s.D == 128) k3_attention<128><<<8 * a.per_xcd, 256, 0, st>>>(a);
-  else k3_attention<64><<<8 * a.per_xcd, 256, 0, st>>>(a);
+template <int D>
+hipError_t launch_fb_t(const FbArgs& a, hipStream_t st) {
+  using G = FbGeo<D>;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k3_attention<D>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+  if (attr != hipSuccess) return attr;
+  k3_attention<D><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_fallback(const FbArgs& a, hipStream_t st) {
+  if (a.s.D == 128) return launch_fb_t<128>(a, st);
+  return launch_fb_t<64>(a, st);
 }
 
 }  // namespace ra
