@@ -10,8 +10,11 @@
 //    v_mfma_i32_32x32x32_i8, so a lane owns one query row and 16 keys of every
 //    32-key tile; its P codes are already laid out as the B operand of the next
 //    MFMA, O^T = V^T P^T, with no LDS round trip.
-//  * K and V stay INT4 in HBM; the workgroup sign-extends each tile once into LDS
-//    as int8 with four bit operations per 8 nibbles.
+//  * K and V stay INT4 in HBM; the workgroup widens each tile once into LDS as
+//    int8 bytes holding 16 c (the nibble moved to the high half of its byte: three
+//    bit operations per 8 nibbles).  Both integer products are then 16 times the
+//    INT4 ones; the factor is a power of two and is divided out exactly in the
+//    score scale and in the output scale.
 //  * The P level r = round-half-even(2^y) is taken from the hardware exp2: with
 //    t = 2^y + 128.5 + 4*2^-16 the level is byte 2 of t's bits and the low 16 bits
 //    carry the rounding margin.  v_exp_f32 is within 1.5 * 2^-24 relative of 2^y,
@@ -48,16 +51,13 @@ struct Ctx {
   const uint8_t* vc;
   const float* ks;
   int64_t Np;
-  int N, qk_blk;
+  int N, qk_shift;
   float C0, L15;
   int dbg_row0, dbg_n;
   int32_t* dbg_aqk;
   int8_t* dbg_p;
   int32_t* dbg_apv;
 };
-
-// value held by lane l ^ 32
-RA_DEV float partner(float v) { return __shfl_xor(v, 32, 64); }
 
 template <int D, int KVB>
 struct Geo {
@@ -69,7 +69,9 @@ struct Geo {
   static constexpr int VROW = TG + 16;            // LDS V^T row stride (bytes)
   static constexpr int KBUF = TG * KROW;
   static constexpr int VBUF = D * VROW;
-  static constexpr int LDS = 2 * KBUF + 2 * VBUF;   // + 17 floats of level thresholds after it
+  static constexpr int SKN = TG / 16;             // K scales per group, one per 16 keys
+  static constexpr int SOFF = 2 * KBUF + 2 * VBUF;  // two groups of K scales (floats)
+  static constexpr int LDS = SOFF + 2 * SKN * 4;    // + 17 floats of level thresholds after it
   static constexpr int KU = TG * D / 16;          // 8-byte global units of a K group
   static constexpr int VU = D * TG / 16;          // 8-byte global units of a V group
   static constexpr int KUT = (KU + 255) / 256;    // per thread
@@ -90,9 +92,9 @@ struct RowState {
 };
 
 template <int D, int KVB>
-RA_DEV void load_k(const Ctx& a, int bh, int g, uint2 (&r)[Geo<D, KVB>::KUT]) {
+RA_DEV void load_k(const Ctx& a, int bh, int g, u32x2 (&r)[Geo<D, KVB>::KUT]) {
   using G = Geo<D, KVB>;
-  const uint2* src = (const uint2*)(a.kc + ((int64_t)bh * a.Np + (int64_t)g * G::TG) * (D / 2));
+  const u32x2* src = (const u32x2*)(a.kc + ((int64_t)bh * a.Np + (int64_t)g * G::TG) * (D / 2));
 #pragma unroll
   for (int i = 0; i < G::KUT; ++i) {
     const int u = threadIdx.x + 256 * i;
@@ -100,21 +102,21 @@ RA_DEV void load_k(const Ctx& a, int bh, int g, uint2 (&r)[Geo<D, KVB>::KUT]) {
   }
 }
 template <int D, int KVB>
-RA_DEV void load_v(const Ctx& a, int bh, int g, uint2 (&r)[Geo<D, KVB>::VUT]) {
+RA_DEV void load_v(const Ctx& a, int bh, int g, u32x2 (&r)[Geo<D, KVB>::VUT]) {
   using G = Geo<D, KVB>;
 #pragma unroll
   for (int i = 0; i < G::VUT; ++i) {
     const int u = threadIdx.x + 256 * i;
     if (G::VU % 256 == 0 || u < G::VU) {
       const int d = u / (G::TG / 16), c = u % (G::TG / 16);
-      r[i] = ((const uint2*)(a.vc + ((int64_t)bh * D + d) * (a.Np / 2) + (int64_t)g * (G::TG / 2)))[c];
+      r[i] = ((const u32x2*)(a.vc + ((int64_t)bh * D + d) * (a.Np / 2) + (int64_t)g * (G::TG / 2)))[c];
     }
   }
 }
 // K rows (sign-extended) are permuted inside each 32-key tile so that the S^T accumulator of lane
 // half h holds keys 16h..16h+15 of the tile in register order.
 template <int D, int KVB>
-RA_DEV void store_k(uint8_t* Kl, const uint2 (&r)[Geo<D, KVB>::KUT]) {
+RA_DEV void store_k(uint8_t* Kl, const u32x2 (&r)[Geo<D, KVB>::KUT]) {
   using G = Geo<D, KVB>;
 #pragma unroll
   for (int i = 0; i < G::KUT; ++i) {
@@ -122,8 +124,8 @@ RA_DEV void store_k(uint8_t* Kl, const uint2 (&r)[Geo<D, KVB>::KUT]) {
     if (G::KU % 256 == 0 || u < G::KU) {
       const int kk = u / (D / 16), c = u % (D / 16);
       uint32_t lo0, hi0, lo1, hi1;
-      widen_signed(r[i].x, lo0, hi0);
-      widen_signed(r[i].y, lo1, hi1);
+      widen_x16(r[i].x, lo0, hi0);
+      widen_x16(r[i].y, lo1, hi1);
       const int rr = kk & 31, hh = rr >> 4, v = rr & 15;
       const int row = (kk & ~31) + (v & 3) + 8 * (v >> 2) + 4 * hh;
       *(uint4*)(Kl + row * G::KROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
@@ -131,7 +133,7 @@ RA_DEV void store_k(uint8_t* Kl, const uint2 (&r)[Geo<D, KVB>::KUT]) {
   }
 }
 template <int D, int KVB>
-RA_DEV void store_v(uint8_t* Vl, const uint2 (&r)[Geo<D, KVB>::VUT]) {
+RA_DEV void store_v(uint8_t* Vl, const u32x2 (&r)[Geo<D, KVB>::VUT]) {
   using G = Geo<D, KVB>;
 #pragma unroll
   for (int i = 0; i < G::VUT; ++i) {
@@ -139,11 +141,20 @@ RA_DEV void store_v(uint8_t* Vl, const uint2 (&r)[Geo<D, KVB>::VUT]) {
     if (G::VU % 256 == 0 || u < G::VU) {
       const int d = u / (G::TG / 16), c = u % (G::TG / 16);
       uint32_t lo0, hi0, lo1, hi1;
-      widen_signed(r[i].x, lo0, hi0);
-      widen_signed(r[i].y, lo1, hi1);
+      widen_x16(r[i].x, lo0, hi0);
+      widen_x16(r[i].y, lo1, hi1);
       *(uint4*)(Vl + d * G::VROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
     }
   }
+}
+
+// K scale of the 16-key unit threadIdx.x of group g (threads below TG / 16); staged
+// through LDS with the K/V tiles
+template <int D, int KVB>
+RA_DEV void load_ks(const Ctx& a, int bh, int g, float& rs) {
+  using G = Geo<D, KVB>;
+  if (threadIdx.x < G::SKN)
+    rs = a.ks[(int64_t)bh * (a.Np >> a.qk_shift) + ((g * G::TG + 16 * (int)threadIdx.x) >> a.qk_shift)];
 }
 
 template <int D, int KVB>
@@ -165,21 +176,17 @@ RA_DEV void qk_tiles(const uint8_t* Kl, const i32x4 (&qop)[Geo<D, KVB>::KC], i32
 // P^T operand, P V MFMAs.  TAIL: the group holds keys >= N.
 template <int D, int KVB, bool DBG, bool TAIL>
 RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
-                       const i32x16 (&st)[Geo<D, KVB>::NT], float sq, int bh, RowState<D / 32>& S,
-                       bool dbg_row, int dr) {
+                       const i32x16 (&st)[Geo<D, KVB>::NT], const float (&sk)[Geo<D, KVB>::NT], float sq,
+                       RowState<D / 32>& S, bool dbg_row, int dr) {
   using G = Geo<D, KVB>;
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
   const int N = (int)a.N;
   const int j0 = g * G::TG;
   const int nsteps = (N + KVB - 1) / KVB;
+  // score scale c = (sq sk) C0 of the spec, over 16 for the x16 integer products
   float ct[G::NT];
 #pragma unroll
-  for (int t = 0; t < G::NT; ++t) {
-    const int key0 = j0 + t * 32 + 16 * h;
-    const float sk = a.ks[(int64_t)bh * (a.Np / a.qk_blk) + key0 / a.qk_blk];
-    const float ss = sq * sk;
-    ct[t] = ss * a.C0;
-  }
+  for (int t = 0; t < G::NT; ++t) ct[t] = ((sq * sk[t]) * a.C0) * 0.0625f;
   constexpr int NSTEP = KVB < 32 ? 2 : 1;
 #pragma unroll
   for (int sidx = 0; sidx < NSTEP; ++sidx) {
@@ -202,7 +209,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
         mloc = fmaxf(mloc, tm);
       }
     }
-    const float mnew = fmaxf(S.m, fmaxf(mloc, partner(mloc)));
+    const float mnew = fmaxf(S.m, pair_max(mloc));
     const float alpha = exp2_hw(S.m - mnew);
     if (DBG || __any(mnew > S.m)) {
       if (!S.fresh) {
@@ -289,7 +296,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
         for (int v = 0; v < 16; ++v) {
           const int key = j0 + t * 32 + 16 * h + v;
           if (key < N) {
-            a.dbg_aqk[(int64_t)dr * N + key] = st[t][v];
+            a.dbg_aqk[(int64_t)dr * N + key] = st[t][v] >> 4;
             a.dbg_p[(int64_t)dr * N + key] = (int8_t)((int)((tt[v] >> 16) & 0xFFu) - 8);
           }
         }
@@ -302,7 +309,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int d = db * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
-          a.dbg_apv[((int64_t)dr * nsteps + step) * D + d] = S.acc[db][v];
+          a.dbg_apv[((int64_t)dr * nsteps + step) * D + d] = S.acc[db][v] >> 4;
         }
       }
     }
@@ -313,8 +320,8 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
 // group g+1 into the other buffer, global loads of group g+2, softmax + P V,
 // one barrier.  MFMA/VALU overlap comes from the second wave on each SIMD.
 template <int D, int KVB, bool DBG, bool TAIL>
-RA_DEV void group_iter(const Ctx& a, int g, int ngroups, uint8_t* lds, uint2 (&rk)[Geo<D, KVB>::KUT],
-                       uint2 (&rv)[Geo<D, KVB>::VUT], const i32x4 (&qop)[Geo<D, KVB>::KC],
+RA_DEV void group_iter(const Ctx& a, int g, int ngroups, uint8_t* lds, u32x2 (&rk)[Geo<D, KVB>::KUT],
+                       u32x2 (&rv)[Geo<D, KVB>::VUT], float& rs, const i32x4 (&qop)[Geo<D, KVB>::KC],
                        float sq, int bh, RowState<D / 32>& S, bool dbg_row, int dr) {
   using G = Geo<D, KVB>;
   const bool odd = g & 1;
@@ -322,17 +329,25 @@ RA_DEV void group_iter(const Ctx& a, int g, int ngroups, uint8_t* lds, uint2 (&r
   uint8_t* const kb_nxt = lds + (odd ? 0 : G::KBUF);
   uint8_t* const vb_cur = lds + 2 * G::KBUF + (odd ? G::VBUF : 0);
   uint8_t* const vb_nxt = lds + 2 * G::KBUF + (odd ? 0 : G::VBUF);
+  float* const sb_cur = (float*)(lds + G::SOFF) + (odd ? G::SKN : 0);
+  float* const sb_nxt = (float*)(lds + G::SOFF) + (odd ? 0 : G::SKN);
   i32x16 st[G::NT];
   qk_tiles<D, KVB>(kb_cur, qop, st);
   if (g + 1 < ngroups) {
     store_k<D, KVB>(kb_nxt, rk);
     store_v<D, KVB>(vb_nxt, rv);
+    if (threadIdx.x < G::SKN) sb_nxt[threadIdx.x] = rs;
   }
   if (g + 2 < ngroups) {
     load_k<D, KVB>(a, bh, g + 2, rk);
     load_v<D, KVB>(a, bh, g + 2, rv);
+    load_ks<D, KVB>(a, bh, g + 2, rs);
   }
-  softmax_pv<D, KVB, DBG, TAIL>(a, g, vb_cur, (const float*)(lds + G::LDS), st, sq, bh, S, dbg_row, dr);
+  float sk[G::NT];
+  const int h = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int t = 0; t < G::NT; ++t) sk[t] = sb_cur[2 * t + h];
+  softmax_pv<D, KVB, DBG, TAIL>(a, g, vb_cur, (const float*)(lds + G::LDS), st, sk, sq, S, dbg_row, dr);
   __syncthreads();
 }
 
@@ -354,7 +369,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int bh = args.heads[hidx];
   Ctx a;
   a.kc = args.kc; a.vc = args.vc; a.ks = args.ks; a.Np = args.Np;
-  a.N = (int)args.N; a.qk_blk = args.qk_blk; a.C0 = args.C0; a.L15 = args.L15;
+  a.N = (int)args.N; a.qk_shift = __builtin_ctz(args.qk_blk); a.C0 = args.C0; a.L15 = args.L15;
   a.dbg_row0 = args.dbg_row0; a.dbg_n = args.dbg_n;
   a.dbg_aqk = args.dbg_aqk; a.dbg_p = args.dbg_p; a.dbg_apv = args.dbg_apv;
   const int N = a.N;
@@ -363,17 +378,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---- Q operand (signed int8) ------------------------------------------------
   i32x4 qop[G::KC];
   {
-    const uint2* qp = (const uint2*)(args.qc + ((int64_t)bh * a.Np + qi) * (D / 2));
+    const u32x2* qp = (const u32x2*)(args.qc + ((int64_t)bh * a.Np + qi) * (D / 2));
 #pragma unroll
     for (int kc = 0; kc < G::KC; ++kc) {
-      const uint2 x = qp[kc * 2 + h];
+      const u32x2 x = qp[kc * 2 + h];
       uint32_t lo0, hi0, lo1, hi1;
       widen_signed(x.x, lo0, hi0);
       widen_signed(x.y, lo1, hi1);
       qop[kc] = i32x4{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
     }
   }
-  const float sq = args.qs[(int64_t)bh * (a.Np / a.qk_blk) + qi / a.qk_blk];
+  const float sq = args.qs[(int64_t)bh * (a.Np >> a.qk_shift) + (qi >> a.qk_shift)];
 
   RowState<G::NDB> S;
   S.m = -INFINITY;
@@ -393,29 +408,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (tid < 17) ((float*)(lds + G::LDS))[tid] = tid < 15 ? args.T[tid] : INFINITY;
 
   // ---- prologue: group 0 in LDS, group 1 in flight -------------------------------
-  uint2 rk[G::KUT], rv[G::VUT];
+  u32x2 rk[G::KUT], rv[G::VUT];
+  float rs = 0.f;
+  load_ks<D, KVB>(a, bh, 0, rs);
   load_k<D, KVB>(a, bh, 0, rk);
   load_v<D, KVB>(a, bh, 0, rv);
   store_k<D, KVB>(lds, rk);
   store_v<D, KVB>(lds + 2 * G::KBUF, rv);
+  if (tid < G::SKN) ((float*)(lds + G::SOFF))[tid] = rs;
   if (ngroups > 1) {
     load_k<D, KVB>(a, bh, 1, rk);
     load_v<D, KVB>(a, bh, 1, rv);
+    load_ks<D, KVB>(a, bh, 1, rs);
   }
   __syncthreads();
   for (int g = 0; g + 1 < ngroups; ++g)
-    group_iter<D, KVB, DBG, false>(a, g, ngroups, lds, rk, rv, qop, sq, bh, S, dbg_row, dr);
-  group_iter<D, KVB, DBG, true>(a, ngroups - 1, ngroups, lds, rk, rv, qop, sq, bh, S, dbg_row, dr);
+    group_iter<D, KVB, DBG, false>(a, g, ngroups, lds, rk, rv, rs, qop, sq, bh, S, dbg_row, dr);
+  group_iter<D, KVB, DBG, true>(a, ngroups - 1, ngroups, lds, rk, rv, rs, qop, sq, bh, S, dbg_row, dr);
 
   // ---- epilogue ---------------------------------------------------------------------
-  const float lq = S.l + partner(S.l);
+  const float lq = pair_sum(S.l);
   const float inv_sigma = 1.0f / S.sigma;
   if (DBG && dbg_row && h == 0) {
     args.dbg_m[dr] = S.m;
     args.dbg_l[dr] = lq;
   }
   if (qi < N) {
-    const float inv = 1.0f / lq;
+    const float inv = 0.0625f / lq;  // also divides out the x16 of the V bytes
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -42,6 +43,14 @@ RA_DEV void widen_signed(uint32_t x, uint32_t& lo, uint32_t& hi) {
   lo = (a + 0x78787878u) ^ 0x78787878u;
   hi = (b + 0x78787878u) ^ 0x78787878u;
 }
+// Widening into the high nibble: the same byte order, each byte holding 16 c as an
+// int8 (a two's-complement nibble shifted up by four is 16 times its value).  Three
+// bit operations per 8 nibbles; the factor 16 is a power of two and is divided out
+// exactly wherever the sums are scaled.
+RA_DEV void widen_x16(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  lo = (x << 4) & 0xF0F0F0F0u;
+  hi = x & 0xF0F0F0F0u;
+}
 
 // ---- wave reductions ------------------------------------------------------------
 RA_DEV float wave_max(float v, int width) {
@@ -50,5 +59,15 @@ RA_DEV float wave_max(float v, int width) {
 }
 
 RA_DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum of a value and the one held by lane l ^ 32 (v_permlane32_swap, no LDS)
+RA_DEV float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+RA_DEV float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace ra
