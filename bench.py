@@ -122,7 +122,8 @@ def main():
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "k2_attention (rotattn_int4_attention)",
                      "achieved": round(k2_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                     "frac": round(k2_tops / PEAK_INT8_TOPS, 4), "traffic": None},
+                     "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": counted_traffic() if args.config == CONFIG and not (args.kv or args.qk) else None},
         "kernels_ms": {"quantize_qk": round(k1_ms, 4), "int4_attention": round(k2_ms, 4)},
         "quantize_qk_GBps": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
         "attention_only_TOPS": round(k2_tops, 1),
@@ -149,6 +150,25 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, rot)
     print(json.dumps(result))
+
+
+def counted_traffic():
+    """HBM bytes per k2_attention launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), or None when
+    the attention source has changed since the counters were taken."""
+    import hashlib
+    src = os.path.join(ROOT, "int4_quantized_attention_amd", "csrc", "attention.hip")
+    summ = os.path.join(ROOT, "profiles", "wan720p_hbm_counters.md")
+    try:
+        text = open(summ).read()
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines()
+                  if l.startswith(("traffic_bytes_per_launch:", "attention_source_sha256_16:")))
+    if fields.get("attention_source_sha256_16", "").strip() != cur:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, rot, rows_target=16384):

@@ -124,7 +124,10 @@ void rope_rotate_token(const Shape& s, int rot, const T* tab, int64_t n, const T
   }
 }
 
-// Symmetric INT4 quantisation of one block (north_star "symmetric per block").
+// Symmetric INT4 quantisation of one block of qk_blk tokens x all channels (the
+// signed symmetric INT4 quantiser of the papernotes.org note, "Key design 2"; one
+// scale per block of tokens generalises the per-token Q/K scales of the
+// paper.gecl.asia analysis, "Key Insight").
 // amax over the block; amax == 0 -> scale 0, codes 0; else inv = 7/amax (IEEE
 // division), code = clamp(rint(x * inv), -7, 7), scale = amax / 7.
 void quant_block(const float* x, int64_t count, int8_t* code, float* scale) {
