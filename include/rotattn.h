@@ -139,7 +139,14 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
  *                  a_qk [n_rows][N] i32, p_codes [n_rows][N] i8 (P~),
  *                  a_pv [n_rows][S][D] i32 with S = ceil(N/kv_blk) (per-step
  *                  sum_j (P~+8) vc), m [n_rows] f32, l [n_rows] f32.  The output
- *                  rows are written as well. */
+ *                  rows are written as well.
+ *   workspace      device, >= rotattn_int4_attention_workspace(s) bytes, 16-byte
+ *                  aligned (2*D bytes per padded token and head: the listed heads'
+ *                  K and V codes restaged as fp8 / int8 MFMA operands).  Contents
+ *                  need no initialisation; a smaller size returns
+ *                  ROTATTN_E_WORKSPACE before any launch.  Shapes whose images
+ *                  exceed 2^31 bytes per head (N beyond about 6.7 million tokens)
+ *                  return ROTATTN_E_UNSUPPORTED. */
 typedef struct {
   int32_t bh, row0, n_rows;
   int32_t* a_qk;
@@ -149,13 +156,15 @@ typedef struct {
   float* l;
 } rotattn_debug;
 
+size_t rotattn_int4_attention_workspace(const rotattn_shape* s);
 rotattn_status rotattn_int4_attention(const rotattn_shape* s,
                                       const uint8_t* q_codes, const float* q_scale,
                                       const uint8_t* k_codes, const float* k_scale,
                                       const uint8_t* v_codes, const float* v_scale,
                                       const int32_t* heads, int32_t n_heads,
                                       rotattn_dtype out_dtype, void* out,
-                                      const rotattn_debug* dbg, void* stream);
+                                      const rotattn_debug* dbg,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- rotattn_fp16_fallback ------------------------------------------------------
  * Full-precision fallback for sensitive heads / denoising steps (Key design 3):

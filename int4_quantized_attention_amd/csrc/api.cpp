@@ -160,16 +160,27 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
   return launch_status(ra::launch_quantize(a, (int)in_dtype, (hipStream_t)stream));
 }
 
+size_t rotattn_int4_attention_workspace(const rotattn_shape* s) {
+  if (!s || rotattn_check_shape(s) != ROTATTN_OK) return 0;
+  return ra::attention_workspace_bytes(s->D, s->kv_blk, (int64_t)s->B * s->H, rotattn_padded_tokens(s));
+}
+
 rotattn_status rotattn_int4_attention(const rotattn_shape* s,
                                       const uint8_t* q_codes, const float* q_scale,
                                       const uint8_t* k_codes, const float* k_scale,
                                       const uint8_t* v_codes, const float* v_scale,
                                       const int32_t* heads, int32_t n_heads,
                                       rotattn_dtype out_dtype, void* out,
-                                      const rotattn_debug* dbg, void* stream) {
+                                      const rotattn_debug* dbg,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
-  if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !out) return ROTATTN_E_NULL;
+  if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !out || !workspace)
+    return ROTATTN_E_NULL;
+  // one head's images are addressed through a buffer resource with a 32-bit range
+  if (rotattn_int4_attention_workspace(s) / ((size_t)s->B * s->H) > (size_t)INT32_MAX) return ROTATTN_E_UNSUPPORTED;
+  if (workspace_bytes < rotattn_int4_attention_workspace(s) || ((uintptr_t)workspace & 15) != 0)
+    return ROTATTN_E_WORKSPACE;
   if (out_dtype != ROTATTN_F32 && out_dtype != ROTATTN_F16) return ROTATTN_E_ARG;
   const int BH = s->B * s->H;
   if (heads) {
@@ -181,6 +192,8 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
   ra::AttnArgs a;
   std::memset(&a, 0, sizeof(a));
   a.qc = q_codes; a.qs = q_scale; a.kc = k_codes; a.ks = k_scale; a.vc = v_codes; a.vs = v_scale;
+  a.img = (uint8_t*)workspace;
+  a.img_bytes = (int64_t)workspace_bytes;
   a.out = out;
   a.out_f16 = out_dtype == ROTATTN_F16;
   a.N = N;

@@ -6,28 +6,36 @@
 // round(15 P) - 8 in [-8, 7], fixed scale 15, zero point -8).
 //
 // gfx950 design
+//  * A staging pass (k2_stage) turns each head's INT4 K and V codes into the exact
+//    byte image one key group occupies in LDS: K as fp8 e4m3 (every INT4 value is
+//    exact in e4m3) with rows permuted for the S^T register layout, V^T as int8,
+//    rows padded by 16 bytes (odd multiples of 16: conflict-free LDS reads with
+//    addresses that stay affine), and the level-threshold table in the tail.  The
+//    main loop copies groups straight from global memory into LDS
+//    (buffer_load_dwordx4 ... lds), three groups ahead into a ring of four slots,
+//    and spends no VALU on staging.
 //  * One workgroup = 4 waves x 32 query rows.  Each wave computes S^T = K Q^T on
-//    v_mfma_i32_32x32x32_i8, so a lane owns one query row and 16 keys of every
-//    32-key tile; its P codes are already laid out as the B operand of the next
-//    MFMA, O^T = V^T P^T, with no LDS round trip.
-//  * K and V stay INT4 in HBM; the workgroup widens each tile once into LDS as
-//    int8 bytes holding 16 c (the nibble moved to the high half of its byte: three
-//    bit operations per 8 nibbles).  Both integer products are then 16 times the
-//    INT4 ones; the factor is a power of two and is divided out exactly in the
-//    score scale and in the output scale.
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales).  Products of INT4 values and
+//    their sums (|A| <= 49 D < 2^24) are exact in fp32, so the scores arrive as
+//    exact integers in float registers.  A lane owns one query row and 16 keys of
+//    every 32-key tile; its P levels are already laid out as the B operand of the
+//    next MFMA, O^T = V^T P^T (v_mfma_i32_32x32x32_i8), with no LDS round trip.
 //  * The P level r = round-half-even(2^y) is taken from the hardware exp2: with
 //    t = 2^y + 128.5 + 4*2^-16 the level is byte 2 of t's bits and the low 16 bits
 //    carry the rounding margin.  v_exp_f32 is within 1.5 * 2^-24 relative of 2^y,
 //    so whenever the margin is above 6/2^16 the level equals the exact one; the
-//    (rare) other elements are decided exactly against the 15 thresholds.
+//    (rare) other elements are decided exactly against the 15 thresholds.  The
+//    level r in [0, 15] is the int8 operand: sum_j (P~_j + 8) v_j = sum_j r_j v_j
+//    folds the zero point into the product.
 //  * The int32 P V accumulator runs across online-softmax steps and is folded
-//    into the fp32 output (one fma per element, in a fixed exponent frame) only
-//    when a row maximum moves; the next MFMA then restarts it from zero.
+//    into the fp32 output (one fma per element, in a fixed exponent frame) and
+//    cleared only when a row maximum moves.
 //  * Two waves per SIMD (<= 256 registers each), so that one wave's MFMAs run
-//    under the other's softmax; one barrier per key group; K and V tiles are
-//    double-buffered in LDS and their global loads run one group ahead.
+//    under the other's softmax; one barrier per key group.
 //  * Workgroup ids are remapped so that all query tiles of a head run on the same
 //    XCD and share its L2 for the K/V stream.
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -35,8 +43,11 @@ namespace ra {
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
+constexpr int kBufs = 4;  // LDS ring: group g computes while g+1..g+3 land
 constexpr float kMagic = 128.5f + 4.0f / 65536.0f;
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 RA_DEV uint32_t pack_b2(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t x = __builtin_amdgcn_perm(b, a, 0x0c0c0602u);
@@ -44,11 +55,76 @@ RA_DEV uint32_t pack_b2(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_amdgcn_perm(y, x, 0x05040100u);
 }
 
+template <int D, int KVB>
+struct Geo {
+  static constexpr int TG = KVB < 32 ? 32 : KVB;  // keys per group (staged together)
+  static constexpr int NT = TG / 32;              // 32-key MFMA tiles per group
+  static constexpr int NDB = D / 32;              // 32-row d blocks of O^T
+  static constexpr int KC = D / 64;               // 64-deep chunks of Q K^T (fp8 MFMA)
+  static constexpr int KROW = D + 16;             // bytes per K row (fp8 + pad)
+  static constexpr int VROW = TG + 16;            // bytes per V^T row (int8 + pad)
+  static constexpr int VOFF = TG * KROW;          // V^T rows start here
+  static constexpr int TOFF = VOFF + D * VROW;    // 17 floats of level thresholds
+  static constexpr int IMG = (TOFF + 128 + 4095) / 4096 * 4096;  // one group's image
+  static constexpr int NDMA = IMG / 4096;         // 16-byte copies per thread per group
+  static constexpr int LDS = kBufs * IMG;
+};
+// key (within its 32-key tile) held by K image row rho: row (v&3) + 8(v>>2) + 4h
+// holds key 16h + v, so lane half h of the S^T accumulator sees keys 16h..16h+15
+RA_DEV int key_of_row(int rho) { return 16 * ((rho >> 2) & 1) + (rho & 3) + 4 * (rho >> 3); }
+
+RA_DEV uint32_t fp8_pair(int c0, int c1) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)c0, (float)c1, 0, false) & 0xFFFFu;
+}
+RA_DEV int nib(uint32_t w, int e) { return (int)((w >> (4 * e)) << 28) >> 28; }  // signed nibble e
+
+// ---- staging: INT4 codes -> per-group LDS images ---------------------------------
+// grid (Np / TG, nheads); the image of group g of head bh is at
+// img + (bh * (Np / TG) + g) * IMG.
+template <int D, int KVB>
+__global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
+  using G = Geo<D, KVB>;
+  const int bh = args.heads[blockIdx.y];
+  const int g = blockIdx.x;
+  const int64_t Np = args.Np;
+  const int64_t at = ((int64_t)bh * (Np / G::TG) + g) * G::IMG;
+  if (at + G::IMG > args.img_bytes) return;
+  uint8_t* img = args.img + at;
+  // K: TG rows x D bytes
+  for (int u = threadIdx.x; u < G::TG * D / 16; u += 256) {
+    const int rho = u / (D / 16), c = u % (D / 16);
+    const int key = g * G::TG + (rho & ~31) + key_of_row(rho & 31);
+    const u32x2 w = *(const u32x2*)(args.kc + ((int64_t)bh * Np + key) * (D / 2) + 8 * c);
+    i32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x = q < 2 ? w.x : w.y;
+      const int e0 = 4 * (q & 1);
+      o[q] = (int)(fp8_pair(nib(x, e0), nib(x, e0 + 1)) | (fp8_pair(nib(x, e0 + 2), nib(x, e0 + 3)) << 16));
+    }
+    *(i32x4*)(img + rho * G::KROW + 16 * c) = o;
+  }
+  // V^T: D rows x TG bytes (keys of the group in order)
+  for (int u = threadIdx.x; u < D * G::TG / 16; u += 256) {
+    const int d = u / (G::TG / 16), c = u % (G::TG / 16);
+    const u32x2 w = *(const u32x2*)(args.vc + ((int64_t)bh * D + d) * (Np / 2) + (g * G::TG + 16 * c) / 2);
+    i32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x = q < 2 ? w.x : w.y;
+      const int e0 = 4 * (q & 1);
+      o[q] = (int)(((uint32_t)nib(x, e0) & 0xFFu) | (((uint32_t)nib(x, e0 + 1) & 0xFFu) << 8) |
+                   (((uint32_t)nib(x, e0 + 2) & 0xFFu) << 16) | (((uint32_t)nib(x, e0 + 3) & 0xFFu) << 24));
+    }
+    *(i32x4*)(img + G::VOFF + d * G::VROW + 16 * c) = o;
+  }
+  if (threadIdx.x < 17) ((float*)(img + G::TOFF))[threadIdx.x] = threadIdx.x < 15 ? args.T[threadIdx.x] : INFINITY;
+}
+
 // The fields the device helpers need, copied out of the kernel argument block
 // (which also holds the head list and stays in the kernarg segment).
 struct Ctx {
-  const uint8_t* kc;
-  const uint8_t* vc;
+  const uint8_t* img;
   const float* ks;
   int64_t Np;
   int N, qk_shift;
@@ -59,115 +135,66 @@ struct Ctx {
   int32_t* dbg_apv;
 };
 
-template <int D, int KVB>
-struct Geo {
-  static constexpr int TG = KVB < 32 ? 32 : KVB;  // keys per group (staged together)
-  static constexpr int NT = TG / 32;              // 32-key MFMA tiles per group
-  static constexpr int NDB = D / 32;              // 32-row d blocks of O^T
-  static constexpr int KC = D / 32;               // 32-deep chunks of Q K^T
-  static constexpr int KROW = D + 16;             // LDS K row stride (bytes)
-  static constexpr int VROW = TG + 16;            // LDS V^T row stride (bytes)
-  static constexpr int KBUF = TG * KROW;
-  static constexpr int VBUF = D * VROW;
-  static constexpr int SKN = TG / 16;             // K scales per group, one per 16 keys
-  static constexpr int SOFF = 2 * KBUF + 2 * VBUF;  // two groups of K scales (floats)
-  static constexpr int LDS = SOFF + 2 * SKN * 4;    // + 17 floats of level thresholds after it
-  static constexpr int KU = TG * D / 16;          // 8-byte global units of a K group
-  static constexpr int VU = D * TG / 16;          // 8-byte global units of a V group
-  static constexpr int KUT = (KU + 255) / 256;    // per thread
-  static constexpr int VUT = (VU + 255) / 256;
-};
-
 // Per-lane running state of one query row (the lane pair l, l^32 shares a row).
 // Of holds the flushed part of the output numerator in a fixed frame: the sum over
-// flushed steps of 2^(m_s - mref) * acc_s, where acc_s is the integer P V sum of a
-// step with running maximum m_s.  sigma = 2^(m - mref) for the current maximum, so
-// a flush is one fma per element; acc restarts from zero in the next MFMA (fresh).
+// flushed steps of 2^(m_s - mref) * acc_s, where acc_s is the integer P V sum of
+// the steps with running maximum m_s.  sigma = 2^(m - mref) for the current
+// maximum, so a flush is one fma per element, after which acc is cleared.
 template <int NDB>
 struct RowState {
   f32x16 Of[NDB];
   i32x16 acc[NDB];
   float m, l, mref, sigma;
-  bool fresh;
 };
 
-template <int D, int KVB>
-RA_DEV void load_k(const Ctx& a, int bh, int g, u32x2 (&r)[Geo<D, KVB>::KUT]) {
-  using G = Geo<D, KVB>;
-  const u32x2* src = (const u32x2*)(a.kc + ((int64_t)bh * a.Np + (int64_t)g * G::TG) * (D / 2));
-#pragma unroll
-  for (int i = 0; i < G::KUT; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    if (G::KU % 256 == 0 || u < G::KU) r[i] = src[u];
-  }
+// Copy the LDS image of group g into ring slot `buf`.  Wave w copies the w-th
+// quarter of the image, one contiguous kilobyte (16 bytes per lane) per copy,
+// through a buffer resource over the head's images: the lane offset is the only
+// vector operand, the group and wave offsets are scalar, and the immediate offset
+// applies to the global and the LDS address alike.  Reads past the resource's
+// range return zero.
+template <int J>
+RA_DEV void dma_one(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int lane_off, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 4096 * (J >> 2)), 16, lane_off,
+                                           soff + 4096 * (J >> 2), 1024 * (J & 3), 0);
+}
+template <int... J>
+RA_DEV void dma_all(std::integer_sequence<int, J...>, __amdgpu_buffer_rsrc_t r, uint8_t* dst, int lane_off,
+                    int soff) {
+  (dma_one<J>(r, dst, lane_off, soff), ...);
 }
 template <int D, int KVB>
-RA_DEV void load_v(const Ctx& a, int bh, int g, u32x2 (&r)[Geo<D, KVB>::VUT]) {
+RA_DEV void dma_group(__amdgpu_buffer_rsrc_t r, int g, uint8_t* buf) {
   using G = Geo<D, KVB>;
-#pragma unroll
-  for (int i = 0; i < G::VUT; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    if (G::VU % 256 == 0 || u < G::VU) {
-      const int d = u / (G::TG / 16), c = u % (G::TG / 16);
-      r[i] = ((const u32x2*)(a.vc + ((int64_t)bh * D + d) * (a.Np / 2) + (int64_t)g * (G::TG / 2)))[c];
-    }
-  }
-}
-// K rows (sign-extended) are permuted inside each 32-key tile so that the S^T accumulator of lane
-// half h holds keys 16h..16h+15 of the tile in register order.
-template <int D, int KVB>
-RA_DEV void store_k(uint8_t* Kl, const u32x2 (&r)[Geo<D, KVB>::KUT]) {
-  using G = Geo<D, KVB>;
-#pragma unroll
-  for (int i = 0; i < G::KUT; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    if (G::KU % 256 == 0 || u < G::KU) {
-      const int kk = u / (D / 16), c = u % (D / 16);
-      uint32_t lo0, hi0, lo1, hi1;
-      widen_x16(r[i].x, lo0, hi0);
-      widen_x16(r[i].y, lo1, hi1);
-      const int rr = kk & 31, hh = rr >> 4, v = rr & 15;
-      const int row = (kk & ~31) + (v & 3) + 8 * (v >> 2) + 4 * hh;
-      *(uint4*)(Kl + row * G::KROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
-    }
-  }
-}
-template <int D, int KVB>
-RA_DEV void store_v(uint8_t* Vl, const u32x2 (&r)[Geo<D, KVB>::VUT]) {
-  using G = Geo<D, KVB>;
-#pragma unroll
-  for (int i = 0; i < G::VUT; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    if (G::VU % 256 == 0 || u < G::VU) {
-      const int d = u / (G::TG / 16), c = u % (G::TG / 16);
-      uint32_t lo0, hi0, lo1, hi1;
-      widen_x16(r[i].x, lo0, hi0);
-      widen_x16(r[i].y, lo1, hi1);
-      *(uint4*)(Vl + d * G::VROW + 16 * c) = make_uint4(lo0, hi0, lo1, hi1);
-    }
-  }
+  constexpr int WB = G::NDMA * 1024;  // bytes per wave
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  dma_all(std::make_integer_sequence<int, G::NDMA>{}, r, buf + w * WB, 16 * (threadIdx.x & 63),
+          g * G::IMG + w * WB);
 }
 
-// K scale of the 16-key unit threadIdx.x of group g (threads below TG / 16); staged
-// through LDS with the K/V tiles
-template <int D, int KVB>
-RA_DEV void load_ks(const Ctx& a, int bh, int g, float& rs) {
-  using G = Geo<D, KVB>;
-  if (threadIdx.x < G::SKN)
-    rs = a.ks[(int64_t)bh * (a.Np >> a.qk_shift) + ((g * G::TG + 16 * (int)threadIdx.x) >> a.qk_shift)];
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left unconstrained)
+template <int n>
+RA_DEV void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
 template <int D, int KVB>
-RA_DEV void qk_tiles(const uint8_t* Kl, const i32x4 (&qop)[Geo<D, KVB>::KC], i32x16 (&st)[Geo<D, KVB>::NT]) {
+RA_DEV void qk_tiles(const uint8_t* Kl, const i32x8 (&qop)[Geo<D, KVB>::KC], f32x16 (&st)[Geo<D, KVB>::NT]) {
   using G = Geo<D, KVB>;
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
 #pragma unroll
   for (int t = 0; t < G::NT; ++t) {
+    const uint8_t* row = Kl + (t * 32 + col) * G::KROW + 32 * h;
 #pragma unroll
     for (int kc = 0; kc < G::KC; ++kc) {
-      const i32x4 kop = *(const i32x4*)(Kl + (t * 32 + col) * G::KROW + kc * 32 + 16 * h);
-      const i32x16 zero = {0};
-      st[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qop[kc], kc == 0 ? zero : st[t], 0, 0, 0);
+      const i32x4 lo = *(const i32x4*)(row + 64 * kc);
+      const i32x4 hi = *(const i32x4*)(row + 64 * kc + 16);
+      const i32x8 kop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const f32x16 zero = {0};
+      st[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[kc], kc == 0 ? zero : st[t], 0, 0, 0,
+                                                               127, 0, 127);
     }
   }
 }
@@ -176,50 +203,43 @@ RA_DEV void qk_tiles(const uint8_t* Kl, const i32x4 (&qop)[Geo<D, KVB>::KC], i32
 // P^T operand, P V MFMAs.  TAIL: the group holds keys >= N.
 template <int D, int KVB, bool DBG, bool TAIL>
 RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
-                       const i32x16 (&st)[Geo<D, KVB>::NT], const float (&sk)[Geo<D, KVB>::NT], float sq,
+                       const f32x16 (&st)[Geo<D, KVB>::NT], const float (&ct)[Geo<D, KVB>::NT],
                        RowState<D / 32>& S, bool dbg_row, int dr) {
   using G = Geo<D, KVB>;
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
   const int N = (int)a.N;
   const int j0 = g * G::TG;
   const int nsteps = (N + KVB - 1) / KVB;
-  // score scale c = (sq sk) C0 of the spec, over 16 for the x16 integer products
-  float ct[G::NT];
-#pragma unroll
-  for (int t = 0; t < G::NT; ++t) ct[t] = ((sq * sk[t]) * a.C0) * 0.0625f;
   constexpr int NSTEP = KVB < 32 ? 2 : 1;
 #pragma unroll
   for (int sidx = 0; sidx < NSTEP; ++sidx) {
     const int step = (KVB < 32) ? g * 2 + sidx : g;
     if (step >= nsteps) break;
     const bool act = (KVB >= 32) || (h == sidx);
-    // ---- running maximum ---------------------------------------------------------
+    // ---- running maximum (max of the exact integer scores, then times c) -----------
     float mloc = -INFINITY;
 #pragma unroll
     for (int t = 0; t < G::NT; ++t) {
-      int im = INT32_MIN;
+      float im = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         bool ok = act;
         if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
-        im = max(im, ok ? st[t][v] : INT32_MIN);
+        im = fmaxf(im, ok ? st[t][v] : -INFINITY);
       }
-      if (im != INT32_MIN) {
-        const float tm = (float)im * ct[t];
-        mloc = fmaxf(mloc, tm);
-      }
+      if (im != -INFINITY) mloc = fmaxf(mloc, im * ct[t]);
     }
     const float mnew = fmaxf(S.m, pair_max(mloc));
     const float alpha = exp2_hw(S.m - mnew);
     if (DBG || __any(mnew > S.m)) {
-      if (!S.fresh) {
 #pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
+      for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) S.Of[db][v] = __builtin_fmaf((float)S.acc[db][v], S.sigma, S.Of[db][v]);
+        for (int v = 0; v < 16; ++v) {
+          S.Of[db][v] = __builtin_fmaf((float)S.acc[db][v], S.sigma, S.Of[db][v]);
+          S.acc[db][v] = 0;
         }
       }
-      S.fresh = true;
       if (g == 0 && sidx == 0) S.mref = mnew;
       if (__any(mnew - S.mref > 64.0f)) {
         // keep sigma far from overflow: move the frame to the current maximum
@@ -240,64 +260,66 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
     // ---- P levels, P^T operand, level sums, P V: one 32-key tile at a time --------
 #pragma unroll
     for (int t = 0; t < G::NT; ++t) {
-      uint32_t tt[16];
+      // fast path: level byte and margin from the hardware exp, packed four at a
+      // time into the P^T operand
+      i32x4 pb;
       u16x2 wmin = {0xFFFF, 0xFFFF};
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        bool ok = act;
-        if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
-        const float y = __builtin_fmaf((float)st[t][v], ct[t], nm);
-        float p = exp2_hw(y);
-        if (TAIL || KVB < 32) p = ok ? p : 0.f;
-        S.l += p;
-        tt[v] = __float_as_uint(p + kMagic);
-        wmin = __builtin_elementwise_min(wmin, __builtin_bit_cast(u16x2, tt[v]));
+      for (int w = 0; w < 4; ++w) {
+        uint32_t tt[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * w + e;
+          bool ok = act;
+          if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+          const float y = __builtin_fmaf(st[t][v], ct[t], nm);
+          float p = exp2_hw(y);
+          if (TAIL || KVB < 32) p = ok ? p : 0.f;
+          S.l += p;
+          tt[e] = __float_as_uint(p + kMagic);
+          wmin = __builtin_elementwise_min(wmin, __builtin_bit_cast(u16x2, tt[e]));
+        }
+        pb[w] = (int)pack_b2(tt[0], tt[1], tt[2], tt[3]);
       }
       if (__any((wmin.x <= 6) || guard)) {
         // A margin is too small somewhere in the wave (rare).  The hardware-exp
         // level r^ is within one of the exact level, which is fixed by the two
-        // thresholds around r^ (an LDS table with +inf above the last one).
+        // thresholds around r^ (an LDS table with +inf above the last one); the
+        // operand is rebuilt from the scores.
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float y = __builtin_fmaf((float)st[t][v], ct[t], nm);
-          const int rh = min((int)((tt[v] >> 16) & 0xFFu), 16);
-          const float lo = Tl[max(rh - 1, 0)], hi = Tl[rh];
-          int r = rh - ((rh > 0 && y < lo) ? 1 : 0) + ((y >= hi) ? 1 : 0);
-          if (TAIL || KVB < 32) {
-            bool ok = act;
-            if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
-            r = ok ? r : 0;
+        for (int w = 0; w < 4; ++w) {
+          uint32_t rr = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * w + e;
+            const float y = __builtin_fmaf(st[t][v], ct[t], nm);
+            const uint32_t tv = __float_as_uint(exp2_hw(y) + kMagic);
+            const int rh = min((int)((tv >> 16) & 0xFFu), 16);
+            const float lo = Tl[max(rh - 1, 0)], hi = Tl[rh];
+            int r = rh - ((rh > 0 && y < lo) ? 1 : 0) + ((y >= hi) ? 1 : 0);
+            if (TAIL || KVB < 32) {
+              bool ok = act;
+              if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+              r = ok ? r : 0;
+            }
+            rr |= (uint32_t)r << (8 * e);
           }
-          tt[v] = (tt[v] & 0xFF00FFFFu) | ((uint32_t)r << 16);
+          pb[w] = (int)rr;
         }
       }
-      i32x4 pb;
-      pb[0] = (int)pack_b2(tt[0], tt[2], tt[4], tt[6]);
-      pb[1] = (int)pack_b2(tt[1], tt[3], tt[5], tt[7]);
-      pb[2] = (int)pack_b2(tt[8], tt[10], tt[12], tt[14]);
-      pb[3] = (int)pack_b2(tt[9], tt[11], tt[13], tt[15]);
-      if (t == 0 && S.fresh) {
-        const i32x16 zero = {0};
+      const int vc = 2 * t + h;  // 16-key chunk of this lane half in the V^T rows
 #pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
-          const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + t * 32 + 16 * h);
-          S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, zero, 0, 0, 0);
-        }
-        S.fresh = false;
-      } else {
-#pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
-          const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + t * 32 + 16 * h);
-          S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, S.acc[db], 0, 0, 0);
-        }
+      for (int db = 0; db < G::NDB; ++db) {
+        const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + 16 * vc);
+        S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, S.acc[db], 0, 0, 0);
       }
       if (DBG && dbg_row && act) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = j0 + t * 32 + 16 * h + v;
           if (key < N) {
-            a.dbg_aqk[(int64_t)dr * N + key] = st[t][v] >> 4;
-            a.dbg_p[(int64_t)dr * N + key] = (int8_t)((int)((tt[v] >> 16) & 0xFFu) - 8);
+            a.dbg_aqk[(int64_t)dr * N + key] = (int32_t)st[t][v];
+            a.dbg_p[(int64_t)dr * N + key] = (int8_t)((int)((uint32_t)pb[v >> 2] >> (8 * (v & 3)) & 0xFFu) - 8);
           }
         }
       }
@@ -309,45 +331,47 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int d = db * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
-          a.dbg_apv[((int64_t)dr * nsteps + step) * D + d] = S.acc[db][v] >> 4;
+          a.dbg_apv[((int64_t)dr * nsteps + step) * D + d] = S.acc[db][v];
         }
       }
     }
   }
 }
 
-// One key group: Q K^T from LDS buffer g&1, widening of the prefetched K/V of
-// group g+1 into the other buffer, global loads of group g+2, softmax + P V,
-// one barrier.  MFMA/VALU overlap comes from the second wave on each SIMD.
+typedef const __attribute__((address_space(4))) float* kscale_ptr;  // read-only: scalar loads
+
+// One key group: the K scales of its 16-key units (scalar loads, so they never
+// wait behind the copies in flight), Q K^T from ring slot g % 4, softmax + P V;
+// then the copy of group g+3 into the slot group g-1 used, a wait until this
+// wave's copy of group g+1 has landed (g+2 and g+3 stay in flight), and one
+// barrier, which also covers the other waves' copies.
 template <int D, int KVB, bool DBG, bool TAIL>
-RA_DEV void group_iter(const Ctx& a, int g, int ngroups, uint8_t* lds, u32x2 (&rk)[Geo<D, KVB>::KUT],
-                       u32x2 (&rv)[Geo<D, KVB>::VUT], float& rs, const i32x4 (&qop)[Geo<D, KVB>::KC],
-                       float sq, int bh, RowState<D / 32>& S, bool dbg_row, int dr) {
+RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngroups, uint8_t* lds,
+                       const i32x8 (&qop)[Geo<D, KVB>::KC], float sq, int bh, RowState<D / 32>& S, bool dbg_row,
+                       int dr) {
   using G = Geo<D, KVB>;
-  const bool odd = g & 1;
-  uint8_t* const kb_cur = lds + (odd ? G::KBUF : 0);
-  uint8_t* const kb_nxt = lds + (odd ? 0 : G::KBUF);
-  uint8_t* const vb_cur = lds + 2 * G::KBUF + (odd ? G::VBUF : 0);
-  uint8_t* const vb_nxt = lds + 2 * G::KBUF + (odd ? 0 : G::VBUF);
-  float* const sb_cur = (float*)(lds + G::SOFF) + (odd ? G::SKN : 0);
-  float* const sb_nxt = (float*)(lds + G::SOFF) + (odd ? 0 : G::SKN);
-  i32x16 st[G::NT];
-  qk_tiles<D, KVB>(kb_cur, qop, st);
-  if (g + 1 < ngroups) {
-    store_k<D, KVB>(kb_nxt, rk);
-    store_v<D, KVB>(vb_nxt, rv);
-    if (threadIdx.x < G::SKN) sb_nxt[threadIdx.x] = rs;
-  }
-  if (g + 2 < ngroups) {
-    load_k<D, KVB>(a, bh, g + 2, rk);
-    load_v<D, KVB>(a, bh, g + 2, rv);
-    load_ks<D, KVB>(a, bh, g + 2, rs);
-  }
-  float sk[G::NT];
   const int h = (threadIdx.x >> 5) & 1;
+  const kscale_ptr ksh = (kscale_ptr)a.ks + (int64_t)bh * (a.Np >> a.qk_shift);
+  float sk[G::NT];
 #pragma unroll
-  for (int t = 0; t < G::NT; ++t) sk[t] = sb_cur[2 * t + h];
-  softmax_pv<D, KVB, DBG, TAIL>(a, g, vb_cur, (const float*)(lds + G::LDS), st, sk, sq, S, dbg_row, dr);
+  for (int t = 0; t < G::NT; ++t) {
+    const int k0 = g * G::TG + 32 * t;
+    const float s0 = ksh[k0 >> a.qk_shift], s1 = ksh[(k0 + 16) >> a.qk_shift];
+    sk[t] = h ? s1 : s0;
+  }
+  uint8_t* const cur = lds + (g % kBufs) * G::IMG;
+  f32x16 st[G::NT];
+  qk_tiles<D, KVB>(cur, qop, st);
+  float ct[G::NT];
+#pragma unroll
+  for (int t = 0; t < G::NT; ++t) ct[t] = (sq * sk[t]) * a.C0;
+  softmax_pv<D, KVB, DBG, TAIL>(a, g, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct, S, dbg_row, dr);
+  if (!TAIL) {
+    if (g + 3 < ngroups) dma_group<D, KVB>(rsrc, g + 3, lds + ((g + 3) % kBufs) * G::IMG);
+    if (DBG || g + 2 >= ngroups) wait_vm<0>();
+    else if (g + 3 >= ngroups) wait_vm<G::NDMA>();
+    else wait_vm<2 * G::NDMA>();
+  }
   __syncthreads();
 }
 
@@ -368,24 +392,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hidx = L / args.nqt, qt = L % args.nqt;
   const int bh = args.heads[hidx];
   Ctx a;
-  a.kc = args.kc; a.vc = args.vc; a.ks = args.ks; a.Np = args.Np;
+  a.img = args.img; a.ks = args.ks; a.Np = args.Np;
   a.N = (int)args.N; a.qk_shift = __builtin_ctz(args.qk_blk); a.C0 = args.C0; a.L15 = args.L15;
   a.dbg_row0 = args.dbg_row0; a.dbg_n = args.dbg_n;
   a.dbg_aqk = args.dbg_aqk; a.dbg_p = args.dbg_p; a.dbg_apv = args.dbg_apv;
   const int N = a.N;
   const int qi = qt * kBM + w * 32 + col;
+  const int ngroups = (N + G::TG - 1) / G::TG;
 
-  // ---- Q operand (signed int8) ------------------------------------------------
-  i32x4 qop[G::KC];
+  // ---- prologue: groups 0, 1, 2 in flight ------------------------------------------
+  const int64_t ngp = a.Np / G::TG;
+  const int64_t head0 = (int64_t)bh * ngp * G::IMG;
+  const int64_t avail = args.img_bytes - head0;  // the resource never reaches past the workspace
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.img + head0), (short)0, (int)(avail < ngp * G::IMG ? (avail > 0 ? avail : 0) : ngp * G::IMG),
+      0x00020000);
+  dma_group<D, KVB>(rsrc, 0, lds);
+  if (ngroups > 1) dma_group<D, KVB>(rsrc, 1, lds + G::IMG);
+  if (ngroups > 2) dma_group<D, KVB>(rsrc, 2, lds + 2 * G::IMG);
+
+  // ---- Q operand: fp8 e4m3 bytes of the lane's 32 channels per 64-deep chunk -------
+  i32x8 qop[G::KC];
   {
-    const u32x2* qp = (const u32x2*)(args.qc + ((int64_t)bh * a.Np + qi) * (D / 2));
+    const u32x4* qp = (const u32x4*)(args.qc + ((int64_t)bh * a.Np + qi) * (D / 2));
 #pragma unroll
     for (int kc = 0; kc < G::KC; ++kc) {
-      const u32x2 x = qp[kc * 2 + h];
-      uint32_t lo0, hi0, lo1, hi1;
-      widen_signed(x.x, lo0, hi0);
-      widen_signed(x.y, lo1, hi1);
-      qop[kc] = i32x4{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
+      const u32x4 x = qp[2 * kc + h];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t wd = x[q >> 1];
+        const int e0 = 4 * (q & 1);
+        qop[kc][q] = (int)(fp8_pair(nib(wd, e0), nib(wd, e0 + 1)) | (fp8_pair(nib(wd, e0 + 2), nib(wd, e0 + 3)) << 16));
+      }
     }
   }
   const float sq = args.qs[(int64_t)bh * (a.Np >> a.qk_shift) + (qi >> a.qk_shift)];
@@ -395,7 +433,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   S.l = 0.f;
   S.mref = 0.f;
   S.sigma = 1.f;
-  S.fresh = true;
 #pragma unroll
   for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
@@ -403,28 +440,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const bool dbg_row = DBG && qi >= a.dbg_row0 && qi < a.dbg_row0 + a.dbg_n && qi < N;
   const int dr = qi - a.dbg_row0;
-  const int ngroups = (N + G::TG - 1) / G::TG;
 
-  if (tid < 17) ((float*)(lds + G::LDS))[tid] = tid < 15 ? args.T[tid] : INFINITY;
-
-  // ---- prologue: group 0 in LDS, group 1 in flight -------------------------------
-  u32x2 rk[G::KUT], rv[G::VUT];
-  float rs = 0.f;
-  load_ks<D, KVB>(a, bh, 0, rs);
-  load_k<D, KVB>(a, bh, 0, rk);
-  load_v<D, KVB>(a, bh, 0, rv);
-  store_k<D, KVB>(lds, rk);
-  store_v<D, KVB>(lds + 2 * G::KBUF, rv);
-  if (tid < G::SKN) ((float*)(lds + G::SOFF))[tid] = rs;
-  if (ngroups > 1) {
-    load_k<D, KVB>(a, bh, 1, rk);
-    load_v<D, KVB>(a, bh, 1, rv);
-    load_ks<D, KVB>(a, bh, 1, rs);
-  }
+  wait_vm<0>();  // groups 0..2 and the Q operand
   __syncthreads();
   for (int g = 0; g + 1 < ngroups; ++g)
-    group_iter<D, KVB, DBG, false>(a, g, ngroups, lds, rk, rv, rs, qop, sq, bh, S, dbg_row, dr);
-  group_iter<D, KVB, DBG, true>(a, ngroups - 1, ngroups, lds, rk, rv, rs, qop, sq, bh, S, dbg_row, dr);
+    group_iter<D, KVB, DBG, false>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+  group_iter<D, KVB, DBG, true>(a, rsrc, ngroups - 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
 
   // ---- epilogue ---------------------------------------------------------------------
   const float lq = pair_sum(S.l);
@@ -434,7 +455,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     args.dbg_l[dr] = lq;
   }
   if (qi < N) {
-    const float inv = 0.0625f / lq;  // also divides out the x16 of the V bytes
+    const float inv = 1.0f / lq;
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
@@ -464,35 +485,61 @@ hipError_t launch_t(const AttnArgs& a, bool dbg, hipStream_t st) {
   using G = Geo<D, KVB>;
   static const hipError_t attr = [] {
     hipError_t e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS + 128);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS + 128);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     return e;
   }();
   if (attr != hipSuccess) return attr;
+  k2_stage<D, KVB><<<dim3((unsigned)(a.Np / G::TG), (unsigned)a.nheads), 256, 0, st>>>(a);
   if (dbg) {
     const int first = a.dbg_row0 / kBM, last = (a.dbg_row0 + a.dbg_n - 1) / kBM;
-    k2_attention<D, KVB, true><<<last - first + 1, 256, G::LDS + 128, st>>>(a);
+    k2_attention<D, KVB, true><<<last - first + 1, 256, G::LDS, st>>>(a);
   } else {
-    k2_attention<D, KVB, false><<<8 * a.per_xcd, 256, G::LDS + 128, st>>>(a);
+    k2_attention<D, KVB, false><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
   }
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_kv(const AttnArgs& a, int kv, bool dbg, hipStream_t st) {
-  switch (kv) {
-    case 16: return launch_t<D, 16>(a, dbg, st);
-    case 32: return launch_t<D, 32>(a, dbg, st);
-    case 64: return launch_t<D, 64>(a, dbg, st);
-    default: return launch_t<D, 128>(a, dbg, st);
+template <int D, int KVB>
+size_t ws_bytes(int64_t BH, int64_t Np) {
+  using G = Geo<D, KVB>;
+  return (size_t)BH * (size_t)(Np / G::TG) * (size_t)G::IMG;
+}
+
+size_t attention_workspace_bytes(int D, int kv_blk, int64_t BH, int64_t Np) {
+  if (D == 128) {
+    switch (kv_blk) {
+      case 16: return ws_bytes<128, 16>(BH, Np);
+      case 32: return ws_bytes<128, 32>(BH, Np);
+      case 64: return ws_bytes<128, 64>(BH, Np);
+      default: return ws_bytes<128, 128>(BH, Np);
+    }
+  }
+  switch (kv_blk) {
+    case 16: return ws_bytes<64, 16>(BH, Np);
+    case 32: return ws_bytes<64, 32>(BH, Np);
+    case 64: return ws_bytes<64, 64>(BH, Np);
+    default: return ws_bytes<64, 128>(BH, Np);
   }
 }
 
 hipError_t launch_attention(const AttnArgs& a, int D, int kv_blk, bool dbg, hipStream_t st) {
-  if (D == 128) return launch_kv<128>(a, kv_blk, dbg, st);
-  return launch_kv<64>(a, kv_blk, dbg, st);
+  if (D == 128) {
+    switch (kv_blk) {
+      case 16: return launch_t<128, 16>(a, dbg, st);
+      case 32: return launch_t<128, 32>(a, dbg, st);
+      case 64: return launch_t<128, 64>(a, dbg, st);
+      default: return launch_t<128, 128>(a, dbg, st);
+    }
+  }
+  switch (kv_blk) {
+    case 16: return launch_t<64, 16>(a, dbg, st);
+    case 32: return launch_t<64, 32>(a, dbg, st);
+    case 64: return launch_t<64, 64>(a, dbg, st);
+    default: return launch_t<64, 128>(a, dbg, st);
+  }
 }
 
 }  // namespace ra

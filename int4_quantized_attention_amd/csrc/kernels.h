@@ -40,6 +40,8 @@ struct AttnArgs {
   const float* ks;
   const uint8_t* vc;
   const float* vs;
+  uint8_t* img;   // workspace: per-group LDS images of K (fp8) and V^T (int8)
+  int64_t img_bytes;  // its size (images that would not fit are neither written nor read)
   void* out;
   int out_f16;
   int64_t N, Np;
@@ -78,6 +80,9 @@ struct FbArgs {
 
 hipError_t launch_quantize(const QuantArgs& a, int dtype, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int D, int kv_blk, bool dbg, hipStream_t st);
+// bytes of the attention workspace: the per-group LDS images of every head (the
+// image geometry lives with the kernel; D, kv_blk as validated by the API)
+size_t attention_workspace_bytes(int D, int kv_blk, int64_t BH, int64_t Np);
 hipError_t launch_fallback_prep(const FbArgs& a, hipStream_t st);
 hipError_t launch_fallback(const FbArgs& a, hipStream_t st);
 

@@ -54,7 +54,9 @@ _SIGS = {
     "rotattn_quantize_qk_workspace": (_SZ, [_VP]),
     "rotattn_quantize_qk": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
                                    _VP, _VP, _VP, _SZ, _VP]),
-    "rotattn_int4_attention": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP]),
+    "rotattn_int4_attention_workspace": (_SZ, [_VP]),
+    "rotattn_int4_attention": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _SZ,
+                                      _VP]),
     "rotattn_fp16_fallback_workspace": (_SZ, [_VP]),
     "rotattn_fp16_fallback": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ, _VP]),
     "rotattn_status_str": (ctypes.c_char_p, [_I32]),
@@ -123,6 +125,10 @@ def rotattn_quantize_qk_workspace(shape: Shape) -> int:
     return int(lib().rotattn_quantize_qk_workspace(ctypes.byref(shape)))
 
 
+def rotattn_int4_attention_workspace(shape: Shape) -> int:
+    return int(lib().rotattn_int4_attention_workspace(ctypes.byref(shape)))
+
+
 def rotattn_fp16_fallback_workspace(shape: Shape) -> int:
     return int(lib().rotattn_fp16_fallback_workspace(ctypes.byref(shape)))
 
@@ -141,6 +147,7 @@ def alloc_codes(shape: Shape, device="cuda", colsum: bool = True) -> dict:
              v_scale=torch.empty((B, H, D), dtype=f32, device=device),
              v_colsum=torch.empty((B, H, nkb, D), dtype=torch.int32, device=device) if colsum else None)
     z["workspace"] = torch.empty(rotattn_quantize_qk_workspace(shape), dtype=torch.uint8, device=device)
+    z["attn_workspace"] = torch.empty(rotattn_int4_attention_workspace(shape), dtype=torch.uint8, device=device)
     return z
 
 
@@ -159,12 +166,14 @@ def rotattn_quantize_qk(shape: Shape, rot: int, q: torch.Tensor, k: torch.Tensor
 
 
 def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Optional[Sequence[int]] = None,
-                           debug: Optional[dict] = None) -> torch.Tensor:
+                           debug: Optional[dict] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out: device [B,H,N,D] float32 or float16.  debug: dict(bh, row0, n_rows) ->
-    filled with device tensors a_qk, p_codes, a_pv, m, l."""
+    filled with device tensors a_qk, p_codes, a_pv, m, l.  workspace: device uint8
+    tensor of rotattn_int4_attention_workspace(shape) bytes (default z["attn_workspace"])."""
     if out.dtype not in (torch.float32, torch.float16):
         raise RotattnError("out must be float32 or float16")
     harr, nh = _heads(heads)
+    ws = workspace if workspace is not None else z["attn_workspace"]
     dbg = None
     if debug is not None:
         n, N = int(debug["n_rows"]), shape.N
@@ -181,7 +190,8 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
     _check(lib().rotattn_int4_attention(
         ctypes.byref(shape), _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
         _ptr(z["v_codes"]), _ptr(z["v_scale"]), harr, nh, F16 if out.dtype == torch.float16 else F32,
-        _ptr(out), ctypes.byref(dbg) if dbg is not None else None, _stream()), "rotattn_int4_attention")
+        _ptr(out), ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(), _stream()),
+        "rotattn_int4_attention")
     return out
 
 

@@ -58,6 +58,10 @@ def test_padded_tokens_and_workspace(L):
     assert ra.rotattn_padded_tokens(s) == 75776
     assert ra.rotattn_quantize_qk_workspace(s) > 0
     assert ra.rotattn_fp16_fallback_workspace(s) >= 3 * 40 * 75776 * 128 * 2
+    # one LDS image per 64-key group: K rows of D+16 bytes, V^T rows of 64+16 bytes,
+    # a 128-byte table, rounded up to 4 KiB
+    img = -(-(64 * (128 + 16) + 128 * (64 + 16) + 128) // 4096) * 4096
+    assert ra.rotattn_int4_attention_workspace(s) == 40 * (75776 // 64) * img
 
 
 def test_null_and_bad_args_return_before_launch(L):
@@ -66,16 +70,24 @@ def test_null_and_bad_args_return_before_launch(L):
     st = L.rotattn_quantize_qk(ctypes.byref(s), 1, 0, nul, nul, nul, nul, 1, nul, nul, nul, nul, nul,
                                nul, nul, nul, 0, nul)
     assert st == 1
-    st = L.rotattn_int4_attention(ctypes.byref(s), nul, nul, nul, nul, nul, nul, nul, 0, 0, nul, nul, nul)
+    st = L.rotattn_int4_attention(ctypes.byref(s), nul, nul, nul, nul, nul, nul, nul, 0, 0, nul, nul, nul, 0,
+                                  nul)
     assert st == 1
     fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
     bad_heads = (ctypes.c_int32 * 1)(5)  # B*H = 2
+    big = 1 << 40
     st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, bad_heads, 1, 0,
-                                  fake, nul, nul)
+                                  fake, nul, fake, big, nul)
     assert st == 6
     st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 2,
-                                  fake, nul, nul)
+                                  fake, nul, fake, big, nul)
     assert st == 6  # bf16 output is not offered
+    st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 0,
+                                  fake, nul, fake, 64, nul)
+    assert st == 4  # attention workspace too small
+    st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 0,
+                                  fake, nul, ctypes.c_void_p(24), big, nul)
+    assert st == 4  # attention workspace not 16-byte aligned
     st = L.rotattn_quantize_qk(ctypes.byref(s), 1, 0, fake, fake, fake, fake, 1, fake, fake, fake, fake,
                                fake, fake, nul, fake, 16, nul)
     assert st == 4  # workspace too small
