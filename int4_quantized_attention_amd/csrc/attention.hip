@@ -372,7 +372,7 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
     else if (g + 3 >= ngroups) wait_vm<G::NDMA>();
     else wait_vm<2 * G::NDMA>();
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 template <int D, int KVB, bool DBG>
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int dr = qi - a.dbg_row0;
 
   wait_vm<0>();  // groups 0..2 and the Q operand
-  __syncthreads();
+  lds_barrier();
   for (int g = 0; g + 1 < ngroups; ++g)
     group_iter<D, KVB, DBG, false>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
   group_iter<D, KVB, DBG, true>(a, rsrc, ngroups - 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);

@@ -61,6 +61,19 @@ RA_DEV float wave_max(float v, int width) {
 
 RA_DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier that orders LDS only: this wave's LDS operations complete
+// (lgkmcnt(0)), then s_barrier.  __syncthreads() also waits for every vector
+// memory operation in flight (vmcnt(0)), which would drain the global loads a
+// pipelined loop issues ahead of time; the kernels that use this barrier wait
+// for the loads they need explicitly.  The scheduling fences keep the compiler
+// from moving memory operations across it.
+RA_DEV void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // max / sum of a value and the one held by lane l ^ 32 (v_permlane32_swap, no LDS)
 RA_DEV float pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

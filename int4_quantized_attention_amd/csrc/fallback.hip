@@ -193,7 +193,7 @@ RA_DEV void fb_group(const FbCtx& a, int g, int ngroups, _Float16* lds, i32x4 (&
       }
     }
   }
-  __syncthreads();
+  lds_barrier();  // the loads of group g+2 stay in flight
 }
 
 template <int D>
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   fb_load<D>(a, bh, 0, rk, rv);
   fb_store<D>(flds, flds + 2 * G::KBUF, rk, rv);
   if (ngroups > 1) fb_load<D>(a, bh, 1, rk, rv);
-  __syncthreads();
+  lds_barrier();
   for (int g = 0; g + 1 < ngroups; ++g) fb_group<D, false>(a, g, ngroups, flds, rk, rv, qop, bh, O, m, l);
   fb_group<D, true>(a, ngroups - 1, ngroups, flds, rk, rv, qop, bh, O, m, l);
 
