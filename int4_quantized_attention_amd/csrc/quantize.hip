@@ -5,10 +5,12 @@
 // D = Df + Dh + Dw; Interleaved rotation fused into the RoPE 2x2 blocks; Half
 // rotation Q Pi R pairing channel i with i + Dj/2 inside each segment).
 //
-// Memory-bound.  Every launch stages a 128-token tile of the input in LDS (one
-// coalesced 16-byte global load per 8 elements), computes the rotated values in
-// registers and writes packed nibbles with 16-byte stores.  K and V need global
-// statistics (the channel mean of K, the channel amax of V), so they are read twice.
+// Memory-bound.  Q and K: a thread owns a slice of consecutive channels of one
+// token, loads it with 16-byte loads, applies RoPE once per channel pair (one table
+// load per pair), exchanges RoPE outputs through LDS only for the Half rotation,
+// and writes packed nibbles with 8/16-byte stores.  V is staged through LDS and
+// written transposed.  K and V need global statistics (the channel mean of K, the
+// channel amax of V), so they are read twice.
 #include "common.h"
 #include "kernels.h"
 #include "rope.h"
@@ -17,42 +19,37 @@ namespace ra {
 
 // ---------------------------------------------------------------------------------
 // K statistics: ordered binary64 partial sums of rotated K over 64-token blocks.
-// grid (ceil(N/64), B*H); 256 threads.  partial [B*H][nblk][D] f64.
-template <int D, int DT>
+// grid (ceil(N/64), B*H); 256 threads, four per token, each owning D/4 channels.
+// partial [B*H][nblk][D] f64.
+template <int D, int DT, int ROT>
 __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
-  extern __shared__ __align__(16) char lds[];
+  constexpr int TPT = 4, CPT = D / TPT;
+  __shared__ float R[kMeanTile * (D + 1)];  // RoPE outputs (Half), then rotated rows
   const Shape s = a.s;
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int bh = blockIdx.y, blk = blockIdx.x;
   const int64_t n0 = (int64_t)blk * kMeanTile;
+  const int lt = threadIdx.x / TPT, c0 = (threadIdx.x % TPT) * CPT;
+  const int64_t n = n0 + lt;
   const void* base = (const char*)a.k + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
-  stage_tile<D, DT>(base, n0, N, kMeanTile, lds);
-  __syncthreads();
-  // rotated values into a float tile after the input tile
-  const size_t in_bytes = (size_t)kMeanTile * (DT == 0 ? (D + 1) * 4 : (D + 2) * 2);
-  float* rot = (float*)(lds + ((in_bytes + 15) & ~(size_t)15));
-  for (int e = threadIdx.x; e < kMeanTile * D; e += blockDim.x) {
-    const int r = e / D, c = e % D;
-    float val = 0.f;
-    if (n0 + r < N) {
-      int f, y, x;
-      token_pos(n0 + r, s, f, y, x);
-      val = rope_rot<D, DT>(lds, r, c, s, a.rot, a.table, f, y, x);
-    }
-    rot[r * (D + 1) + c] = val;
-  }
+  float x[CPT];
+  rotated_slice<DT, ROT, CPT>(base, n, n < N, D, c0, s, a.table, R + lt * (D + 1), x);
+  if (ROT == 2) __syncthreads();  // every row of R read before it is overwritten
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) R[lt * (D + 1) + c0 + i] = x[i];
   __syncthreads();
   if (threadIdx.x < D) {
     const int c = threadIdx.x;
     double part = 0.0;
     const int cnt = (int)min((int64_t)kMeanTile, N - n0);
-    for (int r = 0; r < cnt; ++r) part += (double)rot[r * (D + 1) + c];
+    for (int r = 0; r < cnt; ++r) part += (double)R[r * (D + 1) + c];
     const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
     a.kpart[((int64_t)bh * nblk + blk) * D + c] = part;
   }
 }
 
 // Channel mean of K: binary64 sum of the partials in block order, / N, to binary32.
+// The sum is one dependent chain; the loads run eight ahead of it.
 __global__ void k1_kmean(QuantArgs a) {
   const int D = a.s.D;
   const int64_t N = (int64_t)a.s.F * a.s.Hs * a.s.Ws;
@@ -60,8 +57,17 @@ __global__ void k1_kmean(QuantArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)a.s.B * a.s.H * D) return;
   const int64_t bh = idx / D, c = idx % D;
+  const double* p = a.kpart + bh * nblk * D + c;
   double total = 0.0;
-  for (int64_t b = 0; b < nblk; ++b) total += a.kpart[(bh * nblk + b) * D + c];
+  int64_t b = 0;
+  for (; b + 8 <= nblk; b += 8) {
+    double v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[(b + i) * D];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) total += v[i];
+  }
+  for (; b < nblk; ++b) total += p[b * D];
   a.kmu[idx] = (float)(total / (double)N);
 }
 
@@ -95,56 +101,47 @@ __global__ __launch_bounds__(256) void k1_vamax(QuantArgs a) {
   }
 }
 
-// Q / K quantisation: grid (Np/128, B*H, 2 (0 = Q, 1 = K)); 256 threads, two
-// threads per token, each owning D/2 consecutive output channels.
-template <int D, int DT>
+// Q / K quantisation: grid (Np/TOK, B*H, 2 (0 = Q, 1 = K)); 256 threads, TPT per
+// token (TOK = 256/TPT tokens per workgroup, a multiple of qk_blk), each owning
+// CPT = D/TPT consecutive channels.
+template <int D, int DT, int ROT, int TPT>
 __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
-  extern __shared__ __align__(16) char lds[];
+  constexpr int TOK = 256 / TPT, CPT = D / TPT;
+  extern __shared__ float U[];  // ROT 2: [TOK][D+1] RoPE outputs
   __shared__ float wred[4];
   const Shape s = a.s;
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int64_t Np = a.Np;
   const int bh = blockIdx.y;
   const bool isK = blockIdx.z == 1;
-  const int64_t n0 = (int64_t)blockIdx.x * kTile;
+  const int64_t n0 = (int64_t)blockIdx.x * TOK;
   const void* src = isK ? a.k : a.q;
   const void* base = (const char*)src + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
-  stage_tile<D, DT>(base, n0, N, kTile, lds);
-  __syncthreads();
-
-  constexpr int CPT = D / 2;
-  const int lt = threadIdx.x >> 1, part = threadIdx.x & 1;
+  const int lt = threadIdx.x / TPT, part = threadIdx.x % TPT, c0 = part * CPT;
   const int64_t n = n0 + lt;
   const bool valid = n < N;
-  int f, y, x;
-  token_pos(n, s, f, y, x);
   float v[CPT];
-  if (valid) {
-    // padding tokens (n >= N) have no grid position: never index the table for them
+  rotated_slice<DT, ROT, CPT>(base, n, valid, D, c0, s, a.table, U + lt * (D + 1), v);
+  if (isK && a.smooth && valid) {
+    const f32x4* mu = (const f32x4*)(a.kmu + (int64_t)bh * D + c0);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = part * CPT + i;
-      float t = rope_rot<D, DT>(lds, lt, c, s, a.rot, a.table, f, y, x);
-      if (isK && a.smooth) t = t - a.kmu[(int64_t)bh * D + c];
-      v[i] = t;
+    for (int i = 0; i < CPT / 4; ++i) {
+      const f32x4 m4 = mu[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = v[4 * i + e] - m4[e];
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) v[i] = 0.f;
   }
   float am = 0.f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) am = fmaxf(am, fabsf(v[i]));
-  // reduce over the 2*qk_blk threads of one scale block
-  const int grp = 2 * s.qk_blk;
-  if (grp <= 64) {
-    am = wave_max(am, grp);
-  } else {
-    am = wave_max(am, 64);
+  // reduce over the TPT * qk_blk threads of one scale block (at least one wave)
+  am = wave_max(am, 64);
+  const int grp = TPT * s.qk_blk;
+  if (grp > 64) {
     const int wid = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) wred[wid] = am;
     __syncthreads();
-    const int wpg = grp / 64;  // waves per group
+    const int wpg = grp / 64;  // waves per block
     const int g0 = (wid / wpg) * wpg;
     am = wred[g0];
     for (int k = 1; k < wpg; ++k) am = fmaxf(am, wred[g0 + k]);
@@ -161,10 +158,14 @@ __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
     }
     packed[w] = word;
   }
-  uint8_t* codes = isK ? a.kc : a.qc;
-  uint4* dst = (uint4*)(codes + ((int64_t)bh * Np + n) * (D / 2) + part * (CPT / 2));
+  uint8_t* codes = (isK ? a.kc : a.qc) + ((int64_t)bh * Np + n) * (D / 2) + c0 / 2;
+  if (CPT / 8 == 2) {
+    *(u32x2*)codes = u32x2{packed[0], packed[CPT / 8 - 1]};
+  } else {
 #pragma unroll
-  for (int w = 0; w < CPT / 8; w += 4) dst[w / 4] = make_uint4(packed[w], packed[w + 1], packed[w + 2], packed[w + 3]);
+    for (int w = 0; w < CPT / 8; w += 4)
+      *(u32x4*)(codes + 4 * w) = u32x4{packed[w], packed[w + 1], packed[w + 2], packed[w + 3]};
+  }
   if (part == 0 && (lt % s.qk_blk) == 0) {
     float* sc = isK ? a.ks : a.qs;
     sc[(int64_t)bh * (Np / s.qk_blk) + n / s.qk_blk] = am == 0.f ? 0.f : am / 7.0f;
@@ -249,37 +250,50 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
-template <int D, int DT>
-hipError_t launch_quantize_t(const QuantArgs& a, hipStream_t st) {
+template <int D, int DT, int ROT, int TPT>
+hipError_t launch_qk(const QuantArgs& a, hipStream_t st) {
+  constexpr int TOK = 256 / TPT;
+  const size_t lds = ROT == 2 ? (size_t)TOK * (D + 1) * 4 : 0;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k1_quant_qk<D, DT, ROT, TPT>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  k1_quant_qk<D, DT, ROT, TPT><<<dim3((unsigned)(a.Np / TOK), (unsigned)(a.s.B * a.s.H), 2), 256, lds, st>>>(a);
+  return hipSuccess;
+}
+
+template <int D, int DT, int ROT>
+hipError_t launch_rot(const QuantArgs& a, hipStream_t st) {
   const int64_t N = (int64_t)a.s.F * a.s.Hs * a.s.Ws;
   const int BH = a.s.B * a.s.H;
+  if (a.smooth) {
+    const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
+    const int64_t nmu = (int64_t)BH * D;
+    k1_kstats<D, DT, ROT><<<dim3((unsigned)nblk, BH), 256, 0, st>>>(a);
+    k1_kmean<<<(unsigned)((nmu + 255) / 256), 256, 0, st>>>(a);
+  }
+  // a workgroup covers whole scale blocks: 64 tokens (four threads each) unless
+  // qk_blk is 128 (then 128 tokens, two threads each)
+  return a.s.qk_blk > 64 ? launch_qk<D, DT, ROT, 2>(a, st) : launch_qk<D, DT, ROT, 4>(a, st);
+}
+
+template <int D, int DT>
+hipError_t launch_quantize_t(const QuantArgs& a, hipStream_t st) {
+  const int BH = a.s.B * a.s.H;
   const size_t in_tile = (size_t)kTile * (DT == 0 ? (D + 1) * 4 : (D + 2) * 2);
-  const size_t mean_in = (size_t)kMeanTile * (DT == 0 ? (D + 1) * 4 : (D + 2) * 2);
-  const size_t mean_lds = ((mean_in + 15) & ~(size_t)15) + (size_t)kMeanTile * (D + 1) * 4;
   const int64_t nvamax = (int64_t)BH * D;
   if (DT == 0) {
     // fp32 tiles exceed the default 64 KiB of dynamic LDS; gfx950 has 160 KiB
-    static const hipError_t attr = [&] {
-      hipError_t e = hipFuncSetAttribute((const void*)k1_quant_qk<D, DT>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)in_tile);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void*)k1_quant_v<D, DT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)in_tile);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void*)k1_kstats<D, DT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)mean_lds);
-      return e;
-    }();
+    static const hipError_t attr = hipFuncSetAttribute((const void*)k1_quant_v<D, DT>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)in_tile);
     if (attr != hipSuccess) return attr;
   }
   k1_zero_u32<<<(unsigned)((nvamax + 255) / 256), 256, 0, st>>>(a.vamax, nvamax);
   k1_vamax<D, DT><<<dim3((unsigned)(a.Np / kTile), BH), 256, 0, st>>>(a);
-  if (a.smooth) {
-    const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
-    k1_kstats<D, DT><<<dim3((unsigned)nblk, BH), 256, mean_lds, st>>>(a);
-    k1_kmean<<<(unsigned)((nvamax + 255) / 256), 256, 0, st>>>(a);
-  }
-  k1_quant_qk<D, DT><<<dim3((unsigned)(a.Np / kTile), BH, 2), 256, in_tile, st>>>(a);
+  hipError_t e;
+  if (a.rot == 1) e = launch_rot<D, DT, 1>(a, st);
+  else if (a.rot == 2) e = launch_rot<D, DT, 2>(a, st);
+  else e = launch_rot<D, DT, 0>(a, st);
+  if (e != hipSuccess) return e;
   k1_quant_v<D, DT><<<dim3((unsigned)(a.Np / kTile), BH), 256, in_tile, st>>>(a);
   return hipGetLastError();
 }

@@ -100,6 +100,123 @@ RA_DEV void token_pos(int64_t n, const Shape& s, int& f, int& y, int& x) {
   x = (int)(n % s.Ws);
 }
 
+// ---- per-thread token slices --------------------------------------------------------
+// A thread owns CPT consecutive channels [c0, c0 + CPT) of one token (c0 a multiple
+// of CPT, CPT a multiple of 8): it loads them with 16-byte loads, applies RoPE pair by
+// pair with one table load per pair, and for the Half rotation exchanges the RoPE
+// outputs through an LDS row to pair channel i with i + Dj/2.
+
+template <int DT, int CPT>
+RA_DEV void load_slice(const void* base, int64_t n, int D, int c0, float (&x)[CPT]) {
+  if (DT == 0) {
+    const f32x4* p = (const f32x4*)((const float*)base + n * D + c0);
+#pragma unroll
+    for (int i = 0; i < CPT / 4; ++i) {
+      const f32x4 v = p[i];
+      x[4 * i] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
+    }
+  } else {
+    const u32x4* p = (const u32x4*)((const uint16_t*)base + n * D + c0);
+#pragma unroll
+    for (int i = 0; i < CPT / 8; ++i) {
+      const u32x4 w = p[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = w[e];
+        if (DT == 1) {
+          x[8 * i + 2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+          x[8 * i + 2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+        } else {
+          x[8 * i + 2 * e] = __uint_as_float(u << 16);
+          x[8 * i + 2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
+        }
+      }
+    }
+  }
+}
+
+// Offsets (in floats) of a token's rows in the three axis tables, and the first
+// global pair index of the height and width segments.
+struct SegRows {
+  int base0, base1, base2, p1, p2;
+};
+RA_DEV SegRows seg_rows(const Shape& s, int f, int y, int x) {
+  SegRows g;
+  g.base0 = f * s.Df;
+  g.base1 = s.F * s.Df + y * s.Dh;
+  g.base2 = s.F * s.Df + s.Hs * s.Dh + x * s.Dw;
+  g.p1 = s.Df / 2;
+  g.p2 = (s.Df + s.Dh) / 2;
+  return g;
+}
+
+// RoPE in place on the slice: pair k is global pair p = c0/2 + k.  ROT 1 uses the
+// fused Interleaved table (alpha, beta); otherwise the plain (cos, sin) table.
+//   plain: u0 = fma(a, c, -(b*s)), u1 = fma(a, s, b*c)
+//   fused: o0 = fma(a, al, b*be),  o1 = fma(a, be, -(b*al))
+template <int ROT, int CPT>
+RA_DEV void rope_slice(float (&x)[CPT], int c0, const float* tab, const SegRows& g) {
+#pragma unroll
+  for (int k = 0; k < CPT / 2; ++k) {
+    const int p = c0 / 2 + k;
+    const int off = p < g.p1 ? g.base0 + 2 * p : (p < g.p2 ? g.base1 + 2 * (p - g.p1) : g.base2 + 2 * (p - g.p2));
+    const f32x2 t = *(const f32x2*)(tab + off);
+    const float a = x[2 * k], b = x[2 * k + 1];
+    if (ROT == 1) {
+      const float bb = b * t[1], ba = b * t[0];
+      x[2 * k] = __builtin_fmaf(a, t[0], bb);
+      x[2 * k + 1] = __builtin_fmaf(a, t[1], -ba);
+    } else {
+      const float bs = b * t[1], bc = b * t[0];
+      x[2 * k] = __builtin_fmaf(a, t[0], -bs);
+      x[2 * k + 1] = __builtin_fmaf(a, t[1], bc);
+    }
+  }
+}
+
+// Half rotation of the slice from the token's RoPE outputs U[0..D): output pair
+// (o + 2i, o + 2i + 1) = ((x1 + x2) r, (x1 - x2) r), x1 = U[o+i], x2 = U[o+h+i],
+// h = Dj/2, r = fl(1/sqrt2).
+template <int CPT>
+RA_DEV void half_slice(const float* U, int c0, const Shape& s, float (&x)[CPT]) {
+  const float r = 0.70710678118654752440f;
+#pragma unroll
+  for (int k = 0; k < CPT / 2; ++k) {
+    const int c = c0 + 2 * k;
+    int o, dj;
+    if (c < s.Df) { o = 0; dj = s.Df; }
+    else if (c < s.Df + s.Dh) { o = s.Df; dj = s.Dh; }
+    else { o = s.Df + s.Dh; dj = s.Dw; }
+    const int i = (c - o) >> 1;
+    const float x1 = U[o + i], x2 = U[o + (dj >> 1) + i];
+    const float sm = x1 + x2, df = x1 - x2;
+    x[2 * k] = sm * r;
+    x[2 * k + 1] = df * r;
+  }
+}
+
+// RoPE + rotation of one slice; U is this token's LDS row (D + 1 floats, used by
+// ROT 2 only).  Contains a workgroup barrier when ROT == 2 (all threads must call).
+template <int DT, int ROT, int CPT>
+RA_DEV void rotated_slice(const void* base, int64_t n, bool valid, int D, int c0, const Shape& s,
+                          const float* tab, float* U, float (&x)[CPT]) {
+  if (valid) {
+    int f, y, xx;
+    token_pos(n, s, f, y, xx);
+    load_slice<DT, CPT>(base, n, D, c0, x);
+    rope_slice<ROT, CPT>(x, c0, tab, seg_rows(s, f, y, xx));
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) x[i] = 0.f;
+  }
+  if (ROT == 2) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) U[c0 + i] = x[i];
+    __syncthreads();
+    if (valid) half_slice<CPT>(U, c0, s, x);
+  }
+}
+
 RA_DEV int quant_code(float v, float inv) {
   float t = __builtin_rintf(v * inv);
   t = fminf(7.f, fmaxf(-7.f, t));
