@@ -12,8 +12,9 @@
 //    rows padded by 16 bytes (odd multiples of 16: conflict-free LDS reads with
 //    addresses that stay affine), and the level-threshold table in the tail.  The
 //    main loop copies groups straight from global memory into LDS
-//    (buffer_load_dwordx4 ... lds), three groups ahead into a ring of four slots,
-//    and spends no VALU on staging.
+//    (buffer_load_dwordx4 ... lds) into a ring of LDS slots, up to three groups
+//    ahead, and spends no VALU on staging.  A group of 128 keys holds several
+//    online-softmax steps (one barrier and one copy per group).
 //  * One workgroup = 4 waves x 32 query rows.  Each wave computes S^T = K Q^T on
 //    v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales).  Products of INT4 values and
 //    their sums (|A| <= 49 D < 2^24) are exact in fp32, so the scores arrive as
@@ -43,7 +44,6 @@ namespace ra {
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
-constexpr int kBufs = 4;  // LDS ring: group g computes while g+1..g+3 land
 constexpr float kMagic = 128.5f + 4.0f / 65536.0f;
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -57,8 +57,10 @@ RA_DEV uint32_t pack_b2(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
 
 template <int D, int KVB>
 struct Geo {
-  static constexpr int TG = KVB < 32 ? 32 : KVB;  // keys per group (staged together)
+  static constexpr int TG = KVB < 32 ? 32 : 128;  // keys per group (staged together)
   static constexpr int NT = TG / 32;              // 32-key MFMA tiles per group
+  static constexpr int TPS = KVB < 32 ? 1 : KVB / 32;  // tiles per online-softmax step
+  static constexpr int NSG = NT / TPS;            // steps (tile blocks) per group
   static constexpr int NDB = D / 32;              // 32-row d blocks of O^T
   static constexpr int KC = D / 64;               // 64-deep chunks of Q K^T (fp8 MFMA)
   static constexpr int KROW = D + 16;             // bytes per K row (fp8 + pad)
@@ -67,7 +69,8 @@ struct Geo {
   static constexpr int TOFF = VOFF + D * VROW;    // 17 floats of level thresholds
   static constexpr int IMG = (TOFF + 128 + 4095) / 4096 * 4096;  // one group's image
   static constexpr int NDMA = IMG / 4096;         // 16-byte copies per thread per group
-  static constexpr int LDS = kBufs * IMG;
+  static constexpr int NB = 4 * IMG <= 81920 ? 4 : 2;  // ring slots (two workgroups per CU)
+  static constexpr int LDS = NB * IMG;
 };
 // key (within its 32-key tile) held by K image row rho: row (v&3) + 8(v>>2) + 4h
 // holds key 16h + v, so lane half h of the S^T accumulator sees keys 16h..16h+15
@@ -181,12 +184,13 @@ RA_DEV void wait_vm() {
 }
 
 template <int D, int KVB>
-RA_DEV void qk_tiles(const uint8_t* Kl, const i32x8 (&qop)[Geo<D, KVB>::KC], f32x16 (&st)[Geo<D, KVB>::NT]) {
+RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::KC],
+                     f32x16 (&st)[Geo<D, KVB>::TPS]) {
   using G = Geo<D, KVB>;
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
 #pragma unroll
-  for (int t = 0; t < G::NT; ++t) {
-    const uint8_t* row = Kl + (t * 32 + col) * G::KROW + 32 * h;
+  for (int t = 0; t < G::TPS; ++t) {
+    const uint8_t* row = Kl + ((tb + t) * 32 + col) * G::KROW + 32 * h;
 #pragma unroll
     for (int kc = 0; kc < G::KC; ++kc) {
       const i32x4 lo = *(const i32x4*)(row + 64 * kc);
@@ -199,27 +203,28 @@ RA_DEV void qk_tiles(const uint8_t* Kl, const i32x8 (&qop)[Geo<D, KVB>::KC], f32
   }
 }
 
-// Online-softmax step(s) of one key group: running max, lazy flush, P levels,
-// P^T operand, P V MFMAs.  TAIL: the group holds keys >= N.
+// One online-softmax step on tiles tb..tb+TPS-1 of group g (for kv_blk 16, the two
+// halves of tile tb as two steps): running max, lazy flush, P levels, P^T operand,
+// P V MFMAs.  TAIL: the group holds keys >= N.
 template <int D, int KVB, bool DBG, bool TAIL>
-RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
-                       const f32x16 (&st)[Geo<D, KVB>::NT], const float (&ct)[Geo<D, KVB>::NT],
+RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl, const float* Tl,
+                       const f32x16 (&st)[Geo<D, KVB>::TPS], const float (&ct)[Geo<D, KVB>::TPS],
                        RowState<D / 32>& S, bool dbg_row, int dr) {
   using G = Geo<D, KVB>;
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
   const int N = (int)a.N;
-  const int j0 = g * G::TG;
+  const int j0 = g * G::TG + tb * 32;  // first key of the step's tiles
   const int nsteps = (N + KVB - 1) / KVB;
   constexpr int NSTEP = KVB < 32 ? 2 : 1;
 #pragma unroll
   for (int sidx = 0; sidx < NSTEP; ++sidx) {
-    const int step = (KVB < 32) ? g * 2 + sidx : g;
+    const int step = step0 + sidx;
     if (step >= nsteps) break;
     const bool act = (KVB >= 32) || (h == sidx);
     // ---- running maximum (max of the exact integer scores, then times c) -----------
     float mloc = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < G::NT; ++t) {
+    for (int t = 0; t < G::TPS; ++t) {
       float im = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -240,7 +245,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
           S.acc[db][v] = 0;
         }
       }
-      if (g == 0 && sidx == 0) S.mref = mnew;
+      if (step == 0) S.mref = mnew;
       if (__any(mnew - S.mref > 64.0f)) {
         // keep sigma far from overflow: move the frame to the current maximum
         const float back = exp2_hw(S.mref - mnew);
@@ -259,7 +264,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
     const bool guard = mnew >= 262144.0f;
     // ---- P levels, P^T operand, level sums, P V: one 32-key tile at a time --------
 #pragma unroll
-    for (int t = 0; t < G::NT; ++t) {
+    for (int t = 0; t < G::TPS; ++t) {
       // fast path: level byte and margin from the hardware exp, packed four at a
       // time into the P^T operand
       i32x4 pb;
@@ -307,7 +312,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
           pb[w] = (int)rr;
         }
       }
-      const int vc = 2 * t + h;  // 16-key chunk of this lane half in the V^T rows
+      const int vc = 2 * (tb + t) + h;  // 16-key chunk of this lane half in the V^T rows
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db) {
         const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + 16 * vc);
@@ -340,36 +345,43 @@ RA_DEV void softmax_pv(const Ctx& a, int g, const uint8_t* Vl, const float* Tl,
 
 typedef const __attribute__((address_space(4))) float* kscale_ptr;  // read-only: scalar loads
 
-// One key group: the K scales of its 16-key units (scalar loads, so they never
-// wait behind the copies in flight), Q K^T from ring slot g % 4, softmax + P V;
-// then the copy of group g+3 into the slot group g-1 used, a wait until this
-// wave's copy of group g+1 has landed (g+2 and g+3 stay in flight), and one
+// One key group g in ring slot g % NB: first the copy of group g + NB - 1 into the
+// slot group g-1 used (free since the last barrier); then its online-softmax steps,
+// each with the K scales of its 16-key units (scalar loads, so they never wait
+// behind the copies in flight), Q K^T, softmax + P V; then a wait until this
+// wave's copy of group g+1 has landed (later copies stay in flight) and one
 // barrier, which also covers the other waves' copies.
 template <int D, int KVB, bool DBG, bool TAIL>
 RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngroups, uint8_t* lds,
                        const i32x8 (&qop)[Geo<D, KVB>::KC], float sq, int bh, RowState<D / 32>& S, bool dbg_row,
                        int dr) {
   using G = Geo<D, KVB>;
+  if (!TAIL && g + G::NB - 1 < ngroups)
+    dma_group<D, KVB>(rsrc, g + G::NB - 1, lds + ((g + G::NB - 1) % G::NB) * G::IMG);
   const int h = (threadIdx.x >> 5) & 1;
   const kscale_ptr ksh = (kscale_ptr)a.ks + (int64_t)bh * (a.Np >> a.qk_shift);
-  float sk[G::NT];
+  uint8_t* const cur = lds + (g % G::NB) * G::IMG;
 #pragma unroll
-  for (int t = 0; t < G::NT; ++t) {
-    const int k0 = g * G::TG + 32 * t;
-    const float s0 = ksh[k0 >> a.qk_shift], s1 = ksh[(k0 + 16) >> a.qk_shift];
-    sk[t] = h ? s1 : s0;
+  for (int sg = 0; sg < G::NSG; ++sg) {
+    const int tb = sg * G::TPS;
+    float ct[G::TPS];
+#pragma unroll
+    for (int t = 0; t < G::TPS; ++t) {
+      const int k0 = g * G::TG + 32 * (tb + t);
+      const float s0 = ksh[k0 >> a.qk_shift], s1 = ksh[(k0 + 16) >> a.qk_shift];
+      ct[t] = (sq * (h ? s1 : s0)) * a.C0;
+    }
+    f32x16 st[G::TPS];
+    qk_tiles<D, KVB>(cur, tb, qop, st);
+    const int step0 = KVB < 32 ? 2 * g : g * G::NSG + sg;
+    softmax_pv<D, KVB, DBG, TAIL>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct, S,
+                                  dbg_row, dr);
   }
-  uint8_t* const cur = lds + (g % kBufs) * G::IMG;
-  f32x16 st[G::NT];
-  qk_tiles<D, KVB>(cur, qop, st);
-  float ct[G::NT];
-#pragma unroll
-  for (int t = 0; t < G::NT; ++t) ct[t] = (sq * sk[t]) * a.C0;
-  softmax_pv<D, KVB, DBG, TAIL>(a, g, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct, S, dbg_row, dr);
   if (!TAIL) {
-    if (g + 3 < ngroups) dma_group<D, KVB>(rsrc, g + 3, lds + ((g + 3) % kBufs) * G::IMG);
-    if (DBG || g + 2 >= ngroups) wait_vm<0>();
-    else if (g + 3 >= ngroups) wait_vm<G::NDMA>();
+    // copies issued after group g+1's: those of groups g+2 .. min(g+NB-1, ngroups-1)
+    const int later = min(g + G::NB - 1, ngroups - 1) - (g + 1);
+    if (DBG || later <= 0) wait_vm<0>();
+    else if (later == 1) wait_vm<G::NDMA>();
     else wait_vm<2 * G::NDMA>();
   }
   lds_barrier();
@@ -400,16 +412,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int qi = qt * kBM + w * 32 + col;
   const int ngroups = (N + G::TG - 1) / G::TG;
 
-  // ---- prologue: groups 0, 1, 2 in flight ------------------------------------------
+  // ---- prologue: groups 0 .. NB-2 in flight ----------------------------------------
   const int64_t ngp = a.Np / G::TG;
   const int64_t head0 = (int64_t)bh * ngp * G::IMG;
   const int64_t avail = args.img_bytes - head0;  // the resource never reaches past the workspace
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.img + head0), (short)0, (int)(avail < ngp * G::IMG ? (avail > 0 ? avail : 0) : ngp * G::IMG),
       0x00020000);
-  dma_group<D, KVB>(rsrc, 0, lds);
-  if (ngroups > 1) dma_group<D, KVB>(rsrc, 1, lds + G::IMG);
-  if (ngroups > 2) dma_group<D, KVB>(rsrc, 2, lds + 2 * G::IMG);
+#pragma unroll
+  for (int p = 0; p < G::NB - 1; ++p)
+    if (p < ngroups) dma_group<D, KVB>(rsrc, p, lds + p * G::IMG);
 
   // ---- Q operand: fp8 e4m3 bytes of the lane's 32 channels per 64-deep chunk -------
   i32x8 qop[G::KC];
@@ -441,7 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool dbg_row = DBG && qi >= a.dbg_row0 && qi < a.dbg_row0 + a.dbg_n && qi < N;
   const int dr = qi - a.dbg_row0;
 
-  wait_vm<0>();  // groups 0..2 and the Q operand
+  wait_vm<0>();  // the first groups and the Q operand
   lds_barrier();
   for (int g = 0; g + 1 < ngroups; ++g)
     group_iter<D, KVB, DBG, false>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
