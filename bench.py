@@ -19,6 +19,12 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 CONFIG = "wan720p"
+WORKLOADS = {
+    "wan480p": "Wan-1.3B-480p-like attention layer",
+    "wan720p": "Wan-14B-720p-like attention layer",
+    "hunyuan720p": "HunyuanVideo-720p-like attention layer",
+    "mixed_ragged": "mixed-precision ragged layer (even heads FP16 fallback, odd heads INT4)",
+}
 
 
 def main():
@@ -73,20 +79,33 @@ def main():
     out = torch.empty((B, H, N, D), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
 
+    # the mixed-precision workload routes even flat heads to the FP16 fallback and odd
+    # ones to the INT4 path (both write the one output tensor); the others are all INT4
+    mixed = args.config == "mixed_ragged"
+    q4_heads = [i for i in range(B * H) if i % 2 == 1] if mixed else None
+    fb_heads = [i for i in range(B * H) if i % 2 == 0] if mixed else None
+    if mixed:
+        ws_fb = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
+        tab_fb = ra.rotattn_build_rope_table(shape, 0).cuda()
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, True, z)
         if ev is not None:
             ev[1].record(stream)
-        ra.rotattn_int4_attention(shape, z, out)
+        ra.rotattn_int4_attention(shape, z, out, heads=q4_heads)
         if ev is not None:
             ev[2].record(stream)
+        if mixed:
+            ra.rotattn_fp16_fallback(shape, q, k, v, tab_fb, out, ws_fb, heads=fb_heads)
+            if ev is not None:
+                ev[3].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -95,12 +114,14 @@ def main():
     wall = time.perf_counter() - t0
     k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    k3_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) if mixed else None
     ms_step = wall * 1e3 / args.steps
+    ops_q4 = ops / 2 if mixed else ops  # the INT4 kernel's share of the work
 
     # K1 algorithmic bytes: read Q, K, V (fp16) once, write three INT4 code tensors
     # and the scales: 3*2 + 3*0.5 bytes per element.
     k1_bytes = (3 * 2.0 + 3 * 0.5) * N * D * H * B
-    k2_tops = ops / (k2_ms * 1e-3) / 1e12
+    k2_tops = ops_q4 / (k2_ms * 1e-3) / 1e12
 
     result = {
         "metric": "effective attention TOPS (4*N^2*D*H/s) at Wan-720p-like shape; % int8 MFMA peak",
@@ -115,21 +136,22 @@ def main():
         "vs_baseline": None,
         "dtype": "int4",
         "data": "synthetic",
-        "config": {"workload": "Wan-14B-720p-like attention layer: B=%d H=%d grid %dx%dx%d N=%d D=%d "
+        "config": {"workload": "%s: B=%d H=%d grid %dx%dx%d N=%d D=%d "
                                "(%d/%d/%d), %s rotation, qk_blk=%d kv_blk=%d, fp16 in/out"
-                               % (B, H, cfg["F"], cfg["Hs"], cfg["Ws"], N, D, cfg["Df"], cfg["Dh"], cfg["Dw"],
-                                  cfg["rot"], cfg["qk_blk"], cfg["kv_blk"]),
+                               % (WORKLOADS.get(args.config, args.config), B, H, cfg["F"], cfg["Hs"], cfg["Ws"], N,
+                                  D, cfg["Df"], cfg["Dh"], cfg["Dw"], cfg["rot"], cfg["qk_blk"], cfg["kv_blk"]),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "k2_attention (rotattn_int4_attention)",
                      "achieved": round(k2_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
                      "traffic": counted_traffic() if args.config == CONFIG and not (args.kv or args.qk) else None},
-        "kernels_ms": {"quantize_qk": round(k1_ms, 4), "int4_attention": round(k2_ms, 4)},
+        "kernels_ms": dict({"quantize_qk": round(k1_ms, 4), "int4_attention": round(k2_ms, 4)},
+                           **({"fp16_fallback_even_heads": round(k3_ms, 4)} if mixed else {})),
         "quantize_qk_GBps": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
         "attention_only_TOPS": round(k2_tops, 1),
     }
 
-    if not args.no_fallback:
+    if not args.no_fallback and not mixed:
         ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
         tab0 = ra.rotattn_build_rope_table(shape, 0).cuda()
         ra.rotattn_fp16_fallback(shape, q, k, v, tab0, out, ws)
@@ -171,7 +193,7 @@ def counted_traffic():
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, rot, rows_target=16384):
+def cpu_baseline(cfg, rot, rows_target=40000):
     """The oracle on the host cores: quantisation of one head, then quantised
     attention for a bounded sample of that head's query rows; scaled to TOPS."""
     import numpy as np
