@@ -205,8 +205,9 @@ RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::
 
 // One online-softmax step on tiles tb..tb+TPS-1 of group g (for kv_blk 16, the two
 // halves of tile tb as two steps): running max, lazy flush, P levels, P^T operand,
-// P V MFMAs.  TAIL: the group holds keys >= N.
-template <int D, int KVB, bool DBG, bool TAIL>
+// P V MFMAs.  TAIL: the group holds keys >= N.  US: one K scale for the whole step
+// (qk_blk >= kv_blk), so the maximum needs one multiplication.
+template <int D, int KVB, bool DBG, bool TAIL, bool US>
 RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl, const float* Tl,
                        const f32x16 (&st)[Geo<D, KVB>::TPS], const float (&ct)[Geo<D, KVB>::TPS],
                        RowState<D / 32>& S, bool dbg_row, int dr) {
@@ -223,16 +224,30 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     const bool act = (KVB >= 32) || (h == sidx);
     // ---- running maximum (max of the exact integer scores, then times c) -----------
     float mloc = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < G::TPS; ++t) {
+    if (US) {
       float im = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        bool ok = act;
-        if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
-        im = fmaxf(im, ok ? st[t][v] : -INFINITY);
+      for (int t = 0; t < G::TPS; ++t) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          bool ok = act;
+          if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+          im = fmaxf(im, ok ? st[t][v] : -INFINITY);
+        }
       }
-      if (im != -INFINITY) mloc = fmaxf(mloc, im * ct[t]);
+      if (im != -INFINITY) mloc = im * ct[0];
+    } else {
+#pragma unroll
+      for (int t = 0; t < G::TPS; ++t) {
+        float im = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          bool ok = act;
+          if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+          im = fmaxf(im, ok ? st[t][v] : -INFINITY);
+        }
+        if (im != -INFINITY) mloc = fmaxf(mloc, im * ct[t]);
+      }
     }
     const float mnew = fmaxf(S.m, pair_max(mloc));
     const float alpha = exp2_hw(S.m - mnew);
@@ -351,7 +366,7 @@ typedef const __attribute__((address_space(4))) float* kscale_ptr;  // read-only
 // behind the copies in flight), Q K^T, softmax + P V; then a wait until this
 // wave's copy of group g+1 has landed (later copies stay in flight) and one
 // barrier, which also covers the other waves' copies.
-template <int D, int KVB, bool DBG, bool TAIL>
+template <int D, int KVB, bool DBG, bool TAIL, bool US>
 RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngroups, uint8_t* lds,
                        const i32x8 (&qop)[Geo<D, KVB>::KC], float sq, int bh, RowState<D / 32>& S, bool dbg_row,
                        int dr) {
@@ -365,16 +380,22 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
   for (int sg = 0; sg < G::NSG; ++sg) {
     const int tb = sg * G::TPS;
     float ct[G::TPS];
+    if (US) {
+      const float c = (sq * ksh[(g * G::TG + 32 * tb) >> a.qk_shift]) * a.C0;
 #pragma unroll
-    for (int t = 0; t < G::TPS; ++t) {
-      const int k0 = g * G::TG + 32 * (tb + t);
-      const float s0 = ksh[k0 >> a.qk_shift], s1 = ksh[(k0 + 16) >> a.qk_shift];
-      ct[t] = (sq * (h ? s1 : s0)) * a.C0;
+      for (int t = 0; t < G::TPS; ++t) ct[t] = c;
+    } else {
+#pragma unroll
+      for (int t = 0; t < G::TPS; ++t) {
+        const int k0 = g * G::TG + 32 * (tb + t);
+        const float s0 = ksh[k0 >> a.qk_shift], s1 = ksh[(k0 + 16) >> a.qk_shift];
+        ct[t] = (sq * (h ? s1 : s0)) * a.C0;
+      }
     }
     f32x16 st[G::TPS];
     qk_tiles<D, KVB>(cur, tb, qop, st);
     const int step0 = KVB < 32 ? 2 * g : g * G::NSG + sg;
-    softmax_pv<D, KVB, DBG, TAIL>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct, S,
+    softmax_pv<D, KVB, DBG, TAIL, US>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct, S,
                                   dbg_row, dr);
   }
   if (!TAIL) {
@@ -387,7 +408,7 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
   lds_barrier();
 }
 
-template <int D, int KVB, bool DBG>
+template <int D, int KVB, bool DBG, bool US>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_attention(
     const AttnArgs args) {
   using G = Geo<D, KVB>;
@@ -456,8 +477,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   wait_vm<0>();  // the first groups and the Q operand
   lds_barrier();
   for (int g = 0; g + 1 < ngroups; ++g)
-    group_iter<D, KVB, DBG, false>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
-  group_iter<D, KVB, DBG, true>(a, rsrc, ngroups - 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+    group_iter<D, KVB, DBG, false, US>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+  group_iter<D, KVB, DBG, true, US>(a, rsrc, ngroups - 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
 
   // ---- epilogue ---------------------------------------------------------------------
   const float lq = pair_sum(S.l);
@@ -492,14 +513,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-template <int D, int KVB>
+template <int D, int KVB, bool US>
 hipError_t launch_t(const AttnArgs& a, bool dbg, hipStream_t st) {
   using G = Geo<D, KVB>;
   static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, false>,
+    hipError_t e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, false, US>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, true>,
+      e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, true, US>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     return e;
   }();
@@ -507,11 +528,18 @@ hipError_t launch_t(const AttnArgs& a, bool dbg, hipStream_t st) {
   k2_stage<D, KVB><<<dim3((unsigned)(a.Np / G::TG), (unsigned)a.nheads), 256, 0, st>>>(a);
   if (dbg) {
     const int first = a.dbg_row0 / kBM, last = (a.dbg_row0 + a.dbg_n - 1) / kBM;
-    k2_attention<D, KVB, true><<<last - first + 1, 256, G::LDS, st>>>(a);
+    k2_attention<D, KVB, true, US><<<last - first + 1, 256, G::LDS, st>>>(a);
   } else {
-    k2_attention<D, KVB, false><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
+    k2_attention<D, KVB, false, US><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
   }
   return hipGetLastError();
+}
+
+// a step of kv_blk >= 32 keys lies inside one K-scale block when qk_blk >= kv_blk
+template <int D, int KVB>
+hipError_t launch_s(const AttnArgs& a, bool dbg, hipStream_t st) {
+  if (KVB >= 32 && a.qk_blk >= KVB) return launch_t<D, KVB, true>(a, dbg, st);
+  return launch_t<D, KVB, false>(a, dbg, st);
 }
 
 template <int D, int KVB>
@@ -540,17 +568,17 @@ size_t attention_workspace_bytes(int D, int kv_blk, int64_t BH, int64_t Np) {
 hipError_t launch_attention(const AttnArgs& a, int D, int kv_blk, bool dbg, hipStream_t st) {
   if (D == 128) {
     switch (kv_blk) {
-      case 16: return launch_t<128, 16>(a, dbg, st);
-      case 32: return launch_t<128, 32>(a, dbg, st);
-      case 64: return launch_t<128, 64>(a, dbg, st);
-      default: return launch_t<128, 128>(a, dbg, st);
+      case 16: return launch_s<128, 16>(a, dbg, st);
+      case 32: return launch_s<128, 32>(a, dbg, st);
+      case 64: return launch_s<128, 64>(a, dbg, st);
+      default: return launch_s<128, 128>(a, dbg, st);
     }
   }
   switch (kv_blk) {
-    case 16: return launch_t<64, 16>(a, dbg, st);
-    case 32: return launch_t<64, 32>(a, dbg, st);
-    case 64: return launch_t<64, 64>(a, dbg, st);
-    default: return launch_t<64, 128>(a, dbg, st);
+    case 16: return launch_s<64, 16>(a, dbg, st);
+    case 32: return launch_s<64, 32>(a, dbg, st);
+    case 64: return launch_s<64, 64>(a, dbg, st);
+    default: return launch_s<64, 128>(a, dbg, st);
   }
 }
 
