@@ -278,10 +278,15 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     const float nm = a.L15 - mnew;
     const bool guard = mnew >= 262144.0f;
     // ---- P levels, P^T operand, level sums, P V: one 32-key tile at a time --------
+    // Fast path: level byte and margin from the hardware exp, packed four at a time
+    // into the P^T operand, which goes straight to the P V MFMA.  Only when some
+    // margin in the wave is not clear does the exact path run for the tile: the
+    // hardware-exp level r^ is within one of the exact level r, which is fixed by the
+    // two thresholds around r^ (a table with +inf above the last one); the
+    // accumulator already holds V r^, and one more MFMA adds V (r - r^), each
+    // difference in {-1, 0, 1}.
 #pragma unroll
     for (int t = 0; t < G::TPS; ++t) {
-      // fast path: level byte and margin from the hardware exp, packed four at a
-      // time into the P^T operand
       i32x4 pb;
       u16x2 wmin = {0xFFFF, 0xFFFF};
 #pragma unroll
@@ -301,46 +306,45 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
         }
         pb[w] = (int)pack_b2(tt[0], tt[1], tt[2], tt[3]);
       }
-      if (__any((wmin.x <= 6) || guard)) {
-        // A margin is too small somewhere in the wave (rare).  The hardware-exp
-        // level r^ is within one of the exact level, which is fixed by the two
-        // thresholds around r^ (an LDS table with +inf above the last one); the
-        // operand is rebuilt from the scores.
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t rr = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = 4 * w + e;
-            const float y = __builtin_fmaf(st[t][v], ct[t], nm);
-            const uint32_t tv = __float_as_uint(exp2_hw(y) + kMagic);
-            const int rh = min((int)((tv >> 16) & 0xFFu), 16);
-            const float lo = Tl[max(rh - 1, 0)], hi = Tl[rh];
-            int r = rh - ((rh > 0 && y < lo) ? 1 : 0) + ((y >= hi) ? 1 : 0);
-            if (TAIL || KVB < 32) {
-              bool ok = act;
-              if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
-              r = ok ? r : 0;
-            }
-            rr |= (uint32_t)r << (8 * e);
-          }
-          pb[w] = (int)rr;
-        }
-      }
       const int vc = 2 * (tb + t) + h;  // 16-key chunk of this lane half in the V^T rows
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db) {
         const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + 16 * vc);
         S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, S.acc[db], 0, 0, 0);
       }
-      if (DBG && dbg_row && act) {
+      if (DBG || __any((wmin.x <= 6) || guard)) {
+        i32x4 dl;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = j0 + t * 32 + 16 * h + v;
-          if (key < N) {
-            a.dbg_aqk[(int64_t)dr * N + key] = (int32_t)st[t][v];
-            a.dbg_p[(int64_t)dr * N + key] = (int8_t)((int)((uint32_t)pb[v >> 2] >> (8 * (v & 3)) & 0xFFu) - 8);
+        for (int w = 0; w < 4; ++w) {
+          uint32_t dd = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * w + e;
+            bool ok = act;
+            if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+            const float y = __builtin_fmaf(st[t][v], ct[t], nm);
+            float p = exp2_hw(y);
+            if (TAIL || KVB < 32) p = ok ? p : 0.f;
+            const int rf = (int)((__float_as_uint(p + kMagic) >> 16) & 0xFFu);  // the fast level
+            const int rh = min(rf, 16);
+            const float lo = Tl[max(rh - 1, 0)], hi = Tl[rh];
+            int r = rh - ((rh > 0 && y < lo) ? 1 : 0) + ((y >= hi) ? 1 : 0);
+            if (TAIL || KVB < 32) r = ok ? r : 0;
+            dd |= ((uint32_t)(r - rf) & 0xFFu) << (8 * e);
+            if (DBG && dbg_row && act) {
+              const int key = j0 + t * 32 + 16 * h + v;
+              if (key < N) {
+                a.dbg_aqk[(int64_t)dr * N + key] = (int32_t)st[t][v];
+                a.dbg_p[(int64_t)dr * N + key] = (int8_t)(r - 8);
+              }
+            }
           }
+          dl[w] = (int)dd;
+        }
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+          const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + 16 * vc);
+          S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, dl, S.acc[db], 0, 0, 0);
         }
       }
     }
@@ -396,7 +400,7 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
     qk_tiles<D, KVB>(cur, tb, qop, st);
     const int step0 = KVB < 32 ? 2 * g : g * G::NSG + sg;
     softmax_pv<D, KVB, DBG, TAIL, US>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct, S,
-                                  dbg_row, dr);
+                                      dbg_row, dr);
   }
   if (!TAIL) {
     // copies issued after group g+1's: those of groups g+2 .. min(g+NB-1, ngroups-1)
