@@ -7,16 +7,17 @@
 //
 // gfx950 design
 //  * A staging pass (k2_stage) turns each head's INT4 K and V codes into the exact
-//    byte image one key group occupies in LDS: K as fp8 e4m3 (every INT4 value is
-//    exact in e4m3) with rows permuted for the S^T register layout, V^T as int8,
-//    rows padded by 16 bytes (odd multiples of 16: conflict-free LDS reads with
-//    addresses that stay affine), and the level-threshold table in the tail.  The
+//    byte image one key group occupies in LDS: K as packed fp6 e2m3 (every code in
+//    [-7, 7] is exact in e2m3; 6 bits per value) with rows permuted for the S^T
+//    register layout, V^T as int8, rows padded so that the LDS reads of 32
+//    consecutive rows hit distinct banks, and the level-threshold table in the tail.  The
 //    main loop copies groups straight from global memory into LDS
 //    (buffer_load_dwordx4 ... lds) into a ring of LDS slots, up to three groups
 //    ahead, and spends no VALU on staging.  A group of 128 keys holds several
 //    online-softmax steps (one barrier and one copy per group).
 //  * One workgroup = 4 waves x 32 query rows.  Each wave computes S^T = K Q^T on
-//    v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales).  Products of INT4 values and
+//    v_mfma_scale_f32_32x32x64_f8f6f4 with fp6 operands (unit scales), which runs
+//    at twice the rate of the fp8 and int8 forms.  Products of INT4 values and
 //    their sums (|A| <= 49 D < 2^24) are exact in fp32, so the scores arrive as
 //    exact integers in float registers.  A lane owns one query row and 16 keys of
 //    every 32-key tile; its P levels are already laid out as the B operand of the
@@ -62,8 +63,11 @@ struct Geo {
   static constexpr int TPS = KVB < 32 ? 1 : KVB / 32;  // tiles per online-softmax step
   static constexpr int NSG = NT / TPS;            // steps (tile blocks) per group
   static constexpr int NDB = D / 32;              // 32-row d blocks of O^T
-  static constexpr int KC = D / 64;               // 64-deep chunks of Q K^T (fp8 MFMA)
-  static constexpr int KROW = D + 16;             // bytes per K row (fp8 + pad)
+  static constexpr int KC = D / 64;               // 64-deep chunks of Q K^T (fp6 MFMA)
+  static constexpr int KB = 3 * D / 4;            // packed fp6 bytes per K row
+  // bytes per K row: packed codes + pad, a multiple of 16 that is not a multiple
+  // of 32 dwords' worth of banks for eight consecutive rows
+  static constexpr int KROW = (KB + 16) / 4 % 8 == 0 ? KB + 32 : KB + 16;
   static constexpr int VROW = TG + 16;            // bytes per V^T row (int8 + pad)
   static constexpr int VOFF = TG * KROW;          // V^T rows start here
   static constexpr int TOFF = VOFF + D * VROW;    // 17 floats of level thresholds
@@ -76,10 +80,29 @@ struct Geo {
 // holds key 16h + v, so lane half h of the S^T accumulator sees keys 16h..16h+15
 RA_DEV int key_of_row(int rho) { return 16 * ((rho >> 2) & 1) + (rho & 3) + 4 * (rho >> 3); }
 
-RA_DEV uint32_t fp8_pair(int c0, int c1) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)c0, (float)c1, 0, false) & 0xFFFFu;
-}
 RA_DEV int nib(uint32_t w, int e) { return (int)((w >> (4 * e)) << 28) >> 28; }  // signed nibble e
+
+// fp6 e2m3 code of an integer in [-7, 7]: sign bit 5, exponent bits 4..3 (bias 1),
+// mantissa bits 2..0.  Magnitudes 0..7 encode as 00, 08, 10, 14, 18, 1A, 1C, 1E (hex).
+RA_DEV uint32_t e2m3(int v) {
+  const uint32_t a = (uint32_t)(v < 0 ? -v : v);
+  const uint32_t m = (a < 4 ? 0x14100800u >> (8 * a) : 0x1E1C1A18u >> (8 * (a - 4))) & 0xFFu;
+  return m | (v < 0 ? 0x20u : 0u);
+}
+
+// 32 signed nibbles (code bytes, low nibble first) -> the 32 fp6 values of one MFMA
+// operand: value i at bits 6i .. 6i+5 of six little-endian dwords.
+RA_DEV void pack_fp6(const u32x4 w, uint32_t (&o)[6]) {
+#pragma unroll
+  for (int j = 0; j < 6; ++j) o[j] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = e2m3(nib(w[i >> 3], i & 7));
+    const int b = 6 * i, d = b >> 5, sh = b & 31;
+    o[d] |= c << sh;
+    if (sh > 26) o[d + 1] |= c >> (32 - sh);
+  }
+}
 
 // ---- staging: INT4 codes -> per-group LDS images ---------------------------------
 // grid (Np / TG, nheads); the image of group g of head bh is at
@@ -93,19 +116,19 @@ __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
   const int64_t at = ((int64_t)bh * (Np / G::TG) + g) * G::IMG;
   if (at + G::IMG > args.img_bytes) return;
   uint8_t* img = args.img + at;
-  // K: TG rows x D bytes
-  for (int u = threadIdx.x; u < G::TG * D / 16; u += 256) {
-    const int rho = u / (D / 16), c = u % (D / 16);
+  // K: TG rows of D fp6 values.  Chunk c = 2 kc + h (channels 32c .. 32c+31, the
+  // operand of lane half h for the kc-th 64-deep MFMA) is stored as its first 16
+  // bytes at 16c and its last 8 bytes at D/2 + 8c, so that every lane reads its
+  // operand with one 16-byte and one 8-byte load at offsets affine in h.
+  for (int u = threadIdx.x; u < G::TG * D / 32; u += 256) {
+    const int rho = u / (D / 32), c = u % (D / 32);
     const int key = g * G::TG + (rho & ~31) + key_of_row(rho & 31);
-    const u32x2 w = *(const u32x2*)(args.kc + ((int64_t)bh * Np + key) * (D / 2) + 8 * c);
-    i32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t x = q < 2 ? w.x : w.y;
-      const int e0 = 4 * (q & 1);
-      o[q] = (int)(fp8_pair(nib(x, e0), nib(x, e0 + 1)) | (fp8_pair(nib(x, e0 + 2), nib(x, e0 + 3)) << 16));
-    }
-    *(i32x4*)(img + rho * G::KROW + 16 * c) = o;
+    const u32x4 w = *(const u32x4*)(args.kc + ((int64_t)bh * Np + key) * (D / 2) + 16 * c);
+    uint32_t o[6];
+    pack_fp6(w, o);
+    uint8_t* row = img + rho * G::KROW;
+    *(i32x4*)(row + 16 * c) = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    *(u32x2*)(row + D / 2 + 8 * c) = u32x2{o[4], o[5]};
   }
   // V^T: D rows x TG bytes (keys of the group in order)
   for (int u = threadIdx.x; u < D * G::TG / 16; u += 256) {
@@ -190,14 +213,18 @@ RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
 #pragma unroll
   for (int t = 0; t < G::TPS; ++t) {
-    const uint8_t* row = Kl + ((tb + t) * 32 + col) * G::KROW + 32 * h;
+    const uint8_t* row = Kl + ((tb + t) * 32 + col) * G::KROW;
 #pragma unroll
     for (int kc = 0; kc < G::KC; ++kc) {
-      const i32x4 lo = *(const i32x4*)(row + 64 * kc);
-      const i32x4 hi = *(const i32x4*)(row + 64 * kc + 16);
-      const i32x8 kop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const int c = 2 * kc + h;
+      const i32x4 lo = *(const i32x4*)(row + 16 * c);
+      const i32x2 hi = *(const i32x2*)(row + D / 2 + 8 * c);
+      // six dwords of fp6 values (format 2 = e2m3 for both operands); the last two
+      // operand dwords are not read by the instruction
+      const i32x8 kop = __builtin_shufflevector(lo, __builtin_shufflevector(hi, hi, 0, 1, -1, -1), 0, 1, 2, 3, 4,
+                                                5, -1, -1);
       const f32x16 zero = {0};
-      st[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[kc], kc == 0 ? zero : st[t], 0, 0, 0,
+      st[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[kc], kc == 0 ? zero : st[t], 2, 2, 0,
                                                                127, 0, 127);
     }
   }
@@ -448,19 +475,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int p = 0; p < G::NB - 1; ++p)
     if (p < ngroups) dma_group<D, KVB>(rsrc, p, lds + p * G::IMG);
 
-  // ---- Q operand: fp8 e4m3 bytes of the lane's 32 channels per 64-deep chunk -------
+  // ---- Q operand: packed fp6 e2m3 values of the lane's 32 channels per 64-deep chunk
   i32x8 qop[G::KC];
   {
     const u32x4* qp = (const u32x4*)(args.qc + ((int64_t)bh * a.Np + qi) * (D / 2));
 #pragma unroll
     for (int kc = 0; kc < G::KC; ++kc) {
-      const u32x4 x = qp[2 * kc + h];
+      uint32_t o[6];
+      pack_fp6(qp[2 * kc + h], o);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint32_t wd = x[q >> 1];
-        const int e0 = 4 * (q & 1);
-        qop[kc][q] = (int)(fp8_pair(nib(wd, e0), nib(wd, e0 + 1)) | (fp8_pair(nib(wd, e0 + 2), nib(wd, e0 + 3)) << 16));
-      }
+      for (int q = 0; q < 8; ++q) qop[kc][q] = q < 6 ? (int)o[q] : 0;
     }
   }
   const float sq = args.qs[(int64_t)bh * (a.Np >> a.qk_shift) + (qi >> a.qk_shift)];

@@ -58,10 +58,11 @@ def test_padded_tokens_and_workspace(L):
     assert ra.rotattn_padded_tokens(s) == 75776
     assert ra.rotattn_quantize_qk_workspace(s) > 0
     assert ra.rotattn_fp16_fallback_workspace(s) >= 3 * 40 * 75776 * 128 * 2
-    # one LDS image per 64-key group: K rows of D+16 bytes, V^T rows of 64+16 bytes,
-    # a 128-byte table, rounded up to 4 KiB
-    img = -(-(64 * (128 + 16) + 128 * (64 + 16) + 128) // 4096) * 4096
-    assert ra.rotattn_int4_attention_workspace(s) == 40 * (75776 // 64) * img
+    # one LDS image per 128-key group: K rows of packed fp6 (3D/4 bytes) + 16 pad,
+    # V^T rows of 128+16 bytes, a 128-byte table, rounded up to 4 KiB
+    img = -(-(128 * (96 + 16) + 128 * (128 + 16) + 128) // 4096) * 4096
+    assert img == 36864
+    assert ra.rotattn_int4_attention_workspace(s) == 40 * (75776 // 128) * img
 
 
 def test_null_and_bad_args_return_before_launch(L):
