@@ -118,8 +118,9 @@ __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
   uint8_t* img = args.img + at;
   // K: TG rows of D fp6 values.  Chunk c = 2 kc + h (channels 32c .. 32c+31, the
   // operand of lane half h for the kc-th 64-deep MFMA) is stored as its first 16
-  // bytes at 16c and its last 8 bytes at D/2 + 8c, so that every lane reads its
-  // operand with one 16-byte and one 8-byte load at offsets affine in h.
+  // bytes at 16c and its last 8 bytes at D/2 + 8c (+8 in rows 8..15 and 24..31 of
+  // each tile, which keeps the 8-byte reads of 16 consecutive rows on distinct banks), so that every lane
+  // reads its operand with one 16-byte and one 8-byte load.
   for (int u = threadIdx.x; u < G::TG * D / 32; u += 256) {
     const int rho = u / (D / 32), c = u % (D / 32);
     const int key = g * G::TG + (rho & ~31) + key_of_row(rho & 31);
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
     pack_fp6(w, o);
     uint8_t* row = img + rho * G::KROW;
     *(i32x4*)(row + 16 * c) = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-    *(u32x2*)(row + D / 2 + 8 * c) = u32x2{o[4], o[5]};
+    *(u32x2*)(row + D / 2 + 8 * c + 8 * ((rho >> 3) & 1)) = u32x2{o[4], o[5]};
   }
   // V^T: D rows x TG bytes (keys of the group in order)
   for (int u = threadIdx.x; u < D * G::TG / 16; u += 256) {
@@ -218,7 +219,7 @@ RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::
     for (int kc = 0; kc < G::KC; ++kc) {
       const int c = 2 * kc + h;
       const i32x4 lo = *(const i32x4*)(row + 16 * c);
-      const i32x2 hi = *(const i32x2*)(row + D / 2 + 8 * c);
+      const i32x2 hi = *(const i32x2*)(row + D / 2 + 8 * c + 8 * ((col >> 3) & 1));
       // six dwords of fp6 values (format 2 = e2m3 for both operands); the last two
       // operand dwords are not read by the instruction
       const i32x8 kop = __builtin_shufflevector(lo, __builtin_shufflevector(hi, hi, 0, 1, -1, -1), 0, 1, 2, 3, 4,
