@@ -50,6 +50,14 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
+// minimum of the low 16 bits of three values (v_min3_u16; only the low half of the
+// result is meaningful)
+RA_DEV uint32_t min3_u16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_min3_u16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 RA_DEV uint32_t pack_b2(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t x = __builtin_amdgcn_perm(b, a, 0x0c0c0602u);
   const uint32_t y = __builtin_amdgcn_perm(d, c, 0x0c0c0602u);
@@ -81,6 +89,11 @@ struct Geo {
 RA_DEV int key_of_row(int rho) { return 16 * ((rho >> 2) & 1) + (rho & 3) + 4 * (rho >> 3); }
 
 RA_DEV int nib(uint32_t w, int e) { return (int)((w >> (4 * e)) << 28) >> 28; }  // signed nibble e
+
+// fp8 e4m3 bytes of two integers in [-7, 7] (exact), in the low 16 bits
+RA_DEV uint32_t fp8_pair(int c0, int c1) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((float)c0, (float)c1, 0, false) & 0xFFFFu;
+}
 
 // fp6 e2m3 code of an integer in [-7, 7]: sign bit 5, exponent bits 4..3 (bias 1),
 // mantissa bits 2..0.  Magnitudes 0..7 encode as 00, 08, 10, 14, 18, 1A, 1C, 1E (hex).
@@ -131,7 +144,10 @@ __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
     *(i32x4*)(row + 16 * c) = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
     *(u32x2*)(row + D / 2 + 8 * c + 8 * ((rho >> 3) & 1)) = u32x2{o[4], o[5]};
   }
-  // V^T: D rows x TG bytes (keys of the group in order)
+  // V^T: D rows x TG fp8 e4m3 values.  With steps of 64 or more keys, the 16-key
+  // chunks of each 64-key segment are stored in the k order of one 64-deep MFMA:
+  // position 32h + 16t' holds keys 32t' + 16h .. +15 (tile t' of the pair, lane
+  // half h), so a lane half reads its 32 keys as one contiguous run.
   for (int u = threadIdx.x; u < D * G::TG / 16; u += 256) {
     const int d = u / (G::TG / 16), c = u % (G::TG / 16);
     const u32x2 w = *(const u32x2*)(args.vc + ((int64_t)bh * D + d) * (Np / 2) + (g * G::TG + 16 * c) / 2);
@@ -140,10 +156,10 @@ __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
     for (int q = 0; q < 4; ++q) {
       const uint32_t x = q < 2 ? w.x : w.y;
       const int e0 = 4 * (q & 1);
-      o[q] = (int)(((uint32_t)nib(x, e0) & 0xFFu) | (((uint32_t)nib(x, e0 + 1) & 0xFFu) << 8) |
-                   (((uint32_t)nib(x, e0 + 2) & 0xFFu) << 16) | (((uint32_t)nib(x, e0 + 3) & 0xFFu) << 24));
+      o[q] = (int)(fp8_pair(nib(x, e0), nib(x, e0 + 1)) | (fp8_pair(nib(x, e0 + 2), nib(x, e0 + 3)) << 16));
     }
-    *(i32x4*)(img + G::VOFF + d * G::VROW + 16 * c) = o;
+    const int cq = KVB >= 64 ? (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1) : c;
+    *(i32x4*)(img + G::VOFF + d * G::VROW + 16 * cq) = o;
   }
   if (threadIdx.x < 17) ((float*)(img + G::TOFF))[threadIdx.x] = threadIdx.x < 15 ? args.T[threadIdx.x] : INFINITY;
 }
@@ -162,16 +178,14 @@ struct Ctx {
   int32_t* dbg_apv;
 };
 
-// Per-lane running state of one query row (the lane pair l, l^32 shares a row).
-// Of holds the flushed part of the output numerator in a fixed frame: the sum over
-// flushed steps of 2^(m_s - mref) * acc_s, where acc_s is the integer P V sum of
-// the steps with running maximum m_s.  sigma = 2^(m - mref) for the current
-// maximum, so a flush is one fma per element, after which acc is cleared.
+// Per-lane running state of one query row (the lane pair l, l^32 shares a row):
+// the output numerator sum_j 2^(m_j - m) r_j v_j in fp32 (m_j the running maximum
+// when key j was added), the running maximum m and l = sum_j 2^(y_j + m_j - m).
+// Between moves of m the MFMA adds exact integer sums; a move rescales in place.
 template <int NDB>
 struct RowState {
-  f32x16 Of[NDB];
-  i32x16 acc[NDB];
-  float m, l, mref, sigma;
+  f32x16 acc[NDB];
+  float m, l;
 };
 
 // Copy the LDS image of group g into ring slot `buf`.  Wave w copies the w-th
@@ -278,73 +292,42 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
       }
     }
     const float mnew = fmaxf(S.m, pair_max(mloc));
-    const float alpha = exp2_hw(S.m - mnew);
-    if (DBG || __any(mnew > S.m)) {
+    if (__any(mnew > S.m)) {
+      // 2^(m_old - m_new): 0 on the first step (m_old = -inf), exactly 1 for rows
+      // whose maximum stays
+      const float alpha = exp2_hw(S.m - mnew);
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          S.Of[db][v] = __builtin_fmaf((float)S.acc[db][v], S.sigma, S.Of[db][v]);
-          S.acc[db][v] = 0;
-        }
+        for (int v = 0; v < 16; ++v) S.acc[db][v] *= alpha;
       }
-      if (step == 0) S.mref = mnew;
-      if (__any(mnew - S.mref > 64.0f)) {
-        // keep sigma far from overflow: move the frame to the current maximum
-        const float back = exp2_hw(S.mref - mnew);
-#pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) S.Of[db][v] *= back;
-        }
-        S.mref = mnew;
-      }
-      S.sigma = exp2_hw(mnew - S.mref);
+      S.l = S.l * alpha;
     }
-    S.l = S.l * alpha;
     S.m = mnew;
     const float nm = a.L15 - mnew;
     const bool guard = mnew >= 262144.0f;
-    // ---- P levels, P^T operand, level sums, P V: one 32-key tile at a time --------
+    // ---- P levels, P^T operand, level sums, P V: 64 keys (two tiles) per MFMA ---------
     // Fast path: level byte and margin from the hardware exp, packed four at a time
-    // into the P^T operand, which goes straight to the P V MFMA.  Only when some
-    // margin in the wave is not clear does the exact path run for the tile: the
-    // hardware-exp level r^ is within one of the exact level r, which is fixed by the
-    // two thresholds around r^ (a table with +inf above the last one); the
-    // accumulator already holds V r^, and one more MFMA adds V (r - r^), each
-    // difference in {-1, 0, 1}.
+    // into the P^T operand.  The level bytes r in [0, 15] are read by the MFMA as fp8
+    // e4m3 codes, whose values are r * 2^-9 (subnormals and the first binade), and the
+    // B scale 2^9 makes the products r * v exact; sums stay below 2^24, so the fp32
+    // accumulator adds exact integers.  Only when some margin in the wave is not clear
+    // does the exact path run for the pair: the hardware-exp level r^ is within one of
+    // the exact level r, which is fixed by the two thresholds around r^ (a table with
+    // +inf above the last one); one more MFMA adds V (r - r^), each difference in
+    // {-1, 0, 1} (sign-magnitude fp8 codes 0x81, 0, 0x01).
+    constexpr int PT = G::TPS >= 2 ? 2 : 1;  // tiles per MFMA
 #pragma unroll
-    for (int t = 0; t < G::TPS; ++t) {
-      i32x4 pb;
-      u16x2 wmin = {0xFFFF, 0xFFFF};
+    for (int pp = 0; pp < G::TPS / PT; ++pp) {
+      i32x4 pb[PT];
+      bool flag = guard;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t tt[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * w + e;
-          bool ok = act;
-          if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
-          const float y = __builtin_fmaf(st[t][v], ct[t], nm);
-          float p = exp2_hw(y);
-          if (TAIL || KVB < 32) p = ok ? p : 0.f;
-          S.l += p;
-          tt[e] = __float_as_uint(p + kMagic);
-          wmin = __builtin_elementwise_min(wmin, __builtin_bit_cast(u16x2, tt[e]));
-        }
-        pb[w] = (int)pack_b2(tt[0], tt[1], tt[2], tt[3]);
-      }
-      const int vc = 2 * (tb + t) + h;  // 16-key chunk of this lane half in the V^T rows
-#pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
-        const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + 16 * vc);
-        S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, pb, S.acc[db], 0, 0, 0);
-      }
-      if (DBG || __any((wmin.x <= 6) || guard)) {
-        i32x4 dl;
+      for (int tp = 0; tp < PT; ++tp) {
+        const int t = pp * PT + tp;
+        uint32_t wmin = 0xFFFF;  // low 16 bits: smallest margin (low 16 bits of t) of the tile
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          uint32_t dd = 0;
+          uint32_t tt[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * w + e;
@@ -353,37 +336,91 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
             const float y = __builtin_fmaf(st[t][v], ct[t], nm);
             float p = exp2_hw(y);
             if (TAIL || KVB < 32) p = ok ? p : 0.f;
-            const int rf = (int)((__float_as_uint(p + kMagic) >> 16) & 0xFFu);  // the fast level
-            const int rh = min(rf, 16);
-            const float lo = Tl[max(rh - 1, 0)], hi = Tl[rh];
-            int r = rh - ((rh > 0 && y < lo) ? 1 : 0) + ((y >= hi) ? 1 : 0);
-            if (TAIL || KVB < 32) r = ok ? r : 0;
-            dd |= ((uint32_t)(r - rf) & 0xFFu) << (8 * e);
-            if (DBG && dbg_row && act) {
-              const int key = j0 + t * 32 + 16 * h + v;
-              if (key < N) {
-                a.dbg_aqk[(int64_t)dr * N + key] = (int32_t)st[t][v];
-                a.dbg_p[(int64_t)dr * N + key] = (int8_t)(r - 8);
+            S.l += p;
+            tt[e] = __float_as_uint(p + kMagic);
+          }
+          wmin = min3_u16(wmin, tt[0], tt[1]);
+          wmin = min3_u16(wmin, tt[2], tt[3]);
+          pb[tp][w] = (int)pack_b2(tt[0], tt[1], tt[2], tt[3]);
+        }
+        flag = flag || ((wmin & 0xFFFFu) <= 6u);
+      }
+      const i32x8 pop = PT == 2 ? __builtin_shufflevector(pb[0], pb[PT - 1], 0, 1, 2, 3, 4, 5, 6, 7)
+                                : __builtin_shufflevector(pb[0], i32x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+      // this lane half's 32 keys of the pair in the V^T rows (one 16-key chunk,
+      // repeated, when a step is a single tile: its P^T half is zero)
+      const int voff = PT == 2 ? 32 * (tb + 2 * pp) + 32 * h : 32 * (tb + pp) + 16 * h;
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+        const uint8_t* vp = Vl + (db * 32 + col) * G::VROW + voff;
+        const i32x4 v0 = *(const i32x4*)vp;
+        const i32x4 v1 = PT == 2 ? *(const i32x4*)(vp + 16) : v0;
+        const i32x8 vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        S.acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, S.acc[db], 0, 0, 0, 127, 0, 136);
+      }
+      if (DBG || __any(flag)) {
+        i32x4 dl[PT], ex[PT];
+#pragma unroll
+        for (int tp = 0; tp < PT; ++tp) {
+          const int t = pp * PT + tp;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t dd = 0, rr = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = 4 * w + e;
+              bool ok = act;
+              if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+              const float y = __builtin_fmaf(st[t][v], ct[t], nm);
+              float p = exp2_hw(y);
+              if (TAIL || KVB < 32) p = ok ? p : 0.f;
+              const int rf = (int)((__float_as_uint(p + kMagic) >> 16) & 0xFFu);  // the fast level
+              const int rh = min(rf, 16);
+              const float lo = Tl[max(rh - 1, 0)], hi = Tl[rh];
+              int r = rh - ((rh > 0 && y < lo) ? 1 : 0) + ((y >= hi) ? 1 : 0);
+              if (TAIL || KVB < 32) r = ok ? r : 0;
+              dd |= ((uint32_t)(r - rf) & 0x81u) << (8 * e);
+              rr |= (uint32_t)r << (8 * e);
+              if (DBG && dbg_row && act) {
+                const int key = j0 + t * 32 + 16 * h + v;
+                if (key < N) {
+                  a.dbg_aqk[(int64_t)dr * N + key] = (int32_t)st[t][v];
+                  a.dbg_p[(int64_t)dr * N + key] = (int8_t)(r - 8);
+                }
+              }
+            }
+            dl[tp][w] = (int)dd;
+            ex[tp][w] = (int)rr;
+          }
+        }
+        const i32x8 dop = PT == 2 ? __builtin_shufflevector(dl[0], dl[PT - 1], 0, 1, 2, 3, 4, 5, 6, 7)
+                                  : __builtin_shufflevector(dl[0], i32x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+        const i32x8 xop = PT == 2 ? __builtin_shufflevector(ex[0], ex[PT - 1], 0, 1, 2, 3, 4, 5, 6, 7)
+                                  : __builtin_shufflevector(ex[0], i32x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+          const uint8_t* vp = Vl + (db * 32 + col) * G::VROW + voff;
+          const i32x4 v0 = *(const i32x4*)vp;
+          const i32x4 v1 = PT == 2 ? *(const i32x4*)(vp + 16) : v0;
+          const i32x8 vop = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          S.acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, dop, S.acc[db], 0, 0, 0, 127, 0, 136);
+          if (DBG) {
+            // this pair's sum_j (P~ + 8) vc (exact integers in fp32), added into the
+            // step's entry of the dump (the first pair of the step stores it)
+            const f32x16 zero = {0};
+            const f32x16 ps = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, xop, zero, 0, 0, 0, 127, 0, 136);
+            // an MFMA reads the operands of every lane: keep it (and its operands) out
+            // of the lane-divergent store below
+            asm volatile("" ::"v"(ps));
+            if (dbg_row) {
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int d = db * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
+                int32_t* q = a.dbg_apv + ((int64_t)dr * nsteps + step) * D + d;
+                *q = (pp == 0 ? 0 : *q) + (int32_t)ps[v];
               }
             }
           }
-          dl[w] = (int)dd;
-        }
-#pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
-          const i32x4 vop = *(const i32x4*)(Vl + (db * 32 + col) * G::VROW + 16 * vc);
-          S.acc[db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(vop, dl, S.acc[db], 0, 0, 0);
-        }
-      }
-    }
-    if (DBG && dbg_row) {
-      // per-step accumulator sum_j (P~ + 8) vc (the debug run flushes every step)
-#pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int d = db * 32 + (v & 3) + 8 * (v >> 2) + 4 * h;
-          a.dbg_apv[((int64_t)dr * nsteps + step) * D + d] = S.acc[db][v];
         }
       }
     }
@@ -441,10 +478,8 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
 }
 
 template <int D, int KVB, bool DBG, bool US>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_attention(
-    const AttnArgs args) {
+RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   using G = Geo<D, KVB>;
-  extern __shared__ __align__(16) uint8_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
   int L;
@@ -493,12 +528,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   RowState<G::NDB> S;
   S.m = -INFINITY;
   S.l = 0.f;
-  S.mref = 0.f;
-  S.sigma = 1.f;
 #pragma unroll
   for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { S.Of[db][v] = 0.f; S.acc[db][v] = 0; }
+    for (int v = 0; v < 16; ++v) S.acc[db][v] = 0.f;
   }
   const bool dbg_row = DBG && qi >= a.dbg_row0 && qi < a.dbg_row0 + a.dbg_n && qi < N;
   const int dr = qi - a.dbg_row0;
@@ -511,7 +544,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- epilogue ---------------------------------------------------------------------
   const float lq = pair_sum(S.l);
-  const float inv_sigma = 1.0f / S.sigma;
   if (DBG && dbg_row && h == 0) {
     args.dbg_m[dr] = S.m;
     args.dbg_l[dr] = lq;
@@ -527,8 +559,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = v4 * 4 + e;
-          const float num = __builtin_fmaf(S.Of[db][v], inv_sigma, (float)S.acc[db][v]);
-          o[e] = num * args.vs[(int64_t)bh * D + d0 + e] * inv;
+          o[e] = S.acc[db][v] * args.vs[(int64_t)bh * D + d0 + e] * inv;
         }
         const int64_t off = ((int64_t)bh * N + qi) * D + d0;
         if (args.out_f16) {
@@ -542,14 +573,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// The production kernel: two waves per SIMD (<= 256 registers per wave).
+template <int D, int KVB, bool US>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k2_attention(
+    const AttnArgs args) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  k2_body<D, KVB, false, US>(args, lds);
+}
+
+// The debug run (dumps of one head's row range): one wave per SIMD, so that the
+// extra dump state fits in registers.
+template <int D, int KVB, bool US>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k2_attention_debug(
+    const AttnArgs args) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  k2_body<D, KVB, true, US>(args, lds);
+}
+
 template <int D, int KVB, bool US>
 hipError_t launch_t(const AttnArgs& a, bool dbg, hipStream_t st) {
   using G = Geo<D, KVB>;
   static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, false, US>,
+    hipError_t e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, US>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)k2_attention<D, KVB, true, US>,
+      e = hipFuncSetAttribute((const void*)k2_attention_debug<D, KVB, US>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     return e;
   }();
@@ -557,9 +605,9 @@ hipError_t launch_t(const AttnArgs& a, bool dbg, hipStream_t st) {
   k2_stage<D, KVB><<<dim3((unsigned)(a.Np / G::TG), (unsigned)a.nheads), 256, 0, st>>>(a);
   if (dbg) {
     const int first = a.dbg_row0 / kBM, last = (a.dbg_row0 + a.dbg_n - 1) / kBM;
-    k2_attention<D, KVB, true, US><<<last - first + 1, 256, G::LDS, st>>>(a);
+    k2_attention_debug<D, KVB, US><<<last - first + 1, 256, G::LDS, st>>>(a);
   } else {
-    k2_attention<D, KVB, false, US><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
+    k2_attention<D, KVB, US><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
   }
   return hipGetLastError();
 }

@@ -40,7 +40,7 @@ struct AttnArgs {
   const float* ks;
   const uint8_t* vc;
   const float* vs;
-  uint8_t* img;   // workspace: per-group LDS images of K (fp8) and V^T (int8)
+  uint8_t* img;   // workspace: per-group LDS images of K (packed fp6) and V^T (fp8)
   int64_t img_bytes;  // its size (images that would not fit are neither written nor read)
   void* out;
   int out_f16;
