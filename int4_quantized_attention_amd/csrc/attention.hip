@@ -292,17 +292,9 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
       }
     }
     const float mnew = fmaxf(S.m, pair_max(mloc));
-    if (__any(mnew > S.m)) {
-      // 2^(m_old - m_new): 0 on the first step (m_old = -inf), exactly 1 for rows
-      // whose maximum stays
-      const float alpha = exp2_hw(S.m - mnew);
-#pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) S.acc[db][v] *= alpha;
-      }
-      S.l = S.l * alpha;
-    }
+    const bool moved = __any(mnew > S.m);
+    const float alpha = exp2_hw(S.m - mnew);
+    if (moved) S.l = S.l * alpha;
     S.m = mnew;
     const float nm = a.L15 - mnew;
     const bool guard = mnew >= 262144.0f;
@@ -344,6 +336,13 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
           pb[tp][w] = (int)pack_b2(tt[0], tt[1], tt[2], tt[3]);
         }
         flag = flag || ((wmin & 0xFFFFu) <= 6u);
+      }
+      if (pp == 0 && moved) {
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) S.acc[db][v] *= alpha;
+        }
       }
       const i32x8 pop = PT == 2 ? __builtin_shufflevector(pb[0], pb[PT - 1], 0, 1, 2, 3, 4, 5, 6, 7)
                                 : __builtin_shufflevector(pb[0], i32x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -435,16 +434,19 @@ typedef const __attribute__((address_space(4))) float* kscale_ptr;  // read-only
 // behind the copies in flight), Q K^T, softmax + P V; then a wait until this
 // wave's copy of group g+1 has landed (later copies stay in flight) and one
 // barrier, which also covers the other waves' copies.
-template <int D, int KVB, bool DBG, bool TAIL, bool US>
+template <int D, int KVB, bool DBG, bool TAIL, bool US, int SLOT = -1>
 RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngroups, uint8_t* lds,
                        const i32x8 (&qop)[Geo<D, KVB>::KC], float sq, int bh, RowState<D / 32>& S, bool dbg_row,
                        int dr) {
   using G = Geo<D, KVB>;
+  // ring slot of this group: a compile-time constant when the caller unrolls the
+  // group loop by the slot count (SLOT = g % NB), so LDS addresses stay invariant
+  const int slot = SLOT >= 0 ? SLOT : g % G::NB;
   if (!TAIL && g + G::NB - 1 < ngroups)
-    dma_group<D, KVB>(rsrc, g + G::NB - 1, lds + ((g + G::NB - 1) % G::NB) * G::IMG);
+    dma_group<D, KVB>(rsrc, g + G::NB - 1, lds + ((slot + G::NB - 1) % G::NB) * G::IMG);
   const int h = (threadIdx.x >> 5) & 1;
   const kscale_ptr ksh = (kscale_ptr)a.ks + (int64_t)bh * (a.Np >> a.qk_shift);
-  uint8_t* const cur = lds + (g % G::NB) * G::IMG;
+  uint8_t* const cur = lds + slot * G::IMG;
 #pragma unroll
   for (int sg = 0; sg < G::NSG; ++sg) {
     const int tb = sg * G::TPS;
@@ -538,7 +540,14 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
 
   wait_vm<0>();  // the first groups and the Q operand
   lds_barrier();
-  for (int g = 0; g + 1 < ngroups; ++g)
+  int g = 0;
+  if (G::NB == 2) {
+    for (; g + 2 < ngroups; g += 2) {
+      group_iter<D, KVB, DBG, false, US, 0>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+      group_iter<D, KVB, DBG, false, US, 1>(a, rsrc, g + 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+    }
+  }
+  for (; g + 1 < ngroups; ++g)
     group_iter<D, KVB, DBG, false, US>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
   group_iter<D, KVB, DBG, true, US>(a, rsrc, ngroups - 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
 
