@@ -76,28 +76,43 @@ __global__ void k1_zero_u32(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-// V channel amax over all tokens: tile of 128 tokens, atomic max on the float
-// bits (non-negative floats order like unsigned integers).
+// V channel amax over all tokens.  A workgroup takes kVTile tokens of one head:
+// thread t owns 8 consecutive channels (one 16-byte load per token for 16-bit
+// inputs) of every (256 / (D/8))-th token, the partial maxima meet in LDS, and one
+// atomic max per channel on the float bits (non-negative floats order like unsigned
+// integers) merges the workgroups.
+constexpr int kVTile = 512;
 template <int D, int DT>
 __global__ __launch_bounds__(256) void k1_vamax(QuantArgs a) {
+  constexpr int CG = D / 8, TL = 256 / CG;  // channel groups, tokens in flight
+  __shared__ float red[TL][D + 1];
   const Shape s = a.s;
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int bh = blockIdx.y;
-  const int64_t n0 = (int64_t)blockIdx.x * kTile;
+  const int64_t n0 = (int64_t)blockIdx.x * kVTile;
   const void* base = (const char*)a.v + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
-  constexpr int G = 256 / D;
-  const int c = threadIdx.x % D, g = threadIdx.x / D;
-  float m = 0.f;
-  for (int r = g; r < kTile; r += G) {
+  const int cg = threadIdx.x % CG, tl = threadIdx.x / CG;
+  float m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = 0.f;
+#pragma unroll 4
+  for (int r = tl; r < kVTile; r += TL) {
     const int64_t n = n0 + r;
-    if (n < N) m = fmaxf(m, fabsf(load_elem<DT>(base, n * D + c)));
+    if (n < N) {
+      float x[8];
+      load_slice<DT, 8>(base, n, D, 8 * cg, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(x[e]));
+    }
   }
-  __shared__ float red[256];
-  red[threadIdx.x] = m;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[tl][8 * cg + e] = m[e];
   __syncthreads();
-  if (g == 0) {
-    for (int k = 1; k < G; ++k) m = fmaxf(m, red[k * D + c]);
-    atomicMax(a.vamax + (int64_t)bh * D + c, __float_as_uint(m));
+  if (threadIdx.x < D) {
+    float r = 0.f;
+#pragma unroll
+    for (int k = 0; k < TL; ++k) r = fmaxf(r, red[k][threadIdx.x]);
+    atomicMax(a.vamax + (int64_t)bh * D + threadIdx.x, __float_as_uint(r));
   }
 }
 
@@ -288,7 +303,7 @@ hipError_t launch_quantize_t(const QuantArgs& a, hipStream_t st) {
     if (attr != hipSuccess) return attr;
   }
   k1_zero_u32<<<(unsigned)((nvamax + 255) / 256), 256, 0, st>>>(a.vamax, nvamax);
-  k1_vamax<D, DT><<<dim3((unsigned)(a.Np / kTile), BH), 256, 0, st>>>(a);
+  k1_vamax<D, DT><<<dim3((unsigned)((a.Np + kVTile - 1) / kVTile), BH), 256, 0, st>>>(a);
   hipError_t e;
   if (a.rot == 1) e = launch_rot<D, DT, 1>(a, st);
   else if (a.rot == 2) e = launch_rot<D, DT, 2>(a, st);
