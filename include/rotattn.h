@@ -132,8 +132,8 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
  *   out  = O / l.
  * The rotation mode is not needed: an orthogonal R cancels in Q K^T.
  *   heads/n_heads  host list of flat head ids b*H + h to compute; NULL = all.
- *   out_dtype      F32 or F16; out device [B,H,N,D]; rows of heads not listed are
- *                  left untouched.
+ *   out_dtype      F32, F16 or BF16 (round to nearest even); out device [B,H,N,D];
+ *                  rows of heads not listed are left untouched.
  *   dbg            NULL in production.  Otherwise a debug run for rows
  *                  [row0, row0+n_rows) of head `bh` only, writing (device):
  *                  a_qk [n_rows][N] i32, p_codes [n_rows][N] i8 (P~),
@@ -141,9 +141,11 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
  *                  sum_j (P~+8) vc), m [n_rows] f32, l [n_rows] f32.  The output
  *                  rows are written as well.
  *   workspace      device, >= rotattn_int4_attention_workspace(s) bytes, 16-byte
- *                  aligned (2*D bytes per padded token and head: the listed heads'
- *                  K and V codes restaged as fp8 / int8 MFMA operands).  Contents
- *                  need no initialisation; a smaller size returns
+ *                  aligned: per head and 128-key group (32 keys for kv_blk 16), the
+ *                  listed heads' K and V codes restaged as the LDS image of fp6 K
+ *                  rows and fp8 V^T rows (36 KiB per 128 keys for D = 128, about
+ *                  288 bytes per padded token and head).  Contents need no
+ *                  initialisation; a smaller size returns
  *                  ROTATTN_E_WORKSPACE before any launch.  Shapes whose images
  *                  exceed 2^31 bytes per head (N beyond about 6.7 million tokens)
  *                  return ROTATTN_E_UNSUPPORTED. */
@@ -170,7 +172,8 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
  * Full-precision fallback for sensitive heads / denoising steps (Key design 3):
  * out = softmax(RoPE(Q) RoPE(K)^T / sqrt(D)) V with binary16 MFMA operands and
  * binary32 softmax and accumulation.  RoPE'd Q, K are rounded to binary16.
- *   in_dtype   F16 (the only one implemented).
+ *   in_dtype   F32, F16 or BF16 (Q, K after RoPE and V are rounded to binary16).
+ *   out_dtype  F32, F16 or BF16.
  *   rope_table plain (cos, sin) table: rotattn_build_rope_table(s, NONE, ...).
  *   heads      as above.  workspace >= rotattn_fp16_fallback_workspace(s). */
 size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s);

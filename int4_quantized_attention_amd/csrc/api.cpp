@@ -181,7 +181,7 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
   if (rotattn_int4_attention_workspace(s) / ((size_t)s->B * s->H) > (size_t)INT32_MAX) return ROTATTN_E_UNSUPPORTED;
   if (workspace_bytes < rotattn_int4_attention_workspace(s) || ((uintptr_t)workspace & 15) != 0)
     return ROTATTN_E_WORKSPACE;
-  if (out_dtype != ROTATTN_F32 && out_dtype != ROTATTN_F16) return ROTATTN_E_ARG;
+  if (out_dtype < ROTATTN_F32 || out_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
   const int BH = s->B * s->H;
   if (heads) {
     if (n_heads < 0) return ROTATTN_E_ARG;
@@ -195,7 +195,7 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
   a.img = (uint8_t*)workspace;
   a.img_bytes = (int64_t)workspace_bytes;
   a.out = out;
-  a.out_f16 = out_dtype == ROTATTN_F16;
+  a.out_kind = (int)out_dtype;
   a.N = N;
   a.Np = rotattn_padded_tokens(s);
   a.qk_blk = s->qk_blk;
@@ -243,8 +243,8 @@ rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dt
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rope_table || !out || !workspace) return ROTATTN_E_NULL;
-  if (in_dtype != ROTATTN_F16) return ROTATTN_E_UNSUPPORTED;
-  if (out_dtype != ROTATTN_F32 && out_dtype != ROTATTN_F16) return ROTATTN_E_ARG;
+  if (in_dtype < ROTATTN_F32 || in_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
+  if (out_dtype < ROTATTN_F32 || out_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
   if (workspace_bytes < rotattn_fp16_fallback_workspace(s)) return ROTATTN_E_WORKSPACE;
   const int BH = s->B * s->H;
   if (heads) {
@@ -264,7 +264,7 @@ rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dt
   a.kr = (_Float16*)((char*)workspace + per);
   a.vt = (_Float16*)((char*)workspace + 2 * per);
   a.out = out;
-  a.out_f16 = out_dtype == ROTATTN_F16;
+  a.out_kind = (int)out_dtype;
   a.nqt = (int)((a.N + 127) / 128);
   a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)s->D));
   hipStream_t hs = (hipStream_t)stream;
@@ -274,7 +274,7 @@ rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dt
     a.nheads = cnt;
     for (int i = 0; i < cnt; ++i) a.heads[i] = heads ? heads[h0 + i] : h0 + i;
     grid_map(a.nqt, cnt, a.total, a.per_xcd);
-    if (ra::launch_fallback_prep(a, hs) != hipSuccess) return ROTATTN_E_HIP;
+    if (ra::launch_fallback_prep(a, (int)in_dtype, hs) != hipSuccess) return ROTATTN_E_HIP;
     if (ra::launch_fallback(a, hs) != hipSuccess) return ROTATTN_E_HIP;
   }
   return ROTATTN_OK;

@@ -571,12 +571,7 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
           o[e] = S.acc[db][v] * args.vs[(int64_t)bh * D + d0 + e] * inv;
         }
         const int64_t off = ((int64_t)bh * N + qi) * D + d0;
-        if (args.out_f16) {
-          f16x4 hv = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
-          *(f16x4*)((_Float16*)args.out + off) = hv;
-        } else {
-          *(f32x4*)((float*)args.out + off) = f32x4{o[0], o[1], o[2], o[3]};
-        }
+        store_out4(args.out, args.out_kind, off, o[0], o[1], o[2], o[3]);
       }
     }
   }

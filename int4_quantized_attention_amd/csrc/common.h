@@ -16,6 +16,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 #define RA_DEV __device__ __forceinline__
 
+
 namespace ra {
 
 // ---- input element loads --------------------------------------------------------
@@ -84,6 +85,27 @@ RA_DEV float pair_max(float v) {
 RA_DEV float pair_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// binary32 -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN)
+RA_DEV uint16_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// four consecutive output values at element offset off of a binary32, binary16 or
+// bfloat16 tensor (kind 0, 1, 2)
+RA_DEV void store_out4(void* out, int kind, int64_t off, float o0, float o1, float o2, float o3) {
+  if (kind == 1) {
+    *(f16x4*)((_Float16*)out + off) = f16x4{(_Float16)o0, (_Float16)o1, (_Float16)o2, (_Float16)o3};
+  } else if (kind == 2) {
+    const uint32_t w0 = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
+    *(u32x2*)((uint16_t*)out + off) = u32x2{w0, w1};
+  } else {
+    *(f32x4*)((float*)out + off) = f32x4{o0, o1, o2, o3};
+  }
 }
 
 }  // namespace ra

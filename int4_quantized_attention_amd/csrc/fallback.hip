@@ -244,22 +244,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = O[db][v4 * 4 + e] * inv;
-        if (args.out_f16) {
-          *(f16x4*)((_Float16*)args.out + off) = f16x4{(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
-        } else {
-          *(f32x4*)((float*)args.out + off) = f32x4{o[0], o[1], o[2], o[3]};
-        }
+        store_out4(args.out, args.out_kind, off, o[0], o[1], o[2], o[3]);
       }
     }
   }
 }
 
-hipError_t launch_fallback_prep(const FbArgs& a, hipStream_t st) {
+template <int D, int DT>
+hipError_t launch_prep_t(const FbArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.Np / kFbTile), a.nheads, 3);
-  const size_t lds = (size_t)kFbTile * (a.s.D + 2) * 2;
-  if (a.s.D == 128) k3_prep<128, 1><<<grid, 256, lds, st>>>(a);
-  else k3_prep<64, 1><<<grid, 256, lds, st>>>(a);
+  const size_t lds = (size_t)kFbTile * (DT == 0 ? (D + 1) * 4 : (D + 2) * 2);  // the staged input tile
+  k3_prep<D, DT><<<grid, 256, lds, st>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_fallback_prep(const FbArgs& a, int dtype, hipStream_t st) {
+  if (a.s.D == 128) {
+    if (dtype == 0) return launch_prep_t<128, 0>(a, st);
+    if (dtype == 1) return launch_prep_t<128, 1>(a, st);
+    return launch_prep_t<128, 2>(a, st);
+  }
+  if (dtype == 0) return launch_prep_t<64, 0>(a, st);
+  if (dtype == 1) return launch_prep_t<64, 1>(a, st);
+  return launch_prep_t<64, 2>(a, st);
 }
 
 template <int D>

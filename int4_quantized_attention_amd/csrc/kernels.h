@@ -43,7 +43,7 @@ struct AttnArgs {
   uint8_t* img;   // workspace: per-group LDS images of K (packed fp6) and V^T (fp8)
   int64_t img_bytes;  // its size (images that would not fit are neither written nor read)
   void* out;
-  int out_f16;
+  int out_kind;  // 0 binary32, 1 binary16, 2 bfloat16
   int64_t N, Np;
   int qk_blk;
   int nqt, total, per_xcd;
@@ -71,7 +71,7 @@ struct FbArgs {
   _Float16* kr;   // workspace: RoPE'd K  [B*H][Np][D] f16
   _Float16* vt;   // workspace: V^T       [B*H][D][Np] f16 (32-key groups permuted)
   void* out;
-  int out_f16;
+  int out_kind;  // 0 binary32, 1 binary16, 2 bfloat16
   int nqt, total, per_xcd;
   float scale_log2;  // log2(e) / sqrt(D)
   int nheads;
@@ -83,7 +83,7 @@ hipError_t launch_attention(const AttnArgs& a, int D, int kv_blk, bool dbg, hipS
 // bytes of the attention workspace: the per-group LDS images of every head (the
 // image geometry lives with the kernel; D, kv_blk as validated by the API)
 size_t attention_workspace_bytes(int D, int kv_blk, int64_t BH, int64_t Np);
-hipError_t launch_fallback_prep(const FbArgs& a, hipStream_t st);
+hipError_t launch_fallback_prep(const FbArgs& a, int dtype, hipStream_t st);
 hipError_t launch_fallback(const FbArgs& a, hipStream_t st);
 
 }  // namespace ra

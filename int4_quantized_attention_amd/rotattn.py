@@ -167,11 +167,11 @@ def rotattn_quantize_qk(shape: Shape, rot: int, q: torch.Tensor, k: torch.Tensor
 
 def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Optional[Sequence[int]] = None,
                            debug: Optional[dict] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out: device [B,H,N,D] float32 or float16.  debug: dict(bh, row0, n_rows) ->
+    """out: device [B,H,N,D] float32, float16 or bfloat16.  debug: dict(bh, row0, n_rows) ->
     filled with device tensors a_qk, p_codes, a_pv, m, l.  workspace: device uint8
     tensor of rotattn_int4_attention_workspace(shape) bytes (default z["attn_workspace"])."""
-    if out.dtype not in (torch.float32, torch.float16):
-        raise RotattnError("out must be float32 or float16")
+    if out.dtype not in _DT:
+        raise RotattnError("out must be float32, float16 or bfloat16")
     harr, nh = _heads(heads)
     ws = workspace if workspace is not None else z["attn_workspace"]
     dbg = None
@@ -189,7 +189,7 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
                     debug["l"].data_ptr())
     _check(lib().rotattn_int4_attention(
         ctypes.byref(shape), _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
-        _ptr(z["v_codes"]), _ptr(z["v_scale"]), harr, nh, F16 if out.dtype == torch.float16 else F32,
+        _ptr(z["v_codes"]), _ptr(z["v_scale"]), harr, nh, _DT[out.dtype],
         _ptr(out), ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(), _stream()),
         "rotattn_int4_attention")
     return out
@@ -198,11 +198,15 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
 def rotattn_fp16_fallback(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           rope_table: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
                           heads: Optional[Sequence[int]] = None) -> torch.Tensor:
-    if q.dtype != torch.float16:
-        raise RotattnError("the fallback takes float16 q, k, v")
+    """q, k, v: device [B,H,N,D] of one of float32 / float16 / bfloat16 (rounded to
+    binary16 after RoPE); out: float32, float16 or bfloat16."""
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise RotattnError("q, k, v must share one of float32 / float16 / bfloat16")
+    if out.dtype not in _DT:
+        raise RotattnError("out must be float32, float16 or bfloat16")
     harr, nh = _heads(heads)
     _check(lib().rotattn_fp16_fallback(
-        ctypes.byref(shape), F16, _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table), harr, nh,
-        F16 if out.dtype == torch.float16 else F32, _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
+        ctypes.byref(shape), _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table), harr, nh,
+        _DT[out.dtype], _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
         "rotattn_fp16_fallback")
     return out

@@ -80,9 +80,6 @@ def test_null_and_bad_args_return_before_launch(L):
     st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, bad_heads, 1, 0,
                                   fake, nul, fake, big, nul)
     assert st == 6
-    st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 2,
-                                  fake, nul, fake, big, nul)
-    assert st == 6  # bf16 output is not offered
     st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 0,
                                   fake, nul, fake, 64, nul)
     assert st == 4  # attention workspace too small
@@ -92,9 +89,15 @@ def test_null_and_bad_args_return_before_launch(L):
     st = L.rotattn_quantize_qk(ctypes.byref(s), 1, 0, fake, fake, fake, fake, 1, fake, fake, fake, fake,
                                fake, fake, nul, fake, 16, nul)
     assert st == 4  # workspace too small
-    st = L.rotattn_fp16_fallback(ctypes.byref(s), 0, fake, fake, fake, fake, nul, 0, 0, fake, fake,
+    st = L.rotattn_fp16_fallback(ctypes.byref(s), 7, fake, fake, fake, fake, nul, 0, 0, fake, fake,
                                  1 << 30, nul)
-    assert st == 3  # only float16 inputs
+    assert st == 6  # input dtype outside F32 / F16 / BF16
+    st = L.rotattn_fp16_fallback(ctypes.byref(s), 2, fake, fake, fake, fake, nul, 0, 5, fake, fake,
+                                 1 << 30, nul)
+    assert st == 6  # output dtype outside F32 / F16 / BF16
+    st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 3,
+                                  fake, nul, fake, big, nul)
+    assert st == 6  # output dtype outside F32 / F16 / BF16
     assert L.rotattn_status_str(0) == b"ok"
 
 

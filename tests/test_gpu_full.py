@@ -37,6 +37,27 @@ def test_fallback_parity_medium(orc):
     assert_close(out.cpu().numpy().reshape(-1, 128), ref)
 
 
+@pytest.mark.parametrize("in_dt,out_dt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float16)])
+def test_fallback_input_output_dtypes(orc, in_dt, out_dt):
+    cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float32", recipe="peaked")
+    Q, K, V = synth.make_inputs(cfg)
+    # the oracle sees exactly the values the library reads
+    Qd, Kd, Vd = (torch.from_numpy(x).to(in_dt) for x in (Q, K, V))
+    Qf, Kf, Vf = (x.float().numpy() for x in (Qd, Kd, Vd))
+    shape = ra.Shape.of(cfg)
+    tab = ra.rotattn_build_rope_table(shape, 0).cuda()
+    ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
+    N = synth.n_tokens(cfg)
+    out = torch.full((1, 2, N, 128), float("nan"), dtype=out_dt, device="cuda")
+    ra.rotattn_fp16_fallback(shape, Qd.cuda(), Kd.cuda(), Vd.cuda(), tab, out, ws)
+    ref = orc.fallback_attention(cfg, orc.rope_table(cfg, 0), Qf, Kf, Vf)
+    if out_dt == torch.bfloat16:  # bf16 rounding (unit roundoff 2^-8) on top of the binary32 bar
+        tol = (2e-3 + 2.0**-8 * float(np.abs(ref).max()), 1e-3 + 2.0**-8)
+    else:
+        tol = (4e-3, 1.5e-3)
+    assert_close(out.float().cpu().numpy().reshape(-1, 128), ref, *tol)
+
+
 @pytest.mark.parametrize("name", ["wan480p", "wan720p", "hunyuan720p"])
 def test_full_config_int4(orc, name):
     cfg = synth.CONFIGS[name]
