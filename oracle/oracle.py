@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rotattn_oracle.cpp")
 _LIB = os.path.join(_HERE, "liborc.so")
 
-ROT_NONE, ROT_INTERLEAVED, ROT_HALF = 0, 1, 2
+ROT_NONE, ROT_INTERLEAVED, ROT_HALF, ROT_FULL = 0, 1, 2, 3
 
 _lib = None
 
@@ -123,10 +123,14 @@ def quantize(shape, rot: int, table: np.ndarray, q, k, v, smooth_k: bool = True,
     return r
 
 
-def attention(shape, qz: dict, rows=None, dumps: bool = False):
+def attention(shape, qz: dict, rows=None, dumps: bool = False, pmax: int = 15):
     """Quantised attention for flat rows (b*H + h)*N + i (default: all rows).
     Returns dict with 'out' [rows, D] float64 and, with dumps, 'a_qk' [rows, N]
-    int32, 'pcode' [rows, N] int8, 'a_pv' [rows, S, D] int32, 'm' f32, 'l' f64."""
+    int32, 'pcode' [rows, N] int8, 'a_pv' [rows, S, D] int32, 'm' f32, 'l' f64.
+    pmax = 15: range-rectified P codes r - 8 in [-8, 7] (the method); pmax = 7: the
+    symmetric baseline, codes r = round(7 P) in [0, 7]."""
+    if pmax not in (7, 15):
+        raise ValueError("pmax is 15 (range-rectified) or 7 (symmetric baseline)")
     s = shape_array(shape)
     B, H, D = int(shape["B"]), int(shape["H"]), int(shape["D"])
     N = n_tokens(shape)
@@ -141,12 +145,12 @@ def attention(shape, qz: dict, rows=None, dumps: bool = False):
                    a_pv=np.empty((R, S, D), np.int32), m=np.empty(R, np.float32),
                    l=np.empty(R, np.float64))
     c = lambda a, t: np.ascontiguousarray(a, dtype=t)
-    lib().orc_attention(_p(s), _p(c(qz["qc"], np.int8)), _p(c(qz["qs"], np.float32)),
+    lib().orc_attention_p(_p(s), _p(c(qz["qc"], np.int8)), _p(c(qz["qs"], np.float32)),
                         _p(c(qz["kc"], np.int8)), _p(c(qz["ks"], np.float32)),
                         _p(c(qz["vc"], np.int8)), _p(c(qz["vs"], np.float32)),
                         _p(rows), ctypes.c_int64(R), _p(res["out"]),
                         _p(res.get("a_qk")), _p(res.get("pcode")), _p(res.get("a_pv")),
-                        _p(res.get("m")), _p(res.get("l")))
+                        _p(res.get("m")), _p(res.get("l")), ctypes.c_int32(pmax))
     return res
 
 

@@ -81,6 +81,12 @@ inline double fmaT(double a, double b, double c) { return std::fma(a, b, c); }
 //   rot 0: RoPE only.  rot 1: Interleaved (fused table, H2 on pairs (2i, 2i+1)).
 //   rot 2: Half: RoPE, then per segment pair channel o+i with o+Dj/2+i and apply
 //          H2, writing the pair to channels (o+2i, o+2i+1)  (the QPiR product).
+//   rot 3: Full: RoPE, then the orthonormal D x D Walsh-Hadamard rotation of the
+//          whole vector (the dense rotation the pages compare the Half one with,
+//          papernotes "Key design 1" cost comparison; an ablation, not the method).
+//          Fast Walsh-Hadamard transform: for stride len = 1, 2, 4, ..., D/2, every
+//          pair (x[i], x[i+len]) with i & len == 0 becomes (x[i] + x[i+len],
+//          x[i] - x[i+len]); then every channel times fl(1/sqrt(D)).
 // binary32 op order:  u = fma(a, c, -(b*s)), v = fma(a, s, b*c);
 //   fused: o0 = fma(a, al, b*be), o1 = fma(a, be, -(b*al));
 //   half:  o0 = (x1 + x2) * r, o1 = (x1 - x2) * r, r = (float)(1/sqrt2).
@@ -116,11 +122,22 @@ void rope_rotate_token(const Shape& s, int rot, const T* tab, int64_t n, const T
         out[off + 2 * i] = (x1 + x2) * r;
         out[off + 2 * i + 1] = (x1 - x2) * r;
       }
-    } else {
+    } else if (rot != 3) {
       for (int i = 0; i < dj[ax]; ++i) out[off + i] = u[off + i];
     }
     axtab += (int64_t)npos[ax] * dj[ax];
     off += dj[ax];
+  }
+  if (rot == 3) {
+    for (int len = 1; len < s.D; len *= 2)
+      for (int i = 0; i < s.D; ++i)
+        if ((i & len) == 0) {
+          const T a = u[i], b = u[i + len];
+          u[i] = a + b;
+          u[i + len] = a - b;
+        }
+    const T rd = (T)(1.0 / std::sqrt((double)s.D));
+    for (int i = 0; i < s.D; ++i) out[i] = u[i] * rd;
   }
 }
 
@@ -391,15 +408,21 @@ int64_t orc_p_level_bruteforce(float lo, float hi, float* first) {
 //   out   = O / l.
 // Optional dumps: a_qk [rows][N] int32, pcode [rows][N] int8 (P~),
 // a_pv [rows][S][D] int32 (per-step sum_j r_ij vc_jd), m_out [rows] f32, l_out.
-void orc_attention(const int32_t* shp, const int8_t* qc, const float* qs,
-                   const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
-                   const int64_t* rows, int64_t n_rows, double* out,
-                   int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out) {
+//
+// pmax = 7 gives the symmetric-P baseline the pages argue against (papernotes,
+// "Key design 2": code = round(P / max P * 7) in [0, 7], which leaves the negative
+// half of INT4 unused): the same steps with L = fl(log2 7) in place of L15, so
+// r = round-half-even(7 P) in [0, 7], and the code is r itself (no zero point).
+void orc_attention_p(const int32_t* shp, const int8_t* qc, const float* qs,
+                     const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
+                     const int64_t* rows, int64_t n_rows, double* out,
+                     int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out, int32_t pmax) {
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
   const int64_t nqb = (N + s.qk_blk - 1) / s.qk_blk;
   const int64_t S = (N + s.kv_blk - 1) / s.kv_blk;
-  const float C0 = c0_of(s.D), L15 = l15();
+  const float C0 = c0_of(s.D), L15 = pmax == 7 ? (float)std::log2(7.0) : l15();
+  const int zp = pmax == 7 ? 0 : 8;
 #pragma omp parallel for schedule(dynamic)
   for (int64_t ri = 0; ri < n_rows; ++ri) {
     const int64_t row = rows[ri];
@@ -435,7 +458,7 @@ void orc_attention(const int32_t* shp, const int8_t* qc, const float* qs,
       for (int64_t j = j0; j < j1; ++j) {
         const float y = std::fmaf((float)a[j - j0], c[j - j0], nm);
         const int r = p_level(y);
-        if (pcode) pcode[ri * N + j] = (int8_t)(r - 8);
+        if (pcode) pcode[ri * N + j] = (int8_t)(r - zp);
         l += std::exp2((double)y);
         const int8_t* vrow = vc + (bh * N + j) * D;
         for (int64_t d = 0; d < D; ++d) acc[d] += (int64_t)r * vrow[d];
@@ -450,6 +473,13 @@ void orc_attention(const int32_t* shp, const int8_t* qc, const float* qs,
     if (m_out) m_out[ri] = m;
     if (l_out) l_out[ri] = l;
   }
+}
+
+void orc_attention(const int32_t* shp, const int8_t* qc, const float* qs,
+                   const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
+                   const int64_t* rows, int64_t n_rows, double* out,
+                   int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out) {
+  orc_attention_p(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, 15);
 }
 
 // ---------------------------------------------------------------------------

@@ -375,3 +375,87 @@ def test_report_cosine_vs_exact_tiny(orc, capsys):
         rel = float(np.linalg.norm(o - ex) / np.linalg.norm(ex))
         print("tiny rot=%d cosine=%.4f relL2=%.4f" % (rot, cos, rel))
         assert cos > 0.5
+
+
+# ---- ablation variants ------------------------------------------------------------
+
+def test_full_rotation_is_the_orthonormal_hadamard_after_rope(orc):
+    """rot 3 (Full): the butterfly transform after plain RoPE equals the dense
+    Sylvester-Hadamard product H_D / sqrt(D) applied to the RoPE output (a different
+    algorithm: scipy's matrix, one binary64 matmul), and keeps the norm."""
+    from scipy.linalg import hadamard
+    for D, split in [(64, (24, 20, 20)), (128, (44, 42, 42))]:
+        cfg = synth.custom(1, 2, 2, 3, 4, D, *split, 16, 16, recipe="tiny")
+        q, _, _ = synth.make_inputs(cfg)
+        tab = orc.rope_table(cfg, 0, f64=True)
+        x = q.astype(np.float64)
+        plain = orc.rope_rotate(cfg, 0, tab, x)
+        full = orc.rope_rotate(cfg, 3, tab, x)
+        Hn = hadamard(D).astype(np.float64) / np.sqrt(D)
+        want = plain @ Hn.T
+        assert np.max(np.abs(full - want)) <= 1e-12 * np.max(np.abs(want))
+        assert np.allclose(np.linalg.norm(full, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-12)
+        # binary32 path: the same transform within a few binary32 roundings per stage
+        full32 = orc.rope_rotate(cfg, 3, orc.rope_table(cfg, 0), q)
+        assert np.max(np.abs(full32 - want)) <= 16 * 2.0**-24 * np.sqrt(D) * np.max(np.abs(x))
+
+
+def test_full_rotation_keeps_qk(orc):
+    """Q K^T is unchanged by the Full rotation (orthogonal), in binary64."""
+    cfg = dict(TINY)
+    q, k, _ = synth.make_inputs(cfg)
+    q, k = q.astype(np.float64), k.astype(np.float64)
+    t0 = orc.rope_table(cfg, 0, f64=True)
+    for h in range(cfg["H"]):
+        a = orc.rope_rotate(cfg, 0, t0, q)[0, h] @ orc.rope_rotate(cfg, 0, t0, k)[0, h].T
+        b = orc.rope_rotate(cfg, 3, t0, q)[0, h] @ orc.rope_rotate(cfg, 3, t0, k)[0, h].T
+        assert np.max(np.abs(a - b)) <= 1e-13 * np.max(np.abs(a))
+
+
+def test_symmetric_p_single_token_and_zero_query(orc):
+    """Symmetric baseline (pmax 7): with one key, or with Q = 0, every P is 1, so
+    every code is round(7 * 1) = 7 with no zero point, and the output is the
+    dequantised V row / the mean of the dequantised V rows (closed form)."""
+    cfg = synth.custom(1, 3, 1, 1, 1, 64, 24, 20, 20, 16, 16)
+    q, k, v = synth.make_inputs(cfg)
+    z = orc.quantize(cfg, 2, orc.rope_table(cfg, 2), q, k, v)
+    r = orc.attention(cfg, z, dumps=True, pmax=7)
+    assert np.all(r["pcode"] == 7)
+    assert np.allclose(r["out"], _dequant_v(z).reshape(3, 64), rtol=1e-6, atol=0)
+    cfg = dict(TINY, kv_blk=16)
+    q, k, v = synth.make_inputs(cfg)
+    q[:] = 0
+    z = orc.quantize(cfg, 1, orc.rope_table(cfg, 1), q, k, v)
+    r = orc.attention(cfg, z, dumps=True, pmax=7)
+    assert np.all(r["pcode"] == 7)
+    want = np.repeat(_dequant_v(z).mean(axis=2), 32, axis=1).reshape(-1, 64)
+    assert np.allclose(r["out"], want, rtol=1e-6, atol=1e-7)
+
+
+def test_symmetric_p_codes_are_round_7p(orc):
+    """Symmetric baseline: code = round-half-even(7 P) with P = 2^(t - m_s), m_s the
+    running maximum (binary64 recomputation from the dumped integer scores; ties and
+    near-ties, where binary32 and binary64 may decide differently, are skipped)."""
+    cfg = dict(TINY, kv_blk=16)
+    q, k, v = synth.make_inputs(cfg)
+    z = orc.quantize(cfg, 2, orc.rope_table(cfg, 2), q, k, v)
+    r = orc.attention(cfg, z, dumps=True, pmax=7)
+    N, D = 32, 64
+    C0 = np.float32(orc.c0(D))
+    checked = 0
+    for row in range(2 * N):
+        bh, i = divmod(row, N)
+        sq = z["qs"][0, bh, i // 16]
+        m = -np.inf
+        for s0 in range(0, N, 16):
+            cs = np.float32(np.float32(sq) * z["ks"][0, bh, np.arange(s0, s0 + 16) // 16]) * C0
+            t = (r["a_qk"][row, s0:s0 + 16].astype(np.float32) * cs).astype(np.float32)
+            m = max(m, float(t.max()))
+            x = 7.0 * np.exp2(r["a_qk"][row, s0:s0 + 16].astype(np.float64) * cs.astype(np.float64) - m)
+            frac = np.abs(x - np.floor(x) - 0.5)
+            ok = frac > 1e-5
+            want = np.rint(x)
+            assert np.array_equal(r["pcode"][row, s0:s0 + 16][ok], want[ok].astype(np.int8))
+            checked += int(ok.sum())
+    assert checked > 0.99 * 2 * N * N
+    assert r["pcode"].min() >= 0 and r["pcode"].max() <= 7
