@@ -55,8 +55,10 @@ typedef enum {
   ROTATTN_ROT_NONE = 0,        /* RoPE only                                       */
   ROTATTN_ROT_INTERLEAVED = 1, /* H2 on channel pairs (2i, 2i+1), pre-multiplied   */
                                /* into the RoPE 2x2 blocks (M' = R M)             */
-  ROTATTN_ROT_HALF = 2         /* per segment: pair channel i with i + Dj/2, H2,  */
+  ROTATTN_ROT_HALF = 2,        /* per segment: pair channel i with i + Dj/2, H2,  */
                                /* results at (2i, 2i+1)  (Q Pi R)                 */
+  ROTATTN_ROT_FULL = 3         /* ablation: after plain RoPE, the orthonormal     */
+                               /* D x D Walsh-Hadamard rotation of all channels   */
 } rotattn_rot;
 
 typedef enum { ROTATTN_F32 = 0, ROTATTN_F16 = 1, ROTATTN_BF16 = 2 } rotattn_dtype;
@@ -105,7 +107,10 @@ rotattn_status rotattn_build_rope_table(const rotattn_shape* s, rotattn_rot rot,
  *                                       codes (the zero-point term of P~ V)
  * Binary32 op order (bit-reproducible): RoPE u = fma(a,c,-(b*s)), v = fma(a,s,b*c);
  * fused Interleaved o0 = fma(a,al,b*be), o1 = fma(a,be,-(b*al)); Half
- * o0 = (x1+x2)*r, o1 = (x1-x2)*r with r = (float)(1/sqrt2); K mean = binary64 sum
+ * o0 = (x1+x2)*r, o1 = (x1-x2)*r with r = (float)(1/sqrt2); Full (ablation): plain
+ * RoPE, then for stride len = 1, 2, ..., D/2 every pair (x[i], x[i+len]) with
+ * i & len == 0 becomes (x[i]+x[i+len], x[i]-x[i+len]), then x * fl(1/sqrt(D));
+ * K mean = binary64 sum
  * of in-order 64-token partial sums, in block order, / N, rounded to binary32;
  * code = clamp(rint(x * (7/amax)), -7, 7), scale = amax/7 (IEEE division);
  * amax == 0 gives scale 0 and codes 0.
@@ -183,6 +188,22 @@ rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dt
                                      const int32_t* heads, int32_t n_heads,
                                      rotattn_dtype out_dtype, void* out,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- rotattn_int4_attention_symmetric_p ------------------------------------------
+ * Ablation baseline, not the method: the same INT4 attention with the symmetric
+ * INT4 P code the pages argue against (papernotes note, Key design 2: a symmetric
+ * code round(P / max P * 7) uses only [0, 7], wasting the negative half of INT4).
+ * Identical to rotattn_int4_attention except L15 -> fl(log2 7): r_ij = round-half-
+ * even(7 P_ij) in [0, 7], the code is r itself (debug p_codes hold r), and
+ * l = sum_j 7 P_ij.  Arguments, layouts, workspace and errors as there. */
+rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
+                                                  const uint8_t* q_codes, const float* q_scale,
+                                                  const uint8_t* k_codes, const float* k_scale,
+                                                  const uint8_t* v_codes, const float* v_scale,
+                                                  const int32_t* heads, int32_t n_heads,
+                                                  rotattn_dtype out_dtype, void* out,
+                                                  const rotattn_debug* dbg,
+                                                  void* workspace, size_t workspace_bytes, void* stream);
 
 const char* rotattn_status_str(rotattn_status st);
 

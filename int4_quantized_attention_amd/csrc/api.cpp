@@ -88,7 +88,7 @@ rotattn_status rotattn_build_rope_table(const rotattn_shape* s, rotattn_rot rot,
   if (!s || !host_out) return ROTATTN_E_NULL;
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
-  if (rot < ROTATTN_ROT_NONE || rot > ROTATTN_ROT_HALF || !(base > 1.0)) return ROTATTN_E_ARG;
+  if (rot < ROTATTN_ROT_NONE || rot > ROTATTN_ROT_FULL || !(base > 1.0)) return ROTATTN_E_ARG;
   const int npos[3] = {s->F, s->Hs, s->Ws};
   const int dj[3] = {s->Df, s->Dh, s->Dw};
   const double half_sqrt2 = 0.70710678118654752440;  // nearest binary64 to 1/sqrt(2)
@@ -141,7 +141,7 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
   if (!q || !k || !v || !rope_table || !q_codes || !q_scale || !k_codes || !k_scale || !v_codes ||
       !v_scale || !workspace)
     return ROTATTN_E_NULL;
-  if (rot < ROTATTN_ROT_NONE || rot > ROTATTN_ROT_HALF) return ROTATTN_E_ARG;
+  if (rot < ROTATTN_ROT_NONE || rot > ROTATTN_ROT_FULL) return ROTATTN_E_ARG;
   if (in_dtype < ROTATTN_F32 || in_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
   size_t off_mu, off_amax;
   if (workspace_bytes < q_ws_parts(s, &off_mu, &off_amax)) return ROTATTN_E_WORKSPACE;
@@ -165,14 +165,17 @@ size_t rotattn_int4_attention_workspace(const rotattn_shape* s) {
   return ra::attention_workspace_bytes(s->D, s->kv_blk, (int64_t)s->B * s->H, rotattn_padded_tokens(s));
 }
 
-rotattn_status rotattn_int4_attention(const rotattn_shape* s,
-                                      const uint8_t* q_codes, const float* q_scale,
-                                      const uint8_t* k_codes, const float* k_scale,
-                                      const uint8_t* v_codes, const float* v_scale,
-                                      const int32_t* heads, int32_t n_heads,
-                                      rotattn_dtype out_dtype, void* out,
-                                      const rotattn_debug* dbg,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// Both attention entry points: pmax 15 is the method (range-rectified P codes),
+// pmax 7 the symmetric baseline of the ablation.
+rotattn_status attention_call(const rotattn_shape* s,
+                              const uint8_t* q_codes, const float* q_scale,
+                              const uint8_t* k_codes, const float* k_scale,
+                              const uint8_t* v_codes, const float* v_scale,
+                              const int32_t* heads, int32_t n_heads,
+                              rotattn_dtype out_dtype, void* out,
+                              const rotattn_debug* dbg,
+                              void* workspace, size_t workspace_bytes, void* stream, int pmax) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
   if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !out || !workspace)
@@ -201,7 +204,8 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
   a.qk_blk = s->qk_blk;
   a.nqt = (int)((N + 127) / 128);
   a.C0 = (float)(1.4426950408889634074 / std::sqrt((double)s->D));
-  a.L15 = (float)std::log2(15.0);
+  a.L15 = (float)std::log2((double)pmax);
+  a.p_zero = pmax == 15 ? 8 : 0;
   std::memcpy(a.T, levels().T, sizeof(a.T));
   hipStream_t hs = (hipStream_t)stream;
   if (dbg) {
@@ -226,6 +230,31 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
     if (e != hipSuccess) return ROTATTN_E_HIP;
   }
   return ROTATTN_OK;
+}
+}  // namespace
+
+rotattn_status rotattn_int4_attention(const rotattn_shape* s,
+                                      const uint8_t* q_codes, const float* q_scale,
+                                      const uint8_t* k_codes, const float* k_scale,
+                                      const uint8_t* v_codes, const float* v_scale,
+                                      const int32_t* heads, int32_t n_heads,
+                                      rotattn_dtype out_dtype, void* out,
+                                      const rotattn_debug* dbg,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
+                        dbg, workspace, workspace_bytes, stream, 15);
+}
+
+rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
+                                                  const uint8_t* q_codes, const float* q_scale,
+                                                  const uint8_t* k_codes, const float* k_scale,
+                                                  const uint8_t* v_codes, const float* v_scale,
+                                                  const int32_t* heads, int32_t n_heads,
+                                                  rotattn_dtype out_dtype, void* out,
+                                                  const rotattn_debug* dbg,
+                                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
+                        dbg, workspace, workspace_bytes, stream, 7);
 }
 
 size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s) {

@@ -172,6 +172,7 @@ struct Ctx {
   int64_t Np;
   int N, qk_shift;
   float C0, L15;
+  int p_zero;
   int dbg_row0, dbg_n;
   int32_t* dbg_aqk;
   int8_t* dbg_p;
@@ -384,7 +385,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
                 const int key = j0 + t * 32 + 16 * h + v;
                 if (key < N) {
                   a.dbg_aqk[(int64_t)dr * N + key] = (int32_t)st[t][v];
-                  a.dbg_p[(int64_t)dr * N + key] = (int8_t)(r - 8);
+                  a.dbg_p[(int64_t)dr * N + key] = (int8_t)(r - a.p_zero);
                 }
               }
             }
@@ -496,6 +497,7 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   Ctx a;
   a.img = args.img; a.ks = args.ks; a.Np = args.Np;
   a.N = (int)args.N; a.qk_shift = __builtin_ctz(args.qk_blk); a.C0 = args.C0; a.L15 = args.L15;
+  a.p_zero = args.p_zero;
   a.dbg_row0 = args.dbg_row0; a.dbg_n = args.dbg_n;
   a.dbg_aqk = args.dbg_aqk; a.dbg_p = args.dbg_p; a.dbg_apv = args.dbg_apv;
   const int N = a.N;

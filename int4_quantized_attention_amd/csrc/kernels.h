@@ -47,7 +47,8 @@ struct AttnArgs {
   int64_t N, Np;
   int qk_blk;
   int nqt, total, per_xcd;
-  float C0, L15;
+  float C0, L15;  // L15: fl(log2 15), or fl(log2 7) for the symmetric-P baseline
+  int p_zero;       // zero point of the dumped P codes: 8 (range-rectified) or 0
   float T[16];  // P level thresholds (15 used)
   // debug (rows [dbg_row0, dbg_row0 + dbg_n) of the single listed head)
   int dbg_row0, dbg_n;

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
   const int64_t n = n0 + lt;
   const void* base = (const char*)a.k + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   float x[CPT];
-  rotated_slice<DT, ROT, CPT>(base, n, n < N, D, c0, s, a.table, R + lt * (D + 1), x);
+  rotated_slice<DT, ROT, CPT, D>(base, n, n < N, D, c0, s, a.table, R + lt * (D + 1), x);
   if (ROT == 2) __syncthreads();  // every row of R read before it is overwritten
 #pragma unroll
   for (int i = 0; i < CPT; ++i) R[lt * (D + 1) + c0 + i] = x[i];
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
   const int64_t n = n0 + lt;
   const bool valid = n < N;
   float v[CPT];
-  rotated_slice<DT, ROT, CPT>(base, n, valid, D, c0, s, a.table, U + lt * (D + 1), v);
+  rotated_slice<DT, ROT, CPT, D>(base, n, valid, D, c0, s, a.table, U + lt * (D + 1), v);
   if (isK && a.smooth && valid) {
     const f32x4* mu = (const f32x4*)(a.kmu + (int64_t)bh * D + c0);
 #pragma unroll
@@ -307,6 +307,7 @@ hipError_t launch_quantize_t(const QuantArgs& a, hipStream_t st) {
   hipError_t e;
   if (a.rot == 1) e = launch_rot<D, DT, 1>(a, st);
   else if (a.rot == 2) e = launch_rot<D, DT, 2>(a, st);
+  else if (a.rot == 3) e = launch_rot<D, DT, 3>(a, st);
   else e = launch_rot<D, DT, 0>(a, st);
   if (e != hipSuccess) return e;
   k1_quant_v<D, DT><<<dim3((unsigned)(a.Np / kTile), BH), 256, in_tile, st>>>(a);

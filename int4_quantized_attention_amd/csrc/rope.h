@@ -195,9 +195,43 @@ RA_DEV void half_slice(const float* U, int c0, const Shape& s, float (&x)[CPT]) 
   }
 }
 
+// Full rotation (ROT 3) of the token's RoPE outputs: the orthonormal D x D
+// Walsh-Hadamard transform, stride by stride (1, 2, 4, ..., D/2), every pair
+// (x[i], x[i + len]) with i & len == 0 becoming (x[i] + x[i + len], x[i] - x[i + len]),
+// then every channel times fl(1/sqrt(D)).  Strides below CPT stay inside the
+// thread's slice; larger strides pair the slice with the one of lane ^ (len/CPT)
+// (the token's TPT threads are consecutive lanes).  All lanes must call.
+template <int D, int CPT>
+RA_DEV void hadamard_slice(float (&x)[CPT], int c0) {
+#pragma unroll
+  for (int len = 1; len < CPT; len *= 2) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      if ((i & len) == 0) {
+        const float a = x[i], b = x[i + len];
+        x[i] = a + b;
+        x[i + len] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int len = CPT; len < D; len *= 2) {
+    const bool lower = (c0 & len) == 0;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const float o = __shfl_xor(x[i], len / CPT, 64);
+      x[i] = lower ? x[i] + o : o - x[i];
+    }
+  }
+  const float rd = D == 128 ? 0.08838834764831844055f : 0.125f;  // fl(1/sqrt(D)), D in {64, 128}
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) x[i] = x[i] * rd;
+}
+
 // RoPE + rotation of one slice; U is this token's LDS row (D + 1 floats, used by
-// ROT 2 only).  Contains a workgroup barrier when ROT == 2 (all threads must call).
-template <int DT, int ROT, int CPT>
+// ROT 2 only).  Contains a workgroup barrier when ROT == 2 (all threads must call);
+// ROT 3 exchanges values between the token's lanes (all lanes must call).
+template <int DT, int ROT, int CPT, int DD = 0>
 RA_DEV void rotated_slice(const void* base, int64_t n, bool valid, int D, int c0, const Shape& s,
                           const float* tab, float* U, float (&x)[CPT]) {
   if (valid) {
@@ -215,6 +249,7 @@ RA_DEV void rotated_slice(const void* base, int64_t n, bool valid, int D, int c0
     __syncthreads();
     if (valid) half_slice<CPT>(U, c0, s, x);
   }
+  if (ROT == 3) hadamard_slice<DD, CPT>(x, c0);
 }
 
 RA_DEV int quant_code(float v, float inv) {

@@ -15,10 +15,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librotattn.so")
 
-ROT_NONE, ROT_INTERLEAVED, ROT_HALF = 0, 1, 2
+ROT_NONE, ROT_INTERLEAVED, ROT_HALF, ROT_FULL = 0, 1, 2, 3
 F32, F16, BF16 = 0, 1, 2
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
-ROT_BY_NAME = {"none": ROT_NONE, "interleaved": ROT_INTERLEAVED, "half": ROT_HALF}
+ROT_BY_NAME = {"none": ROT_NONE, "interleaved": ROT_INTERLEAVED, "half": ROT_HALF, "full": ROT_FULL}
 
 
 class Shape(ctypes.Structure):
@@ -57,6 +57,8 @@ _SIGS = {
     "rotattn_int4_attention_workspace": (_SZ, [_VP]),
     "rotattn_int4_attention": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _SZ,
                                       _VP]),
+    "rotattn_int4_attention_symmetric_p": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP,
+                                                  _SZ, _VP]),
     "rotattn_fp16_fallback_workspace": (_SZ, [_VP]),
     "rotattn_fp16_fallback": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ, _VP]),
     "rotattn_status_str": (ctypes.c_char_p, [_I32]),
@@ -166,10 +168,13 @@ def rotattn_quantize_qk(shape: Shape, rot: int, q: torch.Tensor, k: torch.Tensor
 
 
 def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Optional[Sequence[int]] = None,
-                           debug: Optional[dict] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           debug: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+                           symmetric_p: bool = False) -> torch.Tensor:
     """out: device [B,H,N,D] float32, float16 or bfloat16.  debug: dict(bh, row0, n_rows) ->
     filled with device tensors a_qk, p_codes, a_pv, m, l.  workspace: device uint8
-    tensor of rotattn_int4_attention_workspace(shape) bytes (default z["attn_workspace"])."""
+    tensor of rotattn_int4_attention_workspace(shape) bytes (default z["attn_workspace"]).
+    symmetric_p: the ablation baseline rotattn_int4_attention_symmetric_p (P codes
+    round(7P) in [0, 7]) instead of the method's range-rectified codes."""
     if out.dtype not in _DT:
         raise RotattnError("out must be float32, float16 or bfloat16")
     harr, nh = _heads(heads)
@@ -187,7 +192,8 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
         dbg = Debug(int(debug["bh"]), int(debug["row0"]), n, debug["a_qk"].data_ptr(),
                     debug["p_codes"].data_ptr(), debug["a_pv"].data_ptr(), debug["m"].data_ptr(),
                     debug["l"].data_ptr())
-    _check(lib().rotattn_int4_attention(
+    fn = lib().rotattn_int4_attention_symmetric_p if symmetric_p else lib().rotattn_int4_attention
+    _check(fn(
         ctypes.byref(shape), _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
         _ptr(z["v_codes"]), _ptr(z["v_scale"]), harr, nh, _DT[out.dtype],
         _ptr(out), ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(), _stream()),

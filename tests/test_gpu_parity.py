@@ -13,7 +13,7 @@ from gpu_util import assert_close, compare_codes, gpu_quantize, rows_sample, to_
 
 pytestmark = pytest.mark.gpu
 
-ROTS = {"interleaved": 1, "half": 2, "none": 0}
+ROTS = {"interleaved": 1, "half": 2, "none": 0, "full": 3}
 
 
 def _oracle_head_cfg(cfg):
@@ -22,16 +22,16 @@ def _oracle_head_cfg(cfg):
     return c
 
 
-def _run_case(orc, cfg, rot, smooth=True, debug_rows=None, out_dtype=torch.float32, in_dtype=None):
+def _run_case(orc, cfg, rot, smooth=True, debug_rows=None, out_dtype=torch.float32, in_dtype=None, pmax=15):
     Q, K, V = synth.make_inputs(cfg)
     shape, z = gpu_quantize(cfg, rot, Q, K, V, smooth, in_dtype)
     ref = orc.quantize(cfg, rot, orc.rope_table(cfg, rot), Q, K, V, smooth_k=smooth)
     compare_codes(cfg, z, ref)
     N, D = synth.n_tokens(cfg), cfg["D"]
     out = torch.full((cfg["B"], cfg["H"], N, D), float("nan"), dtype=out_dtype, device="cuda")
-    ra.rotattn_int4_attention(shape, z, out)
+    ra.rotattn_int4_attention(shape, z, out, symmetric_p=pmax == 7)
     torch.cuda.synchronize()
-    o = orc.attention(cfg, ref)
+    o = orc.attention(cfg, ref, pmax=pmax)
     if out_dtype == torch.float32:
         tol = (2e-3, 1e-3)
     elif out_dtype == torch.float16:
@@ -46,10 +46,10 @@ def _run_case(orc, cfg, rot, smooth=True, debug_rows=None, out_dtype=torch.float
                 n = min(n, N - r0)
                 dbg = dict(bh=bh, row0=r0, n_rows=n)
                 out2 = torch.zeros_like(out)
-                ra.rotattn_int4_attention(shape, z, out2, debug=dbg)
+                ra.rotattn_int4_attention(shape, z, out2, debug=dbg, symmetric_p=pmax == 7)
                 torch.cuda.synchronize()
                 rows = np.arange(bh * N + r0, bh * N + r0 + n)
-                od = orc.attention(cfg, ref, rows=rows, dumps=True)
+                od = orc.attention(cfg, ref, rows=rows, dumps=True, pmax=pmax)
                 assert np.array_equal(dbg["a_qk"].cpu().numpy(), od["a_qk"]), "a_qk"
                 assert np.array_equal(dbg["p_codes"].cpu().numpy(), od["pcode"]), "P codes"
                 assert np.array_equal(dbg["a_pv"].cpu().numpy(), od["a_pv"]), "a_pv"
@@ -59,7 +59,7 @@ def _run_case(orc, cfg, rot, smooth=True, debug_rows=None, out_dtype=torch.float
     return z, ref
 
 
-@pytest.mark.parametrize("rot", ["interleaved", "half", "none"])
+@pytest.mark.parametrize("rot", ["interleaved", "half", "none", "full"])
 def test_tiny_full_parity(orc, rot):
     cfg = dict(synth.CONFIGS["tiny"])
     _run_case(orc, cfg, ROTS[rot], debug_rows=[(0, 32)])
@@ -102,6 +102,17 @@ def test_d64_and_float32_and_bf16_inputs(orc):
 def test_fp16_output(orc):
     cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
     _run_case(orc, cfg, 2, out_dtype=torch.float16)
+
+
+@pytest.mark.parametrize("rot", ["full", "half"])
+def test_ablation_full_rotation_and_symmetric_p(orc, rot):
+    """Ablation variants: the Full (D x D Hadamard) rotation in the quantiser with the
+    method's P codes, and the symmetric 8-level P baseline."""
+    cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
+    if rot == "full":
+        _run_case(orc, cfg, ROTS[rot], debug_rows=[(0, 40), (1133, 40)])
+    else:
+        _run_case(orc, cfg, ROTS[rot], debug_rows=[(0, 40), (1133, 40)], pmax=7)
 
 
 def test_bf16_output(orc):
