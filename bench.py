@@ -37,6 +37,8 @@ def main():
     ap.add_argument("--config", default=CONFIG)
     ap.add_argument("--kv", type=int, default=0, help="override kv_blk (keys per online-softmax step)")
     ap.add_argument("--qk", type=int, default=0, help="override qk_blk (tokens per Q/K scale)")
+    ap.add_argument("--rot", default="", choices=["", "none", "interleaved", "half", "full"],
+                    help="override the rotation mode (full: the D x D Hadamard ablation)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -65,6 +67,8 @@ def main():
         cfg["kv_blk"] = args.kv
     if args.qk:
         cfg["qk_blk"] = args.qk
+    if args.rot:
+        cfg["rot"] = args.rot
     B, H, D = cfg["B"], cfg["H"], cfg["D"]
     N = synth.n_tokens(cfg)
     rot = ra.ROT_BY_NAME[cfg["rot"]]
@@ -144,7 +148,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "k2_attention (rotattn_int4_attention)",
                      "achieved": round(k2_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
-                     "traffic": counted_traffic() if args.config == CONFIG and not (args.kv or args.qk) else None},
+                     "traffic": counted_traffic() if args.config == CONFIG and not (args.kv or args.qk or args.rot) else None},
         "kernels_ms": dict({"quantize_qk": round(k1_ms, 4), "int4_attention": round(k2_ms, 4)},
                            **({"fp16_fallback_even_heads": round(k3_ms, 4)} if mixed else {})),
         "quantize_qk_GBps": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
