@@ -123,12 +123,23 @@ def quantize(shape, rot: int, table: np.ndarray, q, k, v, smooth_k: bool = True,
     return r
 
 
-def attention(shape, qz: dict, rows=None, dumps: bool = False, pmax: int = 15):
+def key_limit(i, N: int, causal_block: int = 0):
+    """Keys a query token i sees: all N for causal_block 0 (bidirectional), else
+    the keys of its own block of causal_block tokens and every earlier block."""
+    if causal_block <= 0:
+        return np.full(np.shape(i), N, dtype=np.int64)
+    return np.minimum(N, (np.asarray(i) // causal_block + 1) * causal_block)
+
+
+def attention(shape, qz: dict, rows=None, dumps: bool = False, pmax: int = 15,
+              causal_block: int = 0):
     """Quantised attention for flat rows (b*H + h)*N + i (default: all rows).
     Returns dict with 'out' [rows, D] float64 and, with dumps, 'a_qk' [rows, N]
     int32, 'pcode' [rows, N] int8, 'a_pv' [rows, S, D] int32, 'm' f32, 'l' f64.
     pmax = 15: range-rectified P codes r - 8 in [-8, 7] (the method); pmax = 7: the
-    symmetric baseline, codes r = round(7 P) in [0, 7]."""
+    symmetric baseline, codes r = round(7 P) in [0, 7].  causal_block: 0 for
+    bidirectional attention, c > 0 for block-causal attention (key_limit); dump
+    entries of keys a row does not see stay zero."""
     if pmax not in (7, 15):
         raise ValueError("pmax is 15 (range-rectified) or 7 (symmetric baseline)")
     s = shape_array(shape)
@@ -141,20 +152,22 @@ def attention(shape, qz: dict, rows=None, dumps: bool = False, pmax: int = 15):
     R = rows.size
     res = {"out": np.empty((R, D), np.float64)}
     if dumps:
-        res.update(a_qk=np.empty((R, N), np.int32), pcode=np.empty((R, N), np.int8),
-                   a_pv=np.empty((R, S, D), np.int32), m=np.empty(R, np.float32),
+        res.update(a_qk=np.zeros((R, N), np.int32), pcode=np.zeros((R, N), np.int8),
+                   a_pv=np.zeros((R, S, D), np.int32), m=np.empty(R, np.float32),
                    l=np.empty(R, np.float64))
     c = lambda a, t: np.ascontiguousarray(a, dtype=t)
-    lib().orc_attention_p(_p(s), _p(c(qz["qc"], np.int8)), _p(c(qz["qs"], np.float32)),
+    lib().orc_attention_x(_p(s), _p(c(qz["qc"], np.int8)), _p(c(qz["qs"], np.float32)),
                         _p(c(qz["kc"], np.int8)), _p(c(qz["ks"], np.float32)),
                         _p(c(qz["vc"], np.int8)), _p(c(qz["vs"], np.float32)),
                         _p(rows), ctypes.c_int64(R), _p(res["out"]),
                         _p(res.get("a_qk")), _p(res.get("pcode")), _p(res.get("a_pv")),
-                        _p(res.get("m")), _p(res.get("l")), ctypes.c_int32(pmax))
+                        _p(res.get("m")), _p(res.get("l")), ctypes.c_int32(pmax),
+                        ctypes.c_int32(causal_block))
     return res
 
 
-def exact_attention(shape, q, k, v, rows=None, base: float = 10000.0) -> np.ndarray:
+def exact_attention(shape, q, k, v, rows=None, base: float = 10000.0,
+                    causal_block: int = 0) -> np.ndarray:
     s = shape_array(shape)
     B, H, D = int(shape["B"]), int(shape["H"]), int(shape["D"])
     N = n_tokens(shape)
@@ -164,12 +177,12 @@ def exact_attention(shape, q, k, v, rows=None, base: float = 10000.0) -> np.ndar
     tab = rope_table(shape, ROT_NONE, base, f64=True)
     out = np.empty((rows.size, D), np.float64)
     c = lambda a: np.ascontiguousarray(a, dtype=np.float32).reshape(B, H, N, D)
-    lib().orc_exact_attention(_p(s), _p(tab), _p(c(q)), _p(c(k)), _p(c(v)), _p(rows),
-                              ctypes.c_int64(rows.size), _p(out))
+    lib().orc_exact_attention_x(_p(s), _p(tab), _p(c(q)), _p(c(k)), _p(c(v)), _p(rows),
+                                ctypes.c_int64(rows.size), _p(out), ctypes.c_int32(causal_block))
     return out
 
 
-def fallback_attention(shape, table_plain, q, k, v, rows=None) -> np.ndarray:
+def fallback_attention(shape, table_plain, q, k, v, rows=None, causal_block: int = 0) -> np.ndarray:
     s = shape_array(shape)
     B, H, D = int(shape["B"]), int(shape["H"]), int(shape["D"])
     N = n_tokens(shape)
@@ -178,9 +191,9 @@ def fallback_attention(shape, table_plain, q, k, v, rows=None) -> np.ndarray:
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.empty((rows.size, D), np.float64)
     c = lambda a: np.ascontiguousarray(a, dtype=np.float32).reshape(B, H, N, D)
-    lib().orc_fallback_attention(_p(s), _p(np.ascontiguousarray(table_plain, np.float32)),
-                                 _p(c(q)), _p(c(k)), _p(c(v)), _p(rows),
-                                 ctypes.c_int64(rows.size), _p(out))
+    lib().orc_fallback_attention_x(_p(s), _p(np.ascontiguousarray(table_plain, np.float32)),
+                                   _p(c(q)), _p(c(k)), _p(c(v)), _p(rows),
+                                   ctypes.c_int64(rows.size), _p(out), ctypes.c_int32(causal_block))
     return out
 
 

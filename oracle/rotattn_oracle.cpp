@@ -15,6 +15,9 @@
 //     INT4 P V; smoothing of the projected tensors.
 //   * arxivdaily abstract: P = exp(QK - max(QK)) is non-negative; fixed scales and
 //     zero points; mixed-precision INT4 FlashAttention with FP16 fallback.
+//   * the pages name causal as well as bidirectional attention for video DiTs
+//     without fixing its granularity: the *_x entry points take a causal block
+//     size c (key j visible to query i iff j / c <= i / c; c = 0 bidirectional).
 // Readings where the pages are silent (RoPE base, pair layout, block sizes, the
 // normaliser, the exact exp) are listed in the design notes and restated at each
 // function below.
@@ -194,6 +197,15 @@ inline int p_level(float y) {
   int r = 0;
   for (int k = 0; k < 15; ++k) r += (y >= t[k]) ? 1 : 0;
   return r;
+}
+
+// Keys a query token sees.  cb = 0: all N (bidirectional).  cb > 0: block-causal
+// with blocks of cb tokens -- token i sees key j iff j / cb <= i / cb (cb = 1 is
+// token-causal, cb = Hs * Ws frame-causal); the pages name causal attention without
+// fixing its granularity.
+int64_t key_limit(int64_t i, int64_t N, int64_t cb) {
+  if (cb <= 0) return N;
+  return std::min(N, (i / cb + 1) * cb);
 }
 
 float c0_of(int D) { return (float)(1.4426950408889634074 / std::sqrt((double)D)); }
@@ -413,10 +425,13 @@ int64_t orc_p_level_bruteforce(float lo, float hi, float* first) {
 // "Key design 2": code = round(P / max P * 7) in [0, 7], which leaves the negative
 // half of INT4 unused): the same steps with L = fl(log2 7) in place of L15, so
 // r = round-half-even(7 P) in [0, 7], and the code is r itself (no zero point).
-void orc_attention_p(const int32_t* shp, const int8_t* qc, const float* qs,
+// causal_block: see key_limit(); keys at or beyond the row's limit do not exist for
+// it (no score, no code, nothing in m, l or O; their dump entries are not written).
+void orc_attention_x(const int32_t* shp, const int8_t* qc, const float* qs,
                      const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
                      const int64_t* rows, int64_t n_rows, double* out,
-                     int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out, int32_t pmax) {
+                     int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out, int32_t pmax,
+                     int32_t causal_block) {
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
   const int64_t nqb = (N + s.qk_blk - 1) / s.qk_blk;
@@ -427,6 +442,7 @@ void orc_attention_p(const int32_t* shp, const int8_t* qc, const float* qs,
   for (int64_t ri = 0; ri < n_rows; ++ri) {
     const int64_t row = rows[ri];
     const int64_t bh = row / N, i = row % N;
+    const int64_t lim = key_limit(i, N, causal_block);
     const int8_t* qrow = qc + (bh * N + i) * D;
     const float sq = qs[bh * nqb + i / s.qk_blk];
     std::vector<int32_t> a(s.kv_blk);
@@ -436,7 +452,12 @@ void orc_attention_p(const int32_t* shp, const int8_t* qc, const float* qs,
     float m = -std::numeric_limits<float>::infinity();
     double l = 0.0;
     for (int64_t st = 0; st < S; ++st) {
-      const int64_t j0 = st * s.kv_blk, j1 = std::min(N, j0 + s.kv_blk);
+      const int64_t j0 = st * s.kv_blk, j1 = std::min(lim, j0 + s.kv_blk);
+      if (j0 >= lim) {  // a step with no key for this row: nothing changes
+        if (a_pv)
+          for (int64_t d = 0; d < D; ++d) a_pv[(ri * S + st) * D + d] = 0;
+        continue;
+      }
       float mnew = m;
       for (int64_t j = j0; j < j1; ++j) {
         const int8_t* krow = kc + (bh * N + j) * D;
@@ -475,20 +496,27 @@ void orc_attention_p(const int32_t* shp, const int8_t* qc, const float* qs,
   }
 }
 
+void orc_attention_p(const int32_t* shp, const int8_t* qc, const float* qs,
+                     const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
+                     const int64_t* rows, int64_t n_rows, double* out,
+                     int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out, int32_t pmax) {
+  orc_attention_x(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, pmax, 0);
+}
+
 void orc_attention(const int32_t* shp, const int8_t* qc, const float* qs,
                    const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
                    const int64_t* rows, int64_t n_rows, double* out,
                    int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out) {
-  orc_attention_p(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, 15);
+  orc_attention_x(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, 15, 0);
 }
 
 // ---------------------------------------------------------------------------
 // Unquantised attention in binary64 for the listed rows:
 //   out = softmax(RoPE(Q) RoPE(K)^T / sqrt(D)) V, RoPE with a binary64 table.
 // (The rotation is orthogonal and cancels in Q K^T, so none is applied.)
-void orc_exact_attention(const int32_t* shp, const double* tab64_plain,
-                         const float* q, const float* k, const float* v,
-                         const int64_t* rows, int64_t n_rows, double* out) {
+void orc_exact_attention_x(const int32_t* shp, const double* tab64_plain,
+                           const float* q, const float* k, const float* v,
+                           const int64_t* rows, int64_t n_rows, double* out, int32_t causal_block) {
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
   // RoPE every K row of the heads that appear, lazily per head.
@@ -511,11 +539,12 @@ void orc_exact_attention(const int32_t* shp, const double* tab64_plain,
     for (int64_t t = 0; t < (int64_t)mine.size(); ++t) {
       const int64_t r = mine[t], i = rows[r] % N;
       std::vector<double> in(D), qr(D), sc(N);
+      const int64_t lim = key_limit(i, N, causal_block);
       for (int64_t d = 0; d < D; ++d) in[d] = q[(bh * N + i) * D + d];
       rope_rotate_token<double>(s, 0, tab64_plain, i, in.data(), qr.data());
       double mx = -std::numeric_limits<double>::infinity();
       const double inv = 1.0 / std::sqrt((double)D);
-      for (int64_t j = 0; j < N; ++j) {
+      for (int64_t j = 0; j < lim; ++j) {
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += qr[d] * kr[j * D + d];
         sc[j] = dot * inv;
@@ -523,7 +552,7 @@ void orc_exact_attention(const int32_t* shp, const double* tab64_plain,
       }
       double den = 0.0;
       std::vector<double> num(D, 0.0);
-      for (int64_t j = 0; j < N; ++j) {
+      for (int64_t j = 0; j < lim; ++j) {
         const double p = std::exp(sc[j] - mx);
         den += p;
         for (int64_t d = 0; d < D; ++d) num[d] += p * (double)v[(bh * N + j) * D + d];
@@ -539,9 +568,9 @@ void orc_exact_attention(const int32_t* shp, const double* tab64_plain,
 // K rounded to binary16 (round-half-even), then exact binary64 softmax attention
 // with V as given.  The fallback kernel also rounds P to binary16 inside; that
 // rounding is covered by the tolerance, not mirrored here.
-void orc_fallback_attention(const int32_t* shp, const float* tab_plain,
-                            const float* q, const float* k, const float* v,
-                            const int64_t* rows, int64_t n_rows, double* out) {
+void orc_fallback_attention_x(const int32_t* shp, const float* tab_plain,
+                              const float* q, const float* k, const float* v,
+                              const int64_t* rows, int64_t n_rows, double* out, int32_t causal_block) {
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
   std::vector<int64_t> heads;
@@ -564,11 +593,12 @@ void orc_fallback_attention(const int32_t* shp, const float* tab_plain,
       const int64_t r = mine[t], i = rows[r] % N;
       std::vector<float> qr(D);
       std::vector<double> sc(N);
+      const int64_t lim = key_limit(i, N, causal_block);
       rope_rotate_token<float>(s, 0, tab_plain, i, q + (bh * N + i) * D, qr.data());
       for (int64_t d = 0; d < D; ++d) qr[d] = to_half(qr[d]);
       double mx = -std::numeric_limits<double>::infinity();
       const double inv = 1.0 / std::sqrt((double)D);
-      for (int64_t j = 0; j < N; ++j) {
+      for (int64_t j = 0; j < lim; ++j) {
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += (double)qr[d] * (double)kr[j * D + d];
         sc[j] = dot * inv;
@@ -576,7 +606,7 @@ void orc_fallback_attention(const int32_t* shp, const float* tab_plain,
       }
       double den = 0.0;
       std::vector<double> num(D, 0.0);
-      for (int64_t j = 0; j < N; ++j) {
+      for (int64_t j = 0; j < lim; ++j) {
         const double p = std::exp(sc[j] - mx);
         den += p;
         for (int64_t d = 0; d < D; ++d) num[d] += p * (double)v[(bh * N + j) * D + d];
@@ -589,6 +619,16 @@ void orc_fallback_attention(const int32_t* shp, const float* tab_plain,
 // binary16 round trip (exposed for the pins).
 void orc_f32_to_f16(const float* x, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = f32_to_f16_bits(x[i]);
+}
+
+void orc_exact_attention(const int32_t* shp, const double* tab64_plain, const float* q, const float* k,
+                         const float* v, const int64_t* rows, int64_t n_rows, double* out) {
+  orc_exact_attention_x(shp, tab64_plain, q, k, v, rows, n_rows, out, 0);
+}
+
+void orc_fallback_attention(const int32_t* shp, const float* tab_plain, const float* q, const float* k,
+                            const float* v, const int64_t* rows, int64_t n_rows, double* out) {
+  orc_fallback_attention_x(shp, tab_plain, q, k, v, rows, n_rows, out, 0);
 }
 
 }  // extern "C"

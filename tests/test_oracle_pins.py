@@ -459,3 +459,100 @@ def test_symmetric_p_codes_are_round_7p(orc):
             checked += int(ok.sum())
     assert checked > 0.99 * 2 * N * N
     assert r["pcode"].min() >= 0 and r["pcode"].max() <= 7
+
+
+# --- block-causal attention -------------------------------------------------------
+# Query token i sees key j iff j // c <= i // c (c = 1 token-causal, c = Hs*Ws
+# frame-causal, c = 0 bidirectional).  The pins below hold it to the bidirectional
+# oracle on the visible prefix (pinned above) and to a masked binary64 softmax.
+
+def _causal_case(orc, seed=21):
+    cfg = synth.custom(1, 2, 3, 4, 6, 64, 24, 20, 20, 16, 16)   # N = 72: 4.5 steps
+    q, k, v = synth.make_inputs(cfg, seed=seed)
+    z = orc.quantize(cfg, 2, orc.rope_table(cfg, 2), q, k, v)
+    return cfg, q, k, v, z
+
+
+def _prefix(z, n, qk_blk):
+    nb = -(-n // qk_blk)
+    return dict(qc=z["qc"][:, :, :n], kc=z["kc"][:, :, :n], vc=z["vc"][:, :, :n],
+                qs=z["qs"][:, :, :nb], ks=z["ks"][:, :, :nb], vs=z["vs"])
+
+
+@pytest.mark.parametrize("cb", [1, 5, 16, 24])
+def test_causal_row_equals_bidirectional_on_its_prefix(orc, cb):
+    """Row i of block-causal attention == bidirectional attention over the first
+    key_limit(i) tokens (codes and scales sliced, nothing recomputed), bit for bit,
+    dumps included; the entries of keys the row does not see stay zero."""
+    cfg, _, _, _, z = _causal_case(orc)
+    N = orc.n_tokens(cfg)
+    rows = np.array([0, 3, cb - 1, cb, 17, 40, 47, 48, N - 1], np.int64)
+    rows = np.unique(np.concatenate([rows, rows + N]))       # both heads
+    r = orc.attention(cfg, z, rows=rows, dumps=True, causal_block=cb)
+    for idx, row in enumerate(rows):
+        h, i = divmod(int(row), N)
+        lim = int(orc.key_limit(i, N, cb))
+        sub = synth.custom(1, 2, 1, 1, lim, 64, 24, 20, 20, 16, 16)
+        p = orc.attention(sub, _prefix(z, lim, 16), rows=np.array([h * lim + i]), dumps=True)
+        assert np.array_equal(r["out"][idx], p["out"][0]), (cb, row)
+        assert np.array_equal(r["a_qk"][idx, :lim], p["a_qk"][0])
+        assert np.array_equal(r["pcode"][idx, :lim], p["pcode"][0])
+        assert r["m"][idx] == p["m"][0] and r["l"][idx] == p["l"][0]
+        sp = p["a_pv"].shape[1]
+        assert np.array_equal(r["a_pv"][idx, :sp], p["a_pv"][0])
+        assert not r["a_qk"][idx, lim:].any() and not r["pcode"][idx, lim:].any()
+        assert not r["a_pv"][idx, sp:].any()
+
+
+def test_causal_block_at_least_n_is_bidirectional(orc):
+    cfg, q, k, v, z = _causal_case(orc)
+    N = orc.n_tokens(cfg)
+    base = orc.attention(cfg, z, dumps=True)
+    for cb in (N, N + 7, 10 ** 6):
+        r = orc.attention(cfg, z, dumps=True, causal_block=cb)
+        for key in ("out", "a_qk", "pcode", "a_pv", "m", "l"):
+            assert np.array_equal(r[key], base[key]), (cb, key)
+    assert np.array_equal(orc.exact_attention(cfg, q, k, v, causal_block=N),
+                          orc.exact_attention(cfg, q, k, v))
+
+
+@pytest.mark.parametrize("cb", [1, 7, 24])
+def test_causal_exact_equals_masked_softmax(orc, cb):
+    """The binary64 exact oracle with a causal block == textbook masked softmax of
+    the RoPE'd scores (numpy, binary64): -inf where j // c > i // c."""
+    cfg, q, k, v, _ = _causal_case(orc)
+    B, H, N, D = 1, 2, orc.n_tokens(cfg), 64
+    tab = orc.rope_table(cfg, 0, f64=True)
+    qr = orc.rope_rotate(cfg, 0, tab, q.astype(np.float64).reshape(B, H, N, D)).reshape(H, N, D)
+    kr = orc.rope_rotate(cfg, 0, tab, k.astype(np.float64).reshape(B, H, N, D)).reshape(H, N, D)
+    S = np.einsum("hid,hjd->hij", qr, kr) / math.sqrt(D)
+    i = np.arange(N)
+    S[:, (i[None, :] // cb) > (i[:, None] // cb)] = -np.inf
+    P = np.exp(S - S.max(axis=2, keepdims=True))
+    want = np.einsum("hij,hjd->hid", P / P.sum(axis=2, keepdims=True),
+                     v.astype(np.float64).reshape(H, N, D)).reshape(-1, D)
+    got = orc.exact_attention(cfg, q, k, v, causal_block=cb)
+    assert np.allclose(got, want, rtol=1e-10, atol=1e-12)
+    # row 0 under token-causal attention sees only itself: its own value row
+    if cb == 1:
+        assert np.allclose(got[0], v.reshape(H, N, D)[0, 0], rtol=1e-12, atol=0)
+
+
+def test_causal_quantised_and_fallback_close_to_exact(orc):
+    """Frame-causal: the quantised oracle (Half rotation) and the fallback oracle
+    stay as close to exact masked attention as their bidirectional forms do."""
+    cfg, q, k, v, z = _causal_case(orc)
+    cb = 24
+    ex = orc.exact_attention(cfg, q, k, v, causal_block=cb)
+    qa = orc.attention(cfg, z, causal_block=cb)["out"]
+    fb = orc.fallback_attention(cfg, orc.rope_table(cfg, 0), q / 8, k / 8, v, causal_block=cb)
+    ex8 = orc.exact_attention(cfg, q / 8, k / 8, v, causal_block=cb)
+    cosine = lambda a, b: np.sum(a * b) / np.linalg.norm(a) / np.linalg.norm(b)
+    qb = orc.attention(cfg, z)["out"]
+    cos_bi = cosine(qb, orc.exact_attention(cfg, q, k, v))
+    assert cosine(qa, ex) > min(0.85, cos_bi - 0.05)
+    assert np.max(np.abs(fb - ex8)) < 5e-3 * np.max(np.abs(ex8))
+    # first-frame rows see only the first frame: they differ from bidirectional rows;
+    # last-frame rows see every key: they equal them
+    assert not np.allclose(qa[:24], qb[:24])
+    assert np.array_equal(qa[48:72], qb[48:72])
