@@ -39,6 +39,9 @@ def main():
     ap.add_argument("--qk", type=int, default=0, help="override qk_blk (tokens per Q/K scale)")
     ap.add_argument("--rot", default="", choices=["", "none", "interleaved", "half", "full"],
                     help="override the rotation mode (full: the D x D Hadamard ablation)")
+    ap.add_argument("--causal", type=int, default=0,
+                    help="block-causal attention with this block of tokens (0: bidirectional); the "
+                         "operation count is then that of the visible query/key pairs")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -74,6 +77,10 @@ def main():
     rot = ra.ROT_BY_NAME[cfg["rot"]]
     shape = ra.Shape.of(cfg)
     ops = 4.0 * N * N * D * H * B
+    if args.causal:
+        # query i sees keys [0, min(N, (i // c + 1) c))
+        i = np.arange(N, dtype=np.int64)
+        ops = 4.0 * float(np.minimum(N, (i // args.causal + 1) * args.causal).sum()) * D * H * B
 
     Q, K, V = synth.make_inputs(cfg)
     q, k, v = (torch.from_numpy(x).cuda() for x in (Q, K, V))
@@ -98,11 +105,11 @@ def main():
         ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, True, z)
         if ev is not None:
             ev[1].record(stream)
-        ra.rotattn_int4_attention(shape, z, out, heads=q4_heads)
+        ra.rotattn_int4_attention(shape, z, out, heads=q4_heads, causal_block=args.causal)
         if ev is not None:
             ev[2].record(stream)
         if mixed:
-            ra.rotattn_fp16_fallback(shape, q, k, v, tab_fb, out, ws_fb, heads=fb_heads)
+            ra.rotattn_fp16_fallback(shape, q, k, v, tab_fb, out, ws_fb, heads=fb_heads, causal_block=args.causal)
             if ev is not None:
                 ev[3].record(stream)
 
@@ -141,14 +148,16 @@ def main():
         "dtype": "int4",
         "data": "synthetic",
         "config": {"workload": "%s: B=%d H=%d grid %dx%dx%d N=%d D=%d "
-                               "(%d/%d/%d), %s rotation, qk_blk=%d kv_blk=%d, fp16 in/out"
+                               "(%d/%d/%d), %s rotation, qk_blk=%d kv_blk=%d, fp16 in/out%s"
                                % (WORKLOADS.get(args.config, args.config), B, H, cfg["F"], cfg["Hs"], cfg["Ws"], N,
-                                  D, cfg["Df"], cfg["Dh"], cfg["Dw"], cfg["rot"], cfg["qk_blk"], cfg["kv_blk"]),
+                                  D, cfg["Df"], cfg["Dh"], cfg["Dw"], cfg["rot"], cfg["qk_blk"], cfg["kv_blk"],
+                                  ", block-causal c=%d (ops of visible pairs)" % args.causal if args.causal else ""),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "k2_attention (rotattn_int4_attention)",
                      "achieved": round(k2_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
-                     "traffic": counted_traffic() if args.config == CONFIG and not (args.kv or args.qk or args.rot) else None},
+                     "traffic": counted_traffic() if args.config == CONFIG and not (args.kv or args.qk or args.rot or args.causal)
+                     else None},
         "kernels_ms": dict({"quantize_qk": round(k1_ms, 4), "int4_attention": round(k2_ms, 4)},
                            **({"fp16_fallback_even_heads": round(k3_ms, 4)} if mixed else {})),
         "quantize_qk_GBps": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
@@ -158,13 +167,13 @@ def main():
     if not args.no_fallback and not mixed:
         ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
         tab0 = ra.rotattn_build_rope_table(shape, 0).cuda()
-        ra.rotattn_fp16_fallback(shape, q, k, v, tab0, out, ws)
+        ra.rotattn_fp16_fallback(shape, q, k, v, tab0, out, ws, causal_block=args.causal)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 2
         e0.record(stream)
         for _ in range(reps):
-            ra.rotattn_fp16_fallback(shape, q, k, v, tab0, out, ws)
+            ra.rotattn_fp16_fallback(shape, q, k, v, tab0, out, ws, causal_block=args.causal)
         e1.record(stream)
         torch.cuda.synchronize()
         fb_ms = e0.elapsed_time(e1) / reps
@@ -174,7 +183,7 @@ def main():
                               "int4_attention_speedup": round(fb_ms / k2_ms, 3)}
 
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(cfg, rot)
+        result["cpu_baseline"] = cpu_baseline(cfg, rot, causal=args.causal)
     print(json.dumps(result))
 
 
@@ -197,7 +206,7 @@ def counted_traffic():
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, rot, rows_target=40000):
+def cpu_baseline(cfg, rot, rows_target=40000, causal=0):
     """The oracle on the host cores: quantisation of one head, then quantised
     attention for a bounded sample of that head's query rows; scaled to TOPS."""
     import numpy as np
@@ -214,13 +223,13 @@ def cpu_baseline(cfg, rot, rows_target=40000):
     tq = time.perf_counter() - t0
     rows = np.linspace(0, N - 1, rows_target).astype(np.int64)
     t0 = time.perf_counter()
-    orc.attention(c1, z, rows=rows)
+    orc.attention(c1, z, rows=rows, causal_block=causal)
     ta = time.perf_counter() - t0
-    ops = 4.0 * N * D * rows.size
+    ops = 4.0 * D * float(orc.key_limit(rows, N, causal).sum())
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(ops / ta / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
             "sample": "head 0 of the same workload: quantisation of all %d tokens (%.2f s) and "
-                      "attention for %d of its query rows over all keys (%.2f s)" % (N, tq, rows.size, ta)}
+                      "attention for %d of its query rows over the keys each sees (%.2f s)" % (N, tq, rows.size, ta)}
 
 
 if __name__ == "__main__":

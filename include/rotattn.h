@@ -205,6 +205,37 @@ rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
                                                   const rotattn_debug* dbg,
                                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- block-causal variants -------------------------------------------------------
+ * The pages name causal as well as bidirectional attention for video DiTs without
+ * fixing its granularity (papernotes note, Overall framework).  These entry points
+ * take a causal block size c: query token i sees key j iff j / c <= i / c (integer
+ * division), i.e. the keys [0, min(N, (i / c + 1) c)), and absent keys take no part
+ * in the running maximum, in l or in O.  c = 0 is bidirectional (the entry points
+ * above); c = 1 token-causal; c = Hs * Ws frame-causal (a frame sees itself and the
+ * frames before it); c >= N is bidirectional.  c < 0 returns ROTATTN_E_ARG.
+ *   p_max   (int4 only) 15: range-rectified P (the method, as
+ *           rotattn_int4_attention); 7: the symmetric baseline (as
+ *           rotattn_int4_attention_symmetric_p); other values return ROTATTN_E_ARG.
+ * Debug dumps leave the entries of keys a row does not see, and its steps past the
+ * query tile's last key, unwritten: fill them first to compare whole arrays.
+ * Every other argument, layout, workspace and error as the entry points above. */
+rotattn_status rotattn_int4_attention_causal(const rotattn_shape* s,
+                                             const uint8_t* q_codes, const float* q_scale,
+                                             const uint8_t* k_codes, const float* k_scale,
+                                             const uint8_t* v_codes, const float* v_scale,
+                                             const int32_t* heads, int32_t n_heads,
+                                             int32_t causal_block, int32_t p_max,
+                                             rotattn_dtype out_dtype, void* out,
+                                             const rotattn_debug* dbg,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+rotattn_status rotattn_fp16_fallback_causal(const rotattn_shape* s, rotattn_dtype in_dtype,
+                                            const void* q, const void* k, const void* v,
+                                            const float* rope_table,
+                                            const int32_t* heads, int32_t n_heads,
+                                            int32_t causal_block,
+                                            rotattn_dtype out_dtype, void* out,
+                                            void* workspace, size_t workspace_bytes, void* stream);
+
 const char* rotattn_status_str(rotattn_status st);
 
 #ifdef __cplusplus

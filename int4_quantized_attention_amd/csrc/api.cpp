@@ -175,9 +175,10 @@ rotattn_status attention_call(const rotattn_shape* s,
                               const int32_t* heads, int32_t n_heads,
                               rotattn_dtype out_dtype, void* out,
                               const rotattn_debug* dbg,
-                              void* workspace, size_t workspace_bytes, void* stream, int pmax) {
+                              void* workspace, size_t workspace_bytes, void* stream, int pmax, int causal) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
+  if (causal < 0 || (pmax != 15 && pmax != 7)) return ROTATTN_E_ARG;
   if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !out || !workspace)
     return ROTATTN_E_NULL;
   // one head's images are addressed through a buffer resource with a 32-bit range
@@ -206,6 +207,7 @@ rotattn_status attention_call(const rotattn_shape* s,
   a.C0 = (float)(1.4426950408889634074 / std::sqrt((double)s->D));
   a.L15 = (float)std::log2((double)pmax);
   a.p_zero = pmax == 15 ? 8 : 0;
+  a.causal = causal < N ? causal : 0;  // a block of N or more keys is every key
   std::memcpy(a.T, levels().T, sizeof(a.T));
   hipStream_t hs = (hipStream_t)stream;
   if (dbg) {
@@ -242,7 +244,7 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
                                       const rotattn_debug* dbg,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
-                        dbg, workspace, workspace_bytes, stream, 15);
+                        dbg, workspace, workspace_bytes, stream, 15, 0);
 }
 
 rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
@@ -254,7 +256,20 @@ rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
                                                   const rotattn_debug* dbg,
                                                   void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
-                        dbg, workspace, workspace_bytes, stream, 7);
+                        dbg, workspace, workspace_bytes, stream, 7, 0);
+}
+
+rotattn_status rotattn_int4_attention_causal(const rotattn_shape* s,
+                                             const uint8_t* q_codes, const float* q_scale,
+                                             const uint8_t* k_codes, const float* k_scale,
+                                             const uint8_t* v_codes, const float* v_scale,
+                                             const int32_t* heads, int32_t n_heads,
+                                             int32_t causal_block, int32_t p_max,
+                                             rotattn_dtype out_dtype, void* out,
+                                             const rotattn_debug* dbg,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
+                        dbg, workspace, workspace_bytes, stream, p_max, causal_block);
 }
 
 size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s) {
@@ -263,14 +278,16 @@ size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s) {
   return 3 * align256(per);
 }
 
-rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dtype,
-                                     const void* q, const void* k, const void* v,
-                                     const float* rope_table,
-                                     const int32_t* heads, int32_t n_heads,
-                                     rotattn_dtype out_dtype, void* out,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+rotattn_status rotattn_fp16_fallback_causal(const rotattn_shape* s, rotattn_dtype in_dtype,
+                                            const void* q, const void* k, const void* v,
+                                            const float* rope_table,
+                                            const int32_t* heads, int32_t n_heads,
+                                            int32_t causal_block,
+                                            rotattn_dtype out_dtype, void* out,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
+  if (causal_block < 0) return ROTATTN_E_ARG;
   if (!q || !k || !v || !rope_table || !out || !workspace) return ROTATTN_E_NULL;
   if (in_dtype < ROTATTN_F32 || in_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
   if (out_dtype < ROTATTN_F32 || out_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
@@ -296,6 +313,7 @@ rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dt
   a.out_kind = (int)out_dtype;
   a.nqt = (int)((a.N + 127) / 128);
   a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)s->D));
+  a.causal = causal_block < a.N ? causal_block : 0;  // a block of N or more keys is every key
   hipStream_t hs = (hipStream_t)stream;
   const int nh = heads ? n_heads : BH;
   for (int h0 = 0; h0 < nh; h0 += ra::kMaxHeads) {
@@ -307,6 +325,16 @@ rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dt
     if (ra::launch_fallback(a, hs) != hipSuccess) return ROTATTN_E_HIP;
   }
   return ROTATTN_OK;
+}
+
+rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dtype,
+                                     const void* q, const void* k, const void* v,
+                                     const float* rope_table,
+                                     const int32_t* heads, int32_t n_heads,
+                                     rotattn_dtype out_dtype, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return rotattn_fp16_fallback_causal(s, in_dtype, q, k, v, rope_table, heads, n_heads, 0, out_dtype, out,
+                                      workspace, workspace_bytes, stream);
 }
 
 const char* rotattn_status_str(rotattn_status st) {

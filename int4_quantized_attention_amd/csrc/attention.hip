@@ -171,6 +171,7 @@ struct Ctx {
   const float* ks;
   int64_t Np;
   int N, qk_shift;
+  int klim;  // keys this lane's query row sees: N, or its block-causal limit
   float C0, L15;
   int p_zero;
   int dbg_row0, dbg_n;
@@ -248,9 +249,10 @@ RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::
 
 // One online-softmax step on tiles tb..tb+TPS-1 of group g (for kv_blk 16, the two
 // halves of tile tb as two steps): running max, lazy flush, P levels, P^T operand,
-// P V MFMAs.  TAIL: the group holds keys >= N.  US: one K scale for the whole step
-// (qk_blk >= kv_blk), so the maximum needs one multiplication.
-template <int D, int KVB, bool DBG, bool TAIL, bool US>
+// P V MFMAs.  MASK: the group holds keys at or past some row's limit (keys >= N,
+// or keys a block-causal row does not see); they count as absent.  US: one K scale
+// for the whole step (qk_blk >= kv_blk), so the maximum needs one multiplication.
+template <int D, int KVB, bool DBG, bool MASK, bool US>
 RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl, const float* Tl,
                        const f32x16 (&st)[Geo<D, KVB>::TPS], const float (&ct)[Geo<D, KVB>::TPS],
                        RowState<D / 32>& S, bool dbg_row, int dr) {
@@ -274,7 +276,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           bool ok = act;
-          if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+          if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
           im = fmaxf(im, ok ? st[t][v] : -INFINITY);
         }
       }
@@ -286,7 +288,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           bool ok = act;
-          if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+          if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
           im = fmaxf(im, ok ? st[t][v] : -INFINITY);
         }
         if (im != -INFINITY) mloc = fmaxf(mloc, im * ct[t]);
@@ -325,10 +327,10 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * w + e;
             bool ok = act;
-            if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+            if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
             const float y = __builtin_fmaf(st[t][v], ct[t], nm);
             float p = exp2_hw(y);
-            if (TAIL || KVB < 32) p = ok ? p : 0.f;
+            if (MASK || KVB < 32) p = ok ? p : 0.f;
             S.l += p;
             tt[e] = __float_as_uint(p + kMagic);
           }
@@ -370,20 +372,20 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
             for (int e = 0; e < 4; ++e) {
               const int v = 4 * w + e;
               bool ok = act;
-              if (TAIL) ok = ok && (j0 + t * 32 + 16 * h + v < N);
+              if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
               const float y = __builtin_fmaf(st[t][v], ct[t], nm);
               float p = exp2_hw(y);
-              if (TAIL || KVB < 32) p = ok ? p : 0.f;
+              if (MASK || KVB < 32) p = ok ? p : 0.f;
               const int rf = (int)((__float_as_uint(p + kMagic) >> 16) & 0xFFu);  // the fast level
               const int rh = min(rf, 16);
               const float lo = Tl[max(rh - 1, 0)], hi = Tl[rh];
               int r = rh - ((rh > 0 && y < lo) ? 1 : 0) + ((y >= hi) ? 1 : 0);
-              if (TAIL || KVB < 32) r = ok ? r : 0;
+              if (MASK || KVB < 32) r = ok ? r : 0;
               dd |= ((uint32_t)(r - rf) & 0x81u) << (8 * e);
               rr |= (uint32_t)r << (8 * e);
               if (DBG && dbg_row && act) {
                 const int key = j0 + t * 32 + 16 * h + v;
-                if (key < N) {
+                if (key < a.klim) {
                   a.dbg_aqk[(int64_t)dr * N + key] = (int32_t)st[t][v];
                   a.dbg_p[(int64_t)dr * N + key] = (int8_t)(r - a.p_zero);
                 }
@@ -435,7 +437,7 @@ typedef const __attribute__((address_space(4))) float* kscale_ptr;  // read-only
 // behind the copies in flight), Q K^T, softmax + P V; then a wait until this
 // wave's copy of group g+1 has landed (later copies stay in flight) and one
 // barrier, which also covers the other waves' copies.
-template <int D, int KVB, bool DBG, bool TAIL, bool US, int SLOT = -1>
+template <int D, int KVB, bool DBG, bool MASK, bool US, int SLOT = -1>
 RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngroups, uint8_t* lds,
                        const i32x8 (&qop)[Geo<D, KVB>::KC], float sq, int bh, RowState<D / 32>& S, bool dbg_row,
                        int dr) {
@@ -443,7 +445,7 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
   // ring slot of this group: a compile-time constant when the caller unrolls the
   // group loop by the slot count (SLOT = g % NB), so LDS addresses stay invariant
   const int slot = SLOT >= 0 ? SLOT : g % G::NB;
-  if (!TAIL && g + G::NB - 1 < ngroups)
+  if (g + G::NB - 1 < ngroups)
     dma_group<D, KVB>(rsrc, g + G::NB - 1, lds + ((slot + G::NB - 1) % G::NB) * G::IMG);
   const int h = (threadIdx.x >> 5) & 1;
   const kscale_ptr ksh = (kscale_ptr)a.ks + (int64_t)bh * (a.Np >> a.qk_shift);
@@ -467,16 +469,14 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
     f32x16 st[G::TPS];
     qk_tiles<D, KVB>(cur, tb, qop, st);
     const int step0 = KVB < 32 ? 2 * g : g * G::NSG + sg;
-    softmax_pv<D, KVB, DBG, TAIL, US>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct, S,
+    softmax_pv<D, KVB, DBG, MASK, US>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct, S,
                                       dbg_row, dr);
   }
-  if (!TAIL) {
-    // copies issued after group g+1's: those of groups g+2 .. min(g+NB-1, ngroups-1)
-    const int later = min(g + G::NB - 1, ngroups - 1) - (g + 1);
-    if (DBG || later <= 0) wait_vm<0>();
-    else if (later == 1) wait_vm<G::NDMA>();
-    else wait_vm<2 * G::NDMA>();
-  }
+  // copies issued after group g+1's: those of groups g+2 .. min(g+NB-1, ngroups-1)
+  const int later = min(g + G::NB - 1, ngroups - 1) - (g + 1);
+  if (DBG || later <= 0) wait_vm<0>();
+  else if (later == 1) wait_vm<G::NDMA>();
+  else wait_vm<2 * G::NDMA>();
   lds_barrier();
 }
 
@@ -492,7 +492,9 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
     L = (int)(blockIdx.x % 8) * args.per_xcd + (int)(blockIdx.x / 8);
     if (L >= args.total) return;
   }
-  const int hidx = L / args.nqt, qt = L % args.nqt;
+  const int hidx = L / args.nqt;
+  // block-causal tiles: the last query tiles see the most keys, so they go first
+  const int qt = (!DBG && args.causal > 0) ? args.nqt - 1 - L % args.nqt : L % args.nqt;
   const int bh = args.heads[hidx];
   Ctx a;
   a.img = args.img; a.ks = args.ks; a.Np = args.Np;
@@ -502,7 +504,16 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   a.dbg_aqk = args.dbg_aqk; a.dbg_p = args.dbg_p; a.dbg_apv = args.dbg_apv;
   const int N = a.N;
   const int qi = qt * kBM + w * 32 + col;
-  const int ngroups = (N + G::TG - 1) / G::TG;
+  // Keys seen: all N, or under block-causal masking (block c) the keys of the row's
+  // own block and every earlier one, min(N, (i / c + 1) c).  The tile's groups run
+  // up to its last row's limit; groups wholly below its first row's limit need no
+  // per-key test.
+  const int64_t c = args.causal;
+  auto limit = [&](int64_t i) -> int { return c > 0 ? (int)min((int64_t)N, (i / c + 1) * c) : N; };
+  a.klim = limit(qi);
+  const int kmax = limit(min(qt * kBM + kBM - 1, N - 1));
+  const int ngroups = (kmax + G::TG - 1) / G::TG;
+  const int nfull = min(limit(qt * kBM) / G::TG, ngroups);  // groups no row masks
 
   // ---- prologue: groups 0 .. NB-2 in flight ----------------------------------------
   const int64_t ngp = a.Np / G::TG;
@@ -544,14 +555,15 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   lds_barrier();
   int g = 0;
   if (G::NB == 2) {
-    for (; g + 2 < ngroups; g += 2) {
+    for (; g + 2 <= nfull; g += 2) {
       group_iter<D, KVB, DBG, false, US, 0>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
       group_iter<D, KVB, DBG, false, US, 1>(a, rsrc, g + 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
     }
   }
-  for (; g + 1 < ngroups; ++g)
+  for (; g < nfull; ++g)
     group_iter<D, KVB, DBG, false, US>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
-  group_iter<D, KVB, DBG, true, US>(a, rsrc, ngroups - 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+  for (; g < ngroups; ++g)
+    group_iter<D, KVB, DBG, true, US>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
 
   // ---- epilogue ---------------------------------------------------------------------
   const float lq = pair_sum(S.l);

@@ -78,6 +78,7 @@ struct FbCtx {
   const _Float16* vt;
   int64_t Np;
   int N;
+  int klim;  // keys this lane's query row sees: N, or its block-causal limit
   float scale_log2;
 };
 
@@ -125,13 +126,13 @@ RA_DEV void fb_store(_Float16* Kl, _Float16* Vl, const i32x4 (&rk)[FbGeo<D>::KUT
   }
 }
 
-template <int D, bool TAIL>
+// MASK: the group holds keys at or past some row's limit; they count as absent
+template <int D, bool MASK>
 RA_DEV void fb_group(const FbCtx& a, int g, int ngroups, _Float16* lds, i32x4 (&rk)[FbGeo<D>::KUT],
                      i32x4 (&rv)[FbGeo<D>::VUT], const f16x8 (&qop)[FbGeo<D>::KC], int bh,
                      f32x16 (&O)[FbGeo<D>::NDB], float& m, float& l) {
   using G = FbGeo<D>;
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
-  const int N = (int)a.N;
   const bool odd = g & 1;
   _Float16* const kb_cur = lds + (odd ? G::KBUF : 0);
   _Float16* const kb_nxt = lds + (odd ? 0 : G::KBUF);
@@ -155,7 +156,7 @@ RA_DEV void fb_group(const FbCtx& a, int g, int ngroups, _Float16* lds, i32x4 (&
   for (int t = 0; t < G::NT; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const bool ok = !TAIL || (j0 + t * 32 + 16 * h + v < N);
+      const bool ok = !MASK || (j0 + t * 32 + 16 * h + v < a.klim);
       mloc = fmaxf(mloc, ok ? st[t][v] : -INFINITY);
     }
   const float sl2 = a.scale_log2;
@@ -176,9 +177,9 @@ RA_DEV void fb_group(const FbCtx& a, int g, int ngroups, _Float16* lds, i32x4 (&
     for (int v = 0; v < 16; v += 2) {
       float p0 = exp2_hw(__builtin_fmaf(st[t][v], sl2, -mnew));
       float p1 = exp2_hw(__builtin_fmaf(st[t][v + 1], sl2, -mnew));
-      if (TAIL) {
-        p0 = (j0 + t * 32 + 16 * h + v < N) ? p0 : 0.f;
-        p1 = (j0 + t * 32 + 16 * h + v + 1 < N) ? p1 : 0.f;
+      if (MASK) {
+        p0 = (j0 + t * 32 + 16 * h + v < a.klim) ? p0 : 0.f;
+        p1 = (j0 + t * 32 + 16 * h + v + 1 < a.klim) ? p1 : 0.f;
       }
       l += p0 + p1;
       pb[v >> 3][v & 7] = (_Float16)p0;
@@ -203,12 +204,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
   const int L = (int)(blockIdx.x % 8) * args.per_xcd + (int)(blockIdx.x / 8);
   if (L >= args.total) return;
-  const int hidx = L / args.nqt, qt = L % args.nqt;
+  const int hidx = L / args.nqt;
+  // block-causal tiles: the last query tiles see the most keys, so they go first
+  const int qt = args.causal > 0 ? args.nqt - 1 - L % args.nqt : L % args.nqt;
   const int bh = args.heads[hidx];
   FbCtx a;
   a.kr = args.kr; a.vt = args.vt; a.Np = args.Np; a.N = (int)args.N; a.scale_log2 = args.scale_log2;
   const int N = a.N;
   const int qi = qt * kFbBM + w * 32 + col;
+  // keys seen: all N, or min(N, (i / c + 1) c) under block-causal masking (block c);
+  // groups wholly below the tile's first row's limit need no per-key test
+  const int64_t c = args.causal;
+  auto limit = [&](int64_t i) -> int { return c > 0 ? (int)min((int64_t)N, (i / c + 1) * c) : N; };
+  a.klim = limit(qi);
+  const int kmax = limit(min(qt * kFbBM + kFbBM - 1, N - 1));
 
   f16x8 qop[G::KC];
   {
@@ -223,14 +232,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int v = 0; v < 16; ++v) O[db][v] = 0.f;
 
-  const int ngroups = (N + G::TG - 1) / G::TG;
+  const int ngroups = (kmax + G::TG - 1) / G::TG;
+  const int nfull = min(limit(qt * kFbBM) / G::TG, ngroups);  // groups no row masks
   i32x4 rk[G::KUT], rv[G::VUT];
   fb_load<D>(a, bh, 0, rk, rv);
   fb_store<D>(flds, flds + 2 * G::KBUF, rk, rv);
   if (ngroups > 1) fb_load<D>(a, bh, 1, rk, rv);
   lds_barrier();
-  for (int g = 0; g + 1 < ngroups; ++g) fb_group<D, false>(a, g, ngroups, flds, rk, rv, qop, bh, O, m, l);
-  fb_group<D, true>(a, ngroups - 1, ngroups, flds, rk, rv, qop, bh, O, m, l);
+  int g = 0;
+  for (; g < nfull; ++g) fb_group<D, false>(a, g, ngroups, flds, rk, rv, qop, bh, O, m, l);
+  for (; g < ngroups; ++g) fb_group<D, true>(a, g, ngroups, flds, rk, rv, qop, bh, O, m, l);
 
   const float lq = l + __shfl_xor(l, 32, 64);
   if (qi < N) {

@@ -49,6 +49,7 @@ struct AttnArgs {
   int nqt, total, per_xcd;
   float C0, L15;  // L15: fl(log2 15), or fl(log2 7) for the symmetric-P baseline
   int p_zero;       // zero point of the dumped P codes: 8 (range-rectified) or 0
+  int causal;       // 0 bidirectional; c > 0: query i sees key j iff j / c <= i / c (c < N)
   float T[16];  // P level thresholds (15 used)
   // debug (rows [dbg_row0, dbg_row0 + dbg_n) of the single listed head)
   int dbg_row0, dbg_n;
@@ -75,6 +76,7 @@ struct FbArgs {
   int out_kind;  // 0 binary32, 1 binary16, 2 bfloat16
   int nqt, total, per_xcd;
   float scale_log2;  // log2(e) / sqrt(D)
+  int causal;        // 0 bidirectional; c > 0: query i sees key j iff j / c <= i / c (c < N)
   int nheads;
   int heads[kMaxHeads];
 };

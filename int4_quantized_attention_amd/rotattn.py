@@ -59,8 +59,12 @@ _SIGS = {
                                       _VP]),
     "rotattn_int4_attention_symmetric_p": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP,
                                                   _SZ, _VP]),
+    "rotattn_int4_attention_causal": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
+                                             _VP, _VP, _VP, _SZ, _VP]),
     "rotattn_fp16_fallback_workspace": (_SZ, [_VP]),
     "rotattn_fp16_fallback": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ, _VP]),
+    "rotattn_fp16_fallback_causal": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _SZ,
+                                            _VP]),
     "rotattn_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -169,12 +173,14 @@ def rotattn_quantize_qk(shape: Shape, rot: int, q: torch.Tensor, k: torch.Tensor
 
 def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Optional[Sequence[int]] = None,
                            debug: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
-                           symmetric_p: bool = False) -> torch.Tensor:
+                           symmetric_p: bool = False, causal_block: int = 0) -> torch.Tensor:
     """out: device [B,H,N,D] float32, float16 or bfloat16.  debug: dict(bh, row0, n_rows) ->
     filled with device tensors a_qk, p_codes, a_pv, m, l.  workspace: device uint8
     tensor of rotattn_int4_attention_workspace(shape) bytes (default z["attn_workspace"]).
     symmetric_p: the ablation baseline rotattn_int4_attention_symmetric_p (P codes
-    round(7P) in [0, 7]) instead of the method's range-rectified codes."""
+    round(7P) in [0, 7]) instead of the method's range-rectified codes.
+    causal_block: 0 bidirectional; c > 0 block-causal through
+    rotattn_int4_attention_causal (query i sees key j iff j // c <= i // c)."""
     if out.dtype not in _DT:
         raise RotattnError("out must be float32, float16 or bfloat16")
     harr, nh = _heads(heads)
@@ -192,27 +198,35 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
         dbg = Debug(int(debug["bh"]), int(debug["row0"]), n, debug["a_qk"].data_ptr(),
                     debug["p_codes"].data_ptr(), debug["a_pv"].data_ptr(), debug["m"].data_ptr(),
                     debug["l"].data_ptr())
-    fn = lib().rotattn_int4_attention_symmetric_p if symmetric_p else lib().rotattn_int4_attention
-    _check(fn(
-        ctypes.byref(shape), _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
-        _ptr(z["v_codes"]), _ptr(z["v_scale"]), harr, nh, _DT[out.dtype],
-        _ptr(out), ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(), _stream()),
-        "rotattn_int4_attention")
+    codes = (_ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
+             _ptr(z["v_codes"]), _ptr(z["v_scale"]), harr, nh)
+    tail = (_DT[out.dtype], _ptr(out), ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(),
+            _stream())
+    if causal_block:
+        _check(lib().rotattn_int4_attention_causal(ctypes.byref(shape), *codes, int(causal_block),
+                                                   7 if symmetric_p else 15, *tail),
+               "rotattn_int4_attention_causal")
+    else:
+        fn = lib().rotattn_int4_attention_symmetric_p if symmetric_p else lib().rotattn_int4_attention
+        _check(fn(ctypes.byref(shape), *codes, *tail), "rotattn_int4_attention")
     return out
 
 
 def rotattn_fp16_fallback(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           rope_table: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
-                          heads: Optional[Sequence[int]] = None) -> torch.Tensor:
+                          heads: Optional[Sequence[int]] = None, causal_block: int = 0) -> torch.Tensor:
     """q, k, v: device [B,H,N,D] of one of float32 / float16 / bfloat16 (rounded to
-    binary16 after RoPE); out: float32, float16 or bfloat16."""
+    binary16 after RoPE); out: float32, float16 or bfloat16.  causal_block as for
+    rotattn_int4_attention (rotattn_fp16_fallback_causal when non-zero)."""
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise RotattnError("q, k, v must share one of float32 / float16 / bfloat16")
     if out.dtype not in _DT:
         raise RotattnError("out must be float32, float16 or bfloat16")
     harr, nh = _heads(heads)
-    _check(lib().rotattn_fp16_fallback(
-        ctypes.byref(shape), _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table), harr, nh,
-        _DT[out.dtype], _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
-        "rotattn_fp16_fallback")
+    head = (ctypes.byref(shape), _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table), harr, nh)
+    tail = (_DT[out.dtype], _ptr(out), _ptr(workspace), workspace.numel(), _stream())
+    if causal_block:
+        _check(lib().rotattn_fp16_fallback_causal(*head, int(causal_block), *tail), "rotattn_fp16_fallback_causal")
+    else:
+        _check(lib().rotattn_fp16_fallback(*head, *tail), "rotattn_fp16_fallback")
     return out

@@ -98,6 +98,16 @@ def test_null_and_bad_args_return_before_launch(L):
     st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 3,
                                   fake, nul, fake, big, nul)
     assert st == 6  # output dtype outside F32 / F16 / BF16
+    # block-causal entry points: negative block, P maximum other than 15 / 7
+    st = L.rotattn_int4_attention_causal(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, -1, 15,
+                                         0, fake, nul, fake, big, nul)
+    assert st == 6
+    st = L.rotattn_int4_attention_causal(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 4, 8,
+                                         0, fake, nul, fake, big, nul)
+    assert st == 6
+    st = L.rotattn_fp16_fallback_causal(ctypes.byref(s), 1, fake, fake, fake, fake, nul, 0, -3, 0, fake, fake,
+                                        1 << 30, nul)
+    assert st == 6
     assert L.rotattn_status_str(0) == b"ok"
 
 

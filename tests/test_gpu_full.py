@@ -37,6 +37,22 @@ def test_fallback_parity_medium(orc):
     assert_close(out.cpu().numpy().reshape(-1, 128), ref)
 
 
+@pytest.mark.parametrize("cb", [1, 391, 100])
+def test_fallback_causal(orc, cb):
+    """Block-causal fallback (query i sees key j iff j // c <= i // c) against the
+    fallback oracle with the same mask."""
+    cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="peaked")
+    Q, K, V = synth.make_inputs(cfg)
+    shape = ra.Shape.of(cfg)
+    tab = ra.rotattn_build_rope_table(shape, 0).cuda()
+    ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
+    N = synth.n_tokens(cfg)
+    out = torch.full((1, 2, N, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ra.rotattn_fp16_fallback(shape, to_dev(Q), to_dev(K), to_dev(V), tab, out, ws, causal_block=cb)
+    ref = orc.fallback_attention(cfg, orc.rope_table(cfg, 0), Q, K, V, causal_block=cb)
+    assert_close(out.cpu().numpy().reshape(-1, 128), ref)
+
+
 @pytest.mark.parametrize("in_dt,out_dt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float16)])
 def test_fallback_input_output_dtypes(orc, in_dt, out_dt):
     cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float32", recipe="peaked")

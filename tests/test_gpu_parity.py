@@ -22,16 +22,17 @@ def _oracle_head_cfg(cfg):
     return c
 
 
-def _run_case(orc, cfg, rot, smooth=True, debug_rows=None, out_dtype=torch.float32, in_dtype=None, pmax=15):
+def _run_case(orc, cfg, rot, smooth=True, debug_rows=None, out_dtype=torch.float32, in_dtype=None, pmax=15,
+              causal=0):
     Q, K, V = synth.make_inputs(cfg)
     shape, z = gpu_quantize(cfg, rot, Q, K, V, smooth, in_dtype)
     ref = orc.quantize(cfg, rot, orc.rope_table(cfg, rot), Q, K, V, smooth_k=smooth)
     compare_codes(cfg, z, ref)
     N, D = synth.n_tokens(cfg), cfg["D"]
     out = torch.full((cfg["B"], cfg["H"], N, D), float("nan"), dtype=out_dtype, device="cuda")
-    ra.rotattn_int4_attention(shape, z, out, symmetric_p=pmax == 7)
+    ra.rotattn_int4_attention(shape, z, out, symmetric_p=pmax == 7, causal_block=causal)
     torch.cuda.synchronize()
-    o = orc.attention(cfg, ref, pmax=pmax)
+    o = orc.attention(cfg, ref, pmax=pmax, causal_block=causal)
     if out_dtype == torch.float32:
         tol = (2e-3, 1e-3)
     elif out_dtype == torch.float16:
@@ -46,10 +47,10 @@ def _run_case(orc, cfg, rot, smooth=True, debug_rows=None, out_dtype=torch.float
                 n = min(n, N - r0)
                 dbg = dict(bh=bh, row0=r0, n_rows=n)
                 out2 = torch.zeros_like(out)
-                ra.rotattn_int4_attention(shape, z, out2, debug=dbg, symmetric_p=pmax == 7)
+                ra.rotattn_int4_attention(shape, z, out2, debug=dbg, symmetric_p=pmax == 7, causal_block=causal)
                 torch.cuda.synchronize()
                 rows = np.arange(bh * N + r0, bh * N + r0 + n)
-                od = orc.attention(cfg, ref, rows=rows, dumps=True, pmax=pmax)
+                od = orc.attention(cfg, ref, rows=rows, dumps=True, pmax=pmax, causal_block=causal)
                 assert np.array_equal(dbg["a_qk"].cpu().numpy(), od["a_qk"]), "a_qk"
                 assert np.array_equal(dbg["p_codes"].cpu().numpy(), od["pcode"]), "P codes"
                 assert np.array_equal(dbg["a_pv"].cpu().numpy(), od["a_pv"]), "a_pv"
@@ -147,3 +148,32 @@ def test_head_subset_leaves_other_heads(orc):
     assert np.all(o[0, 0] == 7.0) and np.all(o[0, 2] == 7.0)
     assert_close(o[0, 1], full[0, 1])
     assert_close(o[0, 3], full[0, 3])
+
+
+CAUSAL = [
+    # (id, config overrides, causal block): token-causal, frame-causal (one frame is
+    # 391 tokens, so tiles straddle frames), a block that does not divide N, a block
+    # smaller than a step, each kv_blk and D 64
+    ("token_kv64", dict(), 1),
+    ("frame_kv64", dict(), 391),
+    ("block100_kv128_qk128", dict(qk_blk=128, kv_blk=128), 100),
+    ("frame_kv16_qk16", dict(qk_blk=16, kv_blk=16), 391),
+    ("block5_kv32_qk32_symmetric", dict(qk_blk=32, kv_blk=32), 5),
+    ("block_ge_n", dict(), 5000),
+]
+
+
+@pytest.mark.parametrize("case", CAUSAL, ids=[c[0] for c in CAUSAL])
+def test_causal_parity(orc, case):
+    """Block-causal attention (query i sees key j iff j // c <= i // c) against the
+    oracle's, dumps included, on rows around tile and frame boundaries."""
+    name, over, cb = case
+    cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
+    cfg.update(over)
+    pmax = 7 if "symmetric" in name else 15
+    _run_case(orc, cfg, 2, debug_rows=[(0, 40), (360, 48), (1133, 40)], pmax=pmax, causal=cb)
+
+
+def test_causal_d64(orc):
+    cfg = synth.custom(1, 2, 5, 7, 9, 64, 24, 20, 20, 32, 64, dtype="float32", recipe="tiny")
+    _run_case(orc, cfg, 1, debug_rows=[(0, 64), (250, 65)], causal=63)
