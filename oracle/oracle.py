@@ -95,9 +95,11 @@ def rope_rotate(shape, rot: int, table: np.ndarray, x: np.ndarray) -> np.ndarray
     return out
 
 
-def quantize(shape, rot: int, table: np.ndarray, q, k, v, smooth_k: bool = True, diag: bool = False):
+def quantize(shape, rot: int, table: np.ndarray, q, k, v, smooth_k: bool = True, diag: bool = False,
+             smooth_q: bool = False):
     """Returns dict: qc,kc,vc (int8 [B,H,N,D]), qs,ks ([B,H,nqb]), vs ([B,H,D]),
-    vcol ([B,H,nkb,D]); with diag also q_rot, k_rot, k_mu."""
+    vcol ([B,H,nkb,D]); with diag also q_rot, k_rot, k_mu, q_mu.  smooth_q: Q minus
+    its channel mean, and k_bias [B,H,N] f32 = mu_q . K_j (pass it to attention)."""
     s = shape_array(shape)
     B, H, D = int(shape["B"]), int(shape["H"]), int(shape["D"])
     N = n_tokens(shape)
@@ -115,11 +117,16 @@ def quantize(shape, rot: int, table: np.ndarray, q, k, v, smooth_k: bool = True,
         r["q_rot"] = np.empty((B, H, N, D), np.float32)
         r["k_rot"] = np.empty((B, H, N, D), np.float32)
         r["k_mu"] = np.empty((B, H, D), np.float32)
-    lib().orc_quantize(_p(s), ctypes.c_int32(rot), _p(np.ascontiguousarray(table, np.float32)),
-                       ctypes.c_int32(1 if smooth_k else 0), _p(q), _p(k), _p(v),
-                       _p(r["qc"]), _p(r["qs"]), _p(r["kc"]), _p(r["ks"]),
-                       _p(r["vc"]), _p(r["vs"]), _p(r["vcol"]),
-                       _p(r.get("q_rot")), _p(r.get("k_rot")), _p(r.get("k_mu")))
+        r["q_mu"] = np.empty((B, H, D), np.float32)
+    if smooth_q:
+        r["k_bias"] = np.empty((B, H, N), np.float32)
+    flags = (1 if smooth_k else 0) | (2 if smooth_q else 0)
+    lib().orc_quantize_x(_p(s), ctypes.c_int32(rot), _p(np.ascontiguousarray(table, np.float32)),
+                         ctypes.c_int32(flags), _p(q), _p(k), _p(v),
+                         _p(r["qc"]), _p(r["qs"]), _p(r["kc"]), _p(r["ks"]),
+                         _p(r["vc"]), _p(r["vs"]), _p(r["vcol"]),
+                         _p(r.get("q_rot")), _p(r.get("k_rot")), _p(r.get("k_mu")), _p(r.get("q_mu")),
+                         _p(r.get("k_bias")))
     return r
 
 
@@ -139,7 +146,8 @@ def attention(shape, qz: dict, rows=None, dumps: bool = False, pmax: int = 15,
     pmax = 15: range-rectified P codes r - 8 in [-8, 7] (the method); pmax = 7: the
     symmetric baseline, codes r = round(7 P) in [0, 7].  causal_block: 0 for
     bidirectional attention, c > 0 for block-causal attention (key_limit); dump
-    entries of keys a row does not see stay zero."""
+    entries of keys a row does not see stay zero.  A "k_bias" entry in qz (from
+    quantize(..., smooth_q=True)) adds the per-key term Q smoothing leaves."""
     if pmax not in (7, 15):
         raise ValueError("pmax is 15 (range-rectified) or 7 (symmetric baseline)")
     s = shape_array(shape)
@@ -162,7 +170,8 @@ def attention(shape, qz: dict, rows=None, dumps: bool = False, pmax: int = 15,
                         _p(rows), ctypes.c_int64(R), _p(res["out"]),
                         _p(res.get("a_qk")), _p(res.get("pcode")), _p(res.get("a_pv")),
                         _p(res.get("m")), _p(res.get("l")), ctypes.c_int32(pmax),
-                        ctypes.c_int32(causal_block))
+                        ctypes.c_int32(causal_block),
+                        _p(c(qz["k_bias"], np.float32) if qz.get("k_bias") is not None else None))
     return res
 
 

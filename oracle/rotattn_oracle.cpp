@@ -305,11 +305,19 @@ void orc_rope_rotate_f64(const int32_t* shp, int32_t rot, const double* tab, con
 //   qc, kc [B,H,N,D]; qs, ks [B,H,ceil(N/qk_blk)]; vc [B,H,N,D]; vs [B,H,D];
 //   vcol [B,H,ceil(N/kv_blk),D].  Optional (nullable): q_rot, k_rot [B,H,N,D] (K
 //   before smoothing), k_mu [B,H,D].
-void orc_quantize(const int32_t* shp, int32_t rot, const float* tab, int32_t smooth_k,
-                  const float* q, const float* k, const float* v,
-                  int8_t* qc, float* qs, int8_t* kc, float* ks,
-                  int8_t* vc, float* vs, int32_t* vcol,
-                  float* q_rot, float* k_rot, float* k_mu) {
+// flags: bit 0 smooths K as above.  Bit 1 smooths Q the same way (the other reading
+//   of the framework's channel smoothing): Q' = Q - mu_q with mu_q formed like mu
+//   over the rotated Q.  Unlike mu, mu_q does not cancel in softmax: it leaves the
+//   per-key term dS_j = mu_q . K_j (K_j as quantised: rotated, and smoothed when
+//   bit 0 is set), written to k_bias [B,H,N] as float(binary64 sum over channels in
+//   order of the exact products).  The attention adds it back to every score.
+//   q_mu [B,H,D] (nullable) receives mu_q.
+void orc_quantize_x(const int32_t* shp, int32_t rot, const float* tab, int32_t flags,
+                    const float* q, const float* k, const float* v,
+                    int8_t* qc, float* qs, int8_t* kc, float* ks,
+                    int8_t* vc, float* vs, int32_t* vcol,
+                    float* q_rot, float* k_rot, float* k_mu, float* q_mu, float* k_bias) {
+  const int32_t smooth_k = flags & 1, smooth_q = flags & 2;
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
   const int64_t nqb = (N + s.qk_blk - 1) / s.qk_blk;
@@ -326,20 +334,39 @@ void orc_quantize(const int32_t* shp, int32_t rot, const float* tab, int32_t smo
     }
     if (q_rot) std::memcpy(q_rot + bh * N * D, qr.data(), sizeof(float) * N * D);
     if (k_rot) std::memcpy(k_rot + bh * N * D, kr.data(), sizeof(float) * N * D);
+    // channel mean: binary64 sums of 64-token blocks, added in block order, / N
+    auto channel_mean = [&](const std::vector<float>& x, int64_t d) {
+      double total = 0.0;
+      for (int64_t b0 = 0; b0 < N; b0 += kMeanBlk) {
+        double part = 0.0;
+        for (int64_t n = b0; n < std::min(N, b0 + kMeanBlk); ++n) part += (double)x[n * D + d];
+        total += part;
+      }
+      return (float)(total / (double)N);
+    };
     if (smooth_k) {
       for (int64_t d = 0; d < D; ++d) {
-        double total = 0.0;
-        for (int64_t b0 = 0; b0 < N; b0 += kMeanBlk) {
-          double part = 0.0;
-          for (int64_t n = b0; n < std::min(N, b0 + kMeanBlk); ++n) part += (double)kr[n * D + d];
-          total += part;
-        }
-        const float mu = (float)(total / (double)N);
+        const float mu = channel_mean(kr, d);
         if (k_mu) k_mu[bh * D + d] = mu;
         for (int64_t n = 0; n < N; ++n) kr[n * D + d] = kr[n * D + d] - mu;
       }
     } else if (k_mu) {
       for (int64_t d = 0; d < D; ++d) k_mu[bh * D + d] = 0.f;
+    }
+    if (smooth_q) {
+      std::vector<float> muq(D);
+      for (int64_t d = 0; d < D; ++d) {
+        muq[d] = channel_mean(qr, d);
+        if (q_mu) q_mu[bh * D + d] = muq[d];
+        for (int64_t n = 0; n < N; ++n) qr[n * D + d] = qr[n * D + d] - muq[d];
+      }
+      for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;  // each product of two binary32 values is exact in binary64
+        for (int64_t d = 0; d < D; ++d) acc += (double)muq[d] * (double)kr[n * D + d];
+        k_bias[bh * N + n] = (float)acc;
+      }
+    } else if (q_mu) {
+      for (int64_t d = 0; d < D; ++d) q_mu[bh * D + d] = 0.f;
     }
     for (int64_t b = 0; b < nqb; ++b) {
       const int64_t n0 = b * s.qk_blk, cnt = std::min<int64_t>(s.qk_blk, N - n0);
@@ -427,11 +454,15 @@ int64_t orc_p_level_bruteforce(float lo, float hi, float* first) {
 // r = round-half-even(7 P) in [0, 7], and the code is r itself (no zero point).
 // causal_block: see key_limit(); keys at or beyond the row's limit do not exist for
 // it (no score, no code, nothing in m, l or O; their dump entries are not written).
+// k_bias (nullable, [B,H,N] binary32): the per-key term dS_j that Q smoothing
+// leaves (orc_quantize_x).  With it every score gains delta_j = fl(dS_j * C0):
+//   t_ij = fma(a_ij, c_ij, delta_j),  y'_ij = fl(t_ij + fl(L15 - m_s)),
+// the rest unchanged.
 void orc_attention_x(const int32_t* shp, const int8_t* qc, const float* qs,
                      const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
                      const int64_t* rows, int64_t n_rows, double* out,
                      int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out, int32_t pmax,
-                     int32_t causal_block) {
+                     int32_t causal_block, const float* k_bias) {
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
   const int64_t nqb = (N + s.qk_blk - 1) / s.qk_blk;
@@ -446,7 +477,7 @@ void orc_attention_x(const int32_t* shp, const int8_t* qc, const float* qs,
     const int8_t* qrow = qc + (bh * N + i) * D;
     const float sq = qs[bh * nqb + i / s.qk_blk];
     std::vector<int32_t> a(s.kv_blk);
-    std::vector<float> c(s.kv_blk);
+    std::vector<float> c(s.kv_blk), tv(s.kv_blk);
     std::vector<double> O(D, 0.0);
     std::vector<int64_t> acc(D);
     float m = -std::numeric_limits<float>::infinity();
@@ -467,7 +498,8 @@ void orc_attention_x(const int32_t* shp, const int8_t* qc, const float* qs,
         const float sk = ks[bh * nqb + j / s.qk_blk];
         const float cc = (sq * sk) * C0;
         c[j - j0] = cc;
-        const float t = (float)a[j - j0] * cc;
+        const float t = k_bias ? std::fmaf((float)a[j - j0], cc, k_bias[bh * N + j] * C0) : (float)a[j - j0] * cc;
+        tv[j - j0] = t;
         mnew = std::max(mnew, t);
         if (a_qk) a_qk[ri * N + j] = a[j - j0];
       }
@@ -477,7 +509,7 @@ void orc_attention_x(const int32_t* shp, const int8_t* qc, const float* qs,
       for (int64_t d = 0; d < D; ++d) O[d] *= alpha;
       std::fill(acc.begin(), acc.end(), 0);
       for (int64_t j = j0; j < j1; ++j) {
-        const float y = std::fmaf((float)a[j - j0], c[j - j0], nm);
+        const float y = k_bias ? tv[j - j0] + nm : std::fmaf((float)a[j - j0], c[j - j0], nm);
         const int r = p_level(y);
         if (pcode) pcode[ri * N + j] = (int8_t)(r - zp);
         l += std::exp2((double)y);
@@ -500,14 +532,16 @@ void orc_attention_p(const int32_t* shp, const int8_t* qc, const float* qs,
                      const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
                      const int64_t* rows, int64_t n_rows, double* out,
                      int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out, int32_t pmax) {
-  orc_attention_x(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, pmax, 0);
+  orc_attention_x(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, pmax, 0,
+                  nullptr);
 }
 
 void orc_attention(const int32_t* shp, const int8_t* qc, const float* qs,
                    const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
                    const int64_t* rows, int64_t n_rows, double* out,
                    int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out) {
-  orc_attention_x(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, 15, 0);
+  orc_attention_x(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, 15, 0,
+                  nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -629,6 +663,13 @@ void orc_exact_attention(const int32_t* shp, const double* tab64_plain, const fl
 void orc_fallback_attention(const int32_t* shp, const float* tab_plain, const float* q, const float* k,
                             const float* v, const int64_t* rows, int64_t n_rows, double* out) {
   orc_fallback_attention_x(shp, tab_plain, q, k, v, rows, n_rows, out, 0);
+}
+
+void orc_quantize(const int32_t* shp, int32_t rot, const float* tab, int32_t smooth_k, const float* q,
+                  const float* k, const float* v, int8_t* qc, float* qs, int8_t* kc, float* ks, int8_t* vc,
+                  float* vs, int32_t* vcol, float* q_rot, float* k_rot, float* k_mu) {
+  orc_quantize_x(shp, rot, tab, smooth_k ? 1 : 0, q, k, v, qc, qs, kc, ks, vc, vs, vcol, q_rot, k_rot, k_mu,
+                 nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -556,3 +556,86 @@ def test_causal_quantised_and_fallback_close_to_exact(orc):
     # last-frame rows see every key: they equal them
     assert not np.allclose(qa[:24], qb[:24])
     assert np.array_equal(qa[48:72], qb[48:72])
+
+
+# --- Q smoothing (mu_q subtracted from Q; the per-key term mu_q . K_j added back) ----
+
+def _offset_q_case(orc, seed=5):
+    """Wan-like heads whose queries share a large offset in the slow (last) RoPE
+    pairs of each segment, where rotation by position is mild: the case Q smoothing
+    is for."""
+    cfg = synth.custom(1, 2, 3, 8, 10, 64, 24, 20, 20, 16, 16)
+    q, k, v = synth.make_inputs(cfg, seed=seed)
+    rng = np.random.default_rng(seed)
+    off = np.zeros(64, np.float32)
+    for o, w in ((0, 24), (24, 20), (44, 20)):
+        off[o + w - 4:o + w] = rng.uniform(4, 8, 4) * rng.choice([-1, 1], 4)
+    return cfg, (q + off).astype(np.float32), k, v
+
+
+def test_q_smoothing_statistics(orc):
+    """mu_q is the channel mean of the rotated Q, the Q codes quantise Q - mu_q, the
+    K codes do not change, and k_bias_j = mu_q . (K_j - mu_k) (binary64 numpy)."""
+    cfg, q, k, v = _offset_q_case(orc)
+    tab = orc.rope_table(cfg, 2)
+    z = orc.quantize(cfg, 2, tab, q, k, v, diag=True, smooth_q=True)
+    z0 = orc.quantize(cfg, 2, tab, q, k, v)
+    H, N, D = 2, orc.n_tokens(cfg), 64
+    qr = z["q_rot"].astype(np.float64).reshape(H, N, D)
+    mu = qr.mean(axis=1)
+    assert np.allclose(z["q_mu"].reshape(H, D), mu, rtol=2e-7, atol=1e-7)
+    assert np.abs(mu).max() > 1.0
+    # Q codes: within half a step of Q - mu_q in every 16-token block
+    x = (z["q_rot"] - z["q_mu"][:, :, None, :]).reshape(H, N // 16, 16, D)
+    deq = z["qc"].reshape(H, N // 16, 16, D) * z["qs"].reshape(H, N // 16, 1, 1)
+    assert np.all(np.abs(deq - x) <= 0.5 * z["qs"].reshape(H, N // 16, 1, 1) * (1 + 1e-5) + 1e-6)
+    for key in ("kc", "ks", "vc", "vs"):
+        assert np.array_equal(z[key], z0[key]), key
+    kt = (z["k_rot"] - z["k_mu"][:, :, None, :]).astype(np.float32).astype(np.float64).reshape(H, N, D)
+    want = np.einsum("hd,hnd->hn", z["q_mu"].reshape(H, D).astype(np.float64), kt)
+    mag = np.einsum("hd,hnd->hn", np.abs(z["q_mu"].reshape(H, D)).astype(np.float64), np.abs(kt))
+    assert np.all(np.abs(z["k_bias"].reshape(H, N) - want) <= 1e-6 * mag + 1e-30)
+
+
+@pytest.mark.parametrize("kv", [16, 32])
+def test_k_bias_attention_within_rounding_bound(orc, kv):
+    """Lossless codes plus a per-key bias dS_j: the output is within the level
+    rounding bound of textbook softmax of (A_ij sq_i sk_j + dS_j) / sqrt(D)
+    (numpy, binary64); a transposed, unscaled or dropped bias fails it."""
+    rng = np.random.default_rng(17)
+    B, H, F, Hs, Ws, D = 1, 2, 2, 4, 8, 64
+    cfg = synth.custom(B, H, F, Hs, Ws, D, 24, 20, 20, 16, kv)
+    N = F * Hs * Ws
+    z = dict(qc=_ints(rng, (B, H, N, D)), kc=_ints(rng, (B, H, N, D)), vc=_ints(rng, (B, H, N, D)),
+             qs=rng.uniform(0.02, 0.1, (B, H, N // 16)).astype(np.float32),
+             ks=rng.uniform(0.02, 0.1, (B, H, N // 16)).astype(np.float32),
+             vs=rng.uniform(0.5, 1, (B, H, D)).astype(np.float32),
+             k_bias=rng.normal(0, 12, (B, H, N)).astype(np.float32))
+    r = orc.attention(cfg, z, dumps=True)
+    V = _dequant_v(z).reshape(B * H, N, D)
+    sq = np.repeat(z["qs"].astype(np.float64), 16, axis=2).reshape(B * H, N)
+    sk = np.repeat(z["ks"].astype(np.float64), 16, axis=2).reshape(B * H, N)
+    A = np.einsum("hid,hjd->hij", z["qc"].reshape(B * H, N, D).astype(np.float64),
+                  z["kc"].reshape(B * H, N, D).astype(np.float64))
+    S = (A * sq[:, :, None] * sk[:, None, :] + z["k_bias"].reshape(B * H, 1, N)) / math.sqrt(D)
+    P = np.exp(S - S.max(axis=2, keepdims=True))
+    exact = np.einsum("hij,hjd->hid", P / P.sum(axis=2, keepdims=True), V).reshape(-1, D)
+    bound = 0.5 * np.abs(V).sum(axis=1)[:, None, :].repeat(N, axis=1).reshape(-1, D) / r["l"][:, None]
+    assert np.all(np.abs(r["out"] - exact) <= bound * (1 + 1e-5) + 1e-9)
+    # the bias matters here: without it the output is far outside the bound
+    z0 = dict(z)
+    del z0["k_bias"]
+    assert np.max(np.abs(orc.attention(cfg, z0)["out"] - exact) - bound) > 0.05
+
+
+def test_q_smoothing_recovers_offset_queries(orc):
+    """On queries with a shared offset, Q smoothing brings the quantised output
+    closer to exact attention than quantising Q as it is."""
+    cfg, q, k, v = _offset_q_case(orc)
+    tab = orc.rope_table(cfg, 2)
+    ex = orc.exact_attention(cfg, q, k, v)
+    cos = lambda a: float(np.sum(a * ex) / np.linalg.norm(a) / np.linalg.norm(ex))
+    plain = orc.attention(cfg, orc.quantize(cfg, 2, tab, q, k, v))["out"]
+    smooth = orc.attention(cfg, orc.quantize(cfg, 2, tab, q, k, v, smooth_q=True))["out"]
+    print("cosine vs exact: plain %.4f, Q smoothing %.4f" % (cos(plain), cos(smooth)))
+    assert cos(smooth) > cos(plain) + 0.02
