@@ -42,6 +42,8 @@ def main():
     ap.add_argument("--causal", type=int, default=0,
                     help="block-causal attention with this block of tokens (0: bidirectional); the "
                          "operation count is then that of the visible query/key pairs")
+    ap.add_argument("--smooth-q", action="store_true",
+                    help="Q smoothing as well (rotattn_quantize_qk_smooth_q and the per-key score term)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -86,7 +88,7 @@ def main():
     q, k, v = (torch.from_numpy(x).cuda() for x in (Q, K, V))
     del Q, K, V
     tab = ra.rotattn_build_rope_table(shape, rot).cuda()
-    z = ra.alloc_codes(shape)
+    z = ra.alloc_codes(shape, smooth_q=args.smooth_q)
     out = torch.empty((B, H, N, D), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -102,7 +104,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, True, z)
+        ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, True, z, smooth_q=args.smooth_q)
         if ev is not None:
             ev[1].record(stream)
         ra.rotattn_int4_attention(shape, z, out, heads=q4_heads, causal_block=args.causal)
@@ -151,13 +153,14 @@ def main():
                                "(%d/%d/%d), %s rotation, qk_blk=%d kv_blk=%d, fp16 in/out%s"
                                % (WORKLOADS.get(args.config, args.config), B, H, cfg["F"], cfg["Hs"], cfg["Ws"], N,
                                   D, cfg["Df"], cfg["Dh"], cfg["Dw"], cfg["rot"], cfg["qk_blk"], cfg["kv_blk"],
-                                  ", block-causal c=%d (ops of visible pairs)" % args.causal if args.causal else ""),
+                                  (", block-causal c=%d (ops of visible pairs)" % args.causal if args.causal else "")
+                                  + (", Q smoothing" if args.smooth_q else "")),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "k2_attention (rotattn_int4_attention)",
                      "achieved": round(k2_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                      "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
-                     "traffic": counted_traffic() if args.config == CONFIG and not (args.kv or args.qk or args.rot or args.causal)
-                     else None},
+                     "traffic": counted_traffic() if args.config == CONFIG and not (args.kv or args.qk or args.rot or args.causal
+                                                                                   or args.smooth_q) else None},
         "kernels_ms": dict({"quantize_qk": round(k1_ms, 4), "int4_attention": round(k2_ms, 4)},
                            **({"fp16_fallback_even_heads": round(k3_ms, 4)} if mixed else {})),
         "quantize_qk_GBps": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),

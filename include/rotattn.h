@@ -123,6 +123,24 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
                                    uint8_t* v_codes, float* v_scale, int32_t* v_colsum,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- rotattn_quantize_qk_smooth_q ------------------------------------------------
+ * rotattn_quantize_qk with Q smoothing as well: the other reading of the
+ * framework's channel smoothing (papernotes note, Overall framework), as an
+ * accuracy option.  mu_q (the per-(b,h) channel mean of the rotated Q, formed like
+ * the K mean) is subtracted from Q before it is quantised.  Unlike the K mean it
+ * does not cancel in softmax: it leaves the per-key score term dS_j = mu_q . K_j
+ * (K_j as quantised: rotated, and smoothed when smooth_k), written to
+ *   k_bias  device f32 [B,H,Np]: binary64 sum over the channels in order of the
+ *           exact products mu_q[d] K_j[d], rounded to binary32; 0 past N.
+ * Pass k_bias to rotattn_int4_attention_ex, which adds it back to every score.
+ * k_bias NULL returns ROTATTN_E_NULL; everything else as rotattn_quantize_qk. */
+rotattn_status rotattn_quantize_qk_smooth_q(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
+                                            const void* q, const void* k, const void* v,
+                                            const float* rope_table, int32_t smooth_k,
+                                            uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+                                            uint8_t* v_codes, float* v_scale, int32_t* v_colsum, float* k_bias,
+                                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- rotattn_int4_attention -----------------------------------------------------
  * INT4 FlashAttention forward (framework flowchart; Key design 2).  For each query
  * row i and online-softmax step s of kv_blk keys:
@@ -205,29 +223,42 @@ rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
                                                   const rotattn_debug* dbg,
                                                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* ---- block-causal variants -------------------------------------------------------
- * The pages name causal as well as bidirectional attention for video DiTs without
- * fixing its granularity (papernotes note, Overall framework).  These entry points
- * take a causal block size c: query token i sees key j iff j / c <= i / c (integer
- * division), i.e. the keys [0, min(N, (i / c + 1) c)), and absent keys take no part
- * in the running maximum, in l or in O.  c = 0 is bidirectional (the entry points
- * above); c = 1 token-causal; c = Hs * Ws frame-causal (a frame sees itself and the
- * frames before it); c >= N is bidirectional.  c < 0 returns ROTATTN_E_ARG.
- *   p_max   (int4 only) 15: range-rectified P (the method, as
- *           rotattn_int4_attention); 7: the symmetric baseline (as
- *           rotattn_int4_attention_symmetric_p); other values return ROTATTN_E_ARG.
+/* ---- options: block-causal masks, the P code, the Q-smoothing term ---------------
+ * Block-causal attention: the pages name causal as well as bidirectional attention
+ * for video DiTs without fixing its granularity (papernotes note, Overall
+ * framework).  A causal block size c lets query token i see key j iff j / c <= i / c
+ * (integer division), i.e. the keys [0, min(N, (i / c + 1) c)); absent keys take no
+ * part in the running maximum, in l or in O.  c = 0 is bidirectional; c = 1
+ * token-causal; c = Hs * Ws frame-causal (a frame sees itself and the frames before
+ * it); c >= N is bidirectional.  c < 0 returns ROTATTN_E_ARG.
+ *   p_max         0 or 15: range-rectified P (the method); 7: the symmetric
+ *                 baseline (as rotattn_int4_attention_symmetric_p); other values
+ *                 return ROTATTN_E_ARG.
+ *   causal_block  c as above.
+ *   k_bias        NULL, or device f32 [B,H,Np] from rotattn_quantize_qk_smooth_q:
+ *                 every score gains delta_j = fl(k_bias_j * C0) in log2 units,
+ *                 t_ij = fma(a_ij, c_ij, delta_j), y_ij = fl(t_ij + fl(L15 - m_s)).
  * Debug dumps leave the entries of keys a row does not see, and its steps past the
  * query tile's last key, unwritten: fill them first to compare whole arrays.
- * Every other argument, layout, workspace and error as the entry points above. */
-rotattn_status rotattn_int4_attention_causal(const rotattn_shape* s,
-                                             const uint8_t* q_codes, const float* q_scale,
-                                             const uint8_t* k_codes, const float* k_scale,
-                                             const uint8_t* v_codes, const float* v_scale,
-                                             const int32_t* heads, int32_t n_heads,
-                                             int32_t causal_block, int32_t p_max,
-                                             rotattn_dtype out_dtype, void* out,
-                                             const rotattn_debug* dbg,
-                                             void* workspace, size_t workspace_bytes, void* stream);
+ * opts NULL is all defaults.  Every other argument, layout, workspace and error as
+ * rotattn_int4_attention. */
+typedef struct {
+  int32_t p_max;
+  int32_t causal_block;
+  const float* k_bias;
+} rotattn_attention_opts;
+
+rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
+                                         const uint8_t* q_codes, const float* q_scale,
+                                         const uint8_t* k_codes, const float* k_scale,
+                                         const uint8_t* v_codes, const float* v_scale,
+                                         const int32_t* heads, int32_t n_heads,
+                                         const rotattn_attention_opts* opts,
+                                         rotattn_dtype out_dtype, void* out,
+                                         const rotattn_debug* dbg,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* The FP16 fallback with a causal block c as above (c = 0 is rotattn_fp16_fallback). */
 rotattn_status rotattn_fp16_fallback_causal(const rotattn_shape* s, rotattn_dtype in_dtype,
                                             const void* q, const void* k, const void* v,
                                             const float* rope_table,

@@ -113,22 +113,67 @@ rotattn_status rotattn_build_rope_table(const rotattn_shape* s, rotattn_rot rot,
   return ROTATTN_OK;
 }
 
-static size_t q_ws_parts(const rotattn_shape* s, size_t* off_mu, size_t* off_amax) {
+// quantisation workspace: K partial sums, Q partial sums, K mean, Q mean, V amax
+struct QWs {
+  size_t qpart, kmu, qmu, amax, total;
+};
+static QWs q_ws_parts(const rotattn_shape* s) {
   const int64_t N = tokens(s);
   const int64_t BH = (int64_t)s->B * s->H;
   const int64_t nblk = (N + 63) / 64;
-  const size_t kpart = align256((size_t)BH * nblk * s->D * sizeof(double));
+  const size_t part = align256((size_t)BH * nblk * s->D * sizeof(double));
   const size_t mu = align256((size_t)BH * s->D * sizeof(float));
   const size_t amax = align256((size_t)BH * s->D * sizeof(uint32_t));
-  if (off_mu) *off_mu = kpart;
-  if (off_amax) *off_amax = kpart + mu;
-  return kpart + mu + amax;
+  QWs w;
+  w.qpart = part;
+  w.kmu = 2 * part;
+  w.qmu = w.kmu + mu;
+  w.amax = w.qmu + mu;
+  w.total = w.amax + amax;
+  return w;
 }
 
 size_t rotattn_quantize_qk_workspace(const rotattn_shape* s) {
   if (!s || rotattn_check_shape(s) != ROTATTN_OK) return 0;
-  return q_ws_parts(s, nullptr, nullptr);
+  return q_ws_parts(s).total;
 }
+
+namespace {
+rotattn_status quantize_call(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
+                             const void* q, const void* k, const void* v,
+                             const float* rope_table, int32_t smooth_k,
+                             uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+                             uint8_t* v_codes, float* v_scale, int32_t* v_colsum, bool smooth_q, float* k_bias,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  const rotattn_status st = rotattn_check_shape(s);
+  if (st != ROTATTN_OK) return st;
+  if (!q || !k || !v || !rope_table || !q_codes || !q_scale || !k_codes || !k_scale || !v_codes ||
+      !v_scale || !workspace || (smooth_q && !k_bias))
+    return ROTATTN_E_NULL;
+  if (rot < ROTATTN_ROT_NONE || rot > ROTATTN_ROT_FULL) return ROTATTN_E_ARG;
+  if (in_dtype < ROTATTN_F32 || in_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
+  const QWs w = q_ws_parts(s);
+  if (workspace_bytes < w.total) return ROTATTN_E_WORKSPACE;
+  ra::QuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.s = to_shape(s);
+  a.Np = rotattn_padded_tokens(s);
+  a.rot = (int)rot;
+  a.smooth = smooth_k ? 1 : 0;
+  a.smooth_q = smooth_q ? 1 : 0;
+  a.q = q; a.k = k; a.v = v;
+  a.table = rope_table;
+  a.qc = q_codes; a.qs = q_scale; a.kc = k_codes; a.ks = k_scale;
+  a.vc = v_codes; a.vs = v_scale; a.vcol = v_colsum;
+  a.kbias = k_bias;
+  a.kpart = (double*)workspace;
+  a.qpart = (double*)((char*)workspace + w.qpart);
+  a.kmu = (float*)((char*)workspace + w.kmu);
+  a.qmu = (float*)((char*)workspace + w.qmu);
+  a.vamax = (uint32_t*)((char*)workspace + w.amax);
+  return launch_status(ra::launch_quantize(a, (int)in_dtype, (hipStream_t)stream));
+}
+}  // namespace
 
 rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
                                    const void* q, const void* k, const void* v,
@@ -136,28 +181,18 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
                                    uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
                                    uint8_t* v_codes, float* v_scale, int32_t* v_colsum,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  const rotattn_status st = rotattn_check_shape(s);
-  if (st != ROTATTN_OK) return st;
-  if (!q || !k || !v || !rope_table || !q_codes || !q_scale || !k_codes || !k_scale || !v_codes ||
-      !v_scale || !workspace)
-    return ROTATTN_E_NULL;
-  if (rot < ROTATTN_ROT_NONE || rot > ROTATTN_ROT_FULL) return ROTATTN_E_ARG;
-  if (in_dtype < ROTATTN_F32 || in_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
-  size_t off_mu, off_amax;
-  if (workspace_bytes < q_ws_parts(s, &off_mu, &off_amax)) return ROTATTN_E_WORKSPACE;
-  ra::QuantArgs a;
-  a.s = to_shape(s);
-  a.Np = rotattn_padded_tokens(s);
-  a.rot = (int)rot;
-  a.smooth = smooth_k ? 1 : 0;
-  a.q = q; a.k = k; a.v = v;
-  a.table = rope_table;
-  a.qc = q_codes; a.qs = q_scale; a.kc = k_codes; a.ks = k_scale;
-  a.vc = v_codes; a.vs = v_scale; a.vcol = v_colsum;
-  a.kpart = (double*)workspace;
-  a.kmu = (float*)((char*)workspace + off_mu);
-  a.vamax = (uint32_t*)((char*)workspace + off_amax);
-  return launch_status(ra::launch_quantize(a, (int)in_dtype, (hipStream_t)stream));
+  return quantize_call(s, rot, in_dtype, q, k, v, rope_table, smooth_k, q_codes, q_scale, k_codes, k_scale,
+                       v_codes, v_scale, v_colsum, false, nullptr, workspace, workspace_bytes, stream);
+}
+
+rotattn_status rotattn_quantize_qk_smooth_q(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
+                                            const void* q, const void* k, const void* v,
+                                            const float* rope_table, int32_t smooth_k,
+                                            uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+                                            uint8_t* v_codes, float* v_scale, int32_t* v_colsum, float* k_bias,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_call(s, rot, in_dtype, q, k, v, rope_table, smooth_k, q_codes, q_scale, k_codes, k_scale,
+                       v_codes, v_scale, v_colsum, true, k_bias, workspace, workspace_bytes, stream);
 }
 
 size_t rotattn_int4_attention_workspace(const rotattn_shape* s) {
@@ -175,7 +210,8 @@ rotattn_status attention_call(const rotattn_shape* s,
                               const int32_t* heads, int32_t n_heads,
                               rotattn_dtype out_dtype, void* out,
                               const rotattn_debug* dbg,
-                              void* workspace, size_t workspace_bytes, void* stream, int pmax, int causal) {
+                              void* workspace, size_t workspace_bytes, void* stream, int pmax, int causal,
+                              const float* k_bias) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
   if (causal < 0 || (pmax != 15 && pmax != 7)) return ROTATTN_E_ARG;
@@ -208,6 +244,7 @@ rotattn_status attention_call(const rotattn_shape* s,
   a.L15 = (float)std::log2((double)pmax);
   a.p_zero = pmax == 15 ? 8 : 0;
   a.causal = causal < N ? causal : 0;  // a block of N or more keys is every key
+  a.kbias = k_bias;
   std::memcpy(a.T, levels().T, sizeof(a.T));
   hipStream_t hs = (hipStream_t)stream;
   if (dbg) {
@@ -244,7 +281,7 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
                                       const rotattn_debug* dbg,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
-                        dbg, workspace, workspace_bytes, stream, 15, 0);
+                        dbg, workspace, workspace_bytes, stream, 15, 0, nullptr);
 }
 
 rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
@@ -256,20 +293,22 @@ rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
                                                   const rotattn_debug* dbg,
                                                   void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
-                        dbg, workspace, workspace_bytes, stream, 7, 0);
+                        dbg, workspace, workspace_bytes, stream, 7, 0, nullptr);
 }
 
-rotattn_status rotattn_int4_attention_causal(const rotattn_shape* s,
-                                             const uint8_t* q_codes, const float* q_scale,
-                                             const uint8_t* k_codes, const float* k_scale,
-                                             const uint8_t* v_codes, const float* v_scale,
-                                             const int32_t* heads, int32_t n_heads,
-                                             int32_t causal_block, int32_t p_max,
-                                             rotattn_dtype out_dtype, void* out,
-                                             const rotattn_debug* dbg,
-                                             void* workspace, size_t workspace_bytes, void* stream) {
+rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
+                                         const uint8_t* q_codes, const float* q_scale,
+                                         const uint8_t* k_codes, const float* k_scale,
+                                         const uint8_t* v_codes, const float* v_scale,
+                                         const int32_t* heads, int32_t n_heads,
+                                         const rotattn_attention_opts* opts,
+                                         rotattn_dtype out_dtype, void* out,
+                                         const rotattn_debug* dbg,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  const int pmax = opts && opts->p_max ? opts->p_max : 15;
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
-                        dbg, workspace, workspace_bytes, stream, p_max, causal_block);
+                        dbg, workspace, workspace_bytes, stream, pmax, opts ? opts->causal_block : 0,
+                        opts ? opts->k_bias : nullptr);
 }
 
 size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s) {

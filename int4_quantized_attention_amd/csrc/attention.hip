@@ -79,7 +79,9 @@ struct Geo {
   static constexpr int VROW = TG + 16;            // bytes per V^T row (int8 + pad)
   static constexpr int VOFF = TG * KROW;          // V^T rows start here
   static constexpr int TOFF = VOFF + D * VROW;    // 17 floats of level thresholds
+  static constexpr int DOFF = TOFF + 128;        // TG floats: per-key score terms (Q smoothing)
   static constexpr int IMG = (TOFF + 128 + 4095) / 4096 * 4096;  // one group's image
+  static_assert(DOFF + 4 * TG <= IMG, "the per-key terms fit in the image's padding");
   static constexpr int NDMA = IMG / 4096;         // 16-byte copies per thread per group
   static constexpr int NB = 4 * IMG <= 81920 ? 4 : 2;  // ring slots (two workgroups per CU)
   static constexpr int LDS = NB * IMG;
@@ -162,6 +164,11 @@ __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
     *(i32x4*)(img + G::VOFF + d * G::VROW + 16 * cq) = o;
   }
   if (threadIdx.x < 17) ((float*)(img + G::TOFF))[threadIdx.x] = threadIdx.x < 15 ? args.T[threadIdx.x] : INFINITY;
+  // Q smoothing: the keys' score terms in log2 units, delta_j = fl(dS_j * C0), in
+  // key order (the S^T accumulator holds key 32t + 16h + v of tile t in register v
+  // of lane half h)
+  if (args.kbias && threadIdx.x < G::TG)
+    ((float*)(img + G::DOFF))[threadIdx.x] = args.kbias[(int64_t)bh * Np + g * G::TG + threadIdx.x] * args.C0;
 }
 
 // The fields the device helpers need, copied out of the kernel argument block
@@ -172,6 +179,7 @@ struct Ctx {
   int64_t Np;
   int N, qk_shift;
   int klim;  // keys this lane's query row sees: N, or its block-causal limit
+  bool kb;   // per-key score terms staged (Q smoothing)
   float C0, L15;
   int p_zero;
   int dbg_row0, dbg_n;
@@ -255,7 +263,7 @@ RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::
 template <int D, int KVB, bool DBG, bool MASK, bool US>
 RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl, const float* Tl,
                        const f32x16 (&st)[Geo<D, KVB>::TPS], const float (&ct)[Geo<D, KVB>::TPS],
-                       RowState<D / 32>& S, bool dbg_row, int dr) {
+                       const f32x16 (&sa)[Geo<D, KVB>::TPS], RowState<D / 32>& S, bool dbg_row, int dr) {
   using G = Geo<D, KVB>;
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
   const int N = (int)a.N;
@@ -386,7 +394,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
               if (DBG && dbg_row && act) {
                 const int key = j0 + t * 32 + 16 * h + v;
                 if (key < a.klim) {
-                  a.dbg_aqk[(int64_t)dr * N + key] = (int32_t)st[t][v];
+                  a.dbg_aqk[(int64_t)dr * N + key] = (int32_t)sa[t][v];
                   a.dbg_p[(int64_t)dr * N + key] = (int8_t)(r - a.p_zero);
                 }
               }
@@ -468,9 +476,29 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
     }
     f32x16 st[G::TPS];
     qk_tiles<D, KVB>(cur, tb, qop, st);
+    f32x16 sa[G::TPS];  // the integer scores, kept for the debug dump only
+    if (DBG) {
+#pragma unroll
+      for (int t = 0; t < G::TPS; ++t) sa[t] = st[t];
+    }
+    if (a.kb) {
+      // Q smoothing: t = fma(a, c, delta_j) in place; with c = 1 from here on the max
+      // is max t and y = fma(t, 1, L15 - m) = fl(t + (L15 - m))
+      const float* Dl = (const float*)(cur + G::DOFF) + 32 * tb + 16 * h;
+#pragma unroll
+      for (int t = 0; t < G::TPS; ++t) {
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 d4 = *(const f32x4*)(Dl + 32 * t + 4 * v4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st[t][4 * v4 + e] = __builtin_fmaf(st[t][4 * v4 + e], ct[t], d4[e]);
+        }
+        ct[t] = 1.0f;
+      }
+    }
     const int step0 = KVB < 32 ? 2 * g : g * G::NSG + sg;
-    softmax_pv<D, KVB, DBG, MASK, US>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct, S,
-                                      dbg_row, dr);
+    softmax_pv<D, KVB, DBG, MASK, US>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct,
+                                      DBG ? sa : st, S, dbg_row, dr);
   }
   // copies issued after group g+1's: those of groups g+2 .. min(g+NB-1, ngroups-1)
   const int later = min(g + G::NB - 1, ngroups - 1) - (g + 1);
@@ -511,6 +539,7 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   const int64_t c = args.causal;
   auto limit = [&](int64_t i) -> int { return c > 0 ? (int)min((int64_t)N, (i / c + 1) * c) : N; };
   a.klim = limit(qi);
+  a.kb = args.kbias != nullptr;
   const int kmax = limit(min(qt * kBM + kBM - 1, N - 1));
   const int ngroups = (kmax + G::TG - 1) / G::TG;
   const int nfull = min(limit(qt * kBM) / G::TG, ngroups);  // groups no row masks

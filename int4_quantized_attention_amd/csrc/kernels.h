@@ -16,6 +16,7 @@ struct QuantArgs {
   Shape s;
   int64_t Np;
   int rot, smooth;
+  int smooth_q;   // Q minus its channel mean; the per-key term goes to kbias
   const void* q;
   const void* k;
   const void* v;
@@ -27,9 +28,12 @@ struct QuantArgs {
   uint8_t* vc;
   float* vs;
   int32_t* vcol;
+  float* kbias;  // [B,H,Np] mu_q . K_j (smooth_q only)
   // workspace
   double* kpart;
+  double* qpart;
   float* kmu;
+  float* qmu;
   uint32_t* vamax;
 };
 
@@ -50,6 +54,7 @@ struct AttnArgs {
   float C0, L15;  // L15: fl(log2 15), or fl(log2 7) for the symmetric-P baseline
   int p_zero;       // zero point of the dumped P codes: 8 (range-rectified) or 0
   int causal;       // 0 bidirectional; c > 0: query i sees key j iff j / c <= i / c (c < N)
+  const float* kbias;  // nullable [B,H,Np]: per-key score term left by Q smoothing
   float T[16];  // P level thresholds (15 used)
   // debug (rows [dbg_row0, dbg_row0 + dbg_n) of the single listed head)
   int dbg_row0, dbg_n;

@@ -18,9 +18,10 @@
 namespace ra {
 
 // ---------------------------------------------------------------------------------
-// K statistics: ordered binary64 partial sums of rotated K over 64-token blocks.
-// grid (ceil(N/64), B*H); 256 threads, four per token, each owning D/4 channels.
-// partial [B*H][nblk][D] f64.
+// Channel statistics for smoothing: ordered binary64 partial sums of rotated K (and,
+// with Q smoothing, of rotated Q) over 64-token blocks.  grid (ceil(N/64), B*H, the
+// number of smoothed tensors); z = 0 is K unless only Q is smoothed.  256 threads,
+// four per token, each owning D/4 channels.  partial [B*H][nblk][D] f64.
 template <int D, int DT, int ROT>
 __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
   constexpr int TPT = 4, CPT = D / TPT;
@@ -28,10 +29,11 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
   const Shape s = a.s;
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int bh = blockIdx.y, blk = blockIdx.x;
+  const bool isQ = blockIdx.z + (a.smooth ? 0 : 1) == 1;
   const int64_t n0 = (int64_t)blk * kMeanTile;
   const int lt = threadIdx.x / TPT, c0 = (threadIdx.x % TPT) * CPT;
   const int64_t n = n0 + lt;
-  const void* base = (const char*)a.k + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
+  const void* base = (const char*)(isQ ? a.q : a.k) + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   float x[CPT];
   rotated_slice<DT, ROT, CPT, D>(base, n, n < N, D, c0, s, a.table, R + lt * (D + 1), x);
   if (ROT == 2) __syncthreads();  // every row of R read before it is overwritten
@@ -44,20 +46,25 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
     const int cnt = (int)min((int64_t)kMeanTile, N - n0);
     for (int r = 0; r < cnt; ++r) part += (double)R[r * (D + 1) + c];
     const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
-    a.kpart[((int64_t)bh * nblk + blk) * D + c] = part;
+    (isQ ? a.qpart : a.kpart)[((int64_t)bh * nblk + blk) * D + c] = part;
   }
 }
 
-// Channel mean of K: binary64 sum of the partials in block order, / N, to binary32.
-// The sum is one dependent chain; the loads run eight ahead of it.
+// Channel means of K (and Q): binary64 sum of the partials in block order, / N, to
+// binary32.  Thread idx: tensor idx / (B*H*D) in the order of k1_kstats' z.  The
+// sum is one dependent chain; the loads run eight ahead of it.
 __global__ void k1_kmean(QuantArgs a) {
   const int D = a.s.D;
   const int64_t N = (int64_t)a.s.F * a.s.Hs * a.s.Ws;
   const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)a.s.B * a.s.H * D) return;
+  const int64_t per = (int64_t)a.s.B * a.s.H * D;
+  const int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nz = (a.smooth ? 1 : 0) + (a.smooth_q ? 1 : 0);
+  if (gidx >= nz * per) return;
+  const bool isQ = gidx / per + (a.smooth ? 0 : 1) == 1;
+  const int64_t idx = gidx % per;
   const int64_t bh = idx / D, c = idx % D;
-  const double* p = a.kpart + bh * nblk * D + c;
+  const double* p = (isQ ? a.qpart : a.kpart) + bh * nblk * D + c;
   double total = 0.0;
   int64_t b = 0;
   for (; b + 8 <= nblk; b += 8) {
@@ -68,7 +75,7 @@ __global__ void k1_kmean(QuantArgs a) {
     for (int i = 0; i < 8; ++i) total += v[i];
   }
   for (; b < nblk; ++b) total += p[b * D];
-  a.kmu[idx] = (float)(total / (double)N);
+  (isQ ? a.qmu : a.kmu)[idx] = (float)(total / (double)N);
 }
 
 __global__ void k1_zero_u32(uint32_t* p, int64_t n) {
@@ -137,14 +144,30 @@ __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
   const bool valid = n < N;
   float v[CPT];
   rotated_slice<DT, ROT, CPT, D>(base, n, valid, D, c0, s, a.table, U + lt * (D + 1), v);
-  if (isK && a.smooth && valid) {
-    const f32x4* mu = (const f32x4*)(a.kmu + (int64_t)bh * D + c0);
+  if ((isK ? a.smooth : a.smooth_q) && valid) {
+    const f32x4* mu = (const f32x4*)((isK ? a.kmu : a.qmu) + (int64_t)bh * D + c0);
 #pragma unroll
     for (int i = 0; i < CPT / 4; ++i) {
       const f32x4 m4 = mu[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[4 * i + e] = v[4 * i + e] - m4[e];
     }
+  }
+  if (isK && a.smooth_q) {
+    // dS_n = mu_q . K_n: binary64, channels in order (the products are exact), as one
+    // chain through the token's TPT threads; the last one writes it (0 past N)
+    const float* mq = a.qmu + (int64_t)bh * D + c0;
+    double acc = 0.0;
+#pragma unroll
+    for (int stg = 0; stg < TPT; ++stg) {
+      if (part == stg) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) acc = fma((double)mq[i], (double)v[i], acc);
+      }
+      const double prev = __shfl_up(acc, 1, TPT);
+      if (part == stg + 1) acc = prev;
+    }
+    if (part == TPT - 1) a.kbias[(int64_t)bh * Np + n] = valid ? (float)acc : 0.f;
   }
   float am = 0.f;
 #pragma unroll
@@ -280,10 +303,11 @@ template <int D, int DT, int ROT>
 hipError_t launch_rot(const QuantArgs& a, hipStream_t st) {
   const int64_t N = (int64_t)a.s.F * a.s.Hs * a.s.Ws;
   const int BH = a.s.B * a.s.H;
-  if (a.smooth) {
+  const int nz = (a.smooth ? 1 : 0) + (a.smooth_q ? 1 : 0);
+  if (nz > 0) {
     const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
-    const int64_t nmu = (int64_t)BH * D;
-    k1_kstats<D, DT, ROT><<<dim3((unsigned)nblk, BH), 256, 0, st>>>(a);
+    const int64_t nmu = (int64_t)nz * BH * D;
+    k1_kstats<D, DT, ROT><<<dim3((unsigned)nblk, BH, nz), 256, 0, st>>>(a);
     k1_kmean<<<(unsigned)((nmu + 255) / 256), 256, 0, st>>>(a);
   }
   // a workgroup covers whole scale blocks: 64 tokens (four threads each) unless

@@ -40,6 +40,10 @@ class Debug(ctypes.Structure):
                 ("m", ctypes.c_void_p), ("l", ctypes.c_void_p)]
 
 
+class AttentionOpts(ctypes.Structure):
+    _fields_ = [("p_max", ctypes.c_int32), ("causal_block", ctypes.c_int32), ("k_bias", ctypes.c_void_p)]
+
+
 class RotattnError(RuntimeError):
     pass
 
@@ -59,8 +63,10 @@ _SIGS = {
                                       _VP]),
     "rotattn_int4_attention_symmetric_p": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP,
                                                   _SZ, _VP]),
-    "rotattn_int4_attention_causal": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32,
-                                             _VP, _VP, _VP, _SZ, _VP]),
+    "rotattn_quantize_qk_smooth_q": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
+                                            _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "rotattn_int4_attention_ex": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, _VP,
+                                         _VP, _SZ, _VP]),
     "rotattn_fp16_fallback_workspace": (_SZ, [_VP]),
     "rotattn_fp16_fallback": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ, _VP]),
     "rotattn_fp16_fallback_causal": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _SZ,
@@ -139,8 +145,9 @@ def rotattn_fp16_fallback_workspace(shape: Shape) -> int:
     return int(lib().rotattn_fp16_fallback_workspace(ctypes.byref(shape)))
 
 
-def alloc_codes(shape: Shape, device="cuda", colsum: bool = True) -> dict:
-    """Output buffers of rotattn_quantize_qk (torch device tensors)."""
+def alloc_codes(shape: Shape, device="cuda", colsum: bool = True, smooth_q: bool = False) -> dict:
+    """Output buffers of rotattn_quantize_qk (torch device tensors); smooth_q adds
+    k_bias [B,H,Np] f32 for rotattn_quantize_qk_smooth_q."""
     Np = rotattn_padded_tokens(shape)
     B, H, D = shape.B, shape.H, shape.D
     nkb = -(-shape.N // shape.kv_blk)
@@ -152,22 +159,33 @@ def alloc_codes(shape: Shape, device="cuda", colsum: bool = True) -> dict:
              v_codes=torch.empty((B, H, D, Np // 2), dtype=u8, device=device),
              v_scale=torch.empty((B, H, D), dtype=f32, device=device),
              v_colsum=torch.empty((B, H, nkb, D), dtype=torch.int32, device=device) if colsum else None)
+    if smooth_q:
+        z["k_bias"] = torch.empty((B, H, Np), dtype=f32, device=device)
     z["workspace"] = torch.empty(rotattn_quantize_qk_workspace(shape), dtype=torch.uint8, device=device)
     z["attn_workspace"] = torch.empty(rotattn_int4_attention_workspace(shape), dtype=torch.uint8, device=device)
     return z
 
 
 def rotattn_quantize_qk(shape: Shape, rot: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                        rope_table: torch.Tensor, smooth_k: bool, z: dict) -> dict:
-    """z: buffers from alloc_codes (filled in place, returned)."""
+                        rope_table: torch.Tensor, smooth_k: bool, z: dict, smooth_q: bool = False) -> dict:
+    """z: buffers from alloc_codes (filled in place, returned).  smooth_q: Q smoothing
+    through rotattn_quantize_qk_smooth_q, which fills z["k_bias"] (alloc_codes with
+    smooth_q=True); rotattn_int4_attention then adds it back."""
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise RotattnError("q, k, v must share one of float32 / float16 / bfloat16")
     ws = z["workspace"]
-    _check(lib().rotattn_quantize_qk(
-        ctypes.byref(shape), rot, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table),
-        1 if smooth_k else 0, _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
-        _ptr(z["v_codes"]), _ptr(z["v_scale"]), _ptr(z.get("v_colsum")), _ptr(ws), ws.numel(), _stream()),
-        "rotattn_quantize_qk")
+    head = (ctypes.byref(shape), rot, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table),
+            1 if smooth_k else 0, _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
+            _ptr(z["v_codes"]), _ptr(z["v_scale"]), _ptr(z.get("v_colsum")))
+    tail = (_ptr(ws), ws.numel(), _stream())
+    if smooth_q:
+        if z.get("k_bias") is None:
+            raise RotattnError("Q smoothing needs z['k_bias'] (alloc_codes(..., smooth_q=True))")
+        _check(lib().rotattn_quantize_qk_smooth_q(*head, _ptr(z["k_bias"]), *tail), "rotattn_quantize_qk_smooth_q")
+        z["smooth_q"] = True
+    else:
+        _check(lib().rotattn_quantize_qk(*head, *tail), "rotattn_quantize_qk")
+        z["smooth_q"] = False
     return z
 
 
@@ -179,8 +197,9 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
     tensor of rotattn_int4_attention_workspace(shape) bytes (default z["attn_workspace"]).
     symmetric_p: the ablation baseline rotattn_int4_attention_symmetric_p (P codes
     round(7P) in [0, 7]) instead of the method's range-rectified codes.
-    causal_block: 0 bidirectional; c > 0 block-causal through
-    rotattn_int4_attention_causal (query i sees key j iff j // c <= i // c)."""
+    causal_block: 0 bidirectional; c > 0 block-causal (query i sees key j iff
+    j // c <= i // c).  When z was filled with Q smoothing, its k_bias is passed on.
+    Options other than the defaults go through rotattn_int4_attention_ex."""
     if out.dtype not in _DT:
         raise RotattnError("out must be float32, float16 or bfloat16")
     harr, nh = _heads(heads)
@@ -202,10 +221,11 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
              _ptr(z["v_codes"]), _ptr(z["v_scale"]), harr, nh)
     tail = (_DT[out.dtype], _ptr(out), ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(),
             _stream())
-    if causal_block:
-        _check(lib().rotattn_int4_attention_causal(ctypes.byref(shape), *codes, int(causal_block),
-                                                   7 if symmetric_p else 15, *tail),
-               "rotattn_int4_attention_causal")
+    kb = z.get("k_bias") if z.get("smooth_q") else None
+    if causal_block or kb is not None:
+        opts = AttentionOpts(7 if symmetric_p else 15, int(causal_block), _ptr(kb))
+        _check(lib().rotattn_int4_attention_ex(ctypes.byref(shape), *codes, ctypes.byref(opts), *tail),
+               "rotattn_int4_attention_ex")
     else:
         fn = lib().rotattn_int4_attention_symmetric_p if symmetric_p else lib().rotattn_int4_attention
         _check(fn(ctypes.byref(shape), *codes, *tail), "rotattn_int4_attention")

@@ -17,13 +17,13 @@ def to_dev(x: np.ndarray, dtype=None):
     return t.cuda()
 
 
-def gpu_quantize(cfg, rot: int, Q, K, V, smooth=True, in_dtype=None):
+def gpu_quantize(cfg, rot: int, Q, K, V, smooth=True, in_dtype=None, smooth_q=False):
     shape = ra.Shape.of(cfg)
     tdt = in_dtype or _TDT[cfg["dtype"]]
     q, k, v = (to_dev(x, tdt) for x in (Q, K, V))
     tab = ra.rotattn_build_rope_table(shape, rot).cuda()
-    z = ra.alloc_codes(shape)
-    ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, smooth, z)
+    z = ra.alloc_codes(shape, smooth_q=smooth_q)
+    ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, smooth, z, smooth_q=smooth_q)
     torch.cuda.synchronize()
     return shape, z
 
@@ -65,6 +65,10 @@ def compare_codes(cfg, z, ref, heads=None):
     assert np.array_equal(vs.view(np.uint32), r(ref["vs"]).view(np.uint32)), "v scales"
     if z.get("v_colsum") is not None:
         assert np.array_equal(f(z["v_colsum"]).cpu().numpy()[:, :nkb], r(ref["vcol"])), "v colsums"
+    if z.get("smooth_q"):
+        kb = f(z["k_bias"]).cpu().numpy()
+        assert np.array_equal(kb[:, :N].view(np.uint32), r(ref["k_bias"]).view(np.uint32)), "k bias"
+        assert np.all(kb[:, N:] == 0), "k bias padding"
 
 
 def assert_close(out: np.ndarray, ref: np.ndarray, max_abs=2e-3, rel_l2=1e-3, what="O"):

@@ -98,13 +98,15 @@ def test_null_and_bad_args_return_before_launch(L):
     st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 3,
                                   fake, nul, fake, big, nul)
     assert st == 6  # output dtype outside F32 / F16 / BF16
-    # block-causal entry points: negative block, P maximum other than 15 / 7
-    st = L.rotattn_int4_attention_causal(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, -1, 15,
-                                         0, fake, nul, fake, big, nul)
-    assert st == 6
-    st = L.rotattn_int4_attention_causal(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 4, 8,
-                                         0, fake, nul, fake, big, nul)
-    assert st == 6
+    # options: negative causal block, P maximum other than 15 / 7
+    for opts in (ra.AttentionOpts(15, -1, None), ra.AttentionOpts(8, 4, None)):
+        st = L.rotattn_int4_attention_ex(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0,
+                                         ctypes.byref(opts), 0, fake, nul, fake, big, nul)
+        assert st == 6
+    # Q smoothing without its k_bias output
+    st = L.rotattn_quantize_qk_smooth_q(ctypes.byref(s), 1, 0, fake, fake, fake, fake, 1, fake, fake, fake,
+                                        fake, fake, fake, nul, nul, fake, 1 << 30, nul)
+    assert st == 1
     st = L.rotattn_fp16_fallback_causal(ctypes.byref(s), 1, fake, fake, fake, fake, nul, 0, -3, 0, fake, fake,
                                         1 << 30, nul)
     assert st == 6

@@ -23,10 +23,10 @@ def _oracle_head_cfg(cfg):
 
 
 def _run_case(orc, cfg, rot, smooth=True, debug_rows=None, out_dtype=torch.float32, in_dtype=None, pmax=15,
-              causal=0):
-    Q, K, V = synth.make_inputs(cfg)
-    shape, z = gpu_quantize(cfg, rot, Q, K, V, smooth, in_dtype)
-    ref = orc.quantize(cfg, rot, orc.rope_table(cfg, rot), Q, K, V, smooth_k=smooth)
+              causal=0, smooth_q=False, inputs=None):
+    Q, K, V = inputs if inputs is not None else synth.make_inputs(cfg)
+    shape, z = gpu_quantize(cfg, rot, Q, K, V, smooth, in_dtype, smooth_q=smooth_q)
+    ref = orc.quantize(cfg, rot, orc.rope_table(cfg, rot), Q, K, V, smooth_k=smooth, smooth_q=smooth_q)
     compare_codes(cfg, z, ref)
     N, D = synth.n_tokens(cfg), cfg["D"]
     out = torch.full((cfg["B"], cfg["H"], N, D), float("nan"), dtype=out_dtype, device="cuda")
@@ -177,3 +177,41 @@ def test_causal_parity(orc, case):
 def test_causal_d64(orc):
     cfg = synth.custom(1, 2, 5, 7, 9, 64, 24, 20, 20, 32, 64, dtype="float32", recipe="tiny")
     _run_case(orc, cfg, 1, debug_rows=[(0, 64), (250, 65)], causal=63)
+
+
+def _offset_queries(cfg, seed=7):
+    """Inputs whose queries share a large offset in the slow RoPE pairs of each
+    segment (where Q smoothing matters), in the config's storage dtype."""
+    Q, K, V = synth.make_inputs(cfg)
+    rng = np.random.default_rng(seed)
+    off = np.zeros(cfg["D"], np.float32)
+    o = 0
+    for w in (cfg["Df"], cfg["Dh"], cfg["Dw"]):
+        off[o + w - 4:o + w] = rng.uniform(4, 8, 4) * rng.choice([-1, 1], 4)
+        o += w
+    return (Q.astype(np.float32) + off).astype(Q.dtype), K, V
+
+
+QSMOOTH = [
+    # (id, config overrides, rotation, smooth_k, causal block)
+    ("half_kv64", dict(), 2, True, 0),
+    ("inter_kv16_qk16", dict(qk_blk=16, kv_blk=16), 1, True, 0),
+    ("half_kv128_qk16_nosmoothk", dict(qk_blk=16, kv_blk=128), 2, False, 0),
+    ("full_kv32_frame_causal", dict(qk_blk=32, kv_blk=32), 3, True, 391),
+]
+
+
+@pytest.mark.parametrize("case", QSMOOTH, ids=[c[0] for c in QSMOOTH])
+def test_q_smoothing_parity(orc, case):
+    """Q smoothing: Q codes of Q - mu_q and the per-key term k_bias bit-exact, the
+    attention with the term added back (P codes, m, sums bit-exact; O within the bar)."""
+    name, over, rot, smooth_k, cb = case
+    cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
+    cfg.update(over)
+    _run_case(orc, cfg, rot, smooth=smooth_k, debug_rows=[(0, 40), (1133, 40)], causal=cb, smooth_q=True,
+              inputs=_offset_queries(cfg))
+
+
+def test_q_smoothing_d64_f32(orc):
+    cfg = synth.custom(1, 2, 5, 7, 9, 64, 24, 20, 20, 32, 64, dtype="float32", recipe="tiny")
+    _run_case(orc, cfg, 2, debug_rows=[(0, 64)], smooth_q=True, inputs=_offset_queries(cfg))
