@@ -1,7 +1,8 @@
 """Ablation on synthetic inputs, from the oracle (CPU): attention-output cosine and
 rel-L2 against exact binary64 attention for each rotation mode (none, Interleaved,
 Half, Full D x D Hadamard) with the method's range-rectified P codes and with the
-symmetric 8-level baseline, plus Half without K smoothing.  The GPU computes the
+symmetric 8-level baseline, plus Half without K smoothing and Half / Full with Q
+smoothing as well.  The GPU computes the
 same variants within the parity tolerance of the oracle (tests/test_gpu_parity.py),
 so these figures are the library's too.
 
@@ -30,6 +31,9 @@ def test_ablation_rotation_and_p_code(orc, capsys):
             res[(name, pmax)] = _cos_rel(orc.attention(cfg, z, pmax=pmax)["out"], ex)
     z = orc.quantize(cfg, 2, orc.rope_table(cfg, 2), Q, K, V, smooth_k=False)
     res[("half, no K smoothing", 15)] = _cos_rel(orc.attention(cfg, z)["out"], ex)
+    for rot, name in [(2, "half"), (3, "full")]:
+        z = orc.quantize(cfg, rot, orc.rope_table(cfg, rot), Q, K, V, smooth_q=True)
+        res[(name + ", Q smoothing", 15)] = _cos_rel(orc.attention(cfg, z)["out"], ex)
     with capsys.disabled():
         print("\nablation (Wan-like inputs, B1 H4 N1173 D128, qk_blk 64, kv_blk 64):")
         for (name, pmax), (c, r) in res.items():
@@ -41,3 +45,5 @@ def test_ablation_rotation_and_p_code(orc, capsys):
     assert cos[("half", 15)] > cos[("half, no K smoothing", 15)]
     for name in ("none", "interleaved", "half", "full"):
         assert cos[(name, 15)] >= cos[(name, 7)]
+    for name in ("half", "full"):
+        assert cos[(name + ", Q smoothing", 15)] > cos[(name, 15)]
