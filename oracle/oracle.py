@@ -95,11 +95,21 @@ def rope_rotate(shape, rot: int, table: np.ndarray, x: np.ndarray) -> np.ndarray
     return out
 
 
+def _lens(seq_lens, B):
+    if seq_lens is None:
+        return None
+    a = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if a.shape != (B,):
+        raise ValueError("seq_lens needs one length per batch element")
+    return a
+
+
 def quantize(shape, rot: int, table: np.ndarray, q, k, v, smooth_k: bool = True, diag: bool = False,
-             smooth_q: bool = False):
+             smooth_q: bool = False, seq_lens=None):
     """Returns dict: qc,kc,vc (int8 [B,H,N,D]), qs,ks ([B,H,nqb]), vs ([B,H,D]),
     vcol ([B,H,nkb,D]); with diag also q_rot, k_rot, k_mu, q_mu.  smooth_q: Q minus
-    its channel mean, and k_bias [B,H,N] f32 = mu_q . K_j (pass it to attention)."""
+    its channel mean, and k_bias [B,H,N] f32 = mu_q . K_j (pass it to attention).
+    seq_lens: B lengths of a variable-length batch (kept in the result for attention)."""
     s = shape_array(shape)
     B, H, D = int(shape["B"]), int(shape["H"]), int(shape["D"])
     N = n_tokens(shape)
@@ -121,12 +131,15 @@ def quantize(shape, rot: int, table: np.ndarray, q, k, v, smooth_k: bool = True,
     if smooth_q:
         r["k_bias"] = np.empty((B, H, N), np.float32)
     flags = (1 if smooth_k else 0) | (2 if smooth_q else 0)
+    lens = _lens(seq_lens, B)
+    if lens is not None:
+        r["seq_lens"] = lens
     lib().orc_quantize_x(_p(s), ctypes.c_int32(rot), _p(np.ascontiguousarray(table, np.float32)),
                          ctypes.c_int32(flags), _p(q), _p(k), _p(v),
                          _p(r["qc"]), _p(r["qs"]), _p(r["kc"]), _p(r["ks"]),
                          _p(r["vc"]), _p(r["vs"]), _p(r["vcol"]),
                          _p(r.get("q_rot")), _p(r.get("k_rot")), _p(r.get("k_mu")), _p(r.get("q_mu")),
-                         _p(r.get("k_bias")))
+                         _p(r.get("k_bias")), _p(lens))
     return r
 
 
@@ -147,7 +160,8 @@ def attention(shape, qz: dict, rows=None, dumps: bool = False, pmax: int = 15,
     symmetric baseline, codes r = round(7 P) in [0, 7].  causal_block: 0 for
     bidirectional attention, c > 0 for block-causal attention (key_limit); dump
     entries of keys a row does not see stay zero.  A "k_bias" entry in qz (from
-    quantize(..., smooth_q=True)) adds the per-key term Q smoothing leaves."""
+    quantize(..., smooth_q=True)) adds the per-key term Q smoothing leaves; a
+    "seq_lens" entry (quantize(..., seq_lens=...)) makes the batch variable-length."""
     if pmax not in (7, 15):
         raise ValueError("pmax is 15 (range-rectified) or 7 (symmetric baseline)")
     s = shape_array(shape)
@@ -171,12 +185,13 @@ def attention(shape, qz: dict, rows=None, dumps: bool = False, pmax: int = 15,
                         _p(res.get("a_qk")), _p(res.get("pcode")), _p(res.get("a_pv")),
                         _p(res.get("m")), _p(res.get("l")), ctypes.c_int32(pmax),
                         ctypes.c_int32(causal_block),
-                        _p(c(qz["k_bias"], np.float32) if qz.get("k_bias") is not None else None))
+                        _p(c(qz["k_bias"], np.float32) if qz.get("k_bias") is not None else None),
+                        _p(_lens(qz.get("seq_lens"), B)))
     return res
 
 
 def exact_attention(shape, q, k, v, rows=None, base: float = 10000.0,
-                    causal_block: int = 0) -> np.ndarray:
+                    causal_block: int = 0, seq_lens=None) -> np.ndarray:
     s = shape_array(shape)
     B, H, D = int(shape["B"]), int(shape["H"]), int(shape["D"])
     N = n_tokens(shape)
@@ -187,11 +202,13 @@ def exact_attention(shape, q, k, v, rows=None, base: float = 10000.0,
     out = np.empty((rows.size, D), np.float64)
     c = lambda a: np.ascontiguousarray(a, dtype=np.float32).reshape(B, H, N, D)
     lib().orc_exact_attention_x(_p(s), _p(tab), _p(c(q)), _p(c(k)), _p(c(v)), _p(rows),
-                                ctypes.c_int64(rows.size), _p(out), ctypes.c_int32(causal_block))
+                                ctypes.c_int64(rows.size), _p(out), ctypes.c_int32(causal_block),
+                                _p(_lens(seq_lens, B)))
     return out
 
 
-def fallback_attention(shape, table_plain, q, k, v, rows=None, causal_block: int = 0) -> np.ndarray:
+def fallback_attention(shape, table_plain, q, k, v, rows=None, causal_block: int = 0,
+                       seq_lens=None) -> np.ndarray:
     s = shape_array(shape)
     B, H, D = int(shape["B"]), int(shape["H"]), int(shape["D"])
     N = n_tokens(shape)
@@ -202,7 +219,8 @@ def fallback_attention(shape, table_plain, q, k, v, rows=None, causal_block: int
     c = lambda a: np.ascontiguousarray(a, dtype=np.float32).reshape(B, H, N, D)
     lib().orc_fallback_attention_x(_p(s), _p(np.ascontiguousarray(table_plain, np.float32)),
                                    _p(c(q)), _p(c(k)), _p(c(v)), _p(rows),
-                                   ctypes.c_int64(rows.size), _p(out), ctypes.c_int32(causal_block))
+                                   ctypes.c_int64(rows.size), _p(out), ctypes.c_int32(causal_block),
+                                   _p(_lens(seq_lens, B)))
     return out
 
 

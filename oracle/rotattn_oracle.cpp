@@ -17,7 +17,8 @@
 //     zero points; mixed-precision INT4 FlashAttention with FP16 fallback.
 //   * the pages name causal as well as bidirectional attention for video DiTs
 //     without fixing its granularity: the *_x entry points take a causal block
-//     size c (key j visible to query i iff j / c <= i / c; c = 0 bidirectional).
+//     size c (key j visible to query i iff j / c <= i / c; c = 0 bidirectional),
+//     and per-element valid lengths for a variable-length batch (seq_lens).
 // Readings where the pages are silent (RoPE base, pair layout, block sizes, the
 // normaliser, the exact exp) are listed in the design notes and restated at each
 // function below.
@@ -208,6 +209,12 @@ int64_t key_limit(int64_t i, int64_t N, int64_t cb) {
   return std::min(N, (i / cb + 1) * cb);
 }
 
+// Tokens of batch element b that exist: seq_lens[b] (a variable-length batch in the
+// padded [B,H,N,D] layout; tokens past it are padding, read by nothing), else N.
+int64_t valid_tokens(const int32_t* seq_lens, int64_t bh, int H, int64_t N) {
+  return seq_lens ? (int64_t)seq_lens[bh / H] : N;
+}
+
 float c0_of(int D) { return (float)(1.4426950408889634074 / std::sqrt((double)D)); }
 float l15() { return (float)std::log2(15.0); }
 
@@ -312,11 +319,16 @@ void orc_rope_rotate_f64(const int32_t* shp, int32_t rot, const double* tab, con
 //   bit 0 is set), written to k_bias [B,H,N] as float(binary64 sum over channels in
 //   order of the exact products).  The attention adds it back to every score.
 //   q_mu [B,H,D] (nullable) receives mu_q.
+// seq_lens (nullable, B entries in [1, N]): a variable-length batch.  Batch element b
+//   has seq_lens[b] tokens (positions as in the full grid); every statistic, scale
+//   block and code uses those tokens only, as if N were seq_lens[b], and the codes,
+//   scale blocks, column sums and k_bias entries past it are 0.
 void orc_quantize_x(const int32_t* shp, int32_t rot, const float* tab, int32_t flags,
                     const float* q, const float* k, const float* v,
                     int8_t* qc, float* qs, int8_t* kc, float* ks,
                     int8_t* vc, float* vs, int32_t* vcol,
-                    float* q_rot, float* k_rot, float* k_mu, float* q_mu, float* k_bias) {
+                    float* q_rot, float* k_rot, float* k_mu, float* q_mu, float* k_bias,
+                    const int32_t* seq_lens) {
   const int32_t smooth_k = flags & 1, smooth_q = flags & 2;
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
@@ -324,6 +336,7 @@ void orc_quantize_x(const int32_t* shp, int32_t rot, const float* tab, int32_t f
   const int64_t nkb = (N + s.kv_blk - 1) / s.kv_blk;
 #pragma omp parallel for schedule(dynamic)
   for (int64_t bh = 0; bh < (int64_t)s.B * s.H; ++bh) {
+    const int64_t Nb = valid_tokens(seq_lens, bh, s.H, N);
     std::vector<float> qr(N * D), kr(N * D);
     const float* qh = q + bh * N * D;
     const float* kh = k + bh * N * D;
@@ -334,21 +347,21 @@ void orc_quantize_x(const int32_t* shp, int32_t rot, const float* tab, int32_t f
     }
     if (q_rot) std::memcpy(q_rot + bh * N * D, qr.data(), sizeof(float) * N * D);
     if (k_rot) std::memcpy(k_rot + bh * N * D, kr.data(), sizeof(float) * N * D);
-    // channel mean: binary64 sums of 64-token blocks, added in block order, / N
+    // channel mean: binary64 sums of 64-token blocks, added in block order, / Nb
     auto channel_mean = [&](const std::vector<float>& x, int64_t d) {
       double total = 0.0;
-      for (int64_t b0 = 0; b0 < N; b0 += kMeanBlk) {
+      for (int64_t b0 = 0; b0 < Nb; b0 += kMeanBlk) {
         double part = 0.0;
-        for (int64_t n = b0; n < std::min(N, b0 + kMeanBlk); ++n) part += (double)x[n * D + d];
+        for (int64_t n = b0; n < std::min(Nb, b0 + kMeanBlk); ++n) part += (double)x[n * D + d];
         total += part;
       }
-      return (float)(total / (double)N);
+      return (float)(total / (double)Nb);
     };
     if (smooth_k) {
       for (int64_t d = 0; d < D; ++d) {
         const float mu = channel_mean(kr, d);
         if (k_mu) k_mu[bh * D + d] = mu;
-        for (int64_t n = 0; n < N; ++n) kr[n * D + d] = kr[n * D + d] - mu;
+        for (int64_t n = 0; n < Nb; ++n) kr[n * D + d] = kr[n * D + d] - mu;
       }
     } else if (k_mu) {
       for (int64_t d = 0; d < D; ++d) k_mu[bh * D + d] = 0.f;
@@ -358,30 +371,33 @@ void orc_quantize_x(const int32_t* shp, int32_t rot, const float* tab, int32_t f
       for (int64_t d = 0; d < D; ++d) {
         muq[d] = channel_mean(qr, d);
         if (q_mu) q_mu[bh * D + d] = muq[d];
-        for (int64_t n = 0; n < N; ++n) qr[n * D + d] = qr[n * D + d] - muq[d];
+        for (int64_t n = 0; n < Nb; ++n) qr[n * D + d] = qr[n * D + d] - muq[d];
       }
       for (int64_t n = 0; n < N; ++n) {
         double acc = 0.0;  // each product of two binary32 values is exact in binary64
         for (int64_t d = 0; d < D; ++d) acc += (double)muq[d] * (double)kr[n * D + d];
-        k_bias[bh * N + n] = (float)acc;
+        k_bias[bh * N + n] = n < Nb ? (float)acc : 0.f;
       }
     } else if (q_mu) {
       for (int64_t d = 0; d < D; ++d) q_mu[bh * D + d] = 0.f;
     }
     for (int64_t b = 0; b < nqb; ++b) {
-      const int64_t n0 = b * s.qk_blk, cnt = std::min<int64_t>(s.qk_blk, N - n0);
+      const int64_t n0 = b * s.qk_blk, full = std::min<int64_t>(s.qk_blk, N - n0);
+      const int64_t cnt = std::max<int64_t>(0, std::min<int64_t>(full, Nb - n0));
+      std::fill(qc + (bh * N + n0) * D, qc + (bh * N + n0 + full) * D, (int8_t)0);
+      std::fill(kc + (bh * N + n0) * D, kc + (bh * N + n0 + full) * D, (int8_t)0);
       quant_block(qr.data() + n0 * D, cnt * D, qc + (bh * N + n0) * D, qs + bh * nqb + b);
       quant_block(kr.data() + n0 * D, cnt * D, kc + (bh * N + n0) * D, ks + bh * nqb + b);
     }
     // V: per-channel scale over all tokens, then per-kv-block column sums.
     for (int64_t d = 0; d < D; ++d) {
       float amax = 0.f;
-      for (int64_t n = 0; n < N; ++n) amax = std::max(amax, std::fabs(vh[n * D + d]));
+      for (int64_t n = 0; n < Nb; ++n) amax = std::max(amax, std::fabs(vh[n * D + d]));
       const float inv = amax == 0.f ? 0.f : 7.0f / amax;
       vs[bh * D + d] = amax == 0.f ? 0.f : amax / 7.0f;
       for (int64_t n = 0; n < N; ++n) {
         int8_t c = 0;
-        if (amax != 0.f) {
+        if (amax != 0.f && n < Nb) {
           float t = std::nearbyintf(vh[n * D + d] * inv);
           c = (int8_t)std::min(7.f, std::max(-7.f, t));
         }
@@ -458,11 +474,13 @@ int64_t orc_p_level_bruteforce(float lo, float hi, float* first) {
 // leaves (orc_quantize_x).  With it every score gains delta_j = fl(dS_j * C0):
 //   t_ij = fma(a_ij, c_ij, delta_j),  y'_ij = fl(t_ij + fl(L15 - m_s)),
 // the rest unchanged.
+// seq_lens (nullable): a variable-length batch; a row of batch element b sees only
+// the first seq_lens[b] keys (its rows past that are not meaningful to ask for).
 void orc_attention_x(const int32_t* shp, const int8_t* qc, const float* qs,
                      const int8_t* kc, const float* ks, const int8_t* vc, const float* vs,
                      const int64_t* rows, int64_t n_rows, double* out,
                      int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out, int32_t pmax,
-                     int32_t causal_block, const float* k_bias) {
+                     int32_t causal_block, const float* k_bias, const int32_t* seq_lens) {
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
   const int64_t nqb = (N + s.qk_blk - 1) / s.qk_blk;
@@ -473,7 +491,7 @@ void orc_attention_x(const int32_t* shp, const int8_t* qc, const float* qs,
   for (int64_t ri = 0; ri < n_rows; ++ri) {
     const int64_t row = rows[ri];
     const int64_t bh = row / N, i = row % N;
-    const int64_t lim = key_limit(i, N, causal_block);
+    const int64_t lim = key_limit(i, valid_tokens(seq_lens, bh, s.H, N), causal_block);
     const int8_t* qrow = qc + (bh * N + i) * D;
     const float sq = qs[bh * nqb + i / s.qk_blk];
     std::vector<int32_t> a(s.kv_blk);
@@ -533,7 +551,7 @@ void orc_attention_p(const int32_t* shp, const int8_t* qc, const float* qs,
                      const int64_t* rows, int64_t n_rows, double* out,
                      int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out, int32_t pmax) {
   orc_attention_x(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, pmax, 0,
-                  nullptr);
+                  nullptr, nullptr);
 }
 
 void orc_attention(const int32_t* shp, const int8_t* qc, const float* qs,
@@ -541,7 +559,7 @@ void orc_attention(const int32_t* shp, const int8_t* qc, const float* qs,
                    const int64_t* rows, int64_t n_rows, double* out,
                    int32_t* a_qk, int8_t* pcode, int32_t* a_pv, float* m_out, double* l_out) {
   orc_attention_x(shp, qc, qs, kc, ks, vc, vs, rows, n_rows, out, a_qk, pcode, a_pv, m_out, l_out, 15, 0,
-                  nullptr);
+                  nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -550,7 +568,8 @@ void orc_attention(const int32_t* shp, const int8_t* qc, const float* qs,
 // (The rotation is orthogonal and cancels in Q K^T, so none is applied.)
 void orc_exact_attention_x(const int32_t* shp, const double* tab64_plain,
                            const float* q, const float* k, const float* v,
-                           const int64_t* rows, int64_t n_rows, double* out, int32_t causal_block) {
+                           const int64_t* rows, int64_t n_rows, double* out, int32_t causal_block,
+                           const int32_t* seq_lens) {
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
   // RoPE every K row of the heads that appear, lazily per head.
@@ -573,7 +592,7 @@ void orc_exact_attention_x(const int32_t* shp, const double* tab64_plain,
     for (int64_t t = 0; t < (int64_t)mine.size(); ++t) {
       const int64_t r = mine[t], i = rows[r] % N;
       std::vector<double> in(D), qr(D), sc(N);
-      const int64_t lim = key_limit(i, N, causal_block);
+      const int64_t lim = key_limit(i, valid_tokens(seq_lens, bh, s.H, N), causal_block);
       for (int64_t d = 0; d < D; ++d) in[d] = q[(bh * N + i) * D + d];
       rope_rotate_token<double>(s, 0, tab64_plain, i, in.data(), qr.data());
       double mx = -std::numeric_limits<double>::infinity();
@@ -604,7 +623,8 @@ void orc_exact_attention_x(const int32_t* shp, const double* tab64_plain,
 // rounding is covered by the tolerance, not mirrored here.
 void orc_fallback_attention_x(const int32_t* shp, const float* tab_plain,
                               const float* q, const float* k, const float* v,
-                              const int64_t* rows, int64_t n_rows, double* out, int32_t causal_block) {
+                              const int64_t* rows, int64_t n_rows, double* out, int32_t causal_block,
+                              const int32_t* seq_lens) {
   const Shape s = unpack(shp);
   const int64_t N = s.N(), D = s.D;
   std::vector<int64_t> heads;
@@ -627,7 +647,7 @@ void orc_fallback_attention_x(const int32_t* shp, const float* tab_plain,
       const int64_t r = mine[t], i = rows[r] % N;
       std::vector<float> qr(D);
       std::vector<double> sc(N);
-      const int64_t lim = key_limit(i, N, causal_block);
+      const int64_t lim = key_limit(i, valid_tokens(seq_lens, bh, s.H, N), causal_block);
       rope_rotate_token<float>(s, 0, tab_plain, i, q + (bh * N + i) * D, qr.data());
       for (int64_t d = 0; d < D; ++d) qr[d] = to_half(qr[d]);
       double mx = -std::numeric_limits<double>::infinity();
@@ -657,19 +677,19 @@ void orc_f32_to_f16(const float* x, int64_t n, uint16_t* out) {
 
 void orc_exact_attention(const int32_t* shp, const double* tab64_plain, const float* q, const float* k,
                          const float* v, const int64_t* rows, int64_t n_rows, double* out) {
-  orc_exact_attention_x(shp, tab64_plain, q, k, v, rows, n_rows, out, 0);
+  orc_exact_attention_x(shp, tab64_plain, q, k, v, rows, n_rows, out, 0, nullptr);
 }
 
 void orc_fallback_attention(const int32_t* shp, const float* tab_plain, const float* q, const float* k,
                             const float* v, const int64_t* rows, int64_t n_rows, double* out) {
-  orc_fallback_attention_x(shp, tab_plain, q, k, v, rows, n_rows, out, 0);
+  orc_fallback_attention_x(shp, tab_plain, q, k, v, rows, n_rows, out, 0, nullptr);
 }
 
 void orc_quantize(const int32_t* shp, int32_t rot, const float* tab, int32_t smooth_k, const float* q,
                   const float* k, const float* v, int8_t* qc, float* qs, int8_t* kc, float* ks, int8_t* vc,
                   float* vs, int32_t* vcol, float* q_rot, float* k_rot, float* k_mu) {
   orc_quantize_x(shp, rot, tab, smooth_k ? 1 : 0, q, k, v, qc, qs, kc, ks, vc, vs, vcol, q_rot, k_rot, k_mu,
-                 nullptr, nullptr);
+                 nullptr, nullptr, nullptr);
 }
 
 }  // extern "C"

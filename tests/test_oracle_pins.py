@@ -639,3 +639,99 @@ def test_q_smoothing_recovers_offset_queries(orc):
     smooth = orc.attention(cfg, orc.quantize(cfg, 2, tab, q, k, v, smooth_q=True))["out"]
     print("cosine vs exact: plain %.4f, Q smoothing %.4f" % (cos(plain), cos(smooth)))
     assert cos(smooth) > cos(plain) + 0.02
+
+
+# --- variable-length batches (per-element valid lengths in the padded layout) --------
+
+def _varlen_case(orc, lens, seed=31):
+    cfg = synth.custom(3, 2, 3, 4, 6, 64, 24, 20, 20, 16, 16)   # N = 72, one frame = 24 tokens
+    q, k, v = synth.make_inputs(cfg, seed=seed)
+    for b, n in enumerate(lens):   # padding holds NaN: nothing may read it
+        for x in (q, k, v):
+            x[b, :, n:] = np.nan
+    return cfg, q, k, v
+
+
+@pytest.mark.parametrize("smooth_q", [False, True])
+def test_varlen_equals_each_sequence_alone(orc, smooth_q):
+    """Whole frames: batch element b of a variable-length batch == the plain oracle
+    on that element alone with F = seq_lens[b] / (Hs Ws) frames (same positions),
+    codes, scales, sums, k_bias and the attention of every row; padding codes 0."""
+    lens = [72, 48, 24]
+    cfg, q, k, v = _varlen_case(orc, lens)
+    tab = orc.rope_table(cfg, 2)
+    z = orc.quantize(cfg, 2, tab, q, k, v, smooth_q=smooth_q, seq_lens=lens)
+    N = 72
+    o = orc.attention(cfg, z, rows=np.array([(b * 2 + h) * N + i for b in range(3) for h in range(2)
+                                             for i in range(lens[b])]), dumps=True)
+    at = 0
+    for b, n in enumerate(lens):
+        sub = synth.custom(1, 2, n // 24, 4, 6, 64, 24, 20, 20, 16, 16)
+        zs = orc.quantize(sub, 2, orc.rope_table(sub, 2), q[b:b + 1, :, :n], k[b:b + 1, :, :n],
+                          v[b:b + 1, :, :n], smooth_q=smooth_q)
+        nb = -(-n // 16)
+        assert np.array_equal(z["qc"][b, :, :n], zs["qc"][0]) and not z["qc"][b, :, n:].any()
+        assert np.array_equal(z["kc"][b, :, :n], zs["kc"][0]) and not z["kc"][b, :, n:].any()
+        assert np.array_equal(z["vc"][b, :, :n], zs["vc"][0]) and not z["vc"][b, :, n:].any()
+        assert np.array_equal(z["qs"][b, :, :nb], zs["qs"][0]) and not z["qs"][b, :, nb:].any()
+        assert np.array_equal(z["ks"][b, :, :nb], zs["ks"][0]) and not z["ks"][b, :, nb:].any()
+        assert np.array_equal(z["vs"][b], zs["vs"][0])
+        assert np.array_equal(z["vcol"][b, :, :nb], zs["vcol"][0]) and not z["vcol"][b, :, nb:].any()
+        if smooth_q:
+            assert np.array_equal(z["k_bias"][b, :, :n], zs["k_bias"][0]) and not z["k_bias"][b, :, n:].any()
+        os_ = orc.attention(sub, zs, dumps=True)
+        cnt = 2 * n
+        assert np.array_equal(o["out"][at:at + cnt], os_["out"])
+        assert np.array_equal(o["pcode"][at:at + cnt, :n], os_["pcode"]) and not o["pcode"][at:at + cnt, n:].any()
+        assert np.array_equal(o["m"][at:at + cnt], os_["m"])
+        at += cnt
+
+
+def test_varlen_ragged_equals_zero_padding(orc):
+    """A length that cuts a frame: without smoothing, the codes equal those of the
+    plain oracle on zero-filled padding (zeros move no amax and no column sum),
+    and each row attends over exactly its element's first seq_lens[b] keys
+    (bidirectional oracle on that prefix)."""
+    lens = [72, 30, 7]
+    cfg, q, k, v = _varlen_case(orc, lens)
+    tab = orc.rope_table(cfg, 1)
+    z = orc.quantize(cfg, 1, tab, q, k, v, smooth_k=False, seq_lens=lens)
+    q0, k0, v0 = (np.nan_to_num(x, nan=0.0) for x in (q, k, v))
+    zp = orc.quantize(cfg, 1, tab, q0, k0, v0, smooth_k=False)
+    for key in ("qc", "kc", "vc", "qs", "ks", "vs", "vcol"):
+        assert np.array_equal(z[key], zp[key]), key
+    N = 72
+    for b, n in enumerate(lens):
+        rows = np.array([(b * 2 + 1) * N + i for i in (0, n // 2, n - 1)], np.int64)
+        r = orc.attention(cfg, z, rows=rows)
+        sub = synth.custom(1, 1, 1, 1, n, 64, 24, 20, 20, 16, 16)
+        pre = dict(qc=z["qc"][b, 1:2, :n], kc=z["kc"][b, 1:2, :n], vc=z["vc"][b, 1:2, :n],
+                   qs=z["qs"][b, 1:2, :-(-n // 16)], ks=z["ks"][b, 1:2, :-(-n // 16)], vs=z["vs"][b, 1:2])
+        p = orc.attention(sub, {kk: vv[None] for kk, vv in pre.items()}, rows=rows % N)
+        assert np.array_equal(r["out"], p["out"]), b
+
+
+def test_varlen_exact_and_fallback_see_only_their_prefix(orc):
+    lens = [72, 30, 7]
+    cfg, q, k, v = _varlen_case(orc, lens)
+    N = 72
+    rows = np.array([(b * 2 + h) * N + i for b, n in enumerate(lens) for h in range(2) for i in (0, n - 1)])
+    ex = orc.exact_attention(cfg, q, k, v, rows=rows, seq_lens=lens)
+    fb = orc.fallback_attention(cfg, orc.rope_table(cfg, 0), q / 8, k / 8, v, rows=rows, seq_lens=lens)
+    ex8 = orc.exact_attention(cfg, q / 8, k / 8, v, rows=rows, seq_lens=lens)
+    assert np.isfinite(ex).all() and np.isfinite(fb).all()
+    assert np.max(np.abs(fb - ex8)) < 5e-3 * np.max(np.abs(ex8))
+    # the binary64 oracle against numpy softmax over the prefix (RoPE'd with the
+    # oracle's own rotation, pinned above)
+    tab = orc.rope_table(cfg, 0, f64=True)
+    qz, kz = (np.nan_to_num(x, nan=0.0).astype(np.float64) for x in (q, k))
+    qr = orc.rope_rotate(cfg, 0, tab, qz)
+    kr = orc.rope_rotate(cfg, 0, tab, kz)
+    for t, row in enumerate(rows):
+        bh, i = divmod(int(row), N)
+        b, h = divmod(bh, 2)
+        n = lens[b]
+        sc = kr[b, h, :n] @ qr[b, h, i] / 8.0
+        p = np.exp(sc - sc.max())
+        want = p @ v[b, h, :n].astype(np.float64) / p.sum()
+        assert np.allclose(ex[t], want, rtol=1e-10, atol=1e-12)
