@@ -123,23 +123,42 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
                                    uint8_t* v_codes, float* v_scale, int32_t* v_colsum,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* ---- rotattn_quantize_qk_smooth_q ------------------------------------------------
- * rotattn_quantize_qk with Q smoothing as well: the other reading of the
- * framework's channel smoothing (papernotes note, Overall framework), as an
- * accuracy option.  mu_q (the per-(b,h) channel mean of the rotated Q, formed like
- * the K mean) is subtracted from Q before it is quantised.  Unlike the K mean it
- * does not cancel in softmax: it leaves the per-key score term dS_j = mu_q . K_j
- * (K_j as quantised: rotated, and smoothed when smooth_k), written to
- *   k_bias  device f32 [B,H,Np]: binary64 sum over the channels in order of the
- *           exact products mu_q[d] K_j[d], rounded to binary32; 0 past N.
- * Pass k_bias to rotattn_int4_attention_ex, which adds it back to every score.
- * k_bias NULL returns ROTATTN_E_NULL; everything else as rotattn_quantize_qk. */
-rotattn_status rotattn_quantize_qk_smooth_q(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
-                                            const void* q, const void* k, const void* v,
-                                            const float* rope_table, int32_t smooth_k,
-                                            uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
-                                            uint8_t* v_codes, float* v_scale, int32_t* v_colsum, float* k_bias,
-                                            void* workspace, size_t workspace_bytes, void* stream);
+/* ---- rotattn_quantize_qk_ex: Q smoothing, variable-length batches ----------------
+ * rotattn_quantize_qk with options (opts NULL: smooth_k = 1 and nothing else):
+ *   smooth_k   as rotattn_quantize_qk.
+ *   smooth_q   1: Q smoothing as well, the other reading of the framework's channel
+ *              smoothing (papernotes note, Overall framework), as an accuracy
+ *              option.  mu_q (the per-(b,h) channel mean of the rotated Q, formed
+ *              like the K mean) is subtracted from Q before it is quantised.
+ *              Unlike the K mean it does not cancel in softmax: it leaves the
+ *              per-key score term dS_j = mu_q . K_j (K_j as quantised: rotated, and
+ *              smoothed when smooth_k), written to k_bias.
+ *   k_bias     device f32 [B,H,Np], required with smooth_q (ROTATTN_E_NULL
+ *              otherwise): the binary64 sum over the channels in order of the
+ *              exact products mu_q[d] K_j[d], rounded to binary32; 0 for tokens
+ *              that do not exist.  Pass it to rotattn_int4_attention_ex, which
+ *              adds it back to every score.
+ *   seq_lens   NULL, or host int32 [B] in [1, N]: a variable-length batch in the
+ *              padded layout.  Batch element b has seq_lens[b] tokens (at the
+ *              positions of the full F x Hs x Ws grid); every mean, amax, scale
+ *              block and code uses those only (the means divide by seq_lens[b]),
+ *              tokens past them are never read, and their codes, scale blocks,
+ *              column sums and k_bias entries are 0.  B > 64 returns
+ *              ROTATTN_E_UNSUPPORTED; a length outside [1, N] ROTATTN_E_ARG.
+ * The pages name neither option; both are readings stated with the design. */
+typedef struct {
+  int32_t smooth_k;
+  int32_t smooth_q;
+  float* k_bias;
+  const int32_t* seq_lens;
+} rotattn_quantize_opts;
+
+rotattn_status rotattn_quantize_qk_ex(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
+                                      const void* q, const void* k, const void* v,
+                                      const float* rope_table, const rotattn_quantize_opts* opts,
+                                      uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+                                      uint8_t* v_codes, float* v_scale, int32_t* v_colsum,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- rotattn_int4_attention -----------------------------------------------------
  * INT4 FlashAttention forward (framework flowchart; Key design 2).  For each query
@@ -235,9 +254,13 @@ rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
  *                 baseline (as rotattn_int4_attention_symmetric_p); other values
  *                 return ROTATTN_E_ARG.
  *   causal_block  c as above.
- *   k_bias        NULL, or device f32 [B,H,Np] from rotattn_quantize_qk_smooth_q:
- *                 every score gains delta_j = fl(k_bias_j * C0) in log2 units,
- *                 t_ij = fma(a_ij, c_ij, delta_j), y_ij = fl(t_ij + fl(L15 - m_s)).
+ *   k_bias        NULL, or device f32 [B,H,Np] from rotattn_quantize_qk_ex with
+ *                 smooth_q: every score gains delta_j = fl(k_bias_j * C0) in log2
+ *                 units, t_ij = fma(a_ij, c_ij, delta_j), y_ij = fl(t_ij + fl(L15 - m_s)).
+ *   seq_lens      NULL, or host int32 [B] in [1, N] (the lengths the codes were made
+ *                 with): a row of batch element b sees only its first seq_lens[b]
+ *                 keys, and its rows past them are left untouched (debug rows must
+ *                 lie below it).  B > 64 returns ROTATTN_E_UNSUPPORTED.
  * Debug dumps leave the entries of keys a row does not see, and its steps past the
  * query tile's last key, unwritten: fill them first to compare whole arrays.
  * opts NULL is all defaults.  Every other argument, layout, workspace and error as
@@ -246,6 +269,7 @@ typedef struct {
   int32_t p_max;
   int32_t causal_block;
   const float* k_bias;
+  const int32_t* seq_lens;
 } rotattn_attention_opts;
 
 rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
@@ -258,14 +282,21 @@ rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
                                          const rotattn_debug* dbg,
                                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* The FP16 fallback with a causal block c as above (c = 0 is rotattn_fp16_fallback). */
-rotattn_status rotattn_fp16_fallback_causal(const rotattn_shape* s, rotattn_dtype in_dtype,
-                                            const void* q, const void* k, const void* v,
-                                            const float* rope_table,
-                                            const int32_t* heads, int32_t n_heads,
-                                            int32_t causal_block,
-                                            rotattn_dtype out_dtype, void* out,
-                                            void* workspace, size_t workspace_bytes, void* stream);
+/* The FP16 fallback with options (opts NULL: rotattn_fp16_fallback): a causal
+ * block c and variable-length batches, both as above (tokens past seq_lens[b] are
+ * never read; their output rows are left untouched). */
+typedef struct {
+  int32_t causal_block;
+  const int32_t* seq_lens;
+} rotattn_fallback_opts;
+
+rotattn_status rotattn_fp16_fallback_ex(const rotattn_shape* s, rotattn_dtype in_dtype,
+                                        const void* q, const void* k, const void* v,
+                                        const float* rope_table,
+                                        const int32_t* heads, int32_t n_heads,
+                                        const rotattn_fallback_opts* opts,
+                                        rotattn_dtype out_dtype, void* out,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 const char* rotattn_status_str(rotattn_status st);
 

@@ -139,12 +139,26 @@ size_t rotattn_quantize_qk_workspace(const rotattn_shape* s) {
 }
 
 namespace {
+// Variable-length batch: B lengths in [1, N] copied into the kernel arguments.
+rotattn_status set_lens(const rotattn_shape* s, const int32_t* seq_lens, int& nlens, int* lens) {
+  nlens = 0;
+  if (!seq_lens) return ROTATTN_OK;
+  if (s->B > ra::kMaxBatch) return ROTATTN_E_UNSUPPORTED;
+  const int64_t N = tokens(s);
+  for (int b = 0; b < s->B; ++b) {
+    if (seq_lens[b] < 1 || seq_lens[b] > N) return ROTATTN_E_ARG;
+    lens[b] = seq_lens[b];
+  }
+  nlens = s->B;
+  return ROTATTN_OK;
+}
+
 rotattn_status quantize_call(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
                              const void* q, const void* k, const void* v,
                              const float* rope_table, int32_t smooth_k,
                              uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
                              uint8_t* v_codes, float* v_scale, int32_t* v_colsum, bool smooth_q, float* k_bias,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             const int32_t* seq_lens, void* workspace, size_t workspace_bytes, void* stream) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rope_table || !q_codes || !q_scale || !k_codes || !k_scale || !v_codes ||
@@ -166,6 +180,8 @@ rotattn_status quantize_call(const rotattn_shape* s, rotattn_rot rot, rotattn_dt
   a.qc = q_codes; a.qs = q_scale; a.kc = k_codes; a.ks = k_scale;
   a.vc = v_codes; a.vs = v_scale; a.vcol = v_colsum;
   a.kbias = k_bias;
+  const rotattn_status ls = set_lens(s, seq_lens, a.nlens, a.lens);
+  if (ls != ROTATTN_OK) return ls;
   a.kpart = (double*)workspace;
   a.qpart = (double*)((char*)workspace + w.qpart);
   a.kmu = (float*)((char*)workspace + w.kmu);
@@ -182,17 +198,19 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
                                    uint8_t* v_codes, float* v_scale, int32_t* v_colsum,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   return quantize_call(s, rot, in_dtype, q, k, v, rope_table, smooth_k, q_codes, q_scale, k_codes, k_scale,
-                       v_codes, v_scale, v_colsum, false, nullptr, workspace, workspace_bytes, stream);
+                       v_codes, v_scale, v_colsum, false, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
-rotattn_status rotattn_quantize_qk_smooth_q(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
-                                            const void* q, const void* k, const void* v,
-                                            const float* rope_table, int32_t smooth_k,
-                                            uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
-                                            uint8_t* v_codes, float* v_scale, int32_t* v_colsum, float* k_bias,
-                                            void* workspace, size_t workspace_bytes, void* stream) {
-  return quantize_call(s, rot, in_dtype, q, k, v, rope_table, smooth_k, q_codes, q_scale, k_codes, k_scale,
-                       v_codes, v_scale, v_colsum, true, k_bias, workspace, workspace_bytes, stream);
+rotattn_status rotattn_quantize_qk_ex(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
+                                      const void* q, const void* k, const void* v,
+                                      const float* rope_table, const rotattn_quantize_opts* opts,
+                                      uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+                                      uint8_t* v_codes, float* v_scale, int32_t* v_colsum,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const rotattn_quantize_opts o = opts ? *opts : rotattn_quantize_opts{1, 0, nullptr, nullptr};
+  return quantize_call(s, rot, in_dtype, q, k, v, rope_table, o.smooth_k, q_codes, q_scale, k_codes, k_scale,
+                       v_codes, v_scale, v_colsum, o.smooth_q != 0, o.k_bias, o.seq_lens, workspace,
+                       workspace_bytes, stream);
 }
 
 size_t rotattn_int4_attention_workspace(const rotattn_shape* s) {
@@ -211,7 +229,7 @@ rotattn_status attention_call(const rotattn_shape* s,
                               rotattn_dtype out_dtype, void* out,
                               const rotattn_debug* dbg,
                               void* workspace, size_t workspace_bytes, void* stream, int pmax, int causal,
-                              const float* k_bias) {
+                              const float* k_bias, const int32_t* seq_lens) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
   if (causal < 0 || (pmax != 15 && pmax != 7)) return ROTATTN_E_ARG;
@@ -245,11 +263,15 @@ rotattn_status attention_call(const rotattn_shape* s,
   a.p_zero = pmax == 15 ? 8 : 0;
   a.causal = causal < N ? causal : 0;  // a block of N or more keys is every key
   a.kbias = k_bias;
+  a.H = s->H;
+  const rotattn_status ls = set_lens(s, seq_lens, a.nlens, a.lens);
+  if (ls != ROTATTN_OK) return ls;
   std::memcpy(a.T, levels().T, sizeof(a.T));
   hipStream_t hs = (hipStream_t)stream;
   if (dbg) {
     if (!dbg->a_qk || !dbg->p_codes || !dbg->a_pv || !dbg->m || !dbg->l) return ROTATTN_E_NULL;
-    if (dbg->bh < 0 || dbg->bh >= BH || dbg->row0 < 0 || dbg->n_rows < 1 || (int64_t)dbg->row0 + dbg->n_rows > N)
+    if (dbg->bh < 0 || dbg->bh >= BH || dbg->row0 < 0 || dbg->n_rows < 1 ||
+        (int64_t)dbg->row0 + dbg->n_rows > (seq_lens ? seq_lens[dbg->bh / s->H] : N))
       return ROTATTN_E_ARG;
     a.dbg_row0 = dbg->row0; a.dbg_n = dbg->n_rows;
     a.dbg_aqk = dbg->a_qk; a.dbg_p = dbg->p_codes; a.dbg_apv = dbg->a_pv; a.dbg_m = dbg->m; a.dbg_l = dbg->l;
@@ -281,7 +303,7 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
                                       const rotattn_debug* dbg,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
-                        dbg, workspace, workspace_bytes, stream, 15, 0, nullptr);
+                        dbg, workspace, workspace_bytes, stream, 15, 0, nullptr, nullptr);
 }
 
 rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
@@ -293,7 +315,7 @@ rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
                                                   const rotattn_debug* dbg,
                                                   void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
-                        dbg, workspace, workspace_bytes, stream, 7, 0, nullptr);
+                        dbg, workspace, workspace_bytes, stream, 7, 0, nullptr, nullptr);
 }
 
 rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
@@ -308,7 +330,7 @@ rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
   const int pmax = opts && opts->p_max ? opts->p_max : 15;
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
                         dbg, workspace, workspace_bytes, stream, pmax, opts ? opts->causal_block : 0,
-                        opts ? opts->k_bias : nullptr);
+                        opts ? opts->k_bias : nullptr, opts ? opts->seq_lens : nullptr);
 }
 
 size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s) {
@@ -317,15 +339,16 @@ size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s) {
   return 3 * align256(per);
 }
 
-rotattn_status rotattn_fp16_fallback_causal(const rotattn_shape* s, rotattn_dtype in_dtype,
-                                            const void* q, const void* k, const void* v,
-                                            const float* rope_table,
-                                            const int32_t* heads, int32_t n_heads,
-                                            int32_t causal_block,
-                                            rotattn_dtype out_dtype, void* out,
-                                            void* workspace, size_t workspace_bytes, void* stream) {
+rotattn_status rotattn_fp16_fallback_ex(const rotattn_shape* s, rotattn_dtype in_dtype,
+                                        const void* q, const void* k, const void* v,
+                                        const float* rope_table,
+                                        const int32_t* heads, int32_t n_heads,
+                                        const rotattn_fallback_opts* opts,
+                                        rotattn_dtype out_dtype, void* out,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
+  const int32_t causal_block = opts ? opts->causal_block : 0;
   if (causal_block < 0) return ROTATTN_E_ARG;
   if (!q || !k || !v || !rope_table || !out || !workspace) return ROTATTN_E_NULL;
   if (in_dtype < ROTATTN_F32 || in_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
@@ -353,6 +376,8 @@ rotattn_status rotattn_fp16_fallback_causal(const rotattn_shape* s, rotattn_dtyp
   a.nqt = (int)((a.N + 127) / 128);
   a.scale_log2 = (float)(1.4426950408889634074 / std::sqrt((double)s->D));
   a.causal = causal_block < a.N ? causal_block : 0;  // a block of N or more keys is every key
+  const rotattn_status ls = set_lens(s, opts ? opts->seq_lens : nullptr, a.nlens, a.lens);
+  if (ls != ROTATTN_OK) return ls;
   hipStream_t hs = (hipStream_t)stream;
   const int nh = heads ? n_heads : BH;
   for (int h0 = 0; h0 < nh; h0 += ra::kMaxHeads) {
@@ -372,8 +397,8 @@ rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dt
                                      const int32_t* heads, int32_t n_heads,
                                      rotattn_dtype out_dtype, void* out,
                                      void* workspace, size_t workspace_bytes, void* stream) {
-  return rotattn_fp16_fallback_causal(s, in_dtype, q, k, v, rope_table, heads, n_heads, 0, out_dtype, out,
-                                      workspace, workspace_bytes, stream);
+  return rotattn_fp16_fallback_ex(s, in_dtype, q, k, v, rope_table, heads, n_heads, nullptr, out_dtype, out,
+                                  workspace, workspace_bytes, stream);
 }
 
 const char* rotattn_status_str(rotattn_status st) {

@@ -524,23 +524,27 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   // block-causal tiles: the last query tiles see the most keys, so they go first
   const int qt = (!DBG && args.causal > 0) ? args.nqt - 1 - L % args.nqt : L % args.nqt;
   const int bh = args.heads[hidx];
+  // tokens of this head that exist (a variable-length batch: tiles past them have
+  // no row to write and leave at once, before any copy or barrier)
+  const int Nv = (int)valid_len(args.nlens, args.lens, bh, args.H, args.N);
+  if (!DBG && qt * kBM >= Nv) return;
   Ctx a;
   a.img = args.img; a.ks = args.ks; a.Np = args.Np;
   a.N = (int)args.N; a.qk_shift = __builtin_ctz(args.qk_blk); a.C0 = args.C0; a.L15 = args.L15;
   a.p_zero = args.p_zero;
   a.dbg_row0 = args.dbg_row0; a.dbg_n = args.dbg_n;
   a.dbg_aqk = args.dbg_aqk; a.dbg_p = args.dbg_p; a.dbg_apv = args.dbg_apv;
-  const int N = a.N;
+  const int N = a.N;  // the layout's tokens per head
   const int qi = qt * kBM + w * 32 + col;
-  // Keys seen: all N, or under block-causal masking (block c) the keys of the row's
-  // own block and every earlier one, min(N, (i / c + 1) c).  The tile's groups run
+  // Keys seen: all Nv, or under block-causal masking (block c) the keys of the row's
+  // own block and every earlier one, min(Nv, (i / c + 1) c).  The tile's groups run
   // up to its last row's limit; groups wholly below its first row's limit need no
   // per-key test.
   const int64_t c = args.causal;
-  auto limit = [&](int64_t i) -> int { return c > 0 ? (int)min((int64_t)N, (i / c + 1) * c) : N; };
+  auto limit = [&](int64_t i) -> int { return c > 0 ? (int)min((int64_t)Nv, (i / c + 1) * c) : Nv; };
   a.klim = limit(qi);
   a.kb = args.kbias != nullptr;
-  const int kmax = limit(min(qt * kBM + kBM - 1, N - 1));
+  const int kmax = limit(min(qt * kBM + kBM - 1, Nv - 1));
   const int ngroups = (kmax + G::TG - 1) / G::TG;
   const int nfull = min(limit(qt * kBM) / G::TG, ngroups);  // groups no row masks
 
@@ -577,7 +581,7 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) S.acc[db][v] = 0.f;
   }
-  const bool dbg_row = DBG && qi >= a.dbg_row0 && qi < a.dbg_row0 + a.dbg_n && qi < N;
+  const bool dbg_row = DBG && qi >= a.dbg_row0 && qi < a.dbg_row0 + a.dbg_n && qi < Nv;
   const int dr = qi - a.dbg_row0;
 
   wait_vm<0>();  // the first groups and the Q operand
@@ -600,7 +604,7 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
     args.dbg_m[dr] = S.m;
     args.dbg_l[dr] = lq;
   }
-  if (qi < N) {
+  if (qi < Nv) {
     const float inv = 1.0f / lq;
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {

@@ -87,6 +87,11 @@ RA_DEV float pair_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// tokens of head bh that exist: lens[bh / H] in a variable-length batch, else N
+RA_DEV int64_t valid_len(int nlens, const int* lens, int bh, int H, int64_t N) {
+  return nlens ? (int64_t)lens[bh / H] : N;
+}
+
 // binary32 -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN)
 RA_DEV uint16_t f32_to_bf16(float x) {
   const uint32_t u = __float_as_uint(x);

@@ -31,14 +31,15 @@ __global__ __launch_bounds__(256) void k3_prep(FbArgs a) {
   const int64_t n0 = (int64_t)blockIdx.x * kFbTile;
   const void* src = which == 0 ? a.q : (which == 1 ? a.k : a.v);
   const void* base = (const char*)src + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
-  stage_tile<D, DT>(base, n0, N, kFbTile, lds);
+  const int64_t Nv = valid_len(a.nlens, a.lens, bh, s.H, N);  // tokens that exist
+  stage_tile<D, DT>(base, n0, Nv, kFbTile, lds);
   __syncthreads();
   if (which < 2) {
     _Float16* dst = (which == 0 ? a.qr : a.kr) + ((int64_t)bh * Np + n0) * D;
     for (int e = threadIdx.x; e < kFbTile * D; e += blockDim.x) {
       const int r = e / D, c = e % D;
       float v = 0.f;
-      if (n0 + r < N) {
+      if (n0 + r < Nv) {
         int f, y, x;
         token_pos(n0 + r, s, f, y, x);
         v = rope_rot<D, DT>(lds, r, c, s, 0, a.table, f, y, x);
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void k3_prep(FbArgs a) {
     _Float16* dst = a.vt + (int64_t)bh * D * Np + n0;
     for (int e = threadIdx.x; e < kFbTile * D; e += blockDim.x) {
       const int c = e / kFbTile, r = e % kFbTile;
-      const float v = (n0 + r < N) ? lds_elem<D, DT>(lds, r, c) : 0.f;
+      const float v = (n0 + r < Nv) ? lds_elem<D, DT>(lds, r, c) : 0.f;
       dst[(int64_t)c * Np + r] = (_Float16)v;
     }
   }
@@ -208,16 +209,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // block-causal tiles: the last query tiles see the most keys, so they go first
   const int qt = args.causal > 0 ? args.nqt - 1 - L % args.nqt : L % args.nqt;
   const int bh = args.heads[hidx];
+  // tokens of this head that exist: tiles past them have no row and leave at once
+  const int Nv = (int)valid_len(args.nlens, args.lens, bh, args.s.H, args.N);
+  if (qt * kFbBM >= Nv) return;
   FbCtx a;
   a.kr = args.kr; a.vt = args.vt; a.Np = args.Np; a.N = (int)args.N; a.scale_log2 = args.scale_log2;
-  const int N = a.N;
+  const int N = a.N;  // the layout's tokens per head
   const int qi = qt * kFbBM + w * 32 + col;
-  // keys seen: all N, or min(N, (i / c + 1) c) under block-causal masking (block c);
-  // groups wholly below the tile's first row's limit need no per-key test
+  // keys seen: all Nv, or min(Nv, (i / c + 1) c) under block-causal masking (block
+  // c); groups wholly below the tile's first row's limit need no per-key test
   const int64_t c = args.causal;
-  auto limit = [&](int64_t i) -> int { return c > 0 ? (int)min((int64_t)N, (i / c + 1) * c) : N; };
+  auto limit = [&](int64_t i) -> int { return c > 0 ? (int)min((int64_t)Nv, (i / c + 1) * c) : Nv; };
   a.klim = limit(qi);
-  const int kmax = limit(min(qt * kFbBM + kFbBM - 1, N - 1));
+  const int kmax = limit(min(qt * kFbBM + kFbBM - 1, Nv - 1));
 
   f16x8 qop[G::KC];
   {
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (; g < ngroups; ++g) fb_group<D, true>(a, g, ngroups, flds, rk, rv, qop, bh, O, m, l);
 
   const float lq = l + __shfl_xor(l, 32, 64);
-  if (qi < N) {
+  if (qi < Nv) {
     const float inv = 1.0f / lq;
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {

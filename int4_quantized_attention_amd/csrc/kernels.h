@@ -10,6 +10,7 @@ struct Shape {
 };
 
 constexpr int kTokenPad = 256;   // code tensors hold Np = N rounded up to this
+constexpr int kMaxBatch = 64;    // batch elements of a variable-length call
 constexpr int kMaxHeads = 512;   // heads per attention launch (more -> several launches)
 
 struct QuantArgs {
@@ -29,6 +30,8 @@ struct QuantArgs {
   float* vs;
   int32_t* vcol;
   float* kbias;  // [B,H,Np] mu_q . K_j (smooth_q only)
+  int nlens;     // 0, or B: lens[b] tokens of batch element b exist (variable-length batch)
+  int lens[kMaxBatch];
   // workspace
   double* kpart;
   double* qpart;
@@ -55,6 +58,9 @@ struct AttnArgs {
   int p_zero;       // zero point of the dumped P codes: 8 (range-rectified) or 0
   int causal;       // 0 bidirectional; c > 0: query i sees key j iff j / c <= i / c (c < N)
   const float* kbias;  // nullable [B,H,Np]: per-key score term left by Q smoothing
+  int H;               // heads per batch element (for lens)
+  int nlens;           // 0, or B: lens[b] tokens of batch element b exist
+  int lens[kMaxBatch];
   float T[16];  // P level thresholds (15 used)
   // debug (rows [dbg_row0, dbg_row0 + dbg_n) of the single listed head)
   int dbg_row0, dbg_n;
@@ -82,6 +88,8 @@ struct FbArgs {
   int nqt, total, per_xcd;
   float scale_log2;  // log2(e) / sqrt(D)
   int causal;        // 0 bidirectional; c > 0: query i sees key j iff j / c <= i / c (c < N)
+  int nlens;         // 0, or B: lens[b] tokens of batch element b exist
+  int lens[kMaxBatch];
   int nheads;
   int heads[kMaxHeads];
 };

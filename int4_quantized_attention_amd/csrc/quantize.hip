@@ -30,12 +30,13 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int bh = blockIdx.y, blk = blockIdx.x;
   const bool isQ = blockIdx.z + (a.smooth ? 0 : 1) == 1;
+  const int64_t Nb = valid_len(a.nlens, a.lens, bh, s.H, N);
   const int64_t n0 = (int64_t)blk * kMeanTile;
   const int lt = threadIdx.x / TPT, c0 = (threadIdx.x % TPT) * CPT;
   const int64_t n = n0 + lt;
   const void* base = (const char*)(isQ ? a.q : a.k) + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   float x[CPT];
-  rotated_slice<DT, ROT, CPT, D>(base, n, n < N, D, c0, s, a.table, R + lt * (D + 1), x);
+  rotated_slice<DT, ROT, CPT, D>(base, n, n < Nb, D, c0, s, a.table, R + lt * (D + 1), x);
   if (ROT == 2) __syncthreads();  // every row of R read before it is overwritten
 #pragma unroll
   for (int i = 0; i < CPT; ++i) R[lt * (D + 1) + c0 + i] = x[i];
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
   if (threadIdx.x < D) {
     const int c = threadIdx.x;
     double part = 0.0;
-    const int cnt = (int)min((int64_t)kMeanTile, N - n0);
+    const int cnt = (int)max((int64_t)0, min((int64_t)kMeanTile, Nb - n0));
     for (int r = 0; r < cnt; ++r) part += (double)R[r * (D + 1) + c];
     const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
     (isQ ? a.qpart : a.kpart)[((int64_t)bh * nblk + blk) * D + c] = part;
@@ -75,7 +76,9 @@ __global__ void k1_kmean(QuantArgs a) {
     for (int i = 0; i < 8; ++i) total += v[i];
   }
   for (; b < nblk; ++b) total += p[b * D];
-  (isQ ? a.qmu : a.kmu)[idx] = (float)(total / (double)N);
+  // blocks past the valid tokens hold +0.0 partials: adding them changes nothing
+  const int64_t Nb = valid_len(a.nlens, a.lens, (int)bh, a.s.H, N);
+  (isQ ? a.qmu : a.kmu)[idx] = (float)(total / (double)Nb);
 }
 
 __global__ void k1_zero_u32(uint32_t* p, int64_t n) {
@@ -97,6 +100,7 @@ __global__ __launch_bounds__(256) void k1_vamax(QuantArgs a) {
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int bh = blockIdx.y;
   const int64_t n0 = (int64_t)blockIdx.x * kVTile;
+  const int64_t Nb = valid_len(a.nlens, a.lens, bh, s.H, N);
   const void* base = (const char*)a.v + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   const int cg = threadIdx.x % CG, tl = threadIdx.x / CG;
   float m[8];
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(256) void k1_vamax(QuantArgs a) {
 #pragma unroll 4
   for (int r = tl; r < kVTile; r += TL) {
     const int64_t n = n0 + r;
-    if (n < N) {
+    if (n < Nb) {
       float x[8];
       load_slice<DT, 8>(base, n, D, 8 * cg, x);
 #pragma unroll
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
   const void* base = (const char*)src + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   const int lt = threadIdx.x / TPT, part = threadIdx.x % TPT, c0 = part * CPT;
   const int64_t n = n0 + lt;
-  const bool valid = n < N;
+  const bool valid = n < valid_len(a.nlens, a.lens, bh, s.H, N);
   float v[CPT];
   rotated_slice<DT, ROT, CPT, D>(base, n, valid, D, c0, s, a.table, U + lt * (D + 1), v);
   if ((isK ? a.smooth : a.smooth_q) && valid) {
@@ -155,7 +159,8 @@ __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
   }
   if (isK && a.smooth_q) {
     // dS_n = mu_q . K_n: binary64, channels in order (the products are exact), as one
-    // chain through the token's TPT threads; the last one writes it (0 past N)
+    // chain through the token's TPT threads; the last one writes it (0 for tokens
+    // that do not exist)
     const float* mq = a.qmu + (int64_t)bh * D + c0;
     double acc = 0.0;
 #pragma unroll
@@ -221,7 +226,8 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
   const int bh = blockIdx.y;
   const int64_t n0 = (int64_t)blockIdx.x * kTile;
   const void* base = (const char*)a.v + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
-  stage_tile<D, DT>(base, n0, N, kTile, lds);
+  const int64_t Nb = valid_len(a.nlens, a.lens, bh, s.H, N);
+  stage_tile<D, DT>(base, n0, Nb, kTile, lds);
   __syncthreads();
   constexpr int G = 256 / D, TPG = kTile / G;  // groups, tokens per group
   const int c = threadIdx.x % D, g = threadIdx.x / D;
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
 #pragma unroll
   for (int i = 0; i < TPG; ++i) {
     const int r = g * TPG + i;
-    const bool valid = n0 + r < N;
+    const bool valid = n0 + r < Nb;
     codes[i] = (valid && amax != 0.f) ? quant_code(lds_elem<D, DT>(lds, r, c), inv) : 0;
   }
   uint32_t words[TPG / 8];

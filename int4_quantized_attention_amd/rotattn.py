@@ -40,8 +40,18 @@ class Debug(ctypes.Structure):
                 ("m", ctypes.c_void_p), ("l", ctypes.c_void_p)]
 
 
+class QuantizeOpts(ctypes.Structure):
+    _fields_ = [("smooth_k", ctypes.c_int32), ("smooth_q", ctypes.c_int32), ("k_bias", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p)]
+
+
 class AttentionOpts(ctypes.Structure):
-    _fields_ = [("p_max", ctypes.c_int32), ("causal_block", ctypes.c_int32), ("k_bias", ctypes.c_void_p)]
+    _fields_ = [("p_max", ctypes.c_int32), ("causal_block", ctypes.c_int32), ("k_bias", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p)]
+
+
+class FallbackOpts(ctypes.Structure):
+    _fields_ = [("causal_block", ctypes.c_int32), ("seq_lens", ctypes.c_void_p)]
 
 
 class RotattnError(RuntimeError):
@@ -63,14 +73,14 @@ _SIGS = {
                                       _VP]),
     "rotattn_int4_attention_symmetric_p": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _VP,
                                                   _SZ, _VP]),
-    "rotattn_quantize_qk_smooth_q": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
-                                            _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "rotattn_quantize_qk_ex": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                      _VP, _VP, _VP, _SZ, _VP]),
     "rotattn_int4_attention_ex": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, _VP,
                                          _VP, _SZ, _VP]),
     "rotattn_fp16_fallback_workspace": (_SZ, [_VP]),
     "rotattn_fp16_fallback": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ, _VP]),
-    "rotattn_fp16_fallback_causal": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _SZ,
-                                            _VP]),
+    "rotattn_fp16_fallback_ex": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, _VP, _SZ,
+                                        _VP]),
     "rotattn_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -105,6 +115,13 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _lens(seq_lens: Optional[Sequence[int]]):
+    """Host int32 array of per-element lengths (kept alive by the caller's frame)."""
+    if seq_lens is None:
+        return None
+    return (ctypes.c_int32 * len(seq_lens))(*[int(n) for n in seq_lens])
 
 
 def _heads(heads: Optional[Sequence[int]]):
@@ -167,25 +184,30 @@ def alloc_codes(shape: Shape, device="cuda", colsum: bool = True, smooth_q: bool
 
 
 def rotattn_quantize_qk(shape: Shape, rot: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                        rope_table: torch.Tensor, smooth_k: bool, z: dict, smooth_q: bool = False) -> dict:
-    """z: buffers from alloc_codes (filled in place, returned).  smooth_q: Q smoothing
-    through rotattn_quantize_qk_smooth_q, which fills z["k_bias"] (alloc_codes with
-    smooth_q=True); rotattn_int4_attention then adds it back."""
+                        rope_table: torch.Tensor, smooth_k: bool, z: dict, smooth_q: bool = False,
+                        seq_lens: Optional[Sequence[int]] = None) -> dict:
+    """z: buffers from alloc_codes (filled in place, returned).  smooth_q: Q smoothing,
+    which fills z["k_bias"] (alloc_codes with smooth_q=True); seq_lens: B lengths of
+    a variable-length batch.  Either goes through rotattn_quantize_qk_ex, and
+    rotattn_int4_attention then takes both from z."""
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise RotattnError("q, k, v must share one of float32 / float16 / bfloat16")
     ws = z["workspace"]
-    head = (ctypes.byref(shape), rot, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table),
-            1 if smooth_k else 0, _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
-            _ptr(z["v_codes"]), _ptr(z["v_scale"]), _ptr(z.get("v_colsum")))
+    head = (ctypes.byref(shape), rot, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table))
+    codes = (_ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]),
+             _ptr(z["v_codes"]), _ptr(z["v_scale"]), _ptr(z.get("v_colsum")))
     tail = (_ptr(ws), ws.numel(), _stream())
-    if smooth_q:
-        if z.get("k_bias") is None:
-            raise RotattnError("Q smoothing needs z['k_bias'] (alloc_codes(..., smooth_q=True))")
-        _check(lib().rotattn_quantize_qk_smooth_q(*head, _ptr(z["k_bias"]), *tail), "rotattn_quantize_qk_smooth_q")
-        z["smooth_q"] = True
+    if smooth_q and z.get("k_bias") is None:
+        raise RotattnError("Q smoothing needs z['k_bias'] (alloc_codes(..., smooth_q=True))")
+    if smooth_q or seq_lens is not None:
+        lens = _lens(seq_lens)
+        opts = QuantizeOpts(1 if smooth_k else 0, 1 if smooth_q else 0, _ptr(z["k_bias"]) if smooth_q else None,
+                            ctypes.cast(lens, ctypes.c_void_p) if lens is not None else None)
+        _check(lib().rotattn_quantize_qk_ex(*head, ctypes.byref(opts), *codes, *tail), "rotattn_quantize_qk_ex")
     else:
-        _check(lib().rotattn_quantize_qk(*head, *tail), "rotattn_quantize_qk")
-        z["smooth_q"] = False
+        _check(lib().rotattn_quantize_qk(*head, 1 if smooth_k else 0, *codes, *tail), "rotattn_quantize_qk")
+    z["smooth_q"] = bool(smooth_q)
+    z["seq_lens"] = None if seq_lens is None else [int(n) for n in seq_lens]
     return z
 
 
@@ -198,8 +220,10 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
     symmetric_p: the ablation baseline rotattn_int4_attention_symmetric_p (P codes
     round(7P) in [0, 7]) instead of the method's range-rectified codes.
     causal_block: 0 bidirectional; c > 0 block-causal (query i sees key j iff
-    j // c <= i // c).  When z was filled with Q smoothing, its k_bias is passed on.
-    Options other than the defaults go through rotattn_int4_attention_ex."""
+    j // c <= i // c).  When z was filled with Q smoothing or a variable-length
+    batch, its k_bias and seq_lens are passed on (rows past a sequence's length are
+    left untouched).  Options other than the defaults go through
+    rotattn_int4_attention_ex."""
     if out.dtype not in _DT:
         raise RotattnError("out must be float32, float16 or bfloat16")
     harr, nh = _heads(heads)
@@ -222,8 +246,10 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
     tail = (_DT[out.dtype], _ptr(out), ctypes.byref(dbg) if dbg is not None else None, _ptr(ws), ws.numel(),
             _stream())
     kb = z.get("k_bias") if z.get("smooth_q") else None
-    if causal_block or kb is not None:
-        opts = AttentionOpts(7 if symmetric_p else 15, int(causal_block), _ptr(kb))
+    lens = _lens(z.get("seq_lens"))
+    if causal_block or kb is not None or lens is not None:
+        opts = AttentionOpts(7 if symmetric_p else 15, int(causal_block), _ptr(kb),
+                             ctypes.cast(lens, ctypes.c_void_p) if lens is not None else None)
         _check(lib().rotattn_int4_attention_ex(ctypes.byref(shape), *codes, ctypes.byref(opts), *tail),
                "rotattn_int4_attention_ex")
     else:
@@ -234,10 +260,12 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
 
 def rotattn_fp16_fallback(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           rope_table: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
-                          heads: Optional[Sequence[int]] = None, causal_block: int = 0) -> torch.Tensor:
+                          heads: Optional[Sequence[int]] = None, causal_block: int = 0,
+                          seq_lens: Optional[Sequence[int]] = None) -> torch.Tensor:
     """q, k, v: device [B,H,N,D] of one of float32 / float16 / bfloat16 (rounded to
     binary16 after RoPE); out: float32, float16 or bfloat16.  causal_block as for
-    rotattn_int4_attention (rotattn_fp16_fallback_causal when non-zero)."""
+    rotattn_int4_attention, seq_lens a variable-length batch (both through
+    rotattn_fp16_fallback_ex)."""
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise RotattnError("q, k, v must share one of float32 / float16 / bfloat16")
     if out.dtype not in _DT:
@@ -245,8 +273,10 @@ def rotattn_fp16_fallback(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: tor
     harr, nh = _heads(heads)
     head = (ctypes.byref(shape), _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table), harr, nh)
     tail = (_DT[out.dtype], _ptr(out), _ptr(workspace), workspace.numel(), _stream())
-    if causal_block:
-        _check(lib().rotattn_fp16_fallback_causal(*head, int(causal_block), *tail), "rotattn_fp16_fallback_causal")
+    if causal_block or seq_lens is not None:
+        lens = _lens(seq_lens)
+        opts = FallbackOpts(int(causal_block), ctypes.cast(lens, ctypes.c_void_p) if lens is not None else None)
+        _check(lib().rotattn_fp16_fallback_ex(*head, ctypes.byref(opts), *tail), "rotattn_fp16_fallback_ex")
     else:
         _check(lib().rotattn_fp16_fallback(*head, *tail), "rotattn_fp16_fallback")
     return out

@@ -103,12 +103,27 @@ def test_null_and_bad_args_return_before_launch(L):
         st = L.rotattn_int4_attention_ex(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0,
                                          ctypes.byref(opts), 0, fake, nul, fake, big, nul)
         assert st == 6
-    # Q smoothing without its k_bias output
-    st = L.rotattn_quantize_qk_smooth_q(ctypes.byref(s), 1, 0, fake, fake, fake, fake, 1, fake, fake, fake,
-                                        fake, fake, fake, nul, nul, fake, 1 << 30, nul)
-    assert st == 1
-    st = L.rotattn_fp16_fallback_causal(ctypes.byref(s), 1, fake, fake, fake, fake, nul, 0, -3, 0, fake, fake,
-                                        1 << 30, nul)
+    # Q smoothing without its k_bias output; lengths outside [1, N]; too many elements
+    bad_len = (ctypes.c_int32 * 1)(0)
+    big_len = (ctypes.c_int32 * 1)(10 ** 6)
+    for opts, want in ((ra.QuantizeOpts(1, 1, None, None), 1),
+                       (ra.QuantizeOpts(1, 0, None, ctypes.cast(bad_len, ctypes.c_void_p)), 6),
+                       (ra.QuantizeOpts(1, 0, None, ctypes.cast(big_len, ctypes.c_void_p)), 6)):
+        st = L.rotattn_quantize_qk_ex(ctypes.byref(s), 1, 0, fake, fake, fake, fake, ctypes.byref(opts), fake,
+                                      fake, fake, fake, fake, fake, nul, fake, 1 << 30, nul)
+        assert st == want
+    s65 = _shape(B=65)
+    lens65 = (ctypes.c_int32 * 65)(*([1] * 65))
+    opts = ra.AttentionOpts(15, 0, None, ctypes.cast(lens65, ctypes.c_void_p))
+    st = L.rotattn_int4_attention_ex(ctypes.byref(s65), fake, fake, fake, fake, fake, fake, nul, 0,
+                                     ctypes.byref(opts), 0, fake, nul, fake, big, nul)
+    assert st == 3
+    st = L.rotattn_fp16_fallback_ex(ctypes.byref(s), 1, fake, fake, fake, fake, nul, 0,
+                                    ctypes.byref(ra.FallbackOpts(0, ctypes.cast(bad_len, ctypes.c_void_p))),
+                                    0, fake, fake, 1 << 30, nul)
+    assert st == 6
+    st = L.rotattn_fp16_fallback_ex(ctypes.byref(s), 1, fake, fake, fake, fake, nul, 0,
+                                    ctypes.byref(ra.FallbackOpts(-3, None)), 0, fake, fake, 1 << 30, nul)
     assert st == 6
     assert L.rotattn_status_str(0) == b"ok"
 

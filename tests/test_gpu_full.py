@@ -53,6 +53,32 @@ def test_fallback_causal(orc, cb):
     assert_close(out.cpu().numpy().reshape(-1, 128), ref)
 
 
+def test_fallback_varlen(orc):
+    """Variable-length fallback: NaN padding never read, rows past each length left
+    untouched, valid rows against the fallback oracle (also frame-causal)."""
+    cfg = synth.custom(3, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="peaked")
+    lens = [1173, 500, 37]
+    Q, K, V = synth.make_inputs(cfg)
+    for b, n in enumerate(lens):
+        for x in (Q, K, V):
+            x[b, :, n:] = np.nan
+    shape = ra.Shape.of(cfg)
+    tab = ra.rotattn_build_rope_table(shape, 0).cuda()
+    ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
+    N = synth.n_tokens(cfg)
+    for cb in (0, 391):
+        out = torch.full((3, 2, N, 128), float("nan"), dtype=torch.float32, device="cuda")
+        ra.rotattn_fp16_fallback(shape, to_dev(Q), to_dev(K), to_dev(V), tab, out, ws, causal_block=cb,
+                                 seq_lens=lens)
+        o = out.cpu().numpy()
+        for b, n in enumerate(lens):
+            assert np.isnan(o[b, :, n:]).all()
+            rows = np.array([(b * 2 + h) * N + i for h in range(2) for i in rows_sample(n, 16, seed=b)])
+            ref = orc.fallback_attention(cfg, orc.rope_table(cfg, 0), Q, K, V, rows=rows, causal_block=cb,
+                                         seq_lens=lens)
+            assert_close(o.reshape(-1, 128)[rows], ref)
+
+
 @pytest.mark.parametrize("in_dt,out_dt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float16)])
 def test_fallback_input_output_dtypes(orc, in_dt, out_dt):
     cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float32", recipe="peaked")

@@ -215,3 +215,56 @@ def test_q_smoothing_parity(orc, case):
 def test_q_smoothing_d64_f32(orc):
     cfg = synth.custom(1, 2, 5, 7, 9, 64, 24, 20, 20, 32, 64, dtype="float32", recipe="tiny")
     _run_case(orc, cfg, 2, debug_rows=[(0, 64)], smooth_q=True, inputs=_offset_queries(cfg))
+
+
+VARLEN = [
+    # (id, lengths of the three batch elements, rotation, Q smoothing, causal block, kv_blk)
+    ("frames_and_ragged_kv64", [1173, 782, 500], 2, False, 0, 64),
+    ("ragged_smoothq_kv16", [1173, 129, 1], 1, True, 0, 16),
+    ("ragged_frame_causal_kv128", [600, 1173, 391], 2, False, 391, 128),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=[c[0] for c in VARLEN])
+def test_varlen_parity(orc, case):
+    """Variable-length batch in the padded layout: padding holds NaN (nothing may read
+    it), codes and scales bit-exact with the oracle's, valid rows within the bar with
+    dumps bit-exact, rows past each length left untouched."""
+    name, lens, rot, smooth_q, cb, kv = case
+    cfg = synth.custom(3, 2, 3, 17, 23, 128, 44, 42, 42, min(kv, 64), kv, dtype="float16", recipe="wan")
+    Q, K, V = synth.make_inputs(cfg)
+    for b, n in enumerate(lens):
+        for x in (Q, K, V):
+            x[b, :, n:] = np.nan
+    shape = ra.Shape.of(cfg)
+    q, k, v = (to_dev(x) for x in (Q, K, V))
+    tab = ra.rotattn_build_rope_table(shape, rot).cuda()
+    z = ra.alloc_codes(shape, smooth_q=smooth_q)
+    ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, True, z, smooth_q=smooth_q, seq_lens=lens)
+    ref = orc.quantize(cfg, rot, orc.rope_table(cfg, rot), Q, K, V, smooth_q=smooth_q, seq_lens=lens)
+    compare_codes(cfg, z, ref)
+    N, D = synth.n_tokens(cfg), 128
+    out = torch.full((3, 2, N, D), float("nan"), dtype=torch.float32, device="cuda")
+    ra.rotattn_int4_attention(shape, z, out, causal_block=cb)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    for b, n in enumerate(lens):
+        assert np.isnan(o[b, :, n:]).all(), "rows past the length were written"
+        rows = np.array([(b * 2 + h) * N + i for h in range(2) for i in rows_sample(n, 16, seed=b)], np.int64)
+        want = orc.attention(cfg, ref, rows=rows, causal_block=cb)["out"]
+        assert_close(o.reshape(-1, D)[rows], want)
+    # dumps of the last rows of the shortest element
+    b = int(np.argmin(lens))
+    n = lens[b]
+    r0 = max(0, n - 40)
+    dbg = dict(bh=2 * b + 1, row0=r0, n_rows=n - r0)
+    out2 = torch.zeros_like(out)
+    ra.rotattn_int4_attention(shape, z, out2, debug=dbg, causal_block=cb)
+    torch.cuda.synchronize()
+    od = orc.attention(cfg, ref, rows=np.arange((2 * b + 1) * N + r0, (2 * b + 1) * N + n), dumps=True,
+                       causal_block=cb)
+    assert np.array_equal(dbg["a_qk"].cpu().numpy(), od["a_qk"]), "a_qk"
+    assert np.array_equal(dbg["p_codes"].cpu().numpy(), od["pcode"]), "P codes"
+    assert np.array_equal(dbg["a_pv"].cpu().numpy(), od["a_pv"]), "a_pv"
+    assert np.array_equal(dbg["m"].cpu().numpy().view(np.uint32), od["m"].view(np.uint32)), "m"
+    assert_close(out2.cpu().numpy()[b, 1, r0:n], od["out"])
