@@ -181,6 +181,7 @@ struct Ctx {
   int klim;  // keys this lane's query row sees: N, or its block-causal limit
   bool kb;   // per-key score terms staged (Q smoothing)
   float C0, L15;
+  float T0;  // the first level threshold: r >= 1 iff y >= T0
   int p_zero;
   int dbg_row0, dbg_n;
   int32_t* dbg_aqk;
@@ -276,31 +277,28 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     if (step >= nsteps) break;
     const bool act = (KVB >= 32) || (h == sidx);
     // ---- running maximum (max of the exact integer scores, then times c) -----------
-    float mloc = -INFINITY;
-    if (US) {
+    float imt[G::TPS];  // per tile: the largest score of the lane's present keys
+#pragma unroll
+    for (int t = 0; t < G::TPS; ++t) {
       float im = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < G::TPS; ++t) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          bool ok = act;
-          if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
-          im = fmaxf(im, ok ? st[t][v] : -INFINITY);
-        }
+      for (int v = 0; v < 16; ++v) {
+        bool ok = act;
+        if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
+        im = fmaxf(im, ok ? st[t][v] : -INFINITY);
       }
+      imt[t] = im;
+    }
+    float mloc = -INFINITY;
+    if (US) {
+      float im = imt[0];
+#pragma unroll
+      for (int t = 1; t < G::TPS; ++t) im = fmaxf(im, imt[t]);
       if (im != -INFINITY) mloc = im * ct[0];
     } else {
 #pragma unroll
-      for (int t = 0; t < G::TPS; ++t) {
-        float im = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          bool ok = act;
-          if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
-          im = fmaxf(im, ok ? st[t][v] : -INFINITY);
-        }
-        if (im != -INFINITY) mloc = fmaxf(mloc, im * ct[t]);
-      }
+      for (int t = 0; t < G::TPS; ++t)
+        if (imt[t] != -INFINITY) mloc = fmaxf(mloc, imt[t] * ct[t]);
     }
     const float mnew = fmaxf(S.m, pair_max(mloc));
     const bool moved = __any(mnew > S.m);
@@ -309,6 +307,27 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     S.m = mnew;
     const float nm = a.L15 - mnew;
     const bool guard = mnew >= 262144.0f;
+    // Tiles whose every level is 0: y = fma(A, c, L15 - m) is non-decreasing in the
+    // score A (c >= 0), so the largest y of a lane's keys in a tile is fma(max A, c,
+    // L15 - m), exactly; when it is below the first threshold in every lane, every
+    // exact level of the tile is 0 and its P V products are exact zeros.  (No present
+    // key: -inf, or NaN when c = 0; neither compares true.)  The debug run keeps the
+    // dense path so that it dumps every code.
+    //
+    // Tiles whose every p is below half an ulp of l: adding such a p to l (binary32,
+    // round to nearest even) returns l unchanged, and l only grows for the rest of
+    // the step (the rescale came first), so these additions are exact no-ops and
+    // are skipped too.  The bound is 2^(e-25) for l in [2^e, 2^(e+1)): one binade
+    // below half an ulp covers the hardware exp's error.  While l is 0 (a row's
+    // first step) nothing is skipped this way.
+    const float ythr = S.l > 0.f ? (float)(__builtin_amdgcn_frexp_expf(S.l) - 26) : -INFINITY;
+    bool zt[G::TPS], ngl[G::TPS];
+#pragma unroll
+    for (int t = 0; t < G::TPS; ++t) {
+      const float ymax = __builtin_fmaf(imt[t], ct[t], nm);
+      zt[t] = !DBG && !__any(ymax >= a.T0);
+      ngl[t] = !DBG && __builtin_amdgcn_readfirstlane((int)!__any(ymax >= ythr)) != 0;
+    }
     // ---- P levels, P^T operand, level sums, P V: 64 keys (two tiles) per MFMA ---------
     // Fast path: level byte and margin from the hardware exp, packed four at a time
     // into the P^T operand.  The level bytes r in [0, 15] are read by the MFMA as fp8
@@ -324,6 +343,36 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     for (int pp = 0; pp < G::TPS / PT; ++pp) {
       i32x4 pb[PT];
       bool flag = guard;
+      // (wave-uniform by construction; readfirstlane makes that explicit, so the
+      // branch below stays a scalar branch instead of two masked paths)
+      const bool allz = __builtin_amdgcn_readfirstlane((int)(zt[pp * PT] && zt[pp * PT + PT - 1])) != 0;
+      if (allz) {
+        // every level of the pair is 0: the keys enter the normaliser only (same
+        // order of additions as the level path); no margin, MFMA, V read or exact
+        // path runs.
+        // Each path takes L15 - m through an empty asm of its own, so that the
+        // compiler can neither merge the two paths' exps nor hoist either set above
+        // the branch (where all of them would be computed, and live, at once).
+        flag = false;
+        float nz = nm;
+        asm volatile("" : "+v"(nz));
+#pragma unroll
+        for (int tp = 0; tp < PT; ++tp) {
+          const int t = pp * PT + tp;
+          pb[tp] = i32x4{0, 0, 0, 0};
+          if (ngl[t]) continue;  // no p of the tile moves l
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            bool ok = act;
+            if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
+            float p = exp2_hw(__builtin_fmaf(st[t][v], ct[t], nz));
+            if (MASK || KVB < 32) p = ok ? p : 0.f;
+            S.l += p;
+          }
+        }
+      } else {
+      float nl = nm;
+      asm volatile("" : "+v"(nl));
 #pragma unroll
       for (int tp = 0; tp < PT; ++tp) {
         const int t = pp * PT + tp;
@@ -336,7 +385,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
             const int v = 4 * w + e;
             bool ok = act;
             if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
-            const float y = __builtin_fmaf(st[t][v], ct[t], nm);
+            const float y = __builtin_fmaf(st[t][v], ct[t], nl);
             float p = exp2_hw(y);
             if (MASK || KVB < 32) p = ok ? p : 0.f;
             S.l += p;
@@ -348,6 +397,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
         }
         flag = flag || ((wmin & 0xFFFFu) <= 6u);
       }
+      }  // level path
       if (pp == 0 && moved) {
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db) {
@@ -355,6 +405,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
           for (int v = 0; v < 16; ++v) S.acc[db][v] *= alpha;
         }
       }
+      if (allz) continue;
       const i32x8 pop = PT == 2 ? __builtin_shufflevector(pb[0], pb[PT - 1], 0, 1, 2, 3, 4, 5, 6, 7)
                                 : __builtin_shufflevector(pb[0], i32x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
       // this lane half's 32 keys of the pair in the V^T rows (one 16-key chunk,
@@ -532,6 +583,7 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   a.img = args.img; a.ks = args.ks; a.Np = args.Np;
   a.N = (int)args.N; a.qk_shift = __builtin_ctz(args.qk_blk); a.C0 = args.C0; a.L15 = args.L15;
   a.p_zero = args.p_zero;
+  a.T0 = args.T[0];
   a.dbg_row0 = args.dbg_row0; a.dbg_n = args.dbg_n;
   a.dbg_aqk = args.dbg_aqk; a.dbg_p = args.dbg_p; a.dbg_apv = args.dbg_apv;
   const int N = a.N;  // the layout's tokens per head
