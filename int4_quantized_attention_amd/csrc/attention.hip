@@ -321,12 +321,12 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     // below half an ulp covers the hardware exp's error.  While l is 0 (a row's
     // first step) nothing is skipped this way.
     const float ythr = S.l > 0.f ? (float)(__builtin_amdgcn_frexp_expf(S.l) - 26) : -INFINITY;
-    bool zt[G::TPS], ngl[G::TPS];
+    float ymax[G::TPS];
+    bool ngl[G::TPS];
 #pragma unroll
     for (int t = 0; t < G::TPS; ++t) {
-      const float ymax = __builtin_fmaf(imt[t], ct[t], nm);
-      zt[t] = !DBG && !__any(ymax >= a.T0);
-      ngl[t] = !DBG && __builtin_amdgcn_readfirstlane((int)!__any(ymax >= ythr)) != 0;
+      ymax[t] = __builtin_fmaf(imt[t], ct[t], nm);
+      ngl[t] = !DBG && !__any(ymax[t] >= ythr);
     }
     // ---- P levels, P^T operand, level sums, P V: 64 keys (two tiles) per MFMA ---------
     // Fast path: level byte and margin from the hardware exp, packed four at a time
@@ -343,9 +343,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     for (int pp = 0; pp < G::TPS / PT; ++pp) {
       i32x4 pb[PT];
       bool flag = guard;
-      // (wave-uniform by construction; readfirstlane makes that explicit, so the
-      // branch below stays a scalar branch instead of two masked paths)
-      const bool allz = __builtin_amdgcn_readfirstlane((int)(zt[pp * PT] && zt[pp * PT + PT - 1])) != 0;
+      const bool allz = !DBG && !__any(fmaxf(ymax[pp * PT], ymax[pp * PT + PT - 1]) >= a.T0);
       if (allz) {
         // every level of the pair is 0: the keys enter the normaliser only (same
         // order of additions as the level path); no margin, MFMA, V read or exact
@@ -509,28 +507,35 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
   const int h = (threadIdx.x >> 5) & 1;
   const kscale_ptr ksh = (kscale_ptr)a.ks + (int64_t)bh * (a.Np >> a.qk_shift);
   uint8_t* const cur = lds + slot * G::IMG;
+  // The scores of step sg + 1 are issued on the MFMA before the softmax of step sg,
+  // so that its latency overlaps that step's VALU work.
+  float ct[G::NSG][G::TPS];
+  f32x16 st[G::NSG][G::TPS];
 #pragma unroll
   for (int sg = 0; sg < G::NSG; ++sg) {
     const int tb = sg * G::TPS;
-    float ct[G::TPS];
     if (US) {
       const float c = (sq * ksh[(g * G::TG + 32 * tb) >> a.qk_shift]) * a.C0;
 #pragma unroll
-      for (int t = 0; t < G::TPS; ++t) ct[t] = c;
+      for (int t = 0; t < G::TPS; ++t) ct[sg][t] = c;
     } else {
 #pragma unroll
       for (int t = 0; t < G::TPS; ++t) {
         const int k0 = g * G::TG + 32 * (tb + t);
         const float s0 = ksh[k0 >> a.qk_shift], s1 = ksh[(k0 + 16) >> a.qk_shift];
-        ct[t] = (sq * (h ? s1 : s0)) * a.C0;
+        ct[sg][t] = (sq * (h ? s1 : s0)) * a.C0;
       }
     }
-    f32x16 st[G::TPS];
-    qk_tiles<D, KVB>(cur, tb, qop, st);
+  }
+  qk_tiles<D, KVB>(cur, 0, qop, st[0]);
+#pragma unroll
+  for (int sg = 0; sg < G::NSG; ++sg) {
+    const int tb = sg * G::TPS;
+    if (sg + 1 < G::NSG) qk_tiles<D, KVB>(cur, tb + G::TPS, qop, st[sg + 1 < G::NSG ? sg + 1 : sg]);
     f32x16 sa[G::TPS];  // the integer scores, kept for the debug dump only
     if (DBG) {
 #pragma unroll
-      for (int t = 0; t < G::TPS; ++t) sa[t] = st[t];
+      for (int t = 0; t < G::TPS; ++t) sa[t] = st[sg][t];
     }
     if (a.kb) {
       // Q smoothing: t = fma(a, c, delta_j) in place; with c = 1 from here on the max
@@ -542,14 +547,15 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
         for (int v4 = 0; v4 < 4; ++v4) {
           const f32x4 d4 = *(const f32x4*)(Dl + 32 * t + 4 * v4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) st[t][4 * v4 + e] = __builtin_fmaf(st[t][4 * v4 + e], ct[t], d4[e]);
+          for (int e = 0; e < 4; ++e)
+            st[sg][t][4 * v4 + e] = __builtin_fmaf(st[sg][t][4 * v4 + e], ct[sg][t], d4[e]);
         }
-        ct[t] = 1.0f;
+        ct[sg][t] = 1.0f;
       }
     }
     const int step0 = KVB < 32 ? 2 * g : g * G::NSG + sg;
-    softmax_pv<D, KVB, DBG, MASK, US>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st, ct,
-                                      DBG ? sa : st, S, dbg_row, dr);
+    softmax_pv<D, KVB, DBG, MASK, US>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), st[sg],
+                                      ct[sg], DBG ? sa : st[sg], S, dbg_row, dr);
   }
   // copies issued after group g+1's: those of groups g+2 .. min(g+NB-1, ngroups-1)
   const int later = min(g + G::NB - 1, ngroups - 1) - (g + 1);
