@@ -9,32 +9,37 @@
 //  * A staging pass (k2_stage) turns each head's INT4 K and V codes into the exact
 //    byte image one key group occupies in LDS: K as packed fp6 e2m3 (every code in
 //    [-7, 7] is exact in e2m3; 6 bits per value) with rows permuted for the S^T
-//    register layout, V^T as int8, rows padded so that the LDS reads of 32
-//    consecutive rows hit distinct banks, and the level-threshold table in the tail.  The
-//    main loop copies groups straight from global memory into LDS
-//    (buffer_load_dwordx4 ... lds) into a ring of LDS slots, up to three groups
-//    ahead, and spends no VALU on staging.  A group of 128 keys holds several
-//    online-softmax steps (one barrier and one copy per group).
+//    register layout, V^T as fp8 e4m3 (also exact), rows padded so that the LDS
+//    reads of consecutive rows hit distinct banks, and the level-threshold table in
+//    the tail.  The main loop copies groups straight from global memory into LDS
+//    (buffer_load_dwordx4 ... lds) into a ring of LDS slots and spends no VALU on
+//    staging.  A group of 128 keys holds several online-softmax steps (one barrier
+//    and one copy per group).
 //  * One workgroup = 4 waves x 32 query rows.  Each wave computes S^T = K Q^T on
 //    v_mfma_scale_f32_32x32x64_f8f6f4 with fp6 operands (unit scales), which runs
 //    at twice the rate of the fp8 and int8 forms.  Products of INT4 values and
 //    their sums (|A| <= 49 D < 2^24) are exact in fp32, so the scores arrive as
 //    exact integers in float registers.  A lane owns one query row and 16 keys of
-//    every 32-key tile; its P levels are already laid out as the B operand of the
-//    next MFMA, O^T = V^T P^T (v_mfma_i32_32x32x32_i8), with no LDS round trip.
+//    every 32-key tile; its P levels are already laid out as the B operand of
+//    O^T = V^T P^T on the same instruction in its fp8 form, with no LDS round trip.
+//    The scores of the next step are issued before the softmax of the current one.
 //  * The P level r = round-half-even(2^y) is taken from the hardware exp2: with
 //    t = 2^y + 128.5 + 4*2^-16 the level is byte 2 of t's bits and the low 16 bits
 //    carry the rounding margin.  v_exp_f32 is within 1.5 * 2^-24 relative of 2^y,
 //    so whenever the margin is above 6/2^16 the level equals the exact one; the
 //    (rare) other elements are decided exactly against the 15 thresholds.  The
-//    level r in [0, 15] is the int8 operand: sum_j (P~_j + 8) v_j = sum_j r_j v_j
-//    folds the zero point into the product.
-//  * The int32 P V accumulator runs across online-softmax steps and is folded
-//    into the fp32 output (one fma per element, in a fixed exponent frame) and
-//    cleared only when a row maximum moves.
+//    level byte r in [0, 15], read as the fp8 code r * 2^-9 with a B scale of 2^9,
+//    is the operand: sum_j (P~_j + 8) v_j = sum_j r_j v_j folds the zero point into
+//    the product, and every product and sum is an exact integer in fp32.
+//  * Exact skips: a tile pair whose every level is 0 (decided from the exact tile
+//    maximum of y) adds exact zeros, so it skips the level packing, the P V MFMA
+//    and the V reads; a tile whose every p is below half an ulp of l would not
+//    change l, so it also skips the exp.  Both leave every result bit-identical.
+//  * The fp32 accumulator holds exact integer sums between moves of the row
+//    maximum and is rescaled in place when a maximum in the wave moves.
 //  * Two waves per SIMD (<= 256 registers each), so that one wave's MFMAs run
 //    under the other's softmax; one barrier per key group.
-//  * Workgroup ids are remapped so that all query tiles of a head run on the same
+//  * Workgroup ids are remapped so that the query tiles of a head run on the same
 //    XCD and share its L2 for the K/V stream.
 #include <utility>
 
