@@ -322,10 +322,10 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     // Tiles whose every p is below half an ulp of l: adding such a p to l (binary32,
     // round to nearest even) returns l unchanged, and l only grows for the rest of
     // the step (the rescale came first), so these additions are exact no-ops and
-    // are skipped too.  The bound is 2^(e-25) for l in [2^e, 2^(e+1)): one binade
-    // below half an ulp covers the hardware exp's error.  While l is 0 (a row's
-    // first step) nothing is skipped this way.
-    const float ythr = S.l > 0.f ? (float)(__builtin_amdgcn_frexp_expf(S.l) - 26) : -INFINITY;
+    // are skipped too.  For l in [2^e, 2^(e+1)) half an ulp is 2^(e-24); the bound
+    // on y is e - 24 - 1e-4, so that the hardware exp (within 2^-22 relative of 2^y)
+    // stays below it.  While l is 0 (a row's first step) nothing is skipped this way.
+    const float ythr = S.l > 0.f ? (float)(__builtin_amdgcn_frexp_expf(S.l) - 25) - 1e-4f : -INFINITY;
     float ymax[G::TPS];
     bool ngl[G::TPS];
 #pragma unroll
