@@ -274,3 +274,89 @@ def test_varlen_parity(orc, case):
     assert np.array_equal(dbg["m"].cpu().numpy().view(np.uint32), od["m"].view(np.uint32)), "m"
     assert_close(out2.cpu().numpy()[b, 1, r0:n], od["out"])
     assert np.array_equal(out2.cpu().numpy()[b, 1, r0:n], o[b, 1, r0:n]), "production and debug outputs differ"
+
+
+def _random_config(rng, i):
+    D = int(rng.choice([64, 128]))
+    if D == 64:
+        Df, Dh, Dw = 24, 20, 20
+    else:
+        Df, Dh, Dw = [(44, 42, 42), (16, 56, 56)][int(rng.integers(2))]
+    kv = int(rng.choice([16, 32, 64, 128]))
+    qk = int(rng.choice([16, 32, 64, 128]))
+    F, Hs, Ws = int(rng.integers(1, 4)), int(rng.integers(3, 19)), int(rng.integers(3, 29))
+    B = int(rng.integers(1, 3))
+    dtype = str(rng.choice(["float16", "float32"]))
+    cfg = synth.custom(B, 2, F, Hs, Ws, D, Df, Dh, Dw, qk, kv, dtype=dtype,
+                       recipe=str(rng.choice(["wan", "peaked"])) if D == 128 else "tiny")
+    N = F * Hs * Ws
+    # the options alternate with the case number so that every combination class is
+    # covered; the rest is drawn
+    opts = dict(rot=i % 4, smooth_k=bool(rng.integers(2)), smooth_q=i % 2 == 1,
+                causal=[0, 1, Hs * Ws, int(rng.integers(2, 200))][(i // 2) % 4],
+                lens=[int(rng.integers(1, N + 1)) for _ in range(B)] if i % 3 == 0 else None,
+                pmax=7 if i % 5 == 4 else 15)
+    return cfg, opts
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_configs_parity(orc, i):
+    """Seeded random combinations of shape, head split, block sizes, rotation, K and Q
+    smoothing, causal block, variable lengths and P code: codes bit-exact, sampled
+    rows within the bar, and on two row ranges the production output equal to the
+    dense debug run bit for bit with its dumps equal to the oracle's."""
+    rng = np.random.default_rng(1000 + i)
+    cfg, o = _random_config(rng, i)
+    print("case", i, cfg, o, flush=True)
+    B, H, D = cfg["B"], cfg["H"], cfg["D"]
+    N = synth.n_tokens(cfg)
+    Q, K, V = synth.make_inputs(cfg, seed=i)
+    lens = o["lens"]
+    if lens is not None:
+        for b, n in enumerate(lens):
+            for x in (Q, K, V):
+                x[b, :, n:] = np.nan
+    shape = ra.Shape.of(cfg)
+    q, k, v = (to_dev(x) for x in (Q, K, V))
+    tab = ra.rotattn_build_rope_table(shape, o["rot"]).cuda()
+    z = ra.alloc_codes(shape, smooth_q=o["smooth_q"])
+    ra.rotattn_quantize_qk(shape, o["rot"], q, k, v, tab, o["smooth_k"], z, smooth_q=o["smooth_q"], seq_lens=lens)
+    ref = orc.quantize(cfg, o["rot"], orc.rope_table(cfg, o["rot"]), Q, K, V, smooth_k=o["smooth_k"],
+                       smooth_q=o["smooth_q"], seq_lens=lens)
+    compare_codes(cfg, z, ref)
+    out = torch.full((B, H, N, D), float("nan"), dtype=torch.float32, device="cuda")
+    ra.rotattn_int4_attention(shape, z, out, causal_block=o["causal"], symmetric_p=o["pmax"] == 7)
+    torch.cuda.synchronize()
+    ob = out.cpu().numpy()
+    for bh in range(B * H):
+        n = lens[bh // H] if lens is not None else N
+        rows = rows_sample(n, 12, seed=bh)
+        want = orc.attention(cfg, ref, rows=bh * N + rows, causal_block=o["causal"], pmax=o["pmax"])["out"]
+        assert_close(ob[bh // H, bh % H][rows], want)
+        assert np.isnan(ob[bh // H, bh % H, n:]).all()
+    for bh, r0 in ((0, 0), (B * H - 1, None)):
+        n = lens[bh // H] if lens is not None else N
+        r0 = max(0, n - 33) if r0 is None else 0
+        cnt = min(33, n - r0)
+        dbg = dict(bh=bh, row0=r0, n_rows=cnt)
+        out2 = torch.zeros_like(out)
+        ra.rotattn_int4_attention(shape, z, out2, debug=dbg, causal_block=o["causal"], symmetric_p=o["pmax"] == 7)
+        torch.cuda.synchronize()
+        od = orc.attention(cfg, ref, rows=np.arange(bh * N + r0, bh * N + r0 + cnt), dumps=True,
+                           causal_block=o["causal"], pmax=o["pmax"])
+        assert np.array_equal(dbg["p_codes"].cpu().numpy(), od["pcode"]), "P codes"
+        assert np.array_equal(dbg["a_pv"].cpu().numpy(), od["a_pv"]), "a_pv"
+        assert np.array_equal(out2.cpu().numpy()[bh // H, bh % H, r0:r0 + cnt], ob[bh // H, bh % H, r0:r0 + cnt])
+
+
+def test_empty_head_list_writes_nothing(orc):
+    cfg = synth.custom(1, 2, 2, 5, 7, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
+    Q, K, V = synth.make_inputs(cfg)
+    shape, z = gpu_quantize(cfg, 2, Q, K, V)
+    out = torch.full((1, 2, 70, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ra.rotattn_int4_attention(shape, z, out, heads=[])
+    tab = ra.rotattn_build_rope_table(shape, 0).cuda()
+    ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
+    ra.rotattn_fp16_fallback(shape, to_dev(Q), to_dev(K), to_dev(V), tab, out, ws, heads=[])
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
