@@ -173,6 +173,10 @@ rotattn_status rotattn_quantize_qk_ex(const rotattn_shape* s, rotattn_rot rot, r
  *   O_d  = 2^(m_{s-1}-m_s) O_d + sv_d sum_j (P~_ij + 8) vc_jd
  *   out  = O / l.
  * The rotation mode is not needed: an orthogonal R cancels in Q K^T.
+ * Work whose result is exactly nothing is skipped: 32-key tile pairs whose every
+ * level r is 0 add no P V products, and tiles whose every 2^y is below half an ulp
+ * of the running l would not change it.  The output is bit-identical to the dense
+ * evaluation, which the debug run performs (it skips nothing and dumps every code).
  *   heads/n_heads  host list of flat head ids b*H + h to compute; NULL = all.
  *   out_dtype      F32, F16 or BF16 (round to nearest even); out device [B,H,N,D];
  *                  rows of heads not listed are left untouched.

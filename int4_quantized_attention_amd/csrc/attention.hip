@@ -262,8 +262,8 @@ RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::
 }
 
 // One online-softmax step on tiles tb..tb+TPS-1 of group g (for kv_blk 16, the two
-// halves of tile tb as two steps): running max, lazy flush, P levels, P^T operand,
-// P V MFMAs.  MASK: the group holds keys at or past some row's limit (keys >= N,
+// halves of tile tb as two steps): running max, rescale, the exact skips, P levels,
+// P^T operand, P V MFMAs.  MASK: the group holds keys at or past some row's limit (keys >= N,
 // or keys a block-causal row does not see); they count as absent.  US: one K scale
 // for the whole step (qk_blk >= kv_blk), so the maximum needs one multiplication.
 template <int D, int KVB, bool DBG, bool MASK, bool US>
