@@ -18,7 +18,7 @@
 namespace ra {
 
 constexpr int kFbTile = 64;
-constexpr int kFbKV = 32;   // keys per online-softmax step
+constexpr int kFbKV = 64;   // keys per online-softmax step (and per LDS group)
 constexpr int kFbBM = 128;  // query rows per workgroup
 
 // grid (Np/64, B*H, 3): z = 0 Q, 1 K (RoPE -> f16), 2 V (transpose -> f16)
