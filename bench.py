@@ -43,7 +43,7 @@ def main():
                     help="block-causal attention with this block of tokens (0: bidirectional); the "
                          "operation count is then that of the visible query/key pairs")
     ap.add_argument("--smooth-q", action="store_true",
-                    help="Q smoothing as well (rotattn_quantize_qk_smooth_q and the per-key score term)")
+                    help="Q smoothing as well (rotattn_quantize_qk_ex with smooth_q set, and the per-key score term)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()

@@ -164,7 +164,7 @@ def rotattn_fp16_fallback_workspace(shape: Shape) -> int:
 
 def alloc_codes(shape: Shape, device="cuda", colsum: bool = True, smooth_q: bool = False) -> dict:
     """Output buffers of rotattn_quantize_qk (torch device tensors); smooth_q adds
-    k_bias [B,H,Np] f32 for rotattn_quantize_qk_smooth_q."""
+    k_bias [B,H,Np] f32 for Q smoothing (rotattn_quantize_qk_ex with smooth_q set)."""
     Np = rotattn_padded_tokens(shape)
     B, H, D = shape.B, shape.H, shape.D
     nkb = -(-shape.N // shape.kv_blk)
