@@ -141,32 +141,63 @@ __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
   // bytes at 16c and its last 8 bytes at D/2 + 8c (+8 in rows 8..15 and 24..31 of
   // each tile, which keeps the 8-byte reads of 16 consecutive rows on distinct banks), so that every lane
   // reads its operand with one 16-byte and one 8-byte load.
-  for (int u = threadIdx.x; u < G::TG * D / 32; u += 256) {
-    const int rho = u / (D / 32), c = u % (D / 32);
-    const int key = g * G::TG + (rho & ~31) + key_of_row(rho & 31);
-    const u32x4 w = *(const u32x4*)(args.kc + ((int64_t)bh * Np + key) * (D / 2) + 16 * c);
-    uint32_t o[6];
-    pack_fp6(w, o);
-    uint8_t* row = img + rho * G::KROW;
-    *(i32x4*)(row + 16 * c) = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-    *(u32x2*)(row + D / 2 + 8 * c + 8 * ((rho >> 3) & 1)) = u32x2{o[4], o[5]};
-  }
   // V^T: D rows x TG fp8 e4m3 values.  With steps of 64 or more keys, the 16-key
   // chunks of each 64-key segment are stored in the k order of one 64-deep MFMA:
   // position 32h + 16t' holds keys 32t' + 16h .. +15 (tile t' of the pair, lane
   // half h), so a lane half reads its 32 keys as one contiguous run.
-  for (int u = threadIdx.x; u < D * G::TG / 16; u += 256) {
-    const int d = u / (G::TG / 16), c = u % (G::TG / 16);
-    const u32x2 w = *(const u32x2*)(args.vc + ((int64_t)bh * D + d) * (Np / 2) + (g * G::TG + 16 * c) / 2);
-    i32x4 o;
+  // Every thread issues all of its 16-byte loads (K: one row chunk; V: 32 keys of
+  // one channel) before it converts and stores any of them.
+  constexpr int KU = G::TG * D / 32, KIT = (KU + 255) / 256;
+  constexpr int VU = D * G::TG / 32, VIT = (VU + 255) / 256;
+  u32x4 kw[KIT], vw[VIT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t x = q < 2 ? w.x : w.y;
-      const int e0 = 4 * (q & 1);
-      o[q] = (int)(fp8_pair(nib(x, e0), nib(x, e0 + 1)) | (fp8_pair(nib(x, e0 + 2), nib(x, e0 + 3)) << 16));
+  for (int i = 0; i < KIT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (KU % 256 == 0 || u < KU) {
+      const int rho = u / (D / 32), c = u % (D / 32);
+      const int key = g * G::TG + (rho & ~31) + key_of_row(rho & 31);
+      kw[i] = *(const u32x4*)(args.kc + ((int64_t)bh * Np + key) * (D / 2) + 16 * c);
     }
-    const int cq = KVB >= 64 ? (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1) : c;
-    *(i32x4*)(img + G::VOFF + d * G::VROW + 16 * cq) = o;
+  }
+#pragma unroll
+  for (int i = 0; i < VIT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (VU % 256 == 0 || u < VU) {
+      const int d = u / (G::TG / 32), c2 = u % (G::TG / 32);
+      vw[i] = *(const u32x4*)(args.vc + ((int64_t)bh * D + d) * (Np / 2) + (g * G::TG + 32 * c2) / 2);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KIT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (KU % 256 == 0 || u < KU) {
+      const int rho = u / (D / 32), c = u % (D / 32);
+      uint32_t o[6];
+      pack_fp6(kw[i], o);
+      uint8_t* row = img + rho * G::KROW;
+      *(i32x4*)(row + 16 * c) = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+      *(u32x2*)(row + D / 2 + 8 * c + 8 * ((rho >> 3) & 1)) = u32x2{o[4], o[5]};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < VIT; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    if (VU % 256 == 0 || u < VU) {
+      const int d = u / (G::TG / 32), c2 = u % (G::TG / 32);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int c = 2 * c2 + half;  // 16-key chunk
+        i32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t x = vw[i][2 * half + (q >> 1)];
+          const int e0 = 4 * (q & 1);
+          o[q] = (int)(fp8_pair(nib(x, e0), nib(x, e0 + 1)) | (fp8_pair(nib(x, e0 + 2), nib(x, e0 + 3)) << 16));
+        }
+        const int cq = KVB >= 64 ? (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1) : c;
+        *(i32x4*)(img + G::VOFF + d * G::VROW + 16 * cq) = o;
+      }
+    }
   }
   if (threadIdx.x < 17) ((float*)(img + G::TOFF))[threadIdx.x] = threadIdx.x < 15 ? args.T[threadIdx.x] : INFINITY;
   // Q smoothing: the keys' score terms in log2 units, delta_j = fl(dS_j * C0), in
