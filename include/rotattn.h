@@ -104,7 +104,10 @@ rotattn_status rotattn_build_rope_table(const rotattn_shape* s, rotattn_rot rot,
  *                                       codes in [-7, 7]
  *   v_scale           f32 [B,H,D]       per-channel amax/7 over all N tokens
  *   v_colsum          i32 [B,H,ceil(N/kv_blk),D] or NULL: per kv block sums of V
- *                                       codes (the zero-point term of P~ V)
+ *                                       codes, the zero-point term of P~ V for a
+ *                                       caller that dequantises P~ V itself
+ *                                       (rotattn_int4_attention does not read it:
+ *                                       its P operand is P~ + 8)
  * Binary32 op order (bit-reproducible): RoPE u = fma(a,c,-(b*s)), v = fma(a,s,b*c);
  * fused Interleaved o0 = fma(a,al,b*be), o1 = fma(a,be,-(b*al)); Half
  * o0 = (x1+x2)*r, o1 = (x1-x2)*r with r = (float)(1/sqrt2); Full (ablation): plain
@@ -114,7 +117,8 @@ rotattn_status rotattn_build_rope_table(const rotattn_shape* s, rotattn_rot rot,
  * of in-order 64-token partial sums, in block order, / N, rounded to binary32;
  * code = clamp(rint(x * (7/amax)), -7, 7), scale = amax/7 (IEEE division);
  * amax == 0 gives scale 0 and codes 0.
- * workspace: device, >= rotattn_quantize_qk_workspace(s) bytes. */
+ * workspace: device, >= rotattn_quantize_qk_workspace(s) bytes, scratch of the call
+ * (calls that may run at the same time need workspaces of their own). */
 size_t rotattn_quantize_qk_workspace(const rotattn_shape* s);
 rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
                                    const void* q, const void* k, const void* v,
@@ -177,7 +181,9 @@ rotattn_status rotattn_quantize_qk_ex(const rotattn_shape* s, rotattn_rot rot, r
  * level r is 0 add no P V products, and tiles whose every 2^y is below half an ulp
  * of the running l would not change it.  The output is bit-identical to the dense
  * evaluation, which the debug run performs (it skips nothing and dumps every code).
- *   heads/n_heads  host list of flat head ids b*H + h to compute; NULL = all.
+ *   heads/n_heads  host list of flat head ids b*H + h to compute; NULL = all.  A
+ *                  repeated id is computed once per listing, each time writing the
+ *                  same values.
  *   out_dtype      F32, F16 or BF16 (round to nearest even); out device [B,H,N,D];
  *                  rows of heads not listed are left untouched.
  *   dbg            NULL in production.  Otherwise a debug run for rows
@@ -191,8 +197,9 @@ rotattn_status rotattn_quantize_qk_ex(const rotattn_shape* s, rotattn_rot rot, r
  *                  listed heads' K and V codes restaged as the LDS image of fp6 K
  *                  rows and fp8 V^T rows (36 KiB per 128 keys for D = 128, about
  *                  288 bytes per padded token and head).  Contents need no
- *                  initialisation; a smaller size returns
- *                  ROTATTN_E_WORKSPACE before any launch.  Shapes whose images
+ *                  initialisation, and it is scratch of the call (calls that may
+ *                  run at the same time need workspaces of their own); a smaller
+ *                  size returns ROTATTN_E_WORKSPACE before any launch.  Shapes whose images
  *                  exceed 2^31 bytes per head (N beyond about 6.7 million tokens)
  *                  return ROTATTN_E_UNSUPPORTED. */
 typedef struct {
