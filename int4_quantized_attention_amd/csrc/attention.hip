@@ -81,7 +81,7 @@ struct Geo {
   // bytes per K row: packed codes + pad, a multiple of 16 that is not a multiple
   // of 32 dwords' worth of banks for eight consecutive rows
   static constexpr int KROW = (KB + 16) / 4 % 8 == 0 ? KB + 32 : KB + 16;
-  static constexpr int VROW = TG + 16;            // bytes per V^T row (int8 + pad)
+  static constexpr int VROW = TG + 16;            // bytes per V^T row (fp8 + pad)
   static constexpr int VOFF = TG * KROW;          // V^T rows start here
   static constexpr int TOFF = VOFF + D * VROW;    // 17 floats of level thresholds
   static constexpr int DOFF = TOFF + 128;        // TG floats: per-key score terms (Q smoothing)

@@ -7,7 +7,6 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -18,43 +17,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 
 namespace ra {
-
-// ---- input element loads --------------------------------------------------------
-template <int DT> RA_DEV float load_elem(const void* p, int64_t i);
-template <> RA_DEV float load_elem<0>(const void* p, int64_t i) { return ((const float*)p)[i]; }
-template <> RA_DEV float load_elem<1>(const void* p, int64_t i) {
-  return (float)((const _Float16*)p)[i];
-}
-template <> RA_DEV float load_elem<2>(const void* p, int64_t i) {
-  uint32_t b = (uint32_t)((const uint16_t*)p)[i] << 16;
-  return __uint_as_float(b);
-}
-
-// ---- nibble widening ------------------------------------------------------------
-// A dword holds 8 two's-complement nibbles n0..n7 (n0 in bits 0-3).  "Biased"
-// widening gives the offset-binary bytes n_i + 8 in [0, 15]:
-//   lo = bytes (n0, n2, n4, n6) + 8,  hi = bytes (n1, n3, n5, n7) + 8.
-RA_DEV void widen_biased(uint32_t x, uint32_t& lo, uint32_t& hi) {
-  const uint32_t y = x ^ 0x88888888u;
-  lo = y & 0x0F0F0F0Fu;
-  hi = (y >> 4) & 0x0F0F0F0Fu;
-}
-// Signed widening: the same byte order, bytes sign-extended to int8.
-// Per byte v in [0, 15]: (v + 0x78) ^ 0x78 equals v for v < 8 and v - 16 (mod 256)
-// for v >= 8; v + 0x78 <= 0x87 never carries into the next byte.
-RA_DEV void widen_signed(uint32_t x, uint32_t& lo, uint32_t& hi) {
-  const uint32_t a = x & 0x0F0F0F0Fu, b = (x >> 4) & 0x0F0F0F0Fu;
-  lo = (a + 0x78787878u) ^ 0x78787878u;
-  hi = (b + 0x78787878u) ^ 0x78787878u;
-}
-// Widening into the high nibble: the same byte order, each byte holding 16 c as an
-// int8 (a two's-complement nibble shifted up by four is 16 times its value).  Three
-// bit operations per 8 nibbles; the factor 16 is a power of two and is divided out
-// exactly wherever the sums are scaled.
-RA_DEV void widen_x16(uint32_t x, uint32_t& lo, uint32_t& hi) {
-  lo = (x << 4) & 0xF0F0F0F0u;
-  hi = x & 0xF0F0F0F0u;
-}
 
 // ---- wave reductions ------------------------------------------------------------
 RA_DEV float wave_max(float v, int width) {
