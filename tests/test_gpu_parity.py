@@ -155,6 +155,30 @@ def test_head_subset_leaves_other_heads(orc):
     assert_close(o[0, 3], full[0, 3])
 
 
+def test_quantize_without_column_sums():
+    """The V column sums are optional (the benchmark passes NULL for them): every other
+    output of the quantiser, padding included, and the attention on it are
+    bit-identical with and without them."""
+    cfg = synth.custom(1, 2, 3, 17, 23, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
+    Q, K, V = synth.make_inputs(cfg)
+    shape = ra.Shape.of(cfg)
+    q, k, v = (to_dev(x, torch.float16) for x in (Q, K, V))
+    tab = ra.rotattn_build_rope_table(shape, 2).cuda()
+    runs = []
+    for colsum in (True, False):
+        z = ra.alloc_codes(shape, colsum=colsum)
+        ra.rotattn_quantize_qk(shape, 2, q, k, v, tab, True, z)
+        out = torch.empty((1, 2, synth.n_tokens(cfg), 128), dtype=torch.float32, device="cuda")
+        ra.rotattn_int4_attention(shape, z, out)
+        torch.cuda.synchronize()
+        runs.append((z, out))
+    (za, oa), (zb, ob) = runs
+    assert za["v_colsum"] is not None and zb["v_colsum"] is None
+    for key in ("q_codes", "q_scale", "k_codes", "k_scale", "v_codes", "v_scale"):
+        assert torch.equal(za[key], zb[key]), key
+    assert torch.equal(oa, ob)
+
+
 CAUSAL = [
     # (id, config overrides, causal block): token-causal, frame-causal (one frame is
     # 391 tokens, so tiles straddle frames), a block that does not divide N, a block
