@@ -155,6 +155,29 @@ def test_head_subset_leaves_other_heads(orc):
     assert_close(o[0, 3], full[0, 3])
 
 
+def test_more_heads_than_one_launch(orc):
+    """B*H above the per-launch head limit (512): the INT4 attention and the fallback
+    are split into several launches and every head is computed (heads on both sides
+    of the split are checked against the oracle)."""
+    cfg = synth.custom(1, 520, 1, 2, 16, 64, 24, 20, 20, 16, 16, dtype="float32", recipe="tiny", rot="half")
+    N, D = synth.n_tokens(cfg), 64
+    Q, K, V = synth.make_inputs(cfg)
+    shape, z = gpu_quantize(cfg, 2, Q, K, V)
+    out = torch.empty((1, 520, N, D), dtype=torch.float32, device="cuda")
+    ra.rotattn_int4_attention(shape, z, out)
+    q, k, v = (to_dev(x) for x in (Q, K, V))
+    tab0 = ra.rotattn_build_rope_table(shape, 0).cuda()
+    ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
+    out_fb = torch.empty((1, 520, N, D), dtype=torch.float32, device="cuda")
+    ra.rotattn_fp16_fallback(shape, q, k, v, tab0, out_fb, ws)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(h * N, (h + 1) * N) for h in (0, 511, 512, 519)])
+    ref = orc.quantize(cfg, 2, orc.rope_table(cfg, 2), Q, K, V)
+    assert_close(out.cpu().numpy().reshape(-1, D)[rows], orc.attention(cfg, ref, rows=rows)["out"])
+    want_fb = orc.fallback_attention(cfg, orc.rope_table(cfg, 0), Q, K, V, rows=rows)
+    assert_close(out_fb.cpu().numpy().reshape(-1, D)[rows], want_fb)
+
+
 def test_quantize_without_column_sums():
     """The V column sums are optional (the benchmark passes NULL for them): every other
     output of the quantiser, padding included, and the attention on it are
