@@ -151,9 +151,10 @@ def main():
         "dtype": "int4",
         "data": "synthetic",
         "config": {"workload": "%s: B=%d H=%d grid %dx%dx%d N=%d D=%d "
-                               "(%d/%d/%d), %s rotation, qk_blk=%d kv_blk=%d, fp16 in/out%s"
+                               "(%d/%d/%d), %s rotation, qk_blk=%d kv_blk=%d, %s%s"
                                % (WORKLOADS.get(args.config, args.config), B, H, cfg["F"], cfg["Hs"], cfg["Ws"], N,
                                   D, cfg["Df"], cfg["Dh"], cfg["Dw"], cfg["rot"], cfg["qk_blk"], cfg["kv_blk"],
+                                  io_label(cfg["dtype"]),
                                   (", block-causal c=%d (ops of visible pairs)" % args.causal if args.causal else "")
                                   + (", Q smoothing" if args.smooth_q else "")),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
@@ -189,6 +190,12 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, rot, causal=args.causal)
     print(json.dumps(result))
+
+
+def io_label(dtype: str) -> str:
+    """Input and output types of the workload (the output is always fp16)."""
+    short = {"float16": "fp16", "float32": "fp32", "bfloat16": "bf16"}[dtype]
+    return "fp16 in/out" if short == "fp16" else "%s in, fp16 out" % short
 
 
 def counted_traffic():
