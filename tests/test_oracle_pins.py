@@ -319,10 +319,81 @@ def test_attention_within_rounding_bound_of_exact_softmax(orc, kv):
     S = A * sq[:, :, None] * sk[:, None, :] / math.sqrt(D)
     P = np.exp(S - S.max(axis=2, keepdims=True))
     exact = np.einsum("hij,hjd->hid", P / P.sum(axis=2, keepdims=True), V).reshape(-1, D)
-    bound = 0.5 * np.abs(V).sum(axis=1)[:, None, :].repeat(N, axis=1).reshape(-1, D) / r["l"][:, None]
+    # the normaliser of the definition, 15 sum_j P_ij (P against the row maximum),
+    # computed here rather than read back from the oracle
+    l_def = 15.0 * P.sum(axis=2).reshape(-1)
+    bound = 0.5 * np.abs(V).sum(axis=1)[:, None, :].repeat(N, axis=1).reshape(-1, D) / l_def[:, None]
     assert np.all(np.abs(r["out"] - exact) <= bound * (1 + 1e-5) + 1e-9)
     cos = np.sum(r["out"] * exact) / np.linalg.norm(r["out"]) / np.linalg.norm(exact)
     assert cos > 0.95
+
+
+def _definition_attention(z, N, D, qk_blk, kv):
+    """The method's quantised attention written out in binary64 numpy, from the
+    definition rather than from the oracle's steps (papernotes.org note, Key design
+    2: P = exp(S - m) with m the running row maximum, level round(15 P), zero point
+    folded; the normaliser is the plain softmax sum of the unquantised P).
+    Returns (level, weight, l, x) per [head, row, key]: the exact level of 15 P
+    against the running maximum of its kv-step, the rescale 2^(m_s - m) of its
+    step, the normaliser 15 sum_j 2^(S_j - max S) and the unrounded 15 P."""
+    BH = z["qc"].shape[0] * z["qc"].shape[1]
+    sq = np.repeat(z["qs"].astype(np.float64), qk_blk, axis=2).reshape(BH, -1)[:, :N]
+    sk = np.repeat(z["ks"].astype(np.float64), qk_blk, axis=2).reshape(BH, -1)[:, :N]
+    A = np.einsum("hid,hjd->hij", z["qc"].reshape(BH, N, D).astype(np.int64),
+                  z["kc"].reshape(BH, N, D).astype(np.int64)).astype(np.float64)
+    S2 = A * sq[:, :, None] * sk[:, None, :] * (math.log2(math.e) / math.sqrt(D))  # log2 units
+    S = -(-N // kv)
+    step_max = np.stack([S2[:, :, s * kv:(s + 1) * kv].max(axis=2) for s in range(S)], axis=2)
+    m_run = np.maximum.accumulate(step_max, axis=2)           # running maximum after each step
+    m_key = np.repeat(m_run, kv, axis=2)[:, :, :N]            # the maximum a key's level sees
+    x = 15.0 * np.exp2(S2 - m_key)                             # 15 P against the running maximum
+    level = np.minimum(np.rint(x), 15.0)                       # numpy rint: round half to even
+    weight = np.exp2(m_key - m_run[:, :, -1:])                 # later rescales of the key's step
+    l = 15.0 * np.exp2(S2 - S2.max(axis=2, keepdims=True)).sum(axis=2)
+    return level, weight, l, x
+
+
+@pytest.mark.parametrize("kv,lo,hi", [(16, 0.5, 1.0), (64, 0.5, 1.0), (16, 0.15, 0.4), (64, 0.15, 0.4)])
+def test_normaliser_codes_and_output_against_definition(orc, kv, lo, hi):
+    """Peaked scores (lossless codes, Q/K scales in [lo, hi]: score spreads of 1.5 to
+    10 nat, so most levels are 0 while 15 P is not): the oracle's normaliser l, its
+    P codes and its output against the definition evaluated here in binary64
+    (_definition_attention).  l must be the sum of the unquantised 15 P (a sum of
+    the levels, or a missing rescale, is off by far more than the 5e-5 allowed for
+    the binary32 score pipeline).  Codes must equal round(15 P) against the running
+    maximum except for keys whose 15 P lies within 1e-4 (relative) of a rounding
+    boundary, where the binary32 exponent may fall on either side; each such key
+    widens the output bound by its |v| weight."""
+    rng = np.random.default_rng(23 + kv)
+    B, H, F, Hs, Ws, D = 1, 2, 4, 8, 8, 64
+    cfg = synth.custom(B, H, F, Hs, Ws, D, 24, 20, 20, 16, kv)
+    N = F * Hs * Ws
+    z = dict(qc=_ints(rng, (B, H, N, D)), kc=_ints(rng, (B, H, N, D)), vc=_ints(rng, (B, H, N, D)),
+             qs=rng.uniform(lo, hi, (B, H, N // 16)).astype(np.float32),
+             ks=rng.uniform(lo, hi, (B, H, N // 16)).astype(np.float32),
+             vs=rng.uniform(0.5, 1, (B, H, D)).astype(np.float32))
+    r = orc.attention(cfg, z, dumps=True)
+    level, weight, l, x = _definition_attention(z, N, D, 16, kv)
+    level, weight, x = (a.reshape(B * H * N, N) for a in (level, weight, x))
+    l = l.reshape(-1)
+    # normaliser
+    assert np.allclose(r["l"], l, rtol=5e-5, atol=0)
+    # codes: exact except at rounding boundaries
+    ambiguous = np.abs(x - (np.floor(x) + 0.5)) <= 1e-4 * np.maximum(x, 0.5)
+    got = r["pcode"].astype(np.int64) + 8
+    assert np.array_equal(got[~ambiguous], level[~ambiguous])
+    assert np.all(np.abs(got - level) <= 1)
+    assert ambiguous.mean() < 1e-3
+    # output: sum_j level_j weight_j sv vc_j / l, from the definition
+    V = _dequant_v(z).reshape(B * H, N, D)
+    Vrow = np.repeat(V, N, axis=0)                            # [rows, keys, D] of each row's head
+    want = np.einsum("rj,rjd->rd", level * weight, Vrow) / l[:, None]
+    slack = np.einsum("rj,rjd->rd", ambiguous * weight, np.abs(Vrow)) / l[:, None]
+    scale = np.einsum("rj,rjd->rd", level * weight, np.abs(Vrow)) / l[:, None]
+    assert np.all(np.abs(r["out"] - want) <= slack + 1e-4 * scale + 1e-12)
+    # the levels are far from the unquantised P here: summing them instead of 15 P
+    # would move l of some rows by much more than the tolerance above
+    assert np.max(np.abs((level * weight).sum(axis=1) - l) / l) > 1e-2
 
 
 def test_attention_key_permutation_within_step_and_v_scaling(orc):
@@ -620,7 +691,10 @@ def test_k_bias_attention_within_rounding_bound(orc, kv):
     S = (A * sq[:, :, None] * sk[:, None, :] + z["k_bias"].reshape(B * H, 1, N)) / math.sqrt(D)
     P = np.exp(S - S.max(axis=2, keepdims=True))
     exact = np.einsum("hij,hjd->hid", P / P.sum(axis=2, keepdims=True), V).reshape(-1, D)
-    bound = 0.5 * np.abs(V).sum(axis=1)[:, None, :].repeat(N, axis=1).reshape(-1, D) / r["l"][:, None]
+    # the normaliser of the definition, 15 sum_j P_ij (P against the row maximum),
+    # computed here rather than read back from the oracle
+    l_def = 15.0 * P.sum(axis=2).reshape(-1)
+    bound = 0.5 * np.abs(V).sum(axis=1)[:, None, :].repeat(N, axis=1).reshape(-1, D) / l_def[:, None]
     assert np.all(np.abs(r["out"] - exact) <= bound * (1 + 1e-5) + 1e-9)
     # the bias matters here: without it the output is far outside the bound
     z0 = dict(z)
