@@ -18,6 +18,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+PEAK_FP8_TOPS = 5000.0    # MI355X dense fp8 MFMA (the P V form the attention issues)
+PEAK_FP6_TOPS = 10100.0   # MI355X dense fp6 MFMA (the Q K^T form the attention issues)
 CONFIG = "wan720p"
 WORKLOADS = {
     "wan480p": "Wan-1.3B-480p-like attention layer",
@@ -46,6 +48,8 @@ def main():
                     help="Q smoothing as well (rotattn_quantize_qk_ex with smooth_q set, and the per-key score term)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--no-diffuse", action="store_true",
+                    help="skip the second attention timing on the diffuse (skip-free) recipe")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on exactly one GPU (the path shards by head with no "
@@ -126,6 +130,8 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    stats = skip_stats(lambda st: ra.rotattn_int4_attention(shape, z, out, heads=q4_heads, causal_block=args.causal,
+                                                            skip_stats=st))
     k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     k3_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) if mixed else None
@@ -136,6 +142,7 @@ def main():
     # and the scales: 3*2 + 3*0.5 bytes per element.
     k1_bytes = (3 * 2.0 + 3 * 0.5) * N * D * H * B
     k2_tops = ops_q4 / (k2_ms * 1e-3) / 1e12
+    headline = args.config == CONFIG and not (args.kv or args.qk or args.rot or args.causal or args.smooth_q)
 
     result = {
         "metric": "effective attention TOPS (4*N^2*D*H/s) at Wan-720p-like shape; % int8 MFMA peak",
@@ -158,11 +165,12 @@ def main():
                                   (", block-causal c=%d (ops of visible pairs)" % args.causal if args.causal else "")
                                   + (", Q smoothing" if args.smooth_q else "")),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "k2_attention (rotattn_int4_attention)",
-                     "achieved": round(k2_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                     "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
-                     "traffic": counted_traffic() if args.config == CONFIG and not (args.kv or args.qk or args.rot or args.causal
-                                                                                   or args.smooth_q) else None},
+        "roofline": dict({"bound": "mfma", "kernel": "k2_attention (rotattn_int4_attention)",
+                          "achieved": round(k2_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                          "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
+                          "traffic": counted_traffic() if headline else None},
+                         **issued_mfma(ops_q4, k2_ms, stats), **(counted_limiter() if headline else {})),
+        "skips": stats,
         "kernels_ms": dict({"quantize_qk": round(k1_ms, 4), "int4_attention": round(k2_ms, 4)},
                            **({"fp16_fallback_even_heads": round(k3_ms, 4)} if mixed else {})),
         "quantize_qk_GBps": round(k1_bytes / (k1_ms * 1e-3) / 1e9, 1),
@@ -187,9 +195,88 @@ def main():
                               "frac_f16_peak": round(fb_tops / PEAK_F16_TFLOPS, 4),
                               "int4_attention_speedup": round(fb_ms / k2_ms, 3)}
 
+    if headline and not args.no_diffuse:
+        result["diffuse"] = diffuse_floor(shape, rot, q, k, v, tab, z, out, ops, stream)
+
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, rot, causal=args.causal)
     print(json.dumps(result))
+
+
+def skip_stats(run) -> dict:
+    """One untimed attention call with the skip counters: the share of P V units
+    skipped because every level is 0, of score tiles whose exps were skipped (below
+    half an ulp of l), and of units that took the exact-level path."""
+    import torch
+    st = torch.zeros(5, dtype=torch.int64, device="cuda")
+    run(st)
+    torch.cuda.synchronize()
+    n = [int(x) for x in st.cpu().tolist()]
+    return {"pv_units": n[0], "pv_units_skipped_frac": round(n[1] / max(n[0], 1), 4),
+            "exp_tiles_skipped_frac": round(n[3] / max(n[2], 1), 4),
+            "exact_path_frac": round(n[4] / max(n[0], 1), 6)}
+
+
+def issued_mfma(ops, ms, stats) -> dict:
+    """The attention's time against the peaks of the MFMA forms it issues: Q K^T on
+    fp6 (every score tile is computed) and P V on fp8 (the units not skipped).
+    dense_frac prices all of the algorithmic work at those peaks; issued_frac prices
+    the work actually issued (roughly the MFMA pipe's busy share)."""
+    qk, pv = ops / 2, ops / 2
+    t_dense = qk / (PEAK_FP6_TOPS * 1e12) + pv / (PEAK_FP8_TOPS * 1e12)
+    t_issued = qk / (PEAK_FP6_TOPS * 1e12) + pv * (1 - stats["pv_units_skipped_frac"]) / (PEAK_FP8_TOPS * 1e12)
+    t = ms * 1e-3
+    return {"issued_forms": "QK^T fp6 at %.1f PF, PV fp8 at %.1f PF" % (PEAK_FP6_TOPS / 1e3, PEAK_FP8_TOPS / 1e3),
+            "dense_frac_at_issued_peaks": round(t_dense / t, 4), "issued_frac_at_issued_peaks": round(t_issued / t, 4)}
+
+
+def diffuse_floor(shape, rot, q, k, v, tab, z, out, ops, stream) -> dict:
+    """The attention on the same shape with the diffuse recipe (no outlier channels,
+    unit-variance logits: flat softmax rows, no all-zero units), the floor when the
+    exact skips find nothing to skip.  Reuses the input and code buffers."""
+    import numpy as np
+    import torch
+    from int4_quantized_attention_amd import rotattn as ra
+    from int4_quantized_attention_amd import synth
+    Q, K, V = synth.make_inputs(synth.CONFIGS["wan720p_diffuse"])
+    for dst, src in ((q, Q), (k, K), (v, V)):
+        dst.copy_(torch.from_numpy(src))
+    del Q, K, V
+    ra.rotattn_quantize_qk(shape, rot, q, k, v, tab, True, z)
+    ra.rotattn_int4_attention(shape, z, out)
+    torch.cuda.synchronize()
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        ra.rotattn_int4_attention(shape, z, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tops = ops / (ms * 1e-3) / 1e12
+    st = skip_stats(lambda s: ra.rotattn_int4_attention(shape, z, out, skip_stats=s))
+    return {"recipe": "diffuse: Q, K ~ N(0,1) without outlier channels, V N(0,1) Hadamard-rotated (flat softmax)",
+            "int4_attention_ms": round(ms, 3), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
+            "skips": st, **issued_mfma(ops, ms, st)}
+
+
+def counted_limiter() -> dict:
+    """What limits k2_attention, from the committed SQ counter summary (VALU active
+    vs MFMA busy share of the launch), or nothing when the attention source has
+    changed since the counters were taken."""
+    summ = os.path.join(ROOT, "profiles", "k2_attention_wan720p_sq_counters.md")
+    try:
+        text = open(summ).read()
+        cur = attention_source_sha()
+    except OSError:
+        return {}
+    f = dict(l.split(":", 1) for l in text.splitlines()
+             if l.startswith(("valu_active_frac:", "mfma_busy_frac:", "attention_source_sha256_16:")))
+    if f.get("attention_source_sha256_16", "").strip() != cur or "valu_active_frac" not in f:
+        return {}
+    valu, mfma = float(f["valu_active_frac"]), float(f["mfma_busy_frac"])
+    return {"limiter": "valu" if valu > mfma else "mfma",
+            "counters": {"valu_active_frac": valu, "mfma_busy_frac": mfma}}
 
 
 def io_label(dtype: str) -> str:
@@ -198,16 +285,27 @@ def io_label(dtype: str) -> str:
     return "fp16 in/out" if short == "fp16" else "%s in, fp16 out" % short
 
 
+ATTENTION_SOURCES = ("attention_impl.h", "attention.hip", "attention_inst.hip")
+
+
+def attention_source_sha() -> str:
+    """First 16 hex digits of the sha256 of the K2 sources, concatenated in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTENTION_SOURCES:
+        with open(os.path.join(ROOT, "int4_quantized_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def counted_traffic():
     """HBM bytes per k2_attention launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), or None when
     the attention source has changed since the counters were taken."""
-    import hashlib
-    src = os.path.join(ROOT, "int4_quantized_attention_amd", "csrc", "attention.hip")
     summ = os.path.join(ROOT, "profiles", "wan720p_hbm_counters.md")
     try:
         text = open(summ).read()
-        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        cur = attention_source_sha()
     except OSError:
         return None
     fields = dict(l.split(":", 1) for l in text.splitlines()

@@ -23,13 +23,16 @@
  *   - Errors: arguments are validated on the host before any launch; a bad
  *     argument returns a status without touching the GPU.  A launch failure
  *     returns ROTATTN_E_HIP.  Nothing is thrown across the ABI.
- *   - Thread safety: no mutable global state; calls are reentrant.
+ *   - Thread safety: no mutable global state; calls are reentrant.  (The P level
+ *     threshold table is built once, on first use, with thread-safe static
+ *     initialisation and never changes; kernels' LDS limits are set on each call.)
  *   - Layouts are C-contiguous.  Token n of a head sits at RoPE position
  *     (f, y, x) with n = (f*Hs + y)*Ws + x.  Code tensors are padded to
  *     Np = rotattn_padded_tokens() tokens; padding codes and scales are zero.
  *   - Supported: D in {64, 128}; Df, Dh, Dw even and summing to D;
- *     qk_blk in {16, 32, 64, 128}; kv_blk in {16, 32, 64, 128} with
- *     qk_blk <= max(kv_blk, 32) ... see rotattn_check_shape(); N >= 1.
+ *     qk_blk a power of two in [1, 128] (1 = per-token Q/K scales, the
+ *     granularity of the paper.gecl.asia analysis, "Key Insight"); kv_blk a power
+ *     of two in [16, 256]; any N >= 1 (see rotattn_check_shape()).
  */
 #ifndef ROTATTN_H_
 #define ROTATTN_H_
@@ -272,6 +275,13 @@ rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
  *                 with): a row of batch element b sees only its first seq_lens[b]
  *                 keys, and its rows past them are left untouched (debug rows must
  *                 lie below it).  B > 64 returns ROTATTN_E_UNSUPPORTED.
+ *   skip_stats    NULL, or device u64 [5], 8-byte aligned, that the production run
+ *                 adds its counts of the exact skips to (the caller clears it):
+ *                 [0] P V units (one P V MFMA decision: 64 keys x 32 rows, or 32
+ *                 keys for kv_blk <= 32), [1] those skipped because every level is
+ *                 0, [2] 32 x 32 score tiles, [3] tiles whose exps were skipped as
+ *                 below half an ulp of l, [4] units whose levels took the exact
+ *                 threshold path.  The counts depend on the data, not on timing.
  * Debug dumps leave the entries of keys a row does not see, and its steps past the
  * query tile's last key, unwritten: fill them first to compare whole arrays.
  * opts NULL is all defaults.  Every other argument, layout, workspace and error as
@@ -281,6 +291,7 @@ typedef struct {
   int32_t causal_block;
   const float* k_bias;
   const int32_t* seq_lens;
+  uint64_t* skip_stats;
 } rotattn_attention_opts;
 
 rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
@@ -308,6 +319,19 @@ rotattn_status rotattn_fp16_fallback_ex(const rotattn_shape* s, rotattn_dtype in
                                         const rotattn_fallback_opts* opts,
                                         rotattn_dtype out_dtype, void* out,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- rotattn_p_level_probe: the P level decision of rotattn_int4_attention -----
+ * For tests of the level function (Key design 2: r = round-half-even(15 P), written
+ * with y = log2(15 P) as r = round-half-even(2^y) in [0, 15]).  For the binary32
+ * exponents y_i whose bit patterns are first_bits + i, i < n, writes (device u8)
+ *   out[i] = r_i | (x_i << 4)
+ * where r_i is the level as the attention decides it for a key (the hardware-exp2
+ * level when its rounding margin is clear, else the exact threshold fix) and x_i
+ * the exact threshold fix alone (the attention applies it to every key of a unit
+ * with any unclear margin).  Both must equal round-half-even(2^y_i) for every y the
+ * attention forms, i.e. y up to L15 + 2^-5.  first_bits + n > 2^32 or n < 0 returns
+ * ROTATTN_E_ARG. */
+rotattn_status rotattn_p_level_probe(uint32_t first_bits, int64_t n, uint8_t* out, void* stream);
 
 const char* rotattn_status_str(rotattn_status st);
 

@@ -21,25 +21,31 @@ OUT = os.path.join(HERE, "librotattn.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.cpp", "quantize.hip", "attention.hip", "fallback.hip"]
+# the K2 kernels: attention_inst.hip once per (head dimension, kv step), in parallel
+ATT_INSTANCES = [(d, kv) for d in (128, 64) for kv in (64, 128, 256, 32, 16)]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, defines, tag = job
+    obj = os.path.join(BUILD, src + tag + ".o")
+    cmd = [HIPCC] + FLAGS + defines + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed on %s" % src)
+        raise RuntimeError("hipcc failed on %s %s" % (src, " ".join(defines)))
     return obj
 
 
 def build() -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    jobs = [("attention_inst.hip", ["-DATT_D=%d" % d, "-DATT_KVB=%d" % kv], ".d%d_kv%d" % (d, kv))
+            for d, kv in ATT_INSTANCES] + [(src, [], "") for src in SOURCES]
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(_compile, jobs))
     tmp = OUT + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -66,7 +66,7 @@ rotattn_status rotattn_check_shape(const rotattn_shape* s) {
   if (s->Df < 2 || s->Dh < 2 || s->Dw < 2 || (s->Df | s->Dh | s->Dw) & 1) return ROTATTN_E_SHAPE;
   if (s->Df + s->Dh + s->Dw != s->D) return ROTATTN_E_SHAPE;
   if (s->D != 64 && s->D != 128) return ROTATTN_E_UNSUPPORTED;
-  if (!pow2_in(s->qk_blk, 16, 128) || !pow2_in(s->kv_blk, 16, 128)) return ROTATTN_E_UNSUPPORTED;
+  if (!pow2_in(s->qk_blk, 1, 128) || !pow2_in(s->kv_blk, 16, 256)) return ROTATTN_E_UNSUPPORTED;
   const int64_t N = tokens(s);
   if (N > (int64_t)1 << 28) return ROTATTN_E_UNSUPPORTED;
   if ((int64_t)s->B * s->H > 65535) return ROTATTN_E_UNSUPPORTED;
@@ -215,7 +215,7 @@ rotattn_status rotattn_quantize_qk_ex(const rotattn_shape* s, rotattn_rot rot, r
 
 size_t rotattn_int4_attention_workspace(const rotattn_shape* s) {
   if (!s || rotattn_check_shape(s) != ROTATTN_OK) return 0;
-  return ra::attention_workspace_bytes(s->D, s->kv_blk, (int64_t)s->B * s->H, rotattn_padded_tokens(s));
+  return ra::attention_workspace_bytes(s->D, s->kv_blk, s->qk_blk, (int64_t)s->B * s->H, rotattn_padded_tokens(s));
 }
 
 namespace {
@@ -229,7 +229,7 @@ rotattn_status attention_call(const rotattn_shape* s,
                               rotattn_dtype out_dtype, void* out,
                               const rotattn_debug* dbg,
                               void* workspace, size_t workspace_bytes, void* stream, int pmax, int causal,
-                              const float* k_bias, const int32_t* seq_lens) {
+                              const float* k_bias, const int32_t* seq_lens, uint64_t* skip_stats) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
   if (causal < 0 || (pmax != 15 && pmax != 7)) return ROTATTN_E_ARG;
@@ -240,6 +240,7 @@ rotattn_status attention_call(const rotattn_shape* s,
   if (workspace_bytes < rotattn_int4_attention_workspace(s) || ((uintptr_t)workspace & 15) != 0)
     return ROTATTN_E_WORKSPACE;
   if (out_dtype < ROTATTN_F32 || out_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
+  if (((uintptr_t)skip_stats & 7) != 0) return ROTATTN_E_ARG;
   const int BH = s->B * s->H;
   if (heads) {
     if (n_heads < 0) return ROTATTN_E_ARG;
@@ -263,6 +264,7 @@ rotattn_status attention_call(const rotattn_shape* s,
   a.p_zero = pmax == 15 ? 8 : 0;
   a.causal = causal < N ? causal : 0;  // a block of N or more keys is every key
   a.kbias = k_bias;
+  a.stats = (unsigned long long*)skip_stats;
   a.H = s->H;
   const rotattn_status ls = set_lens(s, seq_lens, a.nlens, a.lens);
   if (ls != ROTATTN_OK) return ls;
@@ -303,7 +305,7 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
                                       const rotattn_debug* dbg,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
-                        dbg, workspace, workspace_bytes, stream, 15, 0, nullptr, nullptr);
+                        dbg, workspace, workspace_bytes, stream, 15, 0, nullptr, nullptr, nullptr);
 }
 
 rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
@@ -315,7 +317,7 @@ rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
                                                   const rotattn_debug* dbg,
                                                   void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
-                        dbg, workspace, workspace_bytes, stream, 7, 0, nullptr, nullptr);
+                        dbg, workspace, workspace_bytes, stream, 7, 0, nullptr, nullptr, nullptr);
 }
 
 rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
@@ -330,7 +332,8 @@ rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
   const int pmax = opts && opts->p_max ? opts->p_max : 15;
   return attention_call(s, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads, n_heads, out_dtype, out,
                         dbg, workspace, workspace_bytes, stream, pmax, opts ? opts->causal_block : 0,
-                        opts ? opts->k_bias : nullptr, opts ? opts->seq_lens : nullptr);
+                        opts ? opts->k_bias : nullptr, opts ? opts->seq_lens : nullptr,
+                        opts ? opts->skip_stats : nullptr);
 }
 
 size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s) {
@@ -399,6 +402,13 @@ rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dt
                                      void* workspace, size_t workspace_bytes, void* stream) {
   return rotattn_fp16_fallback_ex(s, in_dtype, q, k, v, rope_table, heads, n_heads, nullptr, out_dtype, out,
                                   workspace, workspace_bytes, stream);
+}
+
+rotattn_status rotattn_p_level_probe(uint32_t first_bits, int64_t n, uint8_t* out, void* stream) {
+  if (!out) return ROTATTN_E_NULL;
+  if (n < 0 || (uint64_t)first_bits + (uint64_t)n > ((uint64_t)1 << 32)) return ROTATTN_E_ARG;
+  if (n == 0) return ROTATTN_OK;
+  return launch_status(ra::launch_level_probe(first_bits, n, out, levels().T, (hipStream_t)stream));
 }
 
 const char* rotattn_status_str(rotattn_status st) {

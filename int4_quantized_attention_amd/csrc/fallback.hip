@@ -287,7 +287,7 @@ hipError_t launch_fallback_prep(const FbArgs& a, int dtype, hipStream_t st) {
 template <int D>
 hipError_t launch_fb_t(const FbArgs& a, hipStream_t st) {
   using G = FbGeo<D>;
-  static const hipError_t attr = hipFuncSetAttribute((const void*)k3_attention<D>,
+  const hipError_t attr = hipFuncSetAttribute((const void*)k3_attention<D>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   if (attr != hipSuccess) return attr;
   k3_attention<D><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);

@@ -62,6 +62,7 @@ struct AttnArgs {
   int nlens;           // 0, or B: lens[b] tokens of batch element b exist
   int lens[kMaxBatch];
   float T[16];  // P level thresholds (15 used)
+  unsigned long long* stats;  // nullable device u64[5]: skip counters, added to
   // debug (rows [dbg_row0, dbg_row0 + dbg_n) of the single listed head)
   int dbg_row0, dbg_n;
   int32_t* dbg_aqk;
@@ -94,11 +95,19 @@ struct FbArgs {
   int heads[kMaxHeads];
 };
 
+struct LevelTable {
+  float T[17];  // the 15 P level thresholds, then +inf, +inf
+};
+
 hipError_t launch_quantize(const QuantArgs& a, int dtype, hipStream_t st);
+// out[i] = the attention's P level decision for y = bits first + i (low nibble) and
+// the exact fix alone (high nibble), i < n
+hipError_t launch_level_probe(uint32_t first, int64_t n, uint8_t* out, const float* thresholds15,
+                              hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int D, int kv_blk, bool dbg, hipStream_t st);
 // bytes of the attention workspace: the per-group LDS images of every head (the
-// image geometry lives with the kernel; D, kv_blk as validated by the API)
-size_t attention_workspace_bytes(int D, int kv_blk, int64_t BH, int64_t Np);
+// image geometry lives with the kernel; D, kv_blk, qk_blk as validated by the API)
+size_t attention_workspace_bytes(int D, int kv_blk, int qk_blk, int64_t BH, int64_t Np);
 hipError_t launch_fallback_prep(const FbArgs& a, int dtype, hipStream_t st);
 hipError_t launch_fallback(const FbArgs& a, hipStream_t st);
 

@@ -177,9 +177,10 @@ __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
   float am = 0.f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) am = fmaxf(am, fabsf(v[i]));
-  // reduce over the TPT * qk_blk threads of one scale block (at least one wave)
-  am = wave_max(am, 64);
+  // reduce over the TPT * qk_blk threads of one scale block (consecutive lanes, or
+  // whole waves)
   const int grp = TPT * s.qk_blk;
+  am = wave_max(am, grp < 64 ? grp : 64);
   if (grp > 64) {
     const int wid = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) wred[wid] = am;
@@ -283,11 +284,19 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
       for (int ch = 0; ch < TPG / 16; ++ch) acc += chunk[ch];
       part[threadIdx.x] = acc;
       __syncthreads();
-      const int gpb = kvb / TPG;  // groups per block
-      if (g % gpb == 0) {
-        for (int k = 1; k < gpb; ++k) acc += part[(g + k) * D + c];
-        const int64_t sblk = (n0 + g * TPG) / kvb;
-        if (sblk < nkb) a.vcol[((int64_t)bh * nkb + sblk) * D + c] = acc;
+      if (kvb <= kTile) {
+        const int gpb = kvb / TPG;  // groups per block
+        if (g % gpb == 0) {
+          for (int k = 1; k < gpb; ++k) acc += part[(g + k) * D + c];
+          const int64_t sblk = (n0 + g * TPG) / kvb;
+          if (sblk < nkb) a.vcol[((int64_t)bh * nkb + sblk) * D + c] = acc;
+        }
+      } else if (g == 0) {
+        // a kv block spans several workgroups: each adds its tile's sum (integer
+        // atomics, so the result does not depend on their order; cleared first)
+        for (int k = 1; k < G; ++k) acc += part[k * D + c];
+        const int64_t sblk = n0 / kvb;
+        if (sblk < nkb) atomicAdd(a.vcol + ((int64_t)bh * nkb + sblk) * D + c, acc);
       }
     }
   }
@@ -298,7 +307,7 @@ template <int D, int DT, int ROT, int TPT>
 hipError_t launch_qk(const QuantArgs& a, hipStream_t st) {
   constexpr int TOK = 256 / TPT;
   const size_t lds = ROT == 2 ? (size_t)TOK * (D + 1) * 4 : 0;
-  static const hipError_t attr = hipFuncSetAttribute((const void*)k1_quant_qk<D, DT, ROT, TPT>,
+  const hipError_t attr = hipFuncSetAttribute((const void*)k1_quant_qk<D, DT, ROT, TPT>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   k1_quant_qk<D, DT, ROT, TPT><<<dim3((unsigned)(a.Np / TOK), (unsigned)(a.s.B * a.s.H), 2), 256, lds, st>>>(a);
@@ -328,7 +337,7 @@ hipError_t launch_quantize_t(const QuantArgs& a, hipStream_t st) {
   const int64_t nvamax = (int64_t)BH * D;
   if (DT == 0) {
     // fp32 tiles exceed the default 64 KiB of dynamic LDS; gfx950 has 160 KiB
-    static const hipError_t attr = hipFuncSetAttribute((const void*)k1_quant_v<D, DT>,
+    const hipError_t attr = hipFuncSetAttribute((const void*)k1_quant_v<D, DT>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)in_tile);
     if (attr != hipSuccess) return attr;
   }
@@ -340,6 +349,10 @@ hipError_t launch_quantize_t(const QuantArgs& a, hipStream_t st) {
   else if (a.rot == 3) e = launch_rot<D, DT, 3>(a, st);
   else e = launch_rot<D, DT, 0>(a, st);
   if (e != hipSuccess) return e;
+  if (a.vcol && a.s.kv_blk > kTile) {
+    const int64_t ncol = (int64_t)BH * ((a.s.F * (int64_t)a.s.Hs * a.s.Ws + a.s.kv_blk - 1) / a.s.kv_blk) * D;
+    k1_zero_u32<<<(unsigned)((ncol + 255) / 256), 256, 0, st>>>((uint32_t*)a.vcol, ncol);
+  }
   k1_quant_v<D, DT><<<dim3((unsigned)(a.Np / kTile), BH), 256, in_tile, st>>>(a);
   return hipGetLastError();
 }

@@ -47,7 +47,7 @@ class QuantizeOpts(ctypes.Structure):
 
 class AttentionOpts(ctypes.Structure):
     _fields_ = [("p_max", ctypes.c_int32), ("causal_block", ctypes.c_int32), ("k_bias", ctypes.c_void_p),
-                ("seq_lens", ctypes.c_void_p)]
+                ("seq_lens", ctypes.c_void_p), ("skip_stats", ctypes.c_void_p)]
 
 
 class FallbackOpts(ctypes.Structure):
@@ -81,6 +81,7 @@ _SIGS = {
     "rotattn_fp16_fallback": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP, _VP, _SZ, _VP]),
     "rotattn_fp16_fallback_ex": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, _VP, _SZ,
                                         _VP]),
+    "rotattn_p_level_probe": (_I32, [ctypes.c_uint32, ctypes.c_int64, _VP, _VP]),
     "rotattn_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -213,7 +214,8 @@ def rotattn_quantize_qk(shape: Shape, rot: int, q: torch.Tensor, k: torch.Tensor
 
 def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Optional[Sequence[int]] = None,
                            debug: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
-                           symmetric_p: bool = False, causal_block: int = 0) -> torch.Tensor:
+                           symmetric_p: bool = False, causal_block: int = 0,
+                           skip_stats: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out: device [B,H,N,D] float32, float16 or bfloat16.  debug: dict(bh, row0, n_rows) ->
     filled with device tensors a_qk, p_codes, a_pv, m, l.  workspace: device uint8
     tensor of rotattn_int4_attention_workspace(shape) bytes (default z["attn_workspace"]).
@@ -222,8 +224,9 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
     causal_block: 0 bidirectional; c > 0 block-causal (query i sees key j iff
     j // c <= i // c).  When z was filled with Q smoothing or a variable-length
     batch, its k_bias and seq_lens are passed on (rows past a sequence's length are
-    left untouched).  Options other than the defaults go through
-    rotattn_int4_attention_ex."""
+    left untouched).  skip_stats: device int64 tensor of 5 counters that the run adds
+    its counts of the exact skips to (see rotattn_attention_opts in the header).
+    Options other than the defaults go through rotattn_int4_attention_ex."""
     if out.dtype not in _DT:
         raise RotattnError("out must be float32, float16 or bfloat16")
     harr, nh = _heads(heads)
@@ -247,9 +250,12 @@ def rotattn_int4_attention(shape: Shape, z: dict, out: torch.Tensor, heads: Opti
             _stream())
     kb = z.get("k_bias") if z.get("smooth_q") else None
     lens = _lens(z.get("seq_lens"))
-    if causal_block or kb is not None or lens is not None:
+    if skip_stats is not None and (skip_stats.dtype != torch.int64 or skip_stats.numel() != 5):
+        raise RotattnError("skip_stats must be a device int64 tensor of 5 counters")
+    if causal_block or kb is not None or lens is not None or skip_stats is not None:
         opts = AttentionOpts(7 if symmetric_p else 15, int(causal_block), _ptr(kb),
-                             ctypes.cast(lens, ctypes.c_void_p) if lens is not None else None)
+                             ctypes.cast(lens, ctypes.c_void_p) if lens is not None else None,
+                             _ptr(skip_stats))
         _check(lib().rotattn_int4_attention_ex(ctypes.byref(shape), *codes, ctypes.byref(opts), *tail),
                "rotattn_int4_attention_ex")
     else:
@@ -279,4 +285,15 @@ def rotattn_fp16_fallback(shape: Shape, q: torch.Tensor, k: torch.Tensor, v: tor
         _check(lib().rotattn_fp16_fallback_ex(*head, ctypes.byref(opts), *tail), "rotattn_fp16_fallback_ex")
     else:
         _check(lib().rotattn_fp16_fallback(*head, *tail), "rotattn_fp16_fallback")
+    return out
+
+
+def rotattn_p_level_probe(first_bits: int, n: int, out: torch.Tensor) -> torch.Tensor:
+    """out: device uint8 tensor of at least n elements; out[i] = the attention's P
+    level decision for the binary32 exponent with bit pattern first_bits + i (low
+    nibble) and the exact threshold fix alone (high nibble)."""
+    if out.dtype != torch.uint8 or out.numel() < n:
+        raise RotattnError("out must be a device uint8 tensor of at least n elements")
+    _check(lib().rotattn_p_level_probe(ctypes.c_uint32(first_bits), ctypes.c_int64(n), _ptr(out), _stream()),
+           "rotattn_p_level_probe")
     return out

@@ -26,6 +26,10 @@ CONFIGS = {
                         dtype="float16", rot="interleaved", recipe="hunyuan"),
     "mixed_ragged": dict(B=2, H=12, F=13, Hs=30, Ws=53, D=128, Df=44, Dh=42, Dw=42, qk_blk=64, kv_blk=64,
                          dtype="float16", rot="half", recipe="peaked"),
+    # the Wan-720p-like shape on outlier-free inputs: flat, diffuse attention (the
+    # text-to-video regime), where no 64-key unit has all its levels 0
+    "wan720p_diffuse": dict(B=1, H=40, F=21, Hs=45, Ws=80, D=128, Df=44, Dh=42, Dw=42, qk_blk=64, kv_blk=64,
+                            dtype="float16", rot="half", recipe="diffuse"),
 }
 
 
@@ -91,6 +95,10 @@ def make_head(cfg, b: int, h: int, seed: int = 0):
         k[:, ch] *= 12.0
     elif rec == "peaked":
         q *= 4.0
+    elif rec == "diffuse":
+        # no outlier channels and unit-variance logits: the softmax of a row is flat
+        # over many keys (V Hadamard-rotated as for the Wan recipe)
+        v = (v.astype(np.float64) @ (hadamard(D) / np.sqrt(D))).astype(np.float32)
     return q, k, v
 
 

@@ -87,3 +87,74 @@ def rows_sample(N: int, n_rand: int = 32, seed: int = 0):
     rows = set(range(min(N, 40))) | set(range(max(0, N - 40), N))
     rows |= set(rng.integers(0, N, n_rand).tolist())
     return np.array(sorted(rows), np.int64)
+
+
+def pack_rows(codes: np.ndarray) -> np.ndarray:
+    """[..., n] signed nibbles -> [..., n/2] bytes (element 2i in the low nibble)."""
+    c = codes.astype(np.int16) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def upload_codes(cfg, zc: dict) -> dict:
+    """Code tensors in the oracle's layout (qc, kc, vc int8 [B,H,N,D]; qs, ks
+    [B,H,ceil(N/qk_blk)]; vs [B,H,D]) -> the library's padded device layout, as
+    rotattn_quantize_qk would have written them (layout only)."""
+    shape = ra.Shape.of(cfg)
+    B, H, D = cfg["B"], cfg["H"], cfg["D"]
+    N = synth.n_tokens(cfg)
+    Np = ra.rotattn_padded_tokens(shape)
+    qb = cfg["qk_blk"]
+    nqb = -(-N // qb)
+    z = ra.alloc_codes(shape, colsum=False)
+
+    def rows(x):
+        out = np.zeros((B, H, Np, D), np.int8)
+        out[:, :, :N] = x
+        return out
+
+    z["q_codes"].copy_(torch.from_numpy(pack_rows(rows(zc["qc"]))))
+    z["k_codes"].copy_(torch.from_numpy(pack_rows(rows(zc["kc"]))))
+    z["v_codes"].copy_(torch.from_numpy(pack_rows(np.ascontiguousarray(rows(zc["vc"]).transpose(0, 1, 3, 2)))))
+    for name in ("qs", "ks"):
+        s = np.zeros((B, H, Np // qb), np.float32)
+        s[:, :, :nqb] = zc[name]
+        z["q_scale" if name == "qs" else "k_scale"].copy_(torch.from_numpy(s))
+    z["v_scale"].copy_(torch.from_numpy(np.ascontiguousarray(zc["vs"], np.float32)))
+    torch.cuda.synchronize()
+    return z
+
+
+def debug_run(shape, z, out_like, bh, r0, n, **kw):
+    """One debug launch of rotattn_int4_attention over rows [r0, r0+n) of head bh;
+    returns (dumps as numpy, the output rows as numpy)."""
+    dbg = dict(bh=bh, row0=r0, n_rows=n)
+    out2 = torch.zeros_like(out_like)
+    ra.rotattn_int4_attention(shape, z, out2, debug=dbg, **kw)
+    torch.cuda.synchronize()
+    H = out_like.shape[1]
+    d = {k: dbg[k].cpu().numpy() for k in ("a_qk", "p_codes", "a_pv", "m", "l")}
+    return d, out2[bh // H, bh % H, r0:r0 + n].float().cpu().numpy()
+
+
+def l_rtol(n_keys: int, kv_blk: int) -> float:
+    """Relative bound on the GPU's normaliser against the oracle's binary64 sum: each
+    lane adds its half of the keys' p in binary32 one at a time (recursive summation
+    of positive terms: at most one unit roundoff u = 2^-24 of the total per addition;
+    a p below half an ulp of the running sum is dropped, within the same bound), and
+    every move of the running maximum rescales it (a product with the hardware exp2,
+    within 4 u); the halves meet in one more addition."""
+    return max(1e-5, (-(-n_keys // 2) + 4 * -(-n_keys // kv_blk) + 2) * 2.0 ** -24)
+
+
+def assert_dumps_equal(d: dict, od: dict, what="", n_keys=None, kv_blk=None):
+    """Integer dumps bit-exact (A_qk, P codes, per-step P V sums, the running
+    maximum's bits); l within 1e-5 of the oracle's binary64 sum, or within the
+    binary32 summation bound l_rtol for long rows (n_keys and kv_blk given)."""
+    assert np.array_equal(d["a_qk"], od["a_qk"]), what + " a_qk"
+    assert np.array_equal(d["p_codes"], od["pcode"]), what + " P codes"
+    assert np.array_equal(d["a_pv"], od["a_pv"]), what + " a_pv"
+    assert np.array_equal(d["m"].view(np.uint32), od["m"].view(np.uint32)), what + " m"
+    rtol = 1e-5 if n_keys is None else l_rtol(n_keys, kv_blk)
+    err = float(np.max(np.abs(d["l"] - od["l"]) / od["l"]))
+    print("%s: l max rel err %.3g (bound %.3g)" % (what, err, rtol))
+    assert err <= rtol, what + " l"

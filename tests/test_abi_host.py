@@ -47,8 +47,13 @@ def test_check_shape_statuses(L):
     assert ra.rotattn_check_shape(_shape(Df=26)) == 2          # D != Df+Dh+Dw
     assert ra.rotattn_check_shape(_shape(Df=23, Dh=21)) == 2   # odd segments
     assert ra.rotattn_check_shape(_shape(D=96, Df=32, Dh=32, Dw=32)) == 3
-    assert ra.rotattn_check_shape(_shape(qk_blk=8)) == 3
-    assert ra.rotattn_check_shape(_shape(kv_blk=256)) == 3
+    assert ra.rotattn_check_shape(_shape(qk_blk=1)) == 0       # per-token scales
+    assert ra.rotattn_check_shape(_shape(qk_blk=8)) == 0
+    assert ra.rotattn_check_shape(_shape(kv_blk=256)) == 0
+    assert ra.rotattn_check_shape(_shape(qk_blk=3)) == 3
+    assert ra.rotattn_check_shape(_shape(qk_blk=256)) == 3
+    assert ra.rotattn_check_shape(_shape(kv_blk=8)) == 3
+    assert ra.rotattn_check_shape(_shape(kv_blk=512)) == 3
     assert ra.rotattn_check_shape(_shape(F=0)) == 2
     assert L.rotattn_check_shape(None) == 1
 

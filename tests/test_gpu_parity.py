@@ -71,6 +71,15 @@ def test_tiny_full_parity(orc, rot):
     _run_case(orc, cfg, ROTS[rot], debug_rows=[(0, 32)])
 
 
+@pytest.mark.parametrize("qk,kv", [(1, 16), (1, 256), (16, 256), (4, 32)])
+def test_tiny_block_sizes(orc, qk, kv):
+    """The tiny case with per-token Q/K scales (qk_blk 1, the paper.gecl.asia
+    analysis, "Key Insight"), other small scale blocks, and a 256-key online-softmax
+    step (longer than the sequence): codes, dumps and output against the oracle."""
+    cfg = dict(synth.CONFIGS["tiny"], qk_blk=qk, kv_blk=kv)
+    _run_case(orc, cfg, 2, debug_rows=[(0, 32)])
+
+
 MEDIUM = [
     # (id, config overrides)
     ("wan_half_kv64", dict(rot="half")),
@@ -80,6 +89,13 @@ MEDIUM = [
     ("wan_half_kv128_qk16", dict(rot="half", qk_blk=16, kv_blk=128)),
     ("hunyuan_inter_B2", dict(rot="interleaved", recipe="hunyuan", Df=16, Dh=56, Dw=56, B=2)),
     ("peaked_none_nosmooth", dict(rot="none", recipe="peaked")),
+    ("wan_half_kv64_qk1", dict(rot="half", qk_blk=1)),
+    ("wan_inter_kv256_qk64", dict(rot="interleaved", qk_blk=64, kv_blk=256)),
+    ("wan_half_kv256_qk1", dict(rot="half", qk_blk=1, kv_blk=256)),
+    ("wan_half_kv128_qk2", dict(rot="half", qk_blk=2, kv_blk=128)),
+    ("peaked_half_kv16_qk1", dict(rot="half", qk_blk=1, kv_blk=16, recipe="peaked")),
+    ("hunyuan_inter_kv32_qk8_B2", dict(rot="interleaved", recipe="hunyuan", Df=16, Dh=56, Dw=56, B=2, qk_blk=8,
+                                       kv_blk=32)),
 ]
 
 
@@ -212,6 +228,8 @@ CAUSAL = [
     ("frame_kv16_qk16", dict(qk_blk=16, kv_blk=16), 391),
     ("block5_kv32_qk32_symmetric", dict(qk_blk=32, kv_blk=32), 5),
     ("block_ge_n", dict(), 5000),
+    ("frame_kv256_qk1", dict(qk_blk=1, kv_blk=256), 391),
+    ("block100_kv256", dict(kv_blk=256), 100),
 ]
 
 
@@ -250,6 +268,8 @@ QSMOOTH = [
     ("inter_kv16_qk16", dict(qk_blk=16, kv_blk=16), 1, True, 0),
     ("half_kv128_qk16_nosmoothk", dict(qk_blk=16, kv_blk=128), 2, False, 0),
     ("full_kv32_frame_causal", dict(qk_blk=32, kv_blk=32), 3, True, 391),
+    ("half_kv64_qk1", dict(qk_blk=1), 2, True, 0),
+    ("inter_kv256_qk2_frame_causal", dict(qk_blk=2, kv_blk=256), 1, True, 391),
 ]
 
 
@@ -270,10 +290,11 @@ def test_q_smoothing_d64_f32(orc):
 
 
 VARLEN = [
-    # (id, lengths of the three batch elements, rotation, Q smoothing, causal block, kv_blk)
+    # (id, lengths of the three batch elements, rotation, Q smoothing, causal block, kv_blk[, qk_blk])
     ("frames_and_ragged_kv64", [1173, 782, 500], 2, False, 0, 64),
     ("ragged_smoothq_kv16", [1173, 129, 1], 1, True, 0, 16),
     ("ragged_frame_causal_kv128", [600, 1173, 391], 2, False, 391, 128),
+    ("ragged_kv256_qk1", [1173, 300, 77], 2, False, 0, 256, 1),
 ]
 
 
@@ -282,8 +303,9 @@ def test_varlen_parity(orc, case):
     """Variable-length batch in the padded layout: padding holds NaN (nothing may read
     it), codes and scales bit-exact with the oracle's, valid rows within the bar with
     dumps bit-exact, rows past each length left untouched."""
-    name, lens, rot, smooth_q, cb, kv = case
-    cfg = synth.custom(3, 2, 3, 17, 23, 128, 44, 42, 42, min(kv, 64), kv, dtype="float16", recipe="wan")
+    name, lens, rot, smooth_q, cb, kv = case[:6]
+    qk = case[6] if len(case) > 6 else min(kv, 64)
+    cfg = synth.custom(3, 2, 3, 17, 23, 128, 44, 42, 42, qk, kv, dtype="float16", recipe="wan")
     Q, K, V = synth.make_inputs(cfg)
     for b, n in enumerate(lens):
         for x in (Q, K, V):
@@ -329,8 +351,8 @@ def _random_config(rng, i):
         Df, Dh, Dw = 24, 20, 20
     else:
         Df, Dh, Dw = [(44, 42, 42), (16, 56, 56)][int(rng.integers(2))]
-    kv = int(rng.choice([16, 32, 64, 128]))
-    qk = int(rng.choice([16, 32, 64, 128]))
+    kv = int(rng.choice([16, 32, 64, 128, 256]))
+    qk = int(rng.choice([1, 2, 16, 32, 64, 128]))
     F, Hs, Ws = int(rng.integers(1, 4)), int(rng.integers(3, 19)), int(rng.integers(3, 29))
     B = int(rng.integers(1, 3))
     dtype = str(rng.choice(["float16", "float32"]))
@@ -346,7 +368,7 @@ def _random_config(rng, i):
     return cfg, opts
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(16))
 def test_random_configs_parity(orc, i):
     """Seeded random combinations of shape, head split, block sizes, rotation, K and Q
     smoothing, causal block, variable lengths and P code: codes bit-exact, sampled

@@ -196,9 +196,11 @@ def test_rope_table_closed_form(orc):
 
 # --- quantisation ---------------------------------------------------------------
 
-@pytest.mark.parametrize("rot", [1, 2])
-def test_quantize_invariants(orc, rot):
-    cfg = dict(TINY)
+@pytest.mark.parametrize("rot,qb,kv", [(1, 16, 16), (2, 16, 16), (2, 1, 16), (1, 2, 32), (2, 16, 256)])
+def test_quantize_invariants(orc, rot, qb, kv):
+    """qb = 1 is the per-token Q/K quantiser (paper.gecl.asia analysis, "Key
+    Insight"); kv = 256 a column-sum block longer than the sequence."""
+    cfg = dict(TINY, qk_blk=qb, kv_blk=kv)
     q, k, v = synth.make_inputs(cfg)
     tab = orc.rope_table(cfg, rot)
     z = orc.quantize(cfg, rot, tab, q, k, v, smooth_k=True, diag=True)
@@ -353,8 +355,10 @@ def _definition_attention(z, N, D, qk_blk, kv):
     return level, weight, l, x
 
 
-@pytest.mark.parametrize("kv,lo,hi", [(16, 0.5, 1.0), (64, 0.5, 1.0), (16, 0.15, 0.4), (64, 0.15, 0.4)])
-def test_normaliser_codes_and_output_against_definition(orc, kv, lo, hi):
+@pytest.mark.parametrize("kv,lo,hi,qb", [(16, 0.5, 1.0, 16), (64, 0.5, 1.0, 16), (16, 0.15, 0.4, 16),
+                                         (64, 0.15, 0.4, 16), (256, 0.15, 0.4, 16), (64, 0.15, 0.4, 1),
+                                         (256, 0.5, 1.0, 1)])
+def test_normaliser_codes_and_output_against_definition(orc, kv, lo, hi, qb):
     """Peaked scores (lossless codes, Q/K scales in [lo, hi]: score spreads of 1.5 to
     10 nat, so most levels are 0 while 15 P is not): the oracle's normaliser l, its
     P codes and its output against the definition evaluated here in binary64
@@ -363,17 +367,18 @@ def test_normaliser_codes_and_output_against_definition(orc, kv, lo, hi):
     the binary32 score pipeline).  Codes must equal round(15 P) against the running
     maximum except for keys whose 15 P lies within 1e-4 (relative) of a rounding
     boundary, where the binary32 exponent may fall on either side; each such key
-    widens the output bound by its |v| weight."""
-    rng = np.random.default_rng(23 + kv)
+    widens the output bound by its |v| weight.  qb: tokens per Q/K scale (1: the
+    per-token scales of the paper.gecl.asia analysis, "Key Insight")."""
+    rng = np.random.default_rng(23 + kv + qb)
     B, H, F, Hs, Ws, D = 1, 2, 4, 8, 8, 64
-    cfg = synth.custom(B, H, F, Hs, Ws, D, 24, 20, 20, 16, kv)
+    cfg = synth.custom(B, H, F, Hs, Ws, D, 24, 20, 20, qb, kv)
     N = F * Hs * Ws
     z = dict(qc=_ints(rng, (B, H, N, D)), kc=_ints(rng, (B, H, N, D)), vc=_ints(rng, (B, H, N, D)),
-             qs=rng.uniform(lo, hi, (B, H, N // 16)).astype(np.float32),
-             ks=rng.uniform(lo, hi, (B, H, N // 16)).astype(np.float32),
+             qs=rng.uniform(lo, hi, (B, H, N // qb)).astype(np.float32),
+             ks=rng.uniform(lo, hi, (B, H, N // qb)).astype(np.float32),
              vs=rng.uniform(0.5, 1, (B, H, D)).astype(np.float32))
     r = orc.attention(cfg, z, dumps=True)
-    level, weight, l, x = _definition_attention(z, N, D, 16, kv)
+    level, weight, l, x = _definition_attention(z, N, D, qb, kv)
     level, weight, x = (a.reshape(B * H * N, N) for a in (level, weight, x))
     l = l.reshape(-1)
     # normaliser
