@@ -26,6 +26,8 @@
  *   - Thread safety: no mutable global state; calls are reentrant.  (The P level
  *     threshold table is built once, on first use, with thread-safe static
  *     initialisation and never changes; kernels' LDS limits are set on each call.)
+ *     The one exception is rotattn_quantize_qk_noalloc, whose calls share a fixed
+ *     per-device scratch array (see there).
  *   - Layouts are C-contiguous.  Token n of a head sits at RoPE position
  *     (f, y, x) with n = (f*Hs + y)*Ws + x.  Code tensors are padded to
  *     Np = rotattn_padded_tokens() tokens; padding codes and scales are zero.
@@ -129,6 +131,30 @@ rotattn_status rotattn_quantize_qk(const rotattn_shape* s, rotattn_rot rot, rota
                                    uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
                                    uint8_t* v_codes, float* v_scale, int32_t* v_colsum,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- rotattn_quantize_qk_noalloc: for callers that cannot allocate ---------------
+ * For code that must not allocate device memory (work under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): rotattn_quantize_qk with
+ * the same arguments and results, minus the workspace.  Its scratch (the ordered
+ * binary64 partial sums of K, the channel means and the V amax) lives in a fixed
+ * device array of rotattn_quantize_qk_noalloc_max_scratch() bytes (64 MiB) that the
+ * library holds on every device it runs on until the process ends; the call itself
+ * allocates nothing (no hipMalloc, no allocating library routine).  A shape whose
+ * scratch, rotattn_quantize_qk_noalloc_scratch(s) (about 8 D bytes per token and
+ * head: the Wan-720p-like layer needs 48.5 MB), exceeds it returns
+ * ROTATTN_E_WORKSPACE before any launch.  Every call on a device shares that
+ * device's array, and each call overwrites it (what must start at zero is cleared
+ * by the call's own kernels): calls that overlap on one device, on different
+ * streams or threads, race and must be serialised by the caller.  The first call
+ * on each device looks up the array's device address (hipGetSymbolAddress) and keeps
+ * it; a failed lookup returns ROTATTN_E_HIP. */
+size_t rotattn_quantize_qk_noalloc_max_scratch(void);
+size_t rotattn_quantize_qk_noalloc_scratch(const rotattn_shape* s);
+rotattn_status rotattn_quantize_qk_noalloc(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
+                                           const void* q, const void* k, const void* v,
+                                           const float* rope_table, int32_t smooth_k,
+                                           uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+                                           uint8_t* v_codes, float* v_scale, int32_t* v_colsum, void* stream);
 
 /* ---- rotattn_quantize_qk_ex: Q smoothing, variable-length batches ----------------
  * rotattn_quantize_qk with options (opts NULL: smooth_k = 1 and nothing else):

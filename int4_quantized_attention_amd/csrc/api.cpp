@@ -113,11 +113,12 @@ rotattn_status rotattn_build_rope_table(const rotattn_shape* s, rotattn_rot rot,
   return ROTATTN_OK;
 }
 
-// quantisation workspace: K partial sums, Q partial sums, K mean, Q mean, V amax
+// quantisation workspace: K partial sums, Q partial sums (with_q: room for Q
+// smoothing), K mean, Q mean, V amax
 struct QWs {
   size_t qpart, kmu, qmu, amax, total;
 };
-static QWs q_ws_parts(const rotattn_shape* s) {
+static QWs q_ws_parts(const rotattn_shape* s, bool with_q = true) {
   const int64_t N = tokens(s);
   const int64_t BH = (int64_t)s->B * s->H;
   const int64_t nblk = (N + 63) / 64;
@@ -126,7 +127,7 @@ static QWs q_ws_parts(const rotattn_shape* s) {
   const size_t amax = align256((size_t)BH * s->D * sizeof(uint32_t));
   QWs w;
   w.qpart = part;
-  w.kmu = 2 * part;
+  w.kmu = (with_q ? 2 : 1) * part;
   w.qmu = w.kmu + mu;
   w.amax = w.qmu + mu;
   w.total = w.amax + amax;
@@ -153,20 +154,28 @@ rotattn_status set_lens(const rotattn_shape* s, const int32_t* seq_lens, int& nl
   return ROTATTN_OK;
 }
 
+// noalloc: use the library's fixed scratch (workspace is ignored); without Q
+// smoothing, so no room is kept for Q partial sums.
 rotattn_status quantize_call(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
                              const void* q, const void* k, const void* v,
                              const float* rope_table, int32_t smooth_k,
                              uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
                              uint8_t* v_codes, float* v_scale, int32_t* v_colsum, bool smooth_q, float* k_bias,
-                             const int32_t* seq_lens, void* workspace, size_t workspace_bytes, void* stream) {
+                             const int32_t* seq_lens, void* workspace, size_t workspace_bytes, void* stream,
+                             bool noalloc = false) {
   const rotattn_status st = rotattn_check_shape(s);
   if (st != ROTATTN_OK) return st;
   if (!q || !k || !v || !rope_table || !q_codes || !q_scale || !k_codes || !k_scale || !v_codes ||
-      !v_scale || !workspace || (smooth_q && !k_bias))
+      !v_scale || (!workspace && !noalloc) || (smooth_q && !k_bias))
     return ROTATTN_E_NULL;
   if (rot < ROTATTN_ROT_NONE || rot > ROTATTN_ROT_FULL) return ROTATTN_E_ARG;
   if (in_dtype < ROTATTN_F32 || in_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
-  const QWs w = q_ws_parts(s);
+  const QWs w = q_ws_parts(s, !noalloc);
+  if (noalloc) {
+    if (w.total > ra::kQuantScratchBytes) return ROTATTN_E_WORKSPACE;
+    if (ra::quant_scratch(&workspace) != hipSuccess) return ROTATTN_E_HIP;
+    workspace_bytes = ra::kQuantScratchBytes;
+  }
   if (workspace_bytes < w.total) return ROTATTN_E_WORKSPACE;
   ra::QuantArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -211,6 +220,22 @@ rotattn_status rotattn_quantize_qk_ex(const rotattn_shape* s, rotattn_rot rot, r
   return quantize_call(s, rot, in_dtype, q, k, v, rope_table, o.smooth_k, q_codes, q_scale, k_codes, k_scale,
                        v_codes, v_scale, v_colsum, o.smooth_q != 0, o.k_bias, o.seq_lens, workspace,
                        workspace_bytes, stream);
+}
+
+size_t rotattn_quantize_qk_noalloc_scratch(const rotattn_shape* s) {
+  if (!s || rotattn_check_shape(s) != ROTATTN_OK) return 0;
+  return q_ws_parts(s, false).total;
+}
+
+size_t rotattn_quantize_qk_noalloc_max_scratch(void) { return ra::kQuantScratchBytes; }
+
+rotattn_status rotattn_quantize_qk_noalloc(const rotattn_shape* s, rotattn_rot rot, rotattn_dtype in_dtype,
+                                           const void* q, const void* k, const void* v,
+                                           const float* rope_table, int32_t smooth_k,
+                                           uint8_t* q_codes, float* q_scale, uint8_t* k_codes, float* k_scale,
+                                           uint8_t* v_codes, float* v_scale, int32_t* v_colsum, void* stream) {
+  return quantize_call(s, rot, in_dtype, q, k, v, rope_table, smooth_k, q_codes, q_scale, k_codes, k_scale,
+                       v_codes, v_scale, v_colsum, false, nullptr, nullptr, nullptr, 0, stream, true);
 }
 
 size_t rotattn_int4_attention_workspace(const rotattn_shape* s) {

@@ -12,6 +12,8 @@ struct Shape {
 constexpr int kTokenPad = 256;   // code tensors hold Np = N rounded up to this
 constexpr int kMaxBatch = 64;    // batch elements of a variable-length call
 constexpr int kMaxHeads = 512;   // heads per attention launch (more -> several launches)
+constexpr int kMaxDevices = 64;  // devices the no-allocation entry point keeps a scratch address for
+constexpr size_t kQuantScratchBytes = (size_t)64 << 20;  // its fixed scratch per device
 
 struct QuantArgs {
   Shape s;
@@ -100,6 +102,8 @@ struct LevelTable {
 };
 
 hipError_t launch_quantize(const QuantArgs& a, int dtype, hipStream_t st);
+// the device address of this device's kQuantScratchBytes of library scratch
+hipError_t quant_scratch(void** out);
 // out[i] = the attention's P level decision for y = bits first + i (low nibble) and
 // the exact fix alone (high nibble), i < n
 hipError_t launch_level_probe(uint32_t first, int64_t n, uint8_t* out, const float* thresholds15,

@@ -11,11 +11,38 @@
 // and writes packed nibbles with 8/16-byte stores.  V is staged through LDS and
 // written transposed.  K and V need global statistics (the channel mean of K, the
 // channel amax of V), so they are read twice.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 #include "rope.h"
 
 namespace ra {
+
+// Scratch of rotattn_quantize_qk_noalloc: a fixed device array (each device holds
+// its own copy from module load until the process ends), for callers that cannot
+// allocate.  Host code never uses the array's name as an address: the device
+// address of this device's copy comes from hipGetSymbolAddress, looked up once per
+// device and kept.
+static __device__ __align__(256) uint8_t scratch[kQuantScratchBytes];
+
+hipError_t quant_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------------------------
 // Channel statistics for smoothing: ordered binary64 partial sums of rotated K (and,

@@ -82,6 +82,10 @@ _SIGS = {
     "rotattn_fp16_fallback_ex": (_I32, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _I32, _VP, _VP, _SZ,
                                         _VP]),
     "rotattn_p_level_probe": (_I32, [ctypes.c_uint32, ctypes.c_int64, _VP, _VP]),
+    "rotattn_quantize_qk_noalloc_max_scratch": (_SZ, []),
+    "rotattn_quantize_qk_noalloc_scratch": (_SZ, [_VP]),
+    "rotattn_quantize_qk_noalloc": (_I32, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP,
+                                           _VP, _VP, _VP]),
     "rotattn_status_str": (ctypes.c_char_p, [_I32]),
 }
 
@@ -297,3 +301,19 @@ def rotattn_p_level_probe(first_bits: int, n: int, out: torch.Tensor) -> torch.T
     _check(lib().rotattn_p_level_probe(ctypes.c_uint32(first_bits), ctypes.c_int64(n), _ptr(out), _stream()),
            "rotattn_p_level_probe")
     return out
+
+
+def rotattn_quantize_qk_noalloc(shape: Shape, rot: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                rope_table: torch.Tensor, smooth_k: bool, z: dict) -> dict:
+    """rotattn_quantize_qk without a workspace: the library's fixed per-device scratch
+    (calls on one device must not overlap).  z: code buffers as from alloc_codes
+    (its workspaces are not used)."""
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise RotattnError("q, k, v must share one of float32 / float16 / bfloat16")
+    _check(lib().rotattn_quantize_qk_noalloc(
+        ctypes.byref(shape), rot, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(rope_table), 1 if smooth_k else 0,
+        _ptr(z["q_codes"]), _ptr(z["q_scale"]), _ptr(z["k_codes"]), _ptr(z["k_scale"]), _ptr(z["v_codes"]),
+        _ptr(z["v_scale"]), _ptr(z.get("v_colsum")), _stream()), "rotattn_quantize_qk_noalloc")
+    z["smooth_q"] = False
+    z["seq_lens"] = None
+    return z
