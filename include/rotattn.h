@@ -301,8 +301,9 @@ rotattn_status rotattn_int4_attention_symmetric_p(const rotattn_shape* s,
  *                 with): a row of batch element b sees only its first seq_lens[b]
  *                 keys, and its rows past them are left untouched (debug rows must
  *                 lie below it).  B > 64 returns ROTATTN_E_UNSUPPORTED.
- *   skip_stats    NULL, or device u64 [5], 8-byte aligned, that the production run
- *                 adds its counts of the exact skips to (the caller clears it):
+ *   skip_stats    NULL, or device u64 [5], 8-byte aligned, that the run adds its
+ *                 counts of the exact skips to (the caller clears it; a kernel
+ *                 instance that also counts runs, with the same decisions):
  *                 [0] P V units (one P V MFMA decision: 64 keys x 32 rows, or 32
  *                 keys for kv_blk <= 32), [1] those skipped because every level is
  *                 0, [2] 32 x 32 score tiles, [3] tiles whose exps were skipped as

@@ -44,6 +44,7 @@
 //  * Workgroup ids are remapped so that the query tiles of a head run on the same
 //    XCD and share its L2 for the K/V stream.
 #pragma once
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -275,14 +276,28 @@ struct Ctx {
 // the output numerator sum_j 2^(m_j - m) r_j v_j in fp32 (m_j the running maximum
 // when key j was added), the running maximum m and l = sum_j 2^(y_j + m_j - m).
 // Between moves of m the MFMA adds exact integer sums; a move rescales in place.
-// The counters (wave-uniform) record what the exact skips saved: P V units (one
-// MFMA decision each), the units skipped as all-zero, their score tiles whose exps
-// were skipped, and the units that took the exact-level path.
-template <int NDB>
+// What the exact skips saved, counted (wave-uniform) only by the instance that
+// reports it: P V units (one MFMA decision each), the units skipped as all-zero,
+// score tiles and those whose exps were skipped, and the units that took the
+// exact-level path.  The timed instance carries NoCount, whose calls vanish.
+struct NoCount {
+  RA_DEV void unit(int) {}
+  RA_DEV void unit_skip() {}
+  RA_DEV void exp_skip() {}
+  RA_DEV void fix() {}
+};
+struct SkipCount {
+  uint32_t n_pv = 0, n_pv_skip = 0, n_tile = 0, n_exp_skip = 0, n_fix = 0;
+  RA_DEV void unit(int tiles) { n_pv += 1; n_tile += tiles; }
+  RA_DEV void unit_skip() { n_pv_skip += 1; }
+  RA_DEV void exp_skip() { n_exp_skip += 1; }
+  RA_DEV void fix() { n_fix += 1; }
+};
+template <int NDB, class C>
 struct RowState {
   f32x16 acc[NDB];
   float m, l;
-  uint32_t n_pv, n_pv_skip, n_tile, n_exp_skip, n_fix;
+  C cnt;
 };
 
 // Copy the LDS image of group g into ring slot `buf`.  Wave w copies the w-th
@@ -349,11 +364,11 @@ RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::
 // for the whole step, so the maximum needs one multiplication; SM 2 (per-key K scales,
 // Sl the group's scales in LDS): without Q smoothing each key's c = fl(fl(sq sk_j) C0)
 // is formed here, and the scores st are replaced by their exponents y.
-template <int D, int KVB, bool DBG, bool MASK, int SM>
+template <int D, int KVB, bool DBG, bool MASK, int SM, class RS>
 RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl, const float* Tl,
                        const float* Sl, float sq, f32x16 (&st)[Geo<D, KVB>::TPS],
                        const float (&ct)[Geo<D, KVB>::TPS], const f32x16 (&sa)[Geo<D, KVB>::TPS],
-                       RowState<D / 32>& S, bool dbg_row, int dr) {
+                       RS& S, bool dbg_row, int dr) {
   using G = Geo<D, KVB>;
   constexpr bool US = SM == 1;
   // per-key scales without Q smoothing (with it, group_iter has already formed the
@@ -484,8 +499,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
       i32x4 pb[PT];
       bool flag = guard;
       const bool allz = !DBG && !__any(fmaxf(ymax[pp * PT], ymax[pp * PT + PT - 1]) >= a.T0);
-      S.n_pv += 1;
-      S.n_tile += PT;
+      S.cnt.unit(PT);
       if (allz) {
         // every level of the pair is 0: the keys enter the normaliser only (same
         // order of additions as the level path); no margin, MFMA, V read or exact
@@ -493,7 +507,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
         // Each path takes L15 - m through an empty asm of its own, so that the
         // compiler can neither merge the two paths' exps nor hoist either set above
         // the branch (where all of them would be computed, and live, at once).
-        S.n_pv_skip += 1;
+        S.cnt.unit_skip();
         flag = false;
         float nz = nm;
         asm volatile("" : "+v"(nz));
@@ -502,7 +516,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
           const int t = pp * PT + tp;
           pb[tp] = i32x4{0, 0, 0, 0};
           if (ngl[t]) {  // no p of the tile moves l
-            S.n_exp_skip += 1;
+            S.cnt.exp_skip();
             continue;
           }
 #pragma unroll
@@ -553,7 +567,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
       if (DBG || __any(flag)) {
         // exact levels of the whole pair (the debug run always takes this path, so
         // that it dumps the exact code of every key)
-        S.n_fix += 1;
+        S.cnt.fix();
 #pragma unroll
         for (int tp = 0; tp < PT; ++tp) {
           const int t = pp * PT + tp;
@@ -619,26 +633,16 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
 
 typedef const __attribute__((address_space(4))) float* kscale_ptr;  // read-only: scalar loads
 
-// One key group g in ring slot g % NB: first the copy of group g + NB - 1 into the
-// slot group g-1 used (free since the last barrier); then its online-softmax steps,
-// each with the K scales of its 16-key units (scalar loads, so they never wait
-// behind the copies in flight), Q K^T, softmax + P V; then a wait until this
-// wave's copy of group g+1 has landed (later copies stay in flight) and one
-// barrier, which also covers the other waves' copies.
-template <int D, int KVB, bool DBG, bool MASK, int SM, int SLOT = -1>
-RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngroups, uint8_t* lds,
-                       const i32x8 (&qop)[Geo<D, KVB>::KC], float sq, int bh, RowState<D / 32>& S, bool dbg_row,
-                       int dr) {
+// The work of key group g on its LDS image cur: the K scales of its 16-key units
+// (scalar loads, so they never wait behind copies in flight), Q K^T, then each
+// online-softmax step's softmax and P V.
+template <int D, int KVB, bool DBG, bool MASK, int SM, class RS>
+RA_DEV void group_compute(const Ctx& a, int g, uint8_t* const cur, const i32x8 (&qop)[Geo<D, KVB>::KC],
+                          float sq, int bh, RS& S, bool dbg_row, int dr) {
   using G = Geo<D, KVB, SM>;
   constexpr bool US = SM == 1;
-  // ring slot of this group: a compile-time constant when the caller unrolls the
-  // group loop by the slot count (SLOT = g % NB), so LDS addresses stay invariant
-  const int slot = SLOT >= 0 ? SLOT : g % G::NB;
-  if (g + G::NB - 1 < ngroups)
-    dma_group<D, KVB, SM>(rsrc, g + G::NB - 1, lds + ((slot + G::NB - 1) % G::NB) * G::IMG);
   const int h = (threadIdx.x >> 5) & 1;
   const kscale_ptr ksh = (kscale_ptr)a.ks + (int64_t)bh * (a.Np >> a.qk_shift);
-  uint8_t* const cur = lds + slot * G::IMG;
   // The scores of step sg + 1 are issued on the MFMA before the softmax of step sg,
   // so that its latency overlaps that step's VALU work.
   float ct[G::NSG][G::TPS];
@@ -696,6 +700,23 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
     softmax_pv<D, KVB, DBG, MASK, SM>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), Sl, sq,
                                       st[sg], ct[sg], DBG ? sa : st[sg], S, dbg_row, dr);
   }
+}
+
+// The barrier pipeline (4-wave workgroups; the debug run, and 256-key steps): group g
+// in ring slot g % NB.  First the copy of group g + NB - 1 into the slot group g-1
+// used (free since the last barrier); then the group's work; then a wait until this
+// wave's copy of group g+1 has landed (later copies stay in flight) and one barrier,
+// which also covers the other waves' copies.
+template <int D, int KVB, bool DBG, bool MASK, int SM, int SLOT = -1, class RS>
+RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngroups, uint8_t* lds,
+                       const i32x8 (&qop)[Geo<D, KVB>::KC], float sq, int bh, RS& S, bool dbg_row, int dr) {
+  using G = Geo<D, KVB, SM>;
+  // ring slot of this group: a compile-time constant when the caller unrolls the
+  // group loop by the slot count (SLOT = g % NB), so LDS addresses stay invariant
+  const int slot = SLOT >= 0 ? SLOT : g % G::NB;
+  if (g + G::NB - 1 < ngroups)
+    dma_group<D, KVB, SM>(rsrc, g + G::NB - 1, lds + ((slot + G::NB - 1) % G::NB) * G::IMG);
+  group_compute<D, KVB, DBG, MASK, SM>(a, g, lds + slot * G::IMG, qop, sq, bh, S, dbg_row, dr);
   // copies issued after group g+1's: those of groups g+2 .. min(g+NB-1, ngroups-1)
   const int later = min(g + G::NB - 1, ngroups - 1) - (g + 1);
   if (DBG || later <= 0) wait_vm<0>();
@@ -704,14 +725,15 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
   lds_barrier();
 }
 
-template <int D, int KVB, bool DBG, int SM>
+template <int D, int KVB, bool DBG, int SM, bool ST = false>
 RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   using G = Geo<D, KVB, SM>;
+  constexpr int BM = kBM;  // query rows per workgroup
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
   int L;
   if (DBG) {
-    L = args.dbg_row0 / kBM + blockIdx.x;
+    L = args.dbg_row0 / BM + blockIdx.x;
   } else {
     L = (int)(blockIdx.x % 8) * args.per_xcd + (int)(blockIdx.x / 8);
     if (L >= args.total) return;
@@ -723,7 +745,7 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   // tokens of this head that exist (a variable-length batch: tiles past them have
   // no row to write and leave at once, before any copy or barrier)
   const int Nv = (int)valid_len(args.nlens, args.lens, bh, args.H, args.N);
-  if (!DBG && qt * kBM >= Nv) return;
+  if (!DBG && qt * BM >= Nv) return;
   Ctx a;
   a.img = args.img; a.ks = args.ks; a.Np = args.Np;
   a.N = (int)args.N; a.qk_shift = __builtin_ctz(args.qk_blk); a.C0 = args.C0; a.L15 = args.L15;
@@ -732,7 +754,7 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   a.dbg_row0 = args.dbg_row0; a.dbg_n = args.dbg_n;
   a.dbg_aqk = args.dbg_aqk; a.dbg_p = args.dbg_p; a.dbg_apv = args.dbg_apv;
   const int N = a.N;  // the layout's tokens per head
-  const int qi = qt * kBM + w * 32 + col;
+  const int qi = qt * BM + w * 32 + col;
   // Keys seen: all Nv, or under block-causal masking (block c) the keys of the row's
   // own block and every earlier one, min(Nv, (i / c + 1) c).  The tile's groups run
   // up to its last row's limit; groups wholly below its first row's limit need no
@@ -741,9 +763,9 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   auto limit = [&](int64_t i) -> int { return c > 0 ? (int)min((int64_t)Nv, (i / c + 1) * c) : Nv; };
   a.klim = limit(qi);
   a.kb = args.kbias != nullptr;
-  const int kmax = limit(min(qt * kBM + kBM - 1, Nv - 1));
+  const int kmax = limit(min(qt * BM + BM - 1, Nv - 1));
   const int ngroups = (kmax + G::TG - 1) / G::TG;
-  const int nfull = min(limit(qt * kBM) / G::TG, ngroups);  // groups no row masks
+  const int nfull = min(limit(qt * BM) / G::TG, ngroups);  // groups no row masks
 
   // ---- prologue: groups 0 .. NB-2 in flight ----------------------------------------
   const int64_t ngp = a.Np / G::TG;
@@ -770,10 +792,9 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   }
   const float sq = args.qs[(int64_t)bh * (a.Np >> a.qk_shift) + (qi >> a.qk_shift)];
 
-  RowState<G::NDB> S;
+  RowState<G::NDB, std::conditional_t<ST, SkipCount, NoCount>> S;
   S.m = -INFINITY;
   S.l = 0.f;
-  S.n_pv = S.n_pv_skip = S.n_tile = S.n_exp_skip = S.n_fix = 0;
 #pragma unroll
   for (int db = 0; db < G::NDB; ++db) {
 #pragma unroll
@@ -797,12 +818,14 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
     group_iter<D, KVB, DBG, true, SM>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
 
   // ---- epilogue ---------------------------------------------------------------------
-  if (!DBG && args.stats && lane == 0) {
-    atomicAdd(args.stats + 0, (unsigned long long)S.n_pv);
-    atomicAdd(args.stats + 1, (unsigned long long)S.n_pv_skip);
-    atomicAdd(args.stats + 2, (unsigned long long)S.n_tile);
-    atomicAdd(args.stats + 3, (unsigned long long)S.n_exp_skip);
-    atomicAdd(args.stats + 4, (unsigned long long)S.n_fix);
+  if constexpr (ST) {
+    if (lane == 0) {
+      atomicAdd(args.stats + 0, (unsigned long long)S.cnt.n_pv);
+      atomicAdd(args.stats + 1, (unsigned long long)S.cnt.n_pv_skip);
+      atomicAdd(args.stats + 2, (unsigned long long)S.cnt.n_tile);
+      atomicAdd(args.stats + 3, (unsigned long long)S.cnt.n_exp_skip);
+      atomicAdd(args.stats + 4, (unsigned long long)S.cnt.n_fix);
+    }
   }
   const float lq = pair_sum(S.l);
   if (DBG && dbg_row && h == 0) {
@@ -831,11 +854,12 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
 
 // The production kernel: two waves per SIMD (<= 256 registers per wave), one for
 // 256-key steps.
-template <int D, int KVB, int SM>
+// ST: the instance that also counts the exact skips (args.stats).
+template <int D, int KVB, int SM, bool ST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Geo<D, KVB, SM>::WPE, Geo<D, KVB, SM>::WPE)))
 void k2_attention(const AttnArgs args) {
   extern __shared__ __align__(16) uint8_t lds[];
-  k2_body<D, KVB, false, SM>(args, lds);
+  k2_body<D, KVB, false, SM, ST>(args, lds);
 }
 
 // The debug run (dumps of one head's row range): one wave per SIMD, so that the
@@ -852,7 +876,8 @@ hipError_t launch_t(const AttnArgs& a, bool dbg, hipStream_t st) {
   using G = Geo<D, KVB, SM>;
   // The dynamic LDS limit is raised on every call (for the current device; the
   // setting is idempotent), so the library keeps no state between calls.
-  const void* fn = dbg ? (const void*)k2_attention_debug<D, KVB, SM> : (const void*)k2_attention<D, KVB, SM>;
+  const void* fn = dbg ? (const void*)k2_attention_debug<D, KVB, SM>
+                      : a.stats ? (const void*)k2_attention<D, KVB, SM, true> : (const void*)k2_attention<D, KVB, SM, false>;
   const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   if (attr != hipSuccess) return attr;
   k2_stage<D, KVB, SM><<<dim3((unsigned)(a.Np / G::TG), (unsigned)a.nheads), 256, 0, st>>>(a);
@@ -860,7 +885,8 @@ hipError_t launch_t(const AttnArgs& a, bool dbg, hipStream_t st) {
     const int first = a.dbg_row0 / kBM, last = (a.dbg_row0 + a.dbg_n - 1) / kBM;
     k2_attention_debug<D, KVB, SM><<<last - first + 1, 256, G::LDS, st>>>(a);
   } else {
-    k2_attention<D, KVB, SM><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
+    if (a.stats) k2_attention<D, KVB, SM, true><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
+    else k2_attention<D, KVB, SM, false><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
   }
   return hipGetLastError();
 }
