@@ -3,7 +3,8 @@
     python -m int4_quantized_attention_amd.build_lib
 
 Each source is compiled to an object in parallel, then linked into
-``int4_quantized_attention_amd/librotattn.so``.  Every HIP source is built with
+``int4_quantized_attention_amd/librotattn.so`` (and the micro-benchmarks of
+``kb.hip`` into ``libkb.so``).  Every HIP source is built with
 IEEE-exact single precision (no fp contraction, correctly rounded division) so
 that the code-deciding arithmetic is bit-reproducible, and with packed fp32
 instructions disabled.
@@ -18,6 +19,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "librotattn.so")
+KB_OUT = os.path.join(HERE, "libkb.so")  # micro-benchmarks (kb.py), not part of the product library
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.cpp", "quantize.hip", "attention.hip", "fallback.hip"]
@@ -42,18 +44,24 @@ def _compile(job) -> str:
 def build() -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = [("attention_inst.hip", ["-DATT_D=%d" % d, "-DATT_KVB=%d" % kv], ".d%d_kv%d" % (d, kv))
-            for d, kv in ATT_INSTANCES] + [(src, [], "") for src in SOURCES]
+            for d, kv in ATT_INSTANCES] + [(src, [], "") for src in SOURCES] + [("kb.hip", [], "")]
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(_compile, jobs))
-    tmp = OUT + ".tmp%d" % os.getpid()
+    kb_obj = objs.pop()  # the micro-benchmarks go into a library of their own
+    _link(objs, OUT)
+    _link([kb_obj], KB_OUT)
+    return OUT
+
+
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link failed")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":

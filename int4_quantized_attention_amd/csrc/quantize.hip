@@ -44,11 +44,61 @@ hipError_t quant_scratch(void** out) {
   return hipSuccess;
 }
 
+// V channel amax over all tokens.  A workgroup takes kVTile tokens of one head:
+// thread t owns 8 consecutive channels (one 16-byte load per token for 16-bit
+// inputs) of every (256 / (D/8))-th token, the partial maxima meet in LDS (red,
+// at least (256 / (D/8)) x (D+1) floats), and one atomic max per channel on the
+// float bits (non-negative floats order like unsigned integers) merges the
+// workgroups.
+constexpr int kVTile = 512;
+template <int D, int DT>
+RA_DEV void vamax_tile(const QuantArgs& a, int bh, int64_t tile, float* red) {
+  constexpr int CG = D / 8, TL = 256 / CG;  // channel groups, tokens in flight
+  const Shape s = a.s;
+  const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
+  const int64_t n0 = tile * kVTile;
+  const int64_t Nb = valid_len(a.nlens, a.lens, bh, s.H, N);
+  const void* base = (const char*)a.v + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
+  const int cg = threadIdx.x % CG, tl = threadIdx.x / CG;
+  float m[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m[e] = 0.f;
+#pragma unroll 4
+  for (int r = tl; r < kVTile; r += TL) {
+    const int64_t n = n0 + r;
+    if (n < Nb) {
+      float x[8];
+      load_slice<DT, 8>(base, n, D, 8 * cg, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(x[e]));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[tl * (D + 1) + 8 * cg + e] = m[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float r = 0.f;
+#pragma unroll
+    for (int k = 0; k < TL; ++k) r = fmaxf(r, red[k * (D + 1) + threadIdx.x]);
+    atomicMax(a.vamax + (int64_t)bh * D + threadIdx.x, __float_as_uint(r));
+  }
+}
+
+// V amax on its own (no smoothing statistics to share a launch with): grid
+// (ceil(Np / kVTile), B*H).
+template <int D, int DT>
+__global__ __launch_bounds__(256) void k1_vamax(QuantArgs a) {
+  __shared__ float red[(256 / (D / 8)) * (D + 1)];
+  vamax_tile<D, DT>(a, blockIdx.y, blockIdx.x, red);
+}
+
 // ---------------------------------------------------------------------------------
 // Channel statistics for smoothing: ordered binary64 partial sums of rotated K (and,
 // with Q smoothing, of rotated Q) over 64-token blocks.  grid (ceil(N/64), B*H, the
-// number of smoothed tensors); z = 0 is K unless only Q is smoothed.  256 threads,
-// four per token, each owning D/4 channels.  partial [B*H][nblk][D] f64.
+// number of smoothed tensors + 1); z = 0 is K unless only Q is smoothed; the last z
+// computes the V amax instead (vamax_tile, the first ceil(Np / kVTile) blocks), so
+// that V's pure stream overlaps the statistics' arithmetic.  256 threads, four per
+// token, each owning D/4 channels.  partial [B*H][nblk][D] f64.
 template <int D, int DT, int ROT>
 __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
   constexpr int TPT = 4, CPT = D / TPT;
@@ -56,6 +106,11 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
   const Shape s = a.s;
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int bh = blockIdx.y, blk = blockIdx.x;
+  if (blockIdx.z == gridDim.z - 1) {
+    static_assert((256 / (D / 8)) * (D + 1) <= kMeanTile * (D + 1), "the V amax fits in R");
+    if ((int64_t)blk * kVTile < a.Np) vamax_tile<D, DT>(a, bh, blk, R);
+    return;
+  }
   const bool isQ = blockIdx.z + (a.smooth ? 0 : 1) == 1;
   const int64_t Nb = valid_len(a.nlens, a.lens, bh, s.H, N);
   const int64_t n0 = (int64_t)blk * kMeanTile;
@@ -79,79 +134,52 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
 }
 
 // Channel means of K (and Q): binary64 sum of the partials in block order, / N, to
-// binary32.  Thread idx: tensor idx / (B*H*D) in the order of k1_kstats' z.  The
-// sum is one dependent chain; the loads run eight ahead of it.
-__global__ void k1_kmean(QuantArgs a) {
-  const int D = a.s.D;
+// binary32.  grid (B*H, tensors in the order of k1_kstats' z); thread c < D owns
+// channel c.  The sum is one dependent chain per channel; it runs over chunks of
+// kMeanChunk partial rows staged in LDS, the next chunk's loads in flight (in
+// registers) while the current one is summed.
+constexpr int kMeanChunk = 32;
+template <int D>
+__global__ __launch_bounds__(256) void k1_kmean(QuantArgs a) {
+  constexpr int PER = kMeanChunk * D / 256;  // partials each thread stages per chunk
+  __shared__ double buf[kMeanChunk * D];
   const int64_t N = (int64_t)a.s.F * a.s.Hs * a.s.Ws;
   const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
-  const int64_t per = (int64_t)a.s.B * a.s.H * D;
-  const int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nz = (a.smooth ? 1 : 0) + (a.smooth_q ? 1 : 0);
-  if (gidx >= nz * per) return;
-  const bool isQ = gidx / per + (a.smooth ? 0 : 1) == 1;
-  const int64_t idx = gidx % per;
-  const int64_t bh = idx / D, c = idx % D;
-  const double* p = (isQ ? a.qpart : a.kpart) + bh * nblk * D + c;
+  const int bh = blockIdx.x;
+  const bool isQ = blockIdx.y + (a.smooth ? 0 : 1) == 1;
+  const double* p = (isQ ? a.qpart : a.kpart) + (int64_t)bh * nblk * D;
+  const int tid = threadIdx.x;
+  double nxt[PER];
+  auto fetch = [&](int64_t b0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i;  // row e / D, channel e % D of the chunk
+      nxt[i] = b0 + e / D < nblk ? p[b0 * D + e] : 0.0;
+    }
+  };
   double total = 0.0;
-  int64_t b = 0;
-  for (; b + 8 <= nblk; b += 8) {
-    double v[8];
+  fetch(0);
+  for (int64_t b0 = 0; b0 < nblk; b0 += kMeanChunk) {
+    __syncthreads();  // the previous chunk has been summed
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = p[(b + i) * D];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) total += v[i];
+    for (int i = 0; i < PER; ++i) buf[tid + 256 * i] = nxt[i];
+    __syncthreads();
+    if (b0 + kMeanChunk < nblk) fetch(b0 + kMeanChunk);
+    if (tid < D) {
+      const int rows = (int)min((int64_t)kMeanChunk, nblk - b0);
+      for (int r = 0; r < rows; ++r) total += buf[r * D + tid];
+    }
   }
-  for (; b < nblk; ++b) total += p[b * D];
   // blocks past the valid tokens hold +0.0 partials: adding them changes nothing
-  const int64_t Nb = valid_len(a.nlens, a.lens, (int)bh, a.s.H, N);
-  (isQ ? a.qmu : a.kmu)[idx] = (float)(total / (double)Nb);
+  if (tid < D) {
+    const int64_t Nb = valid_len(a.nlens, a.lens, bh, a.s.H, N);
+    (isQ ? a.qmu : a.kmu)[(int64_t)bh * D + tid] = (float)(total / (double)Nb);
+  }
 }
 
 __global__ void k1_zero_u32(uint32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
-}
-
-// V channel amax over all tokens.  A workgroup takes kVTile tokens of one head:
-// thread t owns 8 consecutive channels (one 16-byte load per token for 16-bit
-// inputs) of every (256 / (D/8))-th token, the partial maxima meet in LDS, and one
-// atomic max per channel on the float bits (non-negative floats order like unsigned
-// integers) merges the workgroups.
-constexpr int kVTile = 512;
-template <int D, int DT>
-__global__ __launch_bounds__(256) void k1_vamax(QuantArgs a) {
-  constexpr int CG = D / 8, TL = 256 / CG;  // channel groups, tokens in flight
-  __shared__ float red[TL][D + 1];
-  const Shape s = a.s;
-  const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
-  const int bh = blockIdx.y;
-  const int64_t n0 = (int64_t)blockIdx.x * kVTile;
-  const int64_t Nb = valid_len(a.nlens, a.lens, bh, s.H, N);
-  const void* base = (const char*)a.v + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
-  const int cg = threadIdx.x % CG, tl = threadIdx.x / CG;
-  float m[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) m[e] = 0.f;
-#pragma unroll 4
-  for (int r = tl; r < kVTile; r += TL) {
-    const int64_t n = n0 + r;
-    if (n < Nb) {
-      float x[8];
-      load_slice<DT, 8>(base, n, D, 8 * cg, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(x[e]));
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[tl][8 * cg + e] = m[e];
-  __syncthreads();
-  if (threadIdx.x < D) {
-    float r = 0.f;
-#pragma unroll
-    for (int k = 0; k < TL; ++k) r = fmaxf(r, red[k][threadIdx.x]);
-    atomicMax(a.vamax + (int64_t)bh * D + threadIdx.x, __float_as_uint(r));
-  }
 }
 
 // Q / K quantisation: grid (Np/TOK, B*H, 2 (0 = Q, 1 = K)); 256 threads, TPT per
@@ -347,10 +375,12 @@ hipError_t launch_rot(const QuantArgs& a, hipStream_t st) {
   const int BH = a.s.B * a.s.H;
   const int nz = (a.smooth ? 1 : 0) + (a.smooth_q ? 1 : 0);
   if (nz > 0) {
+    // the statistics, with the V amax as the launch's last z
     const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
-    const int64_t nmu = (int64_t)nz * BH * D;
-    k1_kstats<D, DT, ROT><<<dim3((unsigned)nblk, BH, nz), 256, 0, st>>>(a);
-    k1_kmean<<<(unsigned)((nmu + 255) / 256), 256, 0, st>>>(a);
+    k1_kstats<D, DT, ROT><<<dim3((unsigned)nblk, BH, nz + 1), 256, 0, st>>>(a);
+    k1_kmean<D><<<dim3((unsigned)BH, nz), 256, 0, st>>>(a);
+  } else {
+    k1_vamax<D, DT><<<dim3((unsigned)((a.Np + kVTile - 1) / kVTile), BH), 256, 0, st>>>(a);
   }
   // a workgroup covers whole scale blocks: 64 tokens (four threads each) unless
   // qk_blk is 128 (then 128 tokens, two threads each)
@@ -368,8 +398,7 @@ hipError_t launch_quantize_t(const QuantArgs& a, hipStream_t st) {
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)in_tile);
     if (attr != hipSuccess) return attr;
   }
-  k1_zero_u32<<<(unsigned)((nvamax + 255) / 256), 256, 0, st>>>(a.vamax, nvamax);
-  k1_vamax<D, DT><<<dim3((unsigned)((a.Np + kVTile - 1) / kVTile), BH), 256, 0, st>>>(a);
+  k1_zero_u32<<<(unsigned)((nvamax + 255) / 256), 256, 0, st>>>(a.vamax, nvamax);  // V amax starts at 0
   hipError_t e;
   if (a.rot == 1) e = launch_rot<D, DT, 1>(a, st);
   else if (a.rot == 2) e = launch_rot<D, DT, 2>(a, st);
