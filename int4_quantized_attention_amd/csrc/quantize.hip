@@ -245,16 +245,15 @@ __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
     am = wred[g0];
     for (int k = 1; k < wpg; ++k) am = fmaxf(am, wred[g0 + k]);
   }
-  const float inv = am == 0.f ? 0.f : 7.0f / am;
+  // tokens that do not exist hold zeros; inv = 0 gives them code 0 also where 7/am
+  // overflows (0 * inf would give the NaN code)
+  const float inv = (am == 0.f || !valid) ? 0.f : 7.0f / am;
   uint32_t packed[CPT / 8];
 #pragma unroll
   for (int w = 0; w < CPT / 8; ++w) {
     uint32_t word = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int code = am == 0.f ? 0 : quant_code(v[w * 8 + e], inv);
-      word |= ((uint32_t)code & 0xFu) << (4 * e);
-    }
+    for (int e = 0; e < 8; ++e) word |= (code_bits(v[w * 8 + e], inv) & 0xFu) << (4 * e);
     packed[w] = word;
   }
   uint8_t* codes = (isK ? a.kc : a.qc) + ((int64_t)bh * Np + n) * (D / 2) + c0 / 2;
@@ -290,19 +289,22 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
   const float amax = __uint_as_float(a.vamax[(int64_t)bh * D + c]);
   const float inv = amax == 0.f ? 0.f : 7.0f / amax;
   if (blockIdx.x == 0 && g == 0) a.vs[(int64_t)bh * D + c] = amax == 0.f ? 0.f : amax / 7.0f;
-  int codes[TPG];
+  uint32_t cb[TPG];
 #pragma unroll
-  for (int i = 0; i < TPG; ++i) {
-    const int r = g * TPG + i;
-    const bool valid = n0 + r < Nb;
-    codes[i] = (valid && amax != 0.f) ? quant_code(lds_elem<D, DT>(lds, r, c), inv) : 0;
+  for (int i = 0; i < TPG; ++i) cb[i] = code_bits(lds_elem<D, DT>(lds, g * TPG + i, c), inv);
+  if (n0 + kTile > Nb) {
+    // rows past the valid tokens (staged as zeros) take code 0, also where 7/amax
+    // overflows and 0 * inf would give the NaN code
+#pragma unroll
+    for (int i = 0; i < TPG; ++i)
+      if (n0 + g * TPG + i >= Nb) cb[i] = kZeroCodeBits;
   }
   uint32_t words[TPG / 8];
 #pragma unroll
   for (int w = 0; w < TPG / 8; ++w) {
     uint32_t word = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) word |= ((uint32_t)codes[w * 8 + e] & 0xFu) << (4 * e);
+    for (int e = 0; e < 8; ++e) word |= (cb[w * 8 + e] & 0xFu) << (4 * e);
     words[w] = word;
   }
   uint4* dst = (uint4*)(a.vc + ((int64_t)bh * D + c) * (Np / 2) + (n0 + g * TPG) / 2);
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
     for (int ch = 0; ch < TPG / 16; ++ch) {
       int acc = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc += codes[ch * 16 + i];
+      for (int i = 0; i < 16; ++i) acc += code_of_bits(cb[ch * 16 + i]);
       chunk[ch] = acc;
     }
     if (kvb <= TPG) {

@@ -93,11 +93,16 @@ RA_DEV float rope_rot(const char* lds, int r, int c, const Shape& s, int rot, co
   return rope_plain<D, DT>(lds, r, o, trow, lc);
 }
 
+// Grid position of token n = (f*Hs + y)*Ws + x.  Token indices stay below 2^29 (the
+// shape check bounds N by 2^28, plus the padding), so two 32-bit divisions give it
+// exactly; 64-bit divisions cost about a hundred instructions each.
 RA_DEV void token_pos(int64_t n, const Shape& s, int& f, int& y, int& x) {
-  const int64_t hw = (int64_t)s.Hs * s.Ws;
-  f = (int)(n / hw);
-  y = (int)((n / s.Ws) % s.Hs);
-  x = (int)(n % s.Ws);
+  const uint32_t u = (uint32_t)n, ws = (uint32_t)s.Ws, hs = (uint32_t)s.Hs;
+  const uint32_t q = u / ws;  // f*Hs + y
+  const uint32_t ff = q / hs;
+  x = (int)(u - q * ws);
+  y = (int)(q - ff * hs);
+  f = (int)ff;
 }
 
 // ---- per-thread token slices --------------------------------------------------------
@@ -252,10 +257,19 @@ RA_DEV void rotated_slice(const void* base, int64_t n, bool valid, int D, int c0
   if (ROT == 3) hadamard_slice<DD, CPT>(x, c0);
 }
 
-RA_DEV int quant_code(float v, float inv) {
-  float t = __builtin_rintf(v * inv);
-  t = fminf(7.f, fmaxf(-7.f, t));
-  return (int)t;
+// The code of v with inv = fl(7/amax), |v| <= amax, as the bits of fl(t + 1.5 2^23)
+// with t = clamp(fl(v inv), -7, 7): that sum rounds t to the nearest integer, ties to
+// even (the ulp is 1 there and 1.5 2^23 is even), exactly as rint does, and the
+// integer k sits in the low mantissa bits: bits = 0x4B400000 + k, so the low nibble is
+// k's two's-complement nibble.  Clamping before rounding equals clamping after it for
+// |t| < 7.5, which holds whenever inv is finite (|fl(v inv)| <= 7 (1 + 2^-24)^2); the
+// clamp still acts when 7/amax overflows (amax below about 2.06e-38), where it turns
+// +-inf into +-7 and the NaN of 0 * inf into -7, as fmin(7, fmax(-7, .)) does on the
+// unclamped code.  amax = 0 (inv = 0, v = 0) gives k = 0.
+RA_DEV uint32_t code_bits(float v, float inv) {
+  return __float_as_uint(fminf(7.f, fmaxf(-7.f, v * inv)) + 12582912.0f);
 }
+constexpr uint32_t kZeroCodeBits = 0x4B400000u;  // code_bits of a 0 code
+RA_DEV int code_of_bits(uint32_t b) { return (int)(b - kZeroCodeBits); }
 
 }  // namespace ra

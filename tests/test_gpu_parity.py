@@ -157,6 +157,42 @@ def test_edge_single_token_and_zero_query(orc):
     assert_close(out.cpu().numpy().reshape(-1, 128), orc.attention(cfg, ref)["out"])
 
 
+def test_edge_tiny_magnitudes(orc):
+    """Blocks whose amax lies in [2^-126, 7 / FLT_MAX): 7 / amax overflows to inf, the
+    scale amax / 7 is subnormal, and the clamp of the code turns +-inf into +-7 and the
+    NaN of 0 * inf into -7.  Codes and scale bits against the oracle."""
+    cfg = synth.custom(1, 2, 1, 4, 8, 64, 24, 20, 20, 16, 16, dtype="float32", recipe="wan")
+    Q, K, V = synth.make_inputs(cfg)
+    rng = np.random.default_rng(7)
+    tiny = np.array([0.0, 1.2e-38, -1.2e-38, 1.5e-38, -1.5e-38, 2.0e-38, -2.0e-38], np.float32)
+    assert np.all(np.isinf(np.float32(7.0) / tiny[1:]))
+    # Q and K are multiplied by constants of about 1.4 before their blocks are
+    # quantised: scaled by 0.9 they land in the same band
+    qk_tiny = tiny[:5] * np.float32(0.9)
+    Q[0, 0, :16] = rng.choice(qk_tiny, size=(16, 64))  # one whole Q scale block
+    K[0, 1, 16:32] = rng.choice(qk_tiny, size=(16, 64))
+    K[0, 1, 16, :] = 0.0
+    V[0, 0, :, 5] = rng.choice(tiny, size=V.shape[2])  # one V channel
+    shape, z = gpu_quantize(cfg, 0, Q, K, V, smooth=False)
+    ref = orc.quantize(cfg, 0, orc.rope_table(cfg, 0), Q, K, V, smooth_k=False)
+    for name, blk in (("qs", (0, 0)), ("ks", (1, 1)), ("vs", (0, 5))):
+        sc = ref[name].reshape(2, -1)[blk]
+        assert 0 < sc < np.finfo(np.float32).tiny, (name, sc)  # the regime is reached
+    assert np.any(ref["qc"].reshape(2, -1, 64)[0, :16][Q[0, 0, :16] == 0] == -7)
+    compare_codes(cfg, z, ref)
+    # ragged: the last Q/K block and the last V tile hold tokens that do not exist,
+    # whose codes stay 0 (and out of the column sums)
+    cfg = synth.custom(1, 1, 1, 3, 7, 64, 24, 20, 20, 16, 16, dtype="float32", recipe="wan")
+    Q, K, V = synth.make_inputs(cfg)
+    Q[0, 0, 16:] = rng.choice(qk_tiny, size=(5, 64))
+    K[0, 0, 16:] = rng.choice(qk_tiny, size=(5, 64))
+    V[0, 0, :, 3] = rng.choice(tiny, size=V.shape[2])
+    shape, z = gpu_quantize(cfg, 0, Q, K, V, smooth=False)
+    ref = orc.quantize(cfg, 0, orc.rope_table(cfg, 0), Q, K, V, smooth_k=False)
+    assert 0 < ref["qs"].reshape(-1)[1] < np.finfo(np.float32).tiny
+    compare_codes(cfg, z, ref)
+
+
 def test_head_subset_leaves_other_heads(orc):
     cfg = synth.custom(1, 4, 3, 10, 11, 128, 44, 42, 42, 64, 64, dtype="float16", recipe="wan")
     Q, K, V = synth.make_inputs(cfg)
