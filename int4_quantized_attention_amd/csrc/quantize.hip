@@ -97,8 +97,9 @@ __global__ __launch_bounds__(256) void k1_vamax(QuantArgs a) {
 // with Q smoothing, of rotated Q) over 64-token blocks.  grid (ceil(N/64), B*H, the
 // number of smoothed tensors + 1); z = 0 is K unless only Q is smoothed; the last z
 // computes the V amax instead (vamax_tile, the first ceil(Np / kVTile) blocks), so
-// that V's pure stream overlaps the statistics' arithmetic.  256 threads, four per
-// token, each owning D/4 channels.  partial [B*H][nblk][D] f64.
+// that V's pure stream overlaps the statistics' arithmetic.  256 threads, each
+// owning D/4 channels of one token: wave slices (lane = token) for ROT 0-2, four
+// consecutive lanes per token for the Full rotation.  partial [B*H][nblk][D] f64.
 template <int D, int DT, int ROT>
 __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
   constexpr int TPT = 4, CPT = D / TPT;
@@ -114,11 +115,14 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
   const bool isQ = blockIdx.z + (a.smooth ? 0 : 1) == 1;
   const int64_t Nb = valid_len(a.nlens, a.lens, bh, s.H, N);
   const int64_t n0 = (int64_t)blk * kMeanTile;
-  const int lt = threadIdx.x / TPT, c0 = (threadIdx.x % TPT) * CPT;
+  static_assert(kMeanTile == 64, "one token per lane");
+  const int lt = ROT == 3 ? threadIdx.x / TPT : threadIdx.x & 63;
+  const int c0 = ROT == 3 ? (threadIdx.x % TPT) * CPT : wave_slice_c0<D>();
   const int64_t n = n0 + lt;
   const void* base = (const char*)(isQ ? a.q : a.k) + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   float x[CPT];
-  rotated_slice<DT, ROT, CPT, D>(base, n, n < Nb, D, c0, s, a.table, R + lt * (D + 1), x);
+  if constexpr (ROT == 3) rotated_slice<DT, ROT, CPT, D>(base, n, n < Nb, D, c0, s, a.table, R + lt * (D + 1), x);
+  else rotated_wave_slice<DT, ROT, D>(base, n, n < Nb, c0, s, a.table, R, lt, x);
   if (ROT == 2) __syncthreads();  // every row of R read before it is overwritten
 #pragma unroll
   for (int i = 0; i < CPT; ++i) R[lt * (D + 1) + c0 + i] = x[i];
@@ -182,7 +186,86 @@ __global__ void k1_zero_u32(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-// Q / K quantisation: grid (Np/TOK, B*H, 2 (0 = Q, 1 = K)); 256 threads, TPT per
+// Q / K quantisation, wave-sliced (ROT 0-2, qk_blk <= 64): grid (Np/64, B*H, 2 (0 =
+// Q, 1 = K)); lane = token, wave w = channels [w D/4, (w+1) D/4).  A scale block is
+// qk_blk consecutive lanes of all four waves: its amax is a lane-group maximum in
+// each wave, then the four waves' values through LDS.
+template <int D, int DT, int ROT>
+__global__ __launch_bounds__(256) void k1_quant_qk_ws(QuantArgs a) {
+  constexpr int CPT = D / 4;
+  __shared__ float U[ROT == 2 ? 64 * (D + 1) : 1];  // Half exchange rows
+  __shared__ uint32_t wred[256];
+  __shared__ double dsacc[64];
+  __shared__ float mus[2 * D];
+  const Shape s = a.s;
+  const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
+  const int64_t Np = a.Np;
+  const int bh = blockIdx.y;
+  const bool isK = blockIdx.z == 1;
+  const int lane = threadIdx.x & 63;
+  const int c0 = wave_slice_c0<D>(), w = c0 / CPT;
+  const int64_t n = (int64_t)blockIdx.x * 64 + lane;
+  const void* base = (const char*)(isK ? a.k : a.q) + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
+  const bool valid = n < valid_len(a.nlens, a.lens, bh, s.H, N);
+  // the smoothing mean (and mu_q for the dS chain) staged in LDS: every lane of a
+  // wave reads the same words
+  const bool smooth = isK ? a.smooth : a.smooth_q, chain = isK && a.smooth_q;
+  if (smooth && threadIdx.x < D) mus[threadIdx.x] = (isK ? a.kmu : a.qmu)[(int64_t)bh * D + threadIdx.x];
+  if (chain && threadIdx.x < D) mus[D + threadIdx.x] = a.qmu[(int64_t)bh * D + threadIdx.x];
+  float v[CPT];
+  rotated_wave_slice<DT, ROT, D>(base, n, valid, c0, s, a.table, U, lane, v);
+  if (ROT != 2 && (smooth || chain)) __syncthreads();  // (ROT 2 passed a barrier already)
+  if (smooth) {
+    // tokens that do not exist are smoothed too: their amax contribution is dropped
+    // below and their codes are 0 (inv = 0)
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) v[i] = v[i] - mus[c0 + i];
+  }
+  if (chain) {
+    // dS_n = mu_q . K_n: binary64, channels in order (the products are exact), one
+    // chain through the four waves' slices in turn; wave 3 writes it (0 for tokens
+    // that do not exist)
+    const float* mq = mus + D + c0;
+    double acc = 0.0;
+    for (int stg = 0; stg < 4; ++stg) {
+      if (w == stg) {
+        if (stg > 0) acc = dsacc[lane];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) acc = fma((double)mq[i], (double)v[i], acc);
+        dsacc[lane] = acc;
+      }
+      __syncthreads();
+    }
+    if (w == 3) a.kbias[(int64_t)bh * Np + n] = valid ? (float)acc : 0.f;
+  }
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) am = fmaxf(am, fabsf(v[i]));
+  if (!valid) am = 0.f;
+  wred[threadIdx.x] = group_max_u32(__float_as_uint(am), s.qk_blk);
+  __syncthreads();
+  am = __uint_as_float(max(max(wred[lane], wred[64 + lane]), max(wred[128 + lane], wred[192 + lane])));
+  // tokens that do not exist hold zeros; inv = 0 gives them code 0 also where 7/am
+  // overflows (0 * inf would give the NaN code)
+  const float inv = (am == 0.f || !valid) ? 0.f : 7.0f / am;
+  uint32_t packed[CPT / 8];
+  pack_codes<CPT>(v, inv, packed);
+  uint8_t* codes = (isK ? a.kc : a.qc) + ((int64_t)bh * Np + n) * (D / 2) + c0 / 2;
+  if (CPT / 8 == 2) {
+    *(u32x2*)codes = u32x2{packed[0], packed[CPT / 8 - 1]};
+  } else {
+#pragma unroll
+    for (int q = 0; q < CPT / 8; q += 4)
+      *(u32x4*)(codes + 4 * q) = u32x4{packed[q], packed[q + 1], packed[q + 2], packed[q + 3]};
+  }
+  if (w == 0 && (lane % s.qk_blk) == 0) {
+    float* sc = isK ? a.ks : a.qs;
+    sc[(int64_t)bh * (Np / s.qk_blk) + n / s.qk_blk] = am == 0.f ? 0.f : am / 7.0f;
+  }
+}
+
+// Q / K quantisation, token-sliced (the Full rotation, and qk_blk = 128): grid
+// (Np/TOK, B*H, 2 (0 = Q, 1 = K)); 256 threads, TPT per
 // token (TOK = 256/TPT tokens per workgroup, a multiple of qk_blk), each owning
 // CPT = D/TPT consecutive channels.
 template <int D, int DT, int ROT, int TPT>
@@ -249,13 +332,7 @@ __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
   // overflows (0 * inf would give the NaN code)
   const float inv = (am == 0.f || !valid) ? 0.f : 7.0f / am;
   uint32_t packed[CPT / 8];
-#pragma unroll
-  for (int w = 0; w < CPT / 8; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) word |= (code_bits(v[w * 8 + e], inv) & 0xFu) << (4 * e);
-    packed[w] = word;
-  }
+  pack_codes<CPT>(v, inv, packed);
   uint8_t* codes = (isK ? a.kc : a.qc) + ((int64_t)bh * Np + n) * (D / 2) + c0 / 2;
   if (CPT / 8 == 2) {
     *(u32x2*)codes = u32x2{packed[0], packed[CPT / 8 - 1]};
@@ -289,9 +366,11 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
   const float amax = __uint_as_float(a.vamax[(int64_t)bh * D + c]);
   const float inv = amax == 0.f ? 0.f : 7.0f / amax;
   if (blockIdx.x == 0 && g == 0) a.vs[(int64_t)bh * D + c] = amax == 0.f ? 0.f : amax / 7.0f;
-  uint32_t cb[TPG];
+  float vals[TPG];
 #pragma unroll
-  for (int i = 0; i < TPG; ++i) cb[i] = code_bits(lds_elem<D, DT>(lds, g * TPG + i, c), inv);
+  for (int i = 0; i < TPG; ++i) vals[i] = lds_elem<D, DT>(lds, g * TPG + i, c);
+  uint32_t cb[TPG];
+  code_bits_n<TPG>(vals, inv, cb);
   if (n0 + kTile > Nb) {
     // rows past the valid tokens (staged as zeros) take code 0, also where 7/amax
     // overflows and 0 * inf would give the NaN code
@@ -301,12 +380,7 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
   }
   uint32_t words[TPG / 8];
 #pragma unroll
-  for (int w = 0; w < TPG / 8; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) word |= (cb[w * 8 + e] & 0xFu) << (4 * e);
-    words[w] = word;
-  }
+  for (int w = 0; w < TPG / 8; ++w) words[w] = pack8(cb + 8 * w);
   uint4* dst = (uint4*)(a.vc + ((int64_t)bh * D + c) * (Np / 2) + (n0 + g * TPG) / 2);
 #pragma unroll
   for (int w = 0; w < TPG / 8; w += 4) dst[w / 4] = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
@@ -319,10 +393,10 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
     int chunk[TPG / 16];
 #pragma unroll
     for (int ch = 0; ch < TPG / 16; ++ch) {
-      int acc = 0;
+      uint32_t acc = 0;  // sum of 16 code bits: the codes' sum plus 16 kZeroCodeBits (mod 2^32)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc += code_of_bits(cb[ch * 16 + i]);
-      chunk[ch] = acc;
+      for (int i = 0; i < 16; ++i) acc += cb[ch * 16 + i];
+      chunk[ch] = (int)(acc - 16u * kZeroCodeBits);
     }
     if (kvb <= TPG) {
       int acc = 0;
@@ -384,9 +458,15 @@ hipError_t launch_rot(const QuantArgs& a, hipStream_t st) {
   } else {
     k1_vamax<D, DT><<<dim3((unsigned)((a.Np + kVTile - 1) / kVTile), BH), 256, 0, st>>>(a);
   }
-  // a workgroup covers whole scale blocks: 64 tokens (four threads each) unless
-  // qk_blk is 128 (then 128 tokens, two threads each)
-  return a.s.qk_blk > 64 ? launch_qk<D, DT, ROT, 2>(a, st) : launch_qk<D, DT, ROT, 4>(a, st);
+  // a workgroup covers whole scale blocks: 64 tokens unless qk_blk is 128 (then 128
+  // tokens, two threads each)
+  if (a.s.qk_blk > 64) return launch_qk<D, DT, ROT, 2>(a, st);
+  if constexpr (ROT == 3) {
+    return launch_qk<D, DT, ROT, 4>(a, st);
+  } else {
+    k1_quant_qk_ws<D, DT, ROT><<<dim3((unsigned)(a.Np / 64), (unsigned)(a.s.B * a.s.H), 2), 256, 0, st>>>(a);
+    return hipSuccess;
+  }
 }
 
 template <int D, int DT>

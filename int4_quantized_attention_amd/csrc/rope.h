@@ -257,19 +257,154 @@ RA_DEV void rotated_slice(const void* base, int64_t n, bool valid, int D, int c0
   if (ROT == 3) hadamard_slice<DD, CPT>(x, c0);
 }
 
-// The code of v with inv = fl(7/amax), |v| <= amax, as the bits of fl(t + 1.5 2^23)
-// with t = clamp(fl(v inv), -7, 7): that sum rounds t to the nearest integer, ties to
-// even (the ulp is 1 there and 1.5 2^23 is even), exactly as rint does, and the
-// integer k sits in the low mantissa bits: bits = 0x4B400000 + k, so the low nibble is
-// k's two's-complement nibble.  Clamping before rounding equals clamping after it for
-// |t| < 7.5, which holds whenever inv is finite (|fl(v inv)| <= 7 (1 + 2^-24)^2); the
-// clamp still acts when 7/amax overflows (amax below about 2.06e-38), where it turns
-// +-inf into +-7 and the NaN of 0 * inf into -7, as fmin(7, fmax(-7, .)) does on the
-// unclamped code.  amax = 0 (inv = 0, v = 0) gives k = 0.
-RA_DEV uint32_t code_bits(float v, float inv) {
-  return __float_as_uint(fminf(7.f, fmaxf(-7.f, v * inv)) + 12582912.0f);
+// ---- wave-sliced token tiles ------------------------------------------------------
+// A workgroup of four waves takes 64 tokens, one per lane; wave w owns the channel
+// slice [w D/4, (w + 1) D/4) of each of them.  The slice start is the same across
+// the wave, so what depends on the channel (the RoPE segment of a pair, the Half
+// partner of a channel) is one scalar decision per wave, and the per-lane work is
+// the arithmetic and one address add per table or LDS access.
+
+// First channel of this wave's slice (a wave-uniform value).
+template <int D>
+RA_DEV int wave_slice_c0() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * (D / 4);
 }
-constexpr uint32_t kZeroCodeBits = 0x4B400000u;  // code_bits of a 0 code
+
+// RoPE in place on a wave slice of token (f, y, x): pair k is global pair p = c0/2 + k,
+// whose table entry sits at byte offset Q_j + 8k, Q_j = 4 (row_j - 2 p_j + c0) for the
+// segment j of p (row_j: the token's row in segment j's table, p_j: its first pair).
+// Every Q_j is >= 0 (segment j's rows start past the 2 p_j floats of the earlier
+// segments' first rows).
+template <int ROT, int CPT>
+RA_DEV void rope_wave_slice(float (&x)[CPT], int c0, const float* tab, const Shape& s, int f, int y, int xx) {
+  const uint32_t Q0 = 4u * (uint32_t)(f * s.Df + c0);
+  const uint32_t Q1 = 4u * (uint32_t)((s.F - 1) * s.Df + y * s.Dh + c0);
+  const uint32_t Q2 = 4u * (uint32_t)((s.F - 1) * s.Df + (s.Hs - 1) * s.Dh + xx * s.Dw + c0);
+  const int k1 = s.Df / 2 - c0 / 2, k2 = (s.Df + s.Dh) / 2 - c0 / 2;  // first slice pair of segments 1, 2
+#pragma unroll
+  for (int k = 0; k < CPT / 2; ++k) {
+    const uint32_t Q = k < k1 ? Q0 : (k < k2 ? Q1 : Q2);
+    const f32x2 t = *(const f32x2*)((const char*)tab + (size_t)Q + 8 * k);
+    const float a = x[2 * k], b = x[2 * k + 1];
+    if (ROT == 1) {
+      const float bb = b * t[1], ba = b * t[0];
+      x[2 * k] = __builtin_fmaf(a, t[0], bb);
+      x[2 * k + 1] = __builtin_fmaf(a, t[1], -ba);
+    } else {
+      const float bs = b * t[1], bc = b * t[0];
+      x[2 * k] = __builtin_fmaf(a, t[0], -bs);
+      x[2 * k + 1] = __builtin_fmaf(a, t[1], bc);
+    }
+  }
+}
+
+// RoPE + rotation (ROT 0, 1, 2) of this wave's slice of token n, in the lane's
+// registers.  U: LDS of 64 token rows of D + 1 floats (ROT 2 exchanges the RoPE
+// outputs through it; output pair (c, c + 1) of segment j takes x1 = U[(c + o_j)/2]
+// and x2 = U[(c + o_j)/2 + Dj/2], the same pairs as half_slice).  Contains a
+// workgroup barrier when ROT == 2 (all threads must call).
+template <int DT, int ROT, int D>
+RA_DEV void rotated_wave_slice(const void* base, int64_t n, bool valid, int c0, const Shape& s,
+                               const float* tab, float* U, int lane, float (&x)[D / 4]) {
+  constexpr int CPT = D / 4;
+  static_assert(ROT >= 0 && ROT <= 2, "the Full rotation mixes all channels: token-sliced path");
+  if (valid) {
+    int f, y, xx;
+    token_pos(n, s, f, y, xx);
+    load_slice<DT, CPT>(base, n, D, c0, x);
+    rope_wave_slice<ROT, CPT>(x, c0, tab, s, f, y, xx);
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) x[i] = 0.f;
+  }
+  if (ROT == 2) {
+    float* row = U + lane * (D + 1);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) row[c0 + i] = x[i];
+    __syncthreads();
+    if (valid) {
+      const float r = 0.70710678118654752440f;
+#pragma unroll
+      for (int k = 0; k < CPT / 2; ++k) {
+        const int c = c0 + 2 * k;
+        const int o = c < s.Df ? 0 : (c < s.Df + s.Dh ? s.Df : s.Df + s.Dh);
+        const int h = (c < s.Df ? s.Df : (c < s.Df + s.Dh ? s.Dh : s.Dw)) >> 1;
+        const int S = (c + o) >> 1;
+        const float x1 = row[S], x2 = row[S + h];
+        const float sm = x1 + x2, df = x1 - x2;
+        x[2 * k] = sm * r;
+        x[2 * k + 1] = df * r;
+      }
+    }
+  }
+}
+
+// Maximum of non-negative binary32 values (as their bits, which order like unsigned
+// integers) over groups of `width` consecutive lanes (a wave-uniform power of two
+// <= 64): quad permutations, the 8- and 16-lane mirrors, a 32-lane swizzle, then
+// the two wave halves.  All lanes must be active.
+RA_DEV uint32_t group_max_u32(uint32_t v, int width) {
+  if (width >= 2) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  if (width >= 4) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  if (width >= 8) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  if (width >= 16) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  if (width >= 32) v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  if (width >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+  return v;
+}
+
+// The code of v with inv = fl(7/amax), |v| <= amax, as the bits of fl(t + M), t =
+// clamp(fl(v inv), -7, 7), M = 1.5 2^23 + 8: in [2^23, 2^24) the ulp is 1, so the sum
+// rounds t to an integer, and as M is even, a tie goes to the even integer exactly
+// as rint(t) would; the bits are then 0x4B400008 + k for the code k.  Clamping before
+// rounding equals clamping after it for |t| < 7.5, which holds whenever inv is finite
+// (|fl(v inv)| <= 7 (1 + 2^-24)^2).  The clamp still acts when 7/amax overflows (amax
+// below about 2.06e-38): it turns +-inf into +-7 and the NaN of 0 * inf into -7, as
+// fmin(7, fmax(-7, .)) does after rounding.  amax = 0 (inv = 0, v = 0) gives k = 0.
+RA_DEV uint32_t code_bits(float v, float inv) {
+  return __float_as_uint(fminf(7.f, fmaxf(-7.f, v * inv)) + 12582920.0f);
+}
+// The same without the clamp, for finite inv (then |fl(v inv)| < 7.5).
+RA_DEV uint32_t code_bits_finite(float v, float inv) { return __float_as_uint(v * inv + 12582920.0f); }
+// The low nibble k + 8 of the bits, in [1, 15], is k in offset binary.
+constexpr uint32_t kZeroCodeBits = 0x4B400008u;  // code_bits of a 0 code
 RA_DEV int code_of_bits(uint32_t b) { return (int)(b - kZeroCodeBits); }
+
+// Eight code_bits values -> one word of two's-complement nibbles, element e in bits
+// [4e, 4e + 4).  sum_e b_e 16^e (mod 2^32) is sum_e (k_e + 8) 16^e plus a constant
+// (the 0x4B400000 parts shifted), the offset-binary nibbles carry nothing, and
+// flipping each nibble's top bit maps k + 8 to k's two's-complement nibble.
+constexpr uint32_t pack_bias() {
+  uint32_t c = 0;
+  for (int e = 0; e < 8; ++e) c += (kZeroCodeBits - 8u) << (4 * e);
+  return c;
+}
+RA_DEV uint32_t pack8(const uint32_t* b) {
+  uint32_t w = b[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) w += b[e] << (4 * e);
+  return (w - pack_bias()) ^ 0x88888888u;
+}
+
+// code_bits of CNT values sharing inv: the clamp-free form unless 7/amax overflowed.
+template <int CNT>
+RA_DEV void code_bits_n(const float* v, float inv, uint32_t* b) {
+  if (__builtin_expect(__builtin_isinf(inv), 0)) {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) b[i] = code_bits(v[i], inv);
+  } else {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) b[i] = code_bits_finite(v[i], inv);
+  }
+}
+
+// CPT values (a multiple of 8) -> CPT/8 words of packed codes.
+template <int CPT>
+RA_DEV void pack_codes(const float (&v)[CPT], float inv, uint32_t (&out)[CPT / 8]) {
+  uint32_t b[CPT];
+  code_bits_n<CPT>(v, inv, b);
+#pragma unroll
+  for (int w = 0; w < CPT / 8; ++w) out[w] = pack8(b + 8 * w);
+}
 
 }  // namespace ra
