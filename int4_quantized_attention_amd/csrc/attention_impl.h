@@ -363,7 +363,9 @@ RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::
 // or keys a block-causal row does not see); they count as absent.  SM 1: one K scale
 // for the whole step, so the maximum needs one multiplication; SM 2 (per-key K scales,
 // Sl the group's scales in LDS): without Q smoothing each key's c = fl(fl(sq sk_j) C0)
-// is formed here, and the scores st are replaced by their exponents y.
+// is formed for the running maximum, and the scores of the tiles whose exps are
+// computed are replaced by their exponents y; the skip tests take a bound of y from
+// the tile's maximum of t_j = fl(A_j c_j).
 template <int D, int KVB, bool DBG, bool MASK, int SM, class RS>
 RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl, const float* Tl,
                        const float* Sl, float sq, f32x16 (&st)[Geo<D, KVB>::TPS],
@@ -387,17 +389,36 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     // ---- running maximum (max of the exact integer scores, then times c) -----------
     float imt[G::TPS];  // per tile: the largest score of the lane's present keys
     if (pk) {
-      // per-key c: the maximum of t = fl(A c_j) over the lane's present keys
+      // per-key c: the maximum of t_j = fl(A_j c_j), c_j = fl(fl(sq sk_j) C0), over the
+      // lane's present keys.  First a bound from W = max_j fl(A_j sk_j): the three
+      // roundings between A_j sq sk_j C0 and t_j, and the one in fl(A_j sk_j), move it
+      // by at most a factor (1 +- 2^-24)^4 each way, so t_j <= fl(fl(fl(W sq) C0) f)
+      // with f = 1 + 2^-20 for W >= 0 and 1 - 2^-20 for W < 0 (those three roundings
+      // taken into account as well: 7 2^-24 < 2^-20); adding 2^-126 covers products
+      // that underflow (a c_j of 0 gives t_j = 0).  When no lane's bound exceeds the
+      // running maximum, the tile cannot move it and the bound, within about 2^-20 of
+      // the exact maximum, stands in for it (here and in the skip tests); otherwise
+      // the exact maximum is formed.
 #pragma unroll
       for (int t = 0; t < G::TPS; ++t) {
-        float im = -INFINITY;
         const float* sk = Sl + 32 * (tb + t) + 16 * h;
+        float wm = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           bool ok = act;
           if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
-          const float c = (sq * sk[v]) * a.C0;
-          im = fmaxf(im, ok ? st[t][v] * c : -INFINITY);
+          wm = fmaxf(wm, ok ? st[t][v] * sk[v] : -INFINITY);
+        }
+        float im = ((wm * sq) * a.C0) * (wm >= 0.f ? 1.0f + 0x1p-20f : 1.0f - 0x1p-20f) + 0x1p-126f;
+        if (__any(im > S.m)) {
+          im = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            bool ok = act;
+            if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
+            const float c = (sq * sk[v]) * a.C0;
+            im = fmaxf(im, ok ? st[t][v] * c : -INFINITY);
+          }
         }
         imt[t] = im;
       }
@@ -435,27 +456,23 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
     S.m = mnew;
     const bool guard = mnew >= 262144.0f;
     // The level code below forms y = fma(st, c, nm).  With per-key scales the
-    // exponents y = fma(A, c_j, L15 - m) are formed here instead, into st, and the
-    // code reads them back through c = 1, nm = 0 (exactly y).
-    float nm = a.L15 - mnew;
+    // exponents y = fma(A, c_j, L15 - m) of a tile whose exps are needed are formed
+    // into st (below, once its pair's skip decision is known), and the code reads
+    // them back through c = 1, nm = 0 (exactly y).  The skip tests take a bound: with
+    // tmax the largest t_j = fl(A_j c_j) of the tile's present keys, A_j c_j <= t_j +
+    // max(|t_j| 2^-24, 2^-150) <= b = fl(fl(tmax + |tmax| 2^-23) + 2^-126) (the inner
+    // sum lies at least one ulp above a normal tmax, the outer one covers 0 and
+    // subnormals), and y_j = fl(A_j c_j + (L15 - m)) is monotone in A_j c_j, so every
+    // exact y_j of the tile is at most fl(b + (L15 - m)).  (No present key: tmax =
+    // -inf and the bound is NaN, which no test passes.)
+    const float ny = a.L15 - mnew;  // L15 - m, for the per-key exponents
+    float nm = ny;
     float cu[G::TPS];
     float ymax[G::TPS];
     if (pk) {
 #pragma unroll
       for (int t = 0; t < G::TPS; ++t) {
-        float ym = -INFINITY;
-        const float* sk = Sl + 32 * (tb + t) + 16 * h;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          bool ok = act;
-          if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
-          const float c = (sq * sk[v]) * a.C0;
-          const float y = __builtin_fmaf(st[t][v], c, nm);
-          // (with kv_blk 16 the other lane half's keys form the next step: keep them)
-          st[t][v] = act ? y : st[t][v];
-          ym = fmaxf(ym, ok ? y : -INFINITY);
-        }
-        ymax[t] = ym;
+        ymax[t] = (__builtin_fmaf(fabsf(imt[t]), 0x1p-23f, imt[t]) + 0x1p-126f) + ny;
         cu[t] = 1.0f;
       }
       nm = 0.f;
@@ -500,6 +517,21 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
       bool flag = guard;
       const bool allz = !DBG && !__any(fmaxf(ymax[pp * PT], ymax[pp * PT + PT - 1]) >= a.T0);
       S.cnt.unit(PT);
+      if (pk) {
+        // per-key scales: the exponents of the pair's tiles whose exps are computed
+#pragma unroll
+        for (int tp = 0; tp < PT; ++tp) {
+          const int t = pp * PT + tp;
+          if (allz && ngl[t]) continue;
+          const float* sk = Sl + 32 * (tb + t) + 16 * h;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float c = (sq * sk[v]) * a.C0;
+            // (with kv_blk 16 the other lane half's keys form the next step: keep them)
+            st[t][v] = act ? __builtin_fmaf(st[t][v], c, ny) : st[t][v];
+          }
+        }
+      }
       if (allz) {
         // every level of the pair is 0: the keys enter the normaliser only (same
         // order of additions as the level path); no margin, MFMA, V read or exact
