@@ -72,15 +72,19 @@ RA_DEV uint32_t min3_u16(uint32_t a, uint32_t b, uint32_t c) {
 // Fast level: with t = p + kMagic, p the hardware exp2 of y (within 1.5 * 2^-24
 // relative of 2^y), the sum lies in [128, 256) where the ulp is 2^-16, so byte 2 of
 // t's bits is the nearest integer to p and the low 16 bits are the distance to the
-// next rounding boundary (the 4 * 2^-16 offset keeps the tie at 7.5 on its correct
-// side).  When that margin exceeds kMarginMin the fast level is the exact one; the
-// exp error, the add's rounding and the offset use at most 6 units of it.
+// rounding boundary below.  In units of 2^-16 the computed value exceeds the exact
+// 2^y + 0.5 by the 4-unit offset, give or take the exp error (at most 1.5 * 2^-24 *
+// 16 = 0.094 units) and the add's rounding (0.5 units), i.e. by 3.4 to 4.6 units: it
+// never falls below a boundary the exact value lies above, and it lies above one the
+// exact value is below (or on: the tie 2^y = 0.5 at y = -1) only with a margin of at
+// most 4.6 units.  A margin above kMarginMin = 4 therefore makes the fast level the
+// exact one.
 // Otherwise the exact level is fixed from y by the two thresholds around the fast
 // level (it is within one of the exact level): T[k-1] is the smallest binary32 y
 // with level >= k, T[15] = T[16] = +inf.  Every y the attention forms is at most
 // L15 plus half an ulp of the running maximum, so p stays below 16 (the maximum
 // guard below sends larger ones to the exact path).
-constexpr uint32_t kMarginMin = 6;
+constexpr uint32_t kMarginMin = 4;
 RA_DEV uint32_t level_bits(float p) { return __float_as_uint(p + kMagic); }
 RA_DEV int fast_level(uint32_t t) { return (int)((t >> 16) & 0xFFu); }
 RA_DEV bool margin_clear(uint32_t t) { return (t & 0xFFFFu) > kMarginMin; }
@@ -598,7 +602,8 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
       if (allz) continue;
       if (DBG || __any(flag)) {
         // exact levels of the whole pair (the debug run always takes this path, so
-        // that it dumps the exact code of every key)
+        // that it dumps the exact code of every key), each fixed from y and the fast
+        // level already packed in pb (no second exp)
         S.cnt.fix();
 #pragma unroll
         for (int tp = 0; tp < PT; ++tp) {
@@ -612,9 +617,7 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
               bool ok = act;
               if (MASK) ok = ok && (j0 + t * 32 + 16 * h + v < a.klim);
               const float y = __builtin_fmaf(st[t][v], cu[t], nm);
-              float p = exp2_hw(y);
-              if (MASK || KVB < 32) p = ok ? p : 0.f;
-              int r = exact_level(y, fast_level(level_bits(p)), Tl);
+              int r = exact_level(y, (int)(((uint32_t)pb[tp][w] >> (8 * e)) & 0xFFu), Tl);
               if (MASK || KVB < 32) r = ok ? r : 0;
               rr |= (uint32_t)r << (8 * e);
               if (DBG && dbg_row && act) {
