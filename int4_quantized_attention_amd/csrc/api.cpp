@@ -361,10 +361,17 @@ rotattn_status rotattn_int4_attention_ex(const rotattn_shape* s,
                         opts ? opts->skip_stats : nullptr);
 }
 
+// the fallback's workspace: RoPE'd fp16 Q [B*H][Np][D], then the K / V^T group images
+static size_t fb_q_bytes(const rotattn_shape* s) {
+  return align256((size_t)s->B * s->H * rotattn_padded_tokens(s) * s->D * sizeof(uint16_t));
+}
+static size_t fb_img_bytes(const rotattn_shape* s) {
+  return align256((size_t)s->B * s->H * (rotattn_padded_tokens(s) / 64) * ra::fallback_image_bytes(s->D));
+}
+
 size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s) {
   if (!s || rotattn_check_shape(s) != ROTATTN_OK) return 0;
-  const size_t per = (size_t)s->B * s->H * rotattn_padded_tokens(s) * s->D * sizeof(uint16_t);
-  return 3 * align256(per);
+  return fb_q_bytes(s) + fb_img_bytes(s);
 }
 
 rotattn_status rotattn_fp16_fallback_ex(const rotattn_shape* s, rotattn_dtype in_dtype,
@@ -395,10 +402,9 @@ rotattn_status rotattn_fp16_fallback_ex(const rotattn_shape* s, rotattn_dtype in
   a.Np = rotattn_padded_tokens(s);
   a.q = q; a.k = k; a.v = v;
   a.table = rope_table;
-  const size_t per = align256((size_t)BH * a.Np * s->D * sizeof(uint16_t));
   a.qr = (_Float16*)workspace;
-  a.kr = (_Float16*)((char*)workspace + per);
-  a.vt = (_Float16*)((char*)workspace + 2 * per);
+  a.img = (uint8_t*)workspace + fb_q_bytes(s);
+  a.img_bytes = (int64_t)fb_img_bytes(s);
   a.out = out;
   a.out_kind = (int)out_dtype;
   a.nqt = (int)((a.N + 127) / 128);

@@ -57,7 +57,6 @@ constexpr int kBM = 32 * kWaves;
 constexpr float kMagic = 128.5f + 4.0f / 65536.0f;
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 // minimum of the low 16 bits of three values (v_min3_u16; only the low half of the
 // result is meaningful)
@@ -304,22 +303,10 @@ struct RowState {
   C cnt;
 };
 
-// Copy the LDS image of group g into ring slot `buf`.  Wave w copies the w-th
-// quarter of the image, one contiguous kilobyte (16 bytes per lane) per copy,
-// through a buffer resource over the head's images: the lane offset is the only
-// vector operand, the group and wave offsets are scalar, and the immediate offset
-// applies to the global and the LDS address alike.  Reads past the resource's
-// range return zero.
-template <int J>
-RA_DEV void dma_one(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int lane_off, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 4096 * (J >> 2)), 16, lane_off,
-                                           soff + 4096 * (J >> 2), 1024 * (J & 3), 0);
-}
-template <int... J>
-RA_DEV void dma_all(std::integer_sequence<int, J...>, __amdgpu_buffer_rsrc_t r, uint8_t* dst, int lane_off,
-                    int soff) {
-  (dma_one<J>(r, dst, lane_off, soff), ...);
-}
+// Copy the LDS image of group g into ring slot `buf`: wave w copies the w-th quarter
+// of the image, one contiguous kilobyte per copy (dma_all), through a buffer resource
+// over the head's images; the lane offset is the only vector operand, the group and
+// wave offsets are scalar.
 template <int D, int KVB, int SM>
 RA_DEV void dma_group(__amdgpu_buffer_rsrc_t r, int g, uint8_t* buf) {
   using G = Geo<D, KVB, SM>;
@@ -327,14 +314,6 @@ RA_DEV void dma_group(__amdgpu_buffer_rsrc_t r, int g, uint8_t* buf) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   dma_all(std::make_integer_sequence<int, G::NDMA>{}, r, buf + w * WB, 16 * (threadIdx.x & 63),
           g * G::IMG + w * WB);
-}
-
-// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
-// lgkmcnt left unconstrained)
-template <int n>
-RA_DEV void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
 template <int D, int KVB>

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -37,6 +39,32 @@ RA_DEV void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copies (buffer_load_dwordx4 ... lds) through a buffer
+// resource: copy J moves one contiguous kilobyte (16 bytes per lane) to dst + 1024 J
+// from the resource's byte offset soff + 1024 J + the lane's offset; the immediate
+// offset applies to the global and the LDS address alike, and reads past the
+// resource's range return zero.
+template <int J>
+RA_DEV void dma_one(__amdgpu_buffer_rsrc_t r, uint8_t* dst, int lane_off, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + 4096 * (J >> 2)), 16, lane_off,
+                                           soff + 4096 * (J >> 2), 1024 * (J & 3), 0);
+}
+template <int... J>
+RA_DEV void dma_all(std::integer_sequence<int, J...>, __amdgpu_buffer_rsrc_t r, uint8_t* dst, int lane_off,
+                    int soff) {
+  (dma_one<J>(r, dst, lane_off, soff), ...);
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left unconstrained)
+template <int n>
+RA_DEV void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
 // max / sum of a value and the one held by lane l ^ 32 (v_permlane32_swap, no LDS)

@@ -7,10 +7,14 @@
 //
 // Pre-pass (k3_prep): plain 3D RoPE of Q and K in binary32 (same op order as the
 // quantisation kernel) rounded to binary16, and V transposed to [D][Np] binary16.
+// The pre-pass writes K and V^T of every 64-key group as one image in exactly the
+// byte layout the group occupies in LDS (K rows permuted for the S^T register
+// layout and padded, then the padded V^T rows).
 // Main kernel (k3_attention): one workgroup = 4 waves x 32 query rows, two waves per
 // SIMD; S^T = K Q^T on v_mfma_f32_32x32x16_f16, online softmax in binary32 with the
 // hardware exp2, P rounded to binary16 and fed straight back as the B operand of
-// O^T = V^T P^T; K/V tiles double-buffered in LDS with loads one group ahead.
+// O^T = V^T P^T; the group images are copied straight from global memory into a
+// two-slot LDS ring (buffer_load ... lds), one group ahead.
 #include "common.h"
 #include "kernels.h"
 #include "rope.h"
@@ -20,6 +24,32 @@ namespace ra {
 constexpr int kFbTile = 64;
 constexpr int kFbKV = 64;   // keys per online-softmax step (and per LDS group)
 constexpr int kFbBM = 128;  // query rows per workgroup
+
+template <int D>
+struct FbGeo {
+  static constexpr int TG = kFbKV;             // keys per group
+  static constexpr int NT = TG / 32;           // 32-key tiles per group
+  static constexpr int NDB = D / 32;           // 32-row d blocks of O^T
+  static constexpr int KC = D / 16;            // 16-deep chunks of Q K^T (f16 MFMA)
+  static constexpr int KROW = D + 8;           // halves
+  static constexpr int VROW = TG + 8;          // halves
+  static constexpr int KBUF = TG * KROW;       // halves
+  static constexpr int VBUF = D * VROW;        // halves
+  static constexpr int IMG = ((KBUF + VBUF) * 2 + 4095) / 4096 * 4096;  // bytes of one group's image
+  static constexpr int NDMA = IMG / 4096;      // 16-byte copies per thread per group
+  static constexpr int LDS = 2 * IMG;          // two ring slots
+};
+
+size_t fallback_image_bytes(int D) { return D == 128 ? FbGeo<128>::IMG : FbGeo<64>::IMG; }
+
+// K rows are permuted inside each 32-key tile so that the S^T accumulator of lane
+// half h holds keys 16h..16h+15 of the tile in register order: key kk of a group
+// sits in image row (kk & ~31) + (v & 3) + 8 (v >> 2) + 4 h, with r = kk & 31,
+// h = r >> 4, v = r & 15.
+RA_DEV int fb_row_of_key(int kk) {
+  const int r = kk & 31, hh = r >> 4, v = r & 15;
+  return (kk & ~31) + (v & 3) + 8 * (v >> 2) + 4 * hh;
+}
 
 // grid (Np/64, B*H, 3): z = 0 Q, 1 K (RoPE -> f16), 2 V (transpose -> f16)
 template <int D, int DT>
@@ -34,8 +64,11 @@ __global__ __launch_bounds__(256) void k3_prep(FbArgs a) {
   const int64_t Nv = valid_len(a.nlens, a.lens, bh, s.H, N);  // tokens that exist
   stage_tile<D, DT>(base, n0, Nv, kFbTile, lds);
   __syncthreads();
+  static_assert(kFbTile == FbGeo<D>::TG, "a pre-pass tile is one key group");
+  // this tile's group image (K and V^T of the 64 keys n0 .. n0+63)
+  _Float16* gimg = (_Float16*)(a.img + ((int64_t)bh * (Np / kFbTile) + blockIdx.x) * FbGeo<D>::IMG);
   if (which < 2) {
-    _Float16* dst = (which == 0 ? a.qr : a.kr) + ((int64_t)bh * Np + n0) * D;
+    _Float16* dst = which == 0 ? a.qr + ((int64_t)bh * Np + n0) * D : nullptr;
     for (int e = threadIdx.x; e < kFbTile * D; e += blockDim.x) {
       const int r = e / D, c = e % D;
       float v = 0.f;
@@ -44,101 +77,47 @@ __global__ __launch_bounds__(256) void k3_prep(FbArgs a) {
         token_pos(n0 + r, s, f, y, x);
         v = rope_rot<D, DT>(lds, r, c, s, 0, a.table, f, y, x);
       }
-      dst[(int64_t)r * D + c] = (_Float16)v;
+      if (which == 0) dst[(int64_t)r * D + c] = (_Float16)v;
+      else gimg[fb_row_of_key(r) * FbGeo<D>::KROW + c] = (_Float16)v;
     }
   } else {
-    _Float16* dst = a.vt + (int64_t)bh * D * Np + n0;
+    _Float16* dst = gimg + FbGeo<D>::KBUF;
     for (int e = threadIdx.x; e < kFbTile * D; e += blockDim.x) {
       const int c = e / kFbTile, r = e % kFbTile;
       const float v = (n0 + r < Nv) ? lds_elem<D, DT>(lds, r, c) : 0.f;
-      dst[(int64_t)c * Np + r] = (_Float16)v;
+      dst[c * FbGeo<D>::VROW + r] = (_Float16)v;
     }
   }
 }
 
-template <int D>
-struct FbGeo {
-  static constexpr int TG = kFbKV;             // keys per group
-  static constexpr int NT = TG / 32;           // 32-key tiles per group
-  static constexpr int NDB = D / 32;           // 32-row d blocks of O^T
-  static constexpr int KC = D / 16;            // 16-deep chunks of Q K^T (f16 MFMA)
-  static constexpr int KROW = D + 8;           // halves
-  static constexpr int VROW = TG + 8;          // halves
-  static constexpr int KBUF = TG * KROW;       // halves
-  static constexpr int VBUF = D * VROW;        // halves
-  static constexpr int LDS = 2 * (KBUF + VBUF) * 2;  // bytes
-  static constexpr int KU = TG * D / 8;        // 16-byte global units of a K group
-  static constexpr int VU = D * TG / 8;
-  static constexpr int KUT = (KU + 255) / 256;
-  static constexpr int VUT = (VU + 255) / 256;
-};
-
 // fields the device helpers need, copied out of the kernel argument block
 struct FbCtx {
-  const _Float16* kr;
-  const _Float16* vt;
   int64_t Np;
   int N;
   int klim;  // keys this lane's query row sees: N, or its block-causal limit
   float scale_log2;
 };
 
+// Copy the image of group g into ring slot buf: wave w copies the w-th quarter of
+// the image, one contiguous kilobyte per copy.
 template <int D>
-RA_DEV void fb_load(const FbCtx& a, int bh, int g, i32x4 (&rk)[FbGeo<D>::KUT], i32x4 (&rv)[FbGeo<D>::VUT]) {
+RA_DEV void fb_dma(__amdgpu_buffer_rsrc_t r, int g, uint8_t* buf) {
   using G = FbGeo<D>;
-  const i32x4* ks = (const i32x4*)(a.kr + ((int64_t)bh * a.Np + (int64_t)g * G::TG) * D);
-#pragma unroll
-  for (int i = 0; i < G::KUT; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    if (G::KU % 256 == 0 || u < G::KU) rk[i] = ks[u];
-  }
-#pragma unroll
-  for (int i = 0; i < G::VUT; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    if (G::VU % 256 == 0 || u < G::VU) {
-      const int d = u / (G::TG / 8), c = u % (G::TG / 8);
-      rv[i] = ((const i32x4*)(a.vt + ((int64_t)bh * D + d) * a.Np + (int64_t)g * G::TG))[c];
-    }
-  }
+  constexpr int WB = G::NDMA * 1024;  // bytes per wave
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  dma_all(std::make_integer_sequence<int, G::NDMA>{}, r, buf + w * WB, 16 * (threadIdx.x & 63), g * G::IMG + w * WB);
 }
 
-// K rows are permuted inside each 32-key tile so that the S^T accumulator of lane
-// half h holds keys 16h..16h+15 of the tile in register order.
-template <int D>
-RA_DEV void fb_store(_Float16* Kl, _Float16* Vl, const i32x4 (&rk)[FbGeo<D>::KUT], const i32x4 (&rv)[FbGeo<D>::VUT]) {
-  using G = FbGeo<D>;
-#pragma unroll
-  for (int i = 0; i < G::KUT; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    if (G::KU % 256 == 0 || u < G::KU) {
-      const int kk = u / (D / 8), c = u % (D / 8);
-      const int r = kk & 31, hh = r >> 4, v = r & 15;
-      const int row = (kk & ~31) + (v & 3) + 8 * (v >> 2) + 4 * hh;
-      *(i32x4*)(Kl + row * G::KROW + 8 * c) = rk[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < G::VUT; ++i) {
-    const int u = threadIdx.x + 256 * i;
-    if (G::VU % 256 == 0 || u < G::VU) {
-      const int d = u / (G::TG / 8), c = u % (G::TG / 8);
-      *(i32x4*)(Vl + d * G::VROW + 8 * c) = rv[i];
-    }
-  }
-}
-
-// MASK: the group holds keys at or past some row's limit; they count as absent
+// Group g on its image in LDS slot cur (K rows, then V^T rows), while the copy of
+// group g + 1 into the other slot is in flight.  MASK: the group holds keys at or
+// past some row's limit; they count as absent.
 template <int D, bool MASK>
-RA_DEV void fb_group(const FbCtx& a, int g, int ngroups, _Float16* lds, i32x4 (&rk)[FbGeo<D>::KUT],
-                     i32x4 (&rv)[FbGeo<D>::VUT], const f16x8 (&qop)[FbGeo<D>::KC], int bh,
+RA_DEV void fb_group(const FbCtx& a, int g, const uint8_t* cur, const f16x8 (&qop)[FbGeo<D>::KC],
                      f32x16 (&O)[FbGeo<D>::NDB], float& m, float& l) {
   using G = FbGeo<D>;
   const int lane = threadIdx.x & 63, h = lane >> 5, col = lane & 31;
-  const bool odd = g & 1;
-  _Float16* const kb_cur = lds + (odd ? G::KBUF : 0);
-  _Float16* const kb_nxt = lds + (odd ? 0 : G::KBUF);
-  _Float16* const vb_cur = lds + 2 * G::KBUF + (odd ? G::VBUF : 0);
-  _Float16* const vb_nxt = lds + 2 * G::KBUF + (odd ? 0 : G::VBUF);
+  const _Float16* const kb_cur = (const _Float16*)cur;
+  const _Float16* const vb_cur = kb_cur + G::KBUF;
   f32x16 st[G::NT];
 #pragma unroll
   for (int t = 0; t < G::NT; ++t) {
@@ -149,8 +128,6 @@ RA_DEV void fb_group(const FbCtx& a, int g, int ngroups, _Float16* lds, i32x4 (&
       st[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop[kc], kc == 0 ? zero : st[t], 0, 0, 0);
     }
   }
-  if (g + 1 < ngroups) fb_store<D>(kb_nxt, vb_nxt, rk, rv);
-  if (g + 2 < ngroups) fb_load<D>(a, bh, g + 2, rk, rv);
   const int j0 = g * G::TG;
   float mloc = -INFINITY;
 #pragma unroll
@@ -195,7 +172,6 @@ RA_DEV void fb_group(const FbCtx& a, int g, int ngroups, _Float16* lds, i32x4 (&
       }
     }
   }
-  lds_barrier();  // the loads of group g+2 stay in flight
 }
 
 template <int D>
@@ -213,7 +189,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int Nv = (int)valid_len(args.nlens, args.lens, bh, args.s.H, args.N);
   if (qt * kFbBM >= Nv) return;
   FbCtx a;
-  a.kr = args.kr; a.vt = args.vt; a.Np = args.Np; a.N = (int)args.N; a.scale_log2 = args.scale_log2;
+  a.Np = args.Np; a.N = (int)args.N; a.scale_log2 = args.scale_log2;
   const int N = a.N;  // the layout's tokens per head
   const int qi = qt * kFbBM + w * 32 + col;
   // keys seen: all Nv, or min(Nv, (i / c + 1) c) under block-causal masking (block
@@ -238,14 +214,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int ngroups = (kmax + G::TG - 1) / G::TG;
   const int nfull = min(limit(qt * kFbBM) / G::TG, ngroups);  // groups no row masks
-  i32x4 rk[G::KUT], rv[G::VUT];
-  fb_load<D>(a, bh, 0, rk, rv);
-  fb_store<D>(flds, flds + 2 * G::KBUF, rk, rv);
-  if (ngroups > 1) fb_load<D>(a, bh, 1, rk, rv);
+  // the head's group images through a buffer resource that never reaches past the
+  // workspace; group 0 in flight, then per group: the copy of group g + 1 into the
+  // slot group g - 1 used (free since the last barrier), the group's work, a wait
+  // for this wave's copy and one barrier (which covers the other waves' copies)
+  const int64_t ngp = a.Np / G::TG;
+  const int64_t head0 = (int64_t)bh * ngp * G::IMG;
+  const int64_t avail = args.img_bytes - head0;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(args.img + head0), (short)0, (int)(avail < ngp * G::IMG ? (avail > 0 ? avail : 0) : ngp * G::IMG),
+      0x00020000);
+  uint8_t* const ring = (uint8_t*)flds;
+  fb_dma<D>(rsrc, 0, ring);
+  wait_vm<0>();
   lds_barrier();
   int g = 0;
-  for (; g < nfull; ++g) fb_group<D, false>(a, g, ngroups, flds, rk, rv, qop, bh, O, m, l);
-  for (; g < ngroups; ++g) fb_group<D, true>(a, g, ngroups, flds, rk, rv, qop, bh, O, m, l);
+  for (; g < nfull; ++g) {
+    if (g + 1 < ngroups) fb_dma<D>(rsrc, g + 1, ring + ((g + 1) & 1) * G::IMG);
+    fb_group<D, false>(a, g, ring + (g & 1) * G::IMG, qop, O, m, l);
+    wait_vm<0>();
+    lds_barrier();
+  }
+  for (; g < ngroups; ++g) {
+    if (g + 1 < ngroups) fb_dma<D>(rsrc, g + 1, ring + ((g + 1) & 1) * G::IMG);
+    fb_group<D, true>(a, g, ring + (g & 1) * G::IMG, qop, O, m, l);
+    wait_vm<0>();
+    lds_barrier();
+  }
 
   const float lq = l + __shfl_xor(l, 32, 64);
   if (qi < Nv) {

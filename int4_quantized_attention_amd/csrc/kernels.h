@@ -83,9 +83,9 @@ struct FbArgs {
   const void* k;
   const void* v;
   const float* table;
-  _Float16* qr;   // workspace: RoPE'd Q  [B*H][Np][D] f16
-  _Float16* kr;   // workspace: RoPE'd K  [B*H][Np][D] f16
-  _Float16* vt;   // workspace: V^T       [B*H][D][Np] f16 (32-key groups permuted)
+  _Float16* qr;     // workspace: RoPE'd Q  [B*H][Np][D] f16
+  uint8_t* img;     // workspace: per head, one LDS image per 64-key group (fallback_image_bytes(D) each)
+  int64_t img_bytes;  // bytes of the image region
   void* out;
   int out_kind;  // 0 binary32, 1 binary16, 2 bfloat16
   int nqt, total, per_xcd;
@@ -114,5 +114,7 @@ hipError_t launch_attention(const AttnArgs& a, int D, int kv_blk, bool dbg, hipS
 size_t attention_workspace_bytes(int D, int kv_blk, int qk_blk, int64_t BH, int64_t Np);
 hipError_t launch_fallback_prep(const FbArgs& a, int dtype, hipStream_t st);
 hipError_t launch_fallback(const FbArgs& a, hipStream_t st);
+// bytes of one 64-key group's LDS image of the fallback (K rows, then V^T rows)
+size_t fallback_image_bytes(int D);
 
 }  // namespace ra
