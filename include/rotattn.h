@@ -257,7 +257,12 @@ rotattn_status rotattn_int4_attention(const rotattn_shape* s,
  *   in_dtype   F32, F16 or BF16 (Q, K after RoPE and V are rounded to binary16).
  *   out_dtype  F32, F16 or BF16.
  *   rope_table plain (cos, sin) table: rotattn_build_rope_table(s, NONE, ...).
- *   heads      as above.  workspace >= rotattn_fp16_fallback_workspace(s). */
+ *   heads      as above.
+ *   workspace  device, >= rotattn_fp16_fallback_workspace(s) bytes: RoPE'd binary16
+ *              Q, then per head and 64-key group the LDS image of K and V^T (36 KiB
+ *              per 64 keys for D = 128, 20 KiB for D = 64); scratch of the call.
+ *              Shapes whose images exceed 2^31 bytes per head (N beyond about 3.7
+ *              million tokens for D = 128) return ROTATTN_E_UNSUPPORTED. */
 size_t rotattn_fp16_fallback_workspace(const rotattn_shape* s);
 rotattn_status rotattn_fp16_fallback(const rotattn_shape* s, rotattn_dtype in_dtype,
                                      const void* q, const void* k, const void* v,

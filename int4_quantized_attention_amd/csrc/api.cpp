@@ -388,6 +388,8 @@ rotattn_status rotattn_fp16_fallback_ex(const rotattn_shape* s, rotattn_dtype in
   if (!q || !k || !v || !rope_table || !out || !workspace) return ROTATTN_E_NULL;
   if (in_dtype < ROTATTN_F32 || in_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
   if (out_dtype < ROTATTN_F32 || out_dtype > ROTATTN_BF16) return ROTATTN_E_ARG;
+  // one head's images are addressed through a buffer resource with a 32-bit range
+  if (fb_img_bytes(s) / ((size_t)s->B * s->H) > (size_t)INT32_MAX) return ROTATTN_E_UNSUPPORTED;
   if (workspace_bytes < rotattn_fp16_fallback_workspace(s)) return ROTATTN_E_WORKSPACE;
   const int BH = s->B * s->H;
   if (heads) {

@@ -119,6 +119,12 @@ RA_DEV void fb_group(const FbCtx& a, int g, const uint8_t* cur, const f16x8 (&qo
   const _Float16* const kb_cur = (const _Float16*)cur;
   const _Float16* const vb_cur = kb_cur + G::KBUF;
   f32x16 st[G::NT];
+  // the score MFMAs at raised wave priority: while they wait for the matrix pipe the
+  // other wave of the SIMD issues its softmax, and each one issues as soon as the
+  // pipe frees (1% faster than without)
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < G::NT; ++t) {
 #pragma unroll
@@ -128,6 +134,9 @@ RA_DEV void fb_group(const FbCtx& a, int g, const uint8_t* cur, const f16x8 (&qo
       st[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop[kc], kc == 0 ? zero : st[t], 0, 0, 0);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
   const int j0 = g * G::TG;
   float mloc = -INFINITY;
 #pragma unroll

@@ -1,11 +1,13 @@
 // Micro-benchmarks of the MI355X (gfx950) rates the kernels are measured against:
-// back-to-back MFMA throughput per instruction form, HBM streaming bandwidth, and
-// the error of the hardware exp2 (v_exp_f32) that the P-level fast path relies on.
+// back-to-back MFMA throughput per instruction form, HBM streaming bandwidth, LDS
+// read bandwidth alone and feeding f16 MFMAs, and the error of the hardware exp2
+// (v_exp_f32) that the P-level fast path relies on.
 // Built into libkb.so, separate from the product library; driven by kb.py.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -85,6 +87,60 @@ __global__ __launch_bounds__(256) void kb_read_k(const f32x4* __restrict__ src, 
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// LDS reads: each wave reads 16 bytes per lane per ds_read_b128, 8 per round at
+// consecutive kilobytes (no bank conflicts), over a 64 KiB buffer (two workgroups per
+// CU).  MFMA = 1: each read instead feeds one v_mfma_f32_32x32x16_f16 as its A
+// operand (B from registers, four accumulator chains), 1 KiB per 32768 flops, the
+// ratio of an attention kernel with 32 query rows per wave.  Per workgroup, lane 0
+// of wave 0 records the shader clocks of its loop (s_memtime).
+constexpr int kLdsBytes = 65536;
+template <int MFMA>
+__global__ __launch_bounds__(256) void kb_lds_k(int iters, float* out, unsigned long long* cycles) {
+  extern __shared__ __align__(16) uint8_t kb_lds[];
+  const int t = threadIdx.x;
+  for (int i = t * 16; i < kLdsBytes; i += 256 * 16) {
+    const u32x4 v = {(unsigned)i, (unsigned)i + 1u, (unsigned)i + 2u, (unsigned)i + 3u};
+    *(u32x4*)(kb_lds + i) = v;
+  }
+  __syncthreads();
+  const unsigned long long c0 = __builtin_readcyclecounter();
+  // wave w reads its own 16 KiB quarter, alternating halves from round to round; the
+  // memory clobber keeps the compiler from reusing a previous round's values
+  const uint8_t* const base = kb_lds + (t >> 6) * 16384 + (t & 63) * 16;
+  float r = 0.f;
+  if constexpr (MFMA == 0) {
+    unsigned acc = 0;
+    for (int i = 0; i < iters; ++i) {
+      const uint8_t* const p = base + (i & 1) * 8192;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const u32x4 v = *(const u32x4*)(p + u * 1024);
+        acc = acc + v[0] + v[1];
+        acc = acc + v[2] + v[3];
+      }
+      asm volatile("" ::: "memory");
+    }
+    r = (float)acc;
+  } else {
+    const f16x8 b = {(_Float16)t, 1, 2, 3, 4, 5, 6, 7};
+    f32x16 acc[kChains] = {};
+    for (int i = 0; i < iters; ++i) {
+      const uint8_t* const p = base + (i & 1) * 8192;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const f16x8 a = *(const f16x8*)(p + u * 1024);
+        acc[u % kChains] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[u % kChains], 0, 0, 0);
+      }
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) r += acc[c][0] + acc[c][15];
+  }
+  const unsigned long long c1 = __builtin_readcyclecounter();
+  out[blockIdx.x * 256 + t] = r;
+  if (t == 0) cycles[blockIdx.x] = c1 - c0;
+}
+
 // out[i] = v_exp_f32 of the binary32 value with bit pattern first + i
 __global__ __launch_bounds__(256) void kb_exp2_k(uint32_t first, int64_t n, float* out) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
@@ -122,6 +178,17 @@ int kb_read_launch(const void* src, int64_t bytes, int blocks, float* out, void*
   kb_read_k<<<blocks, 256, 0, (hipStream_t)stream>>>((const f32x4*)src, bytes / 16, out);
   return (int)hipGetLastError();
 }
+// LDS micro-benchmark (mfma 0: reads alone, 1: reads feeding f16 MFMAs) on `blocks`
+// workgroups of 4 waves with 64 KiB of LDS each, `iters` rounds of 8 reads per wave.
+// out: device float [blocks * 256]; cycles: device u64 [blocks].
+int kb_lds_launch(int mfma, int blocks, int iters, float* out, unsigned long long* cycles, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (mfma) kb_lds_k<1><<<blocks, 256, kLdsBytes, st>>>(iters, out, cycles);
+  else kb_lds_k<0><<<blocks, 256, kLdsBytes, st>>>(iters, out, cycles);
+  return (int)hipGetLastError();
+}
+int kb_lds_bytes(void) { return kLdsBytes; }
+
 // first + n <= 2^32; out: device float [n]
 int kb_exp2_launch(uint32_t first, int64_t n, float* out, void* stream) {
   if (n < 0 || (uint64_t)first + (uint64_t)n > ((uint64_t)1 << 32)) return (int)hipErrorInvalidValue;

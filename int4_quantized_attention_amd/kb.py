@@ -3,6 +3,8 @@
 * back-to-back MFMA throughput of each instruction form the kernels use, against
   the published dense peaks;
 * HBM streaming bandwidth (16-byte copy and read);
+* LDS read bandwidth (ds_read_b128), alone and feeding one f16 MFMA per kilobyte
+  read (an attention kernel's ratio with 32 query rows per wave);
 * the error of the hardware exp2 (v_exp_f32) over every binary32 exponent the P
   level code meets, in units of 2^-24 relative, against binary64 exp2.
 
@@ -46,6 +48,7 @@ def lib():
     L.kb_copy_launch.argtypes = [VP, VP, I64, I32, VP]
     L.kb_read_launch.argtypes = [VP, I64, I32, VP, VP]
     L.kb_exp2_launch.argtypes = [ctypes.c_uint32, I64, VP, VP]
+    L.kb_lds_launch.argtypes = [I32, I32, I32, VP, VP, VP]
     return L
 
 
@@ -95,6 +98,31 @@ def hbm_rates(gib=4):
             "bytes": n}
 
 
+def lds_rates(L, iters=20000):
+    """LDS read bandwidth, alone and feeding f16 MFMAs, with one and two workgroups
+    of 4 waves (64 KiB of LDS each) per CU.  Bytes per clock per CU come from the
+    shader clocks each workgroup counts around its loop; the GB/s from HIP events."""
+    res = {}
+    for mode, name in ((0, "reads"), (1, "reads+f16 mfma")):
+        for per_cu in (1, 2):
+            blocks = 256 * per_cu
+            out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+            cyc = torch.zeros(blocks, dtype=torch.int64, device="cuda")
+            run = lambda: L.kb_lds_launch(mode, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                          ctypes.c_void_p(cyc.data_ptr()), _stream())
+            assert run() == 0
+            torch.cuda.synchronize()
+            ms = _time(run)
+            wg_bytes = 4 * iters * 8 * 1024
+            clocks = float(cyc.double().median())
+            r = {"GBps": round(blocks * wg_bytes / (ms * 1e-3) / 1e9, 1),
+                 "bytes_per_clock_per_cu": round(per_cu * wg_bytes / clocks, 1), "ms": round(ms, 3)}
+            if mode == 1:
+                r["TFLOPS"] = round(blocks * 4 * iters * 8 * 2 * 32 * 32 * 16 / (ms * 1e-3) / 1e12, 1)
+            res["%s, %d workgroup%s per CU" % (name, per_cu, "s" if per_cu > 1 else "")] = r
+    return res
+
+
 def exp2_error(lo=-4.0, hi=4.0, skip_below=2.0 ** -12, chunk=1 << 25):
     """Largest relative error of v_exp_f32 over every binary32 y in [lo, hi] with
     |y| >= skip_below, in units of 2^-24."""
@@ -127,6 +155,7 @@ def main():
     L = lib()
     res = {"mfma": mfma_rates(L, iters=5000 if args.quick else 50000),
            "hbm": hbm_rates(1 if args.quick else 4),
+           "lds": lds_rates(L, iters=2000 if args.quick else 20000),
            "exp2": exp2_error()}
     for name, r in res["mfma"].items():
         print("MFMA %-20s %9.1f TOPS  %5.1f%% of the published dense peak" % (name, r["TOPS"],
@@ -134,6 +163,9 @@ def main():
     h = res["hbm"]
     print("HBM copy %.1f GB/s (%.1f%% of 8 TB/s), read %.1f GB/s (%.1f%%)" % (
         h["copy_GBps"], 100 * h["copy_GBps"] / HBM_PEAK_GBPS, h["read_GBps"], 100 * h["read_GBps"] / HBM_PEAK_GBPS))
+    for name, r in res["lds"].items():
+        print("LDS %-36s %8.1f GB/s  %6.1f B/clock/CU%s" % (
+            name, r["GBps"], r["bytes_per_clock_per_cu"], ("  %.1f TFLOPS" % r["TFLOPS"]) if "TFLOPS" in r else ""))
     e = res["exp2"]
     print("v_exp_f32: max relative error %.4f x 2^-24 at y = %r over %d values" % (
         e["max_rel_err_units_2^-24"], e["at_y"], e["values"]))

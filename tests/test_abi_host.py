@@ -133,6 +133,30 @@ def test_null_and_bad_args_return_before_launch(L):
     assert L.rotattn_status_str(0) == b"ok"
 
 
+def test_images_beyond_a_32bit_range_per_head_are_unsupported(L):
+    """A head's group images are addressed through a buffer resource with a 32-bit
+    range: shapes whose images exceed 2^31 bytes per head return UNSUPPORTED before
+    any launch (the fallback keeps 36 KiB per 64 keys at D = 128, the INT4 path 36 KiB
+    per 128 keys)."""
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    nul = None
+    big = 1 << 44
+    base = dict(synth.CONFIGS["wan720p"], B=1, H=1, F=1, Hs=2048, Ws=2048)  # N = 4.19M tokens
+    s = ra.Shape.of(base)
+    assert ra.rotattn_check_shape(s) == 0
+    st = L.rotattn_fp16_fallback(ctypes.byref(s), 1, fake, fake, fake, fake, nul, 0, 1, fake, fake, big, nul)
+    assert st == 3
+    # the INT4 images still fit at this length, so the call gets as far as the
+    # workspace check; at twice the length they do not
+    st = L.rotattn_int4_attention(ctypes.byref(s), fake, fake, fake, fake, fake, fake, nul, 0, 0,
+                                  fake, nul, fake, 64, nul)
+    assert st == 4
+    s2 = ra.Shape.of(dict(base, F=2))
+    st = L.rotattn_int4_attention(ctypes.byref(s2), fake, fake, fake, fake, fake, fake, nul, 0, 0,
+                                  fake, nul, fake, big, nul)
+    assert st == 3
+
+
 @pytest.mark.parametrize("cfgname", ["tiny", "wan480p", "hunyuan720p"])
 @pytest.mark.parametrize("rot", [0, 1, 2])
 def test_rope_table_matches_oracle(L, orc, cfgname, rot):
