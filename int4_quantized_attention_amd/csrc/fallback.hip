@@ -62,30 +62,47 @@ __global__ __launch_bounds__(256) void k3_prep(FbArgs a) {
   const void* src = which == 0 ? a.q : (which == 1 ? a.k : a.v);
   const void* base = (const char*)src + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   const int64_t Nv = valid_len(a.nlens, a.lens, bh, s.H, N);  // tokens that exist
+  // grid positions of the tile's rows, once per row
+  __shared__ int pos[3][kFbTile];
+  if (which < 2 && threadIdx.x < kFbTile) {
+    int f = 0, y = 0, x = 0;
+    if (n0 + threadIdx.x < Nv) token_pos(n0 + threadIdx.x, s, f, y, x);
+    pos[0][threadIdx.x] = f;
+    pos[1][threadIdx.x] = y;
+    pos[2][threadIdx.x] = x;
+  }
   stage_tile<D, DT>(base, n0, Nv, kFbTile, lds);
   __syncthreads();
   static_assert(kFbTile == FbGeo<D>::TG, "a pre-pass tile is one key group");
+  static_assert(256 % (D / 2) == 0 && 256 % (kFbTile / 2) == 0, "whole rows per pass");
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   // this tile's group image (K and V^T of the 64 keys n0 .. n0+63)
   _Float16* gimg = (_Float16*)(a.img + ((int64_t)bh * (Np / kFbTile) + blockIdx.x) * FbGeo<D>::IMG);
   if (which < 2) {
+    // a thread owns the channel pair (c, c + 1) of rows r, r + 256/(D/2), ...: one
+    // 4-byte store per row
     _Float16* dst = which == 0 ? a.qr + ((int64_t)bh * Np + n0) * D : nullptr;
-    for (int e = threadIdx.x; e < kFbTile * D; e += blockDim.x) {
-      const int r = e / D, c = e % D;
-      float v = 0.f;
+    const int c = 2 * (threadIdx.x % (D / 2));
+    for (int r = threadIdx.x / (D / 2); r < kFbTile; r += 256 / (D / 2)) {
+      float v0 = 0.f, v1 = 0.f;
       if (n0 + r < Nv) {
-        int f, y, x;
-        token_pos(n0 + r, s, f, y, x);
-        v = rope_rot<D, DT>(lds, r, c, s, 0, a.table, f, y, x);
+        const int f = pos[0][r], y = pos[1][r], x = pos[2][r];
+        v0 = rope_rot<D, DT>(lds, r, c, s, 0, a.table, f, y, x);
+        v1 = rope_rot<D, DT>(lds, r, c + 1, s, 0, a.table, f, y, x);
       }
-      if (which == 0) dst[(int64_t)r * D + c] = (_Float16)v;
-      else gimg[fb_row_of_key(r) * FbGeo<D>::KROW + c] = (_Float16)v;
+      const f16x2 o = {(_Float16)v0, (_Float16)v1};
+      if (which == 0) *(f16x2*)(dst + (int64_t)r * D + c) = o;
+      else *(f16x2*)(gimg + fb_row_of_key(r) * FbGeo<D>::KROW + c) = o;
     }
   } else {
+    // V^T: a thread owns the token pair (r, r + 1) of channels c, c + 256/32, ...
     _Float16* dst = gimg + FbGeo<D>::KBUF;
-    for (int e = threadIdx.x; e < kFbTile * D; e += blockDim.x) {
-      const int c = e / kFbTile, r = e % kFbTile;
-      const float v = (n0 + r < Nv) ? lds_elem<D, DT>(lds, r, c) : 0.f;
-      dst[c * FbGeo<D>::VROW + r] = (_Float16)v;
+    const int r = 2 * (threadIdx.x % (kFbTile / 2));
+    for (int c = threadIdx.x / (kFbTile / 2); c < D; c += 256 / (kFbTile / 2)) {
+      const float v0 = (n0 + r < Nv) ? lds_elem<D, DT>(lds, r, c) : 0.f;
+      const float v1 = (n0 + r + 1 < Nv) ? lds_elem<D, DT>(lds, r + 1, c) : 0.f;
+      const f16x2 o = {(_Float16)v0, (_Float16)v1};
+      *(f16x2*)(dst + c * FbGeo<D>::VROW + r) = o;
     }
   }
 }

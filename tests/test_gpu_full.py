@@ -3,8 +3,9 @@ benchmark times: codes of sampled heads bit-exact, outputs of sampled rows (firs
 tile, ragged last tile, random rows) within tolerance of the oracle; on the first,
 a middle and the ragged last query tile of the first and last head, the debug
 dumps (A_qk, P codes, per-step P V sums, m) bit-exact with the oracle and the
-production output equal to the dense debug run bit for bit; the FP16 fallback;
-per-head routing of the mixed-precision config."""
+production output equal to the dense debug run bit for bit; the FP16 fallback,
+on medium ragged shapes and at the full sizes; per-head routing of the
+mixed-precision config."""
 import numpy as np
 import pytest
 import torch
@@ -132,6 +133,34 @@ def test_full_config_int4(orc, case):
         o = orc.attention(c1, ref, rows=rows)["out"]
         assert_close(out[0, h].cpu().numpy()[rows], o)
         _integer_parity(orc, shape, z, out, c1, ref, h, name)
+
+
+@pytest.mark.parametrize("name", ["wan720p", "hunyuan720p"])
+def test_full_config_fallback(orc, name):
+    """The FP16 fallback at the full size, in the configuration the benchmark times
+    (every head in one call, binary16 in and out): sampled rows (first tile, ragged
+    last tile, random rows) of the first and last head against the oracle."""
+    cfg = synth.CONFIGS[name]
+    N, D, H = synth.n_tokens(cfg), cfg["D"], cfg["H"]
+    print("case", name, flush=True)
+    Q, K, V = synth.make_inputs(cfg)
+    shape = ra.Shape.of(cfg)
+    q, k, v = (torch.from_numpy(x).to(torch.float16).cuda() for x in (Q, K, V))
+    del Q, K, V
+    tab = ra.rotattn_build_rope_table(shape, 0).cuda()
+    ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
+    out = torch.full((1, H, N, D), float("nan"), dtype=torch.float16, device="cuda")
+    ra.rotattn_fp16_fallback(shape, q, k, v, tab, out, ws)
+    torch.cuda.synchronize()
+    del q, k, v, ws
+    for h in (0, H - 1):
+        c1, qh, kh, vh = _one_head(cfg, 0, h)
+        rows = rows_sample(N, 24, seed=h)
+        ref = orc.fallback_attention(c1, orc.rope_table(c1, 0), qh, kh, vh, rows=rows)
+        # binary16 output: its rounding (half an ulp, at most 2^-11 relative) on top of
+        # the binary32 bar
+        tol = (2e-3 + 2.0**-11 * float(np.abs(ref).max()), 1e-3 + 2.0**-11)
+        assert_close(out[0, h].float().cpu().numpy()[rows], ref, *tol, what="fallback O")
 
 
 def _windows(N):
