@@ -54,7 +54,7 @@ namespace ra {
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;
-constexpr float kMagic = 128.5f + 4.0f / 65536.0f;
+constexpr float kMagic = 128.5f + 1.0f / 65536.0f;
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -72,18 +72,19 @@ RA_DEV uint32_t min3_u16(uint32_t a, uint32_t b, uint32_t c) {
 // relative of 2^y), the sum lies in [128, 256) where the ulp is 2^-16, so byte 2 of
 // t's bits is the nearest integer to p and the low 16 bits are the distance to the
 // rounding boundary below.  In units of 2^-16 the computed value exceeds the exact
-// 2^y + 0.5 by the 4-unit offset, give or take the exp error (at most 1.5 * 2^-24 *
-// 16 = 0.094 units) and the add's rounding (0.5 units), i.e. by 3.4 to 4.6 units: it
-// never falls below a boundary the exact value lies above, and it lies above one the
-// exact value is below (or on: the tie 2^y = 0.5 at y = -1) only with a margin of at
-// most 4.6 units.  A margin above kMarginMin = 4 therefore makes the fast level the
-// exact one.
+// 2^y + 0.5 by the 1-unit offset, give or take the exp error (at most 1.5 * 2^-24 *
+// 16 = 0.094 units) and the add's rounding (0.5 units), i.e. by 0.406 to 1.594 units:
+// it never falls below a boundary the exact value lies above (the offset is larger
+// than the 0.594 units of error), and it lies above one the exact value is below (or
+// on: the tie 2^y = 0.5 at y = -1) only with a margin of at most 1.594 units, that is
+// at most 1 (t sits on the 2^-16 grid, so the margin is a whole number of units).  A
+// margin above kMarginMin = 1 therefore makes the fast level the exact one.
 // Otherwise the exact level is fixed from y by the two thresholds around the fast
 // level (it is within one of the exact level): T[k-1] is the smallest binary32 y
 // with level >= k, T[15] = T[16] = +inf.  Every y the attention forms is at most
 // L15 plus half an ulp of the running maximum, so p stays below 16 (the maximum
 // guard below sends larger ones to the exact path).
-constexpr uint32_t kMarginMin = 4;
+constexpr uint32_t kMarginMin = 1;
 RA_DEV uint32_t level_bits(float p) { return __float_as_uint(p + kMagic); }
 RA_DEV int fast_level(uint32_t t) { return (int)((t >> 16) & 0xFFu); }
 RA_DEV bool margin_clear(uint32_t t) { return (t & 0xFFFFu) > kMarginMin; }

@@ -5,7 +5,7 @@ method beyond locating the inputs).
   guard_case()       row maxima of at least 2^18 in log2 units, where the kernel
                      sends every non-skipped unit down the exact-level path;
   tie_window_case()  a 64-key unit whose largest exponent y' lies in
-                     [-1 - 1.7e-4, -1]: its exact levels are all 0 (2^-1 is a tie
+                     [-1 - 1.7e-5, -1]: its exact levels are all 0 (2^-1 is a tie
                      that rounds to even, and anything below rounds down), while the
                      hardware-exp level of that key reads 1 with an unclear margin.
                      The running maximum moved before it, so the output accumulator
@@ -52,7 +52,7 @@ def tie_window_case(orc, seed=0):
     cfg = synth.custom(1, 1, 1, 8, 32, 128, 44, 42, 42, 16, 64, dtype="float32", recipe="tiny", rot="none")
     N, D = 256, 128
     C0, L15 = np.float32(orc.c0(D)), np.float32(orc.l15())
-    lo_win, hi_win = np.float32(-1.00017), np.float32(-1.0)
+    lo_win, hi_win = np.float32(-1.000017), np.float32(-1.0)
     found = None
     sk = np.float32(0.05)
     for _ in range(20000):
