@@ -42,7 +42,9 @@ hipError_t launch_level_probe(uint32_t first, int64_t n, uint8_t* out, const flo
 
 template <int D, int KVB>
 size_t ws_bytes(int qk_blk, int64_t BH, int64_t Np) {
-  const size_t img = scale_mode(KVB, qk_blk) == 2 ? Geo<D, KVB, 2>::IMG : Geo<D, KVB, 0>::IMG;
+  // the larger geometry of a call with Q smoothing (its images also carry the per-key
+  // score terms), so that one workspace size serves both
+  const size_t img = scale_mode(KVB, qk_blk) == 2 ? Geo<D, KVB, 2, true>::IMG : Geo<D, KVB, 0, true>::IMG;
   return (size_t)BH * (size_t)(Np / Geo<D, KVB>::TG) * img;
 }
 

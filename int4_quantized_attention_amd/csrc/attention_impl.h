@@ -12,8 +12,9 @@
 //    byte image one key group occupies in LDS: K as packed fp6 e2m3 (every code in
 //    [-7, 7] is exact in e2m3; 6 bits per value) with rows permuted for the S^T
 //    register layout, V^T as fp8 e4m3 (also exact), rows padded so that the LDS
-//    reads of consecutive rows hit distinct banks, and the level-threshold table in
-//    the tail.  The main loop copies groups straight from global memory into LDS
+//    reads of consecutive rows hit distinct banks (32 KiB per 128-key group for
+//    D = 128; the copy stream is a bound at the margin, so the level thresholds live
+//    in a small LDS array of their own).  The main loop copies groups straight from global memory into LDS
 //    (buffer_load_dwordx4 ... lds) into a ring of LDS slots and spends no VALU on
 //    staging.  A group of 128 keys holds several online-softmax steps (one barrier
 //    and one copy per group).
@@ -109,8 +110,9 @@ RA_DEV uint32_t pack_b2(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
 
 // SM, how a step's K scales vary: 0 one per 16-key unit (qk_blk >= 16); 1 one for
 // the whole step (qk_blk >= kv_blk); 2 one per key (qk_blk < 16, per-token scales),
-// staged with the group image.
-template <int D, int KVB, int SM = 0>
+// staged with the group image.  QS: the image also carries the keys' Q-smoothing
+// score terms.
+template <int D, int KVB, int SM = 0, bool QS = false>
 struct Geo {
   // keys per group (staged together; a group holds whole online-softmax steps)
   static constexpr int TG = KVB < 32 ? 32 : (KVB > 128 ? KVB : 128);
@@ -120,16 +122,14 @@ struct Geo {
   static constexpr int NDB = D / 32;              // 32-row d blocks of O^T
   static constexpr int KC = D / 64;               // 64-deep chunks of Q K^T (fp6 MFMA)
   static constexpr int KB = 3 * D / 4;            // packed fp6 bytes per K row
-  // bytes per K row: packed codes + pad, a multiple of 16 that is not a multiple
-  // of 32 dwords' worth of banks for eight consecutive rows
   static constexpr int KROW = (KB + 16) / 4 % 8 == 0 ? KB + 32 : KB + 16;
   static constexpr int VROW = TG + 16;            // bytes per V^T row (fp8 + pad)
   static constexpr int VOFF = TG * KROW;          // V^T rows start here
-  static constexpr int TOFF = VOFF + D * VROW;    // 17 floats of level thresholds
-  static constexpr int DOFF = TOFF + 128;        // TG floats: per-key score terms (Q smoothing)
-  static constexpr int SOFF = DOFF + 4 * TG;     // TG floats: per-key K scales (SM 2)
-  static constexpr int IMG = ((SM == 2 ? SOFF + 4 * TG : TOFF + 128) + 4095) / 4096 * 4096;  // one group's image
-  static_assert(DOFF + 4 * TG <= IMG, "the per-key terms fit in the image's padding");
+  static constexpr int DOFF = VOFF + D * VROW;    // TG floats: per-key score terms (QS)
+  static constexpr int SOFF = DOFF + (QS ? 4 * TG : 0);  // TG floats: per-key K scales (SM 2)
+  // one group's image, a whole number of 4 KiB copy rounds (K and V^T alone are
+  // exactly 32 KiB for D = 128 and 128-key groups)
+  static constexpr int IMG = ((SOFF + (SM == 2 ? 4 * TG : 0)) + 4095) / 4096 * 4096;
   static constexpr int NDMA = IMG / 4096;         // 16-byte copies per thread per group
   static constexpr int NB = 4 * IMG <= 81920 ? 4 : 2;  // ring slots (two workgroups per CU)
   static constexpr int LDS = NB * IMG;
@@ -173,9 +173,9 @@ RA_DEV void pack_fp6(const u32x4 w, uint32_t (&o)[6]) {
 // ---- staging: INT4 codes -> per-group LDS images ---------------------------------
 // grid (Np / TG, nheads); the image of group g of head bh is at
 // img + (bh * (Np / TG) + g) * IMG.
-template <int D, int KVB, int SM>
+template <int D, int KVB, int SM, bool QS>
 __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
-  using G = Geo<D, KVB, SM>;
+  using G = Geo<D, KVB, SM, QS>;
   const int bh = args.heads[blockIdx.y];
   const int g = blockIdx.x;
   const int64_t Np = args.Np;
@@ -183,10 +183,9 @@ __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
   if (at + G::IMG > args.img_bytes) return;
   uint8_t* img = args.img + at;
   // K: TG rows of D fp6 values.  Chunk c = 2 kc + h (channels 32c .. 32c+31, the
-  // operand of lane half h for the kc-th 64-deep MFMA) is stored as its first 16
-  // bytes at 16c and its last 8 bytes at D/2 + 8c (+8 in rows 8..15 and 24..31 of
-  // each tile, which keeps the 8-byte reads of 16 consecutive rows on distinct banks), so that every lane
-  // reads its operand with one 16-byte and one 8-byte load.
+  // operand of lane half h for the kc-th 64-deep MFMA) fills bytes 32c .. 32c+23 of
+  // the row (32c+24 .. 32c+31 hold zeros), so that every lane reads its operand with
+  // two 16-byte loads straight into the operand's registers.
   // V^T: D rows x TG fp8 e4m3 values.  With steps of 64 or more keys, the 16-key
   // chunks of each 64-key segment are stored in the k order of one 64-deep MFMA:
   // position 32h + 16t' holds keys 32t' + 16h .. +15 (tile t' of the pair, lane
@@ -245,11 +244,10 @@ __global__ __launch_bounds__(256) void k2_stage(const AttnArgs args) {
       }
     }
   }
-  if (threadIdx.x < 17) ((float*)(img + G::TOFF))[threadIdx.x] = threadIdx.x < 15 ? args.T[threadIdx.x] : INFINITY;
   // Q smoothing: the keys' score terms in log2 units, delta_j = fl(dS_j * C0), in
   // key order (the S^T accumulator holds key 32t + 16h + v of tile t in register v
   // of lane half h)
-  if (args.kbias && threadIdx.x < G::TG)
+  if (QS && threadIdx.x < G::TG)
     ((float*)(img + G::DOFF))[threadIdx.x] = args.kbias[(int64_t)bh * Np + g * G::TG + threadIdx.x] * args.C0;
   // per-token K scales (qk_blk < 16), in key order
   if (SM == 2 && threadIdx.x < G::TG) {
@@ -269,6 +267,7 @@ struct Ctx {
   bool kb;   // per-key score terms staged (Q smoothing)
   float C0, L15;
   float T0;  // the first level threshold: r >= 1 iff y >= T0
+  const float* T;  // the 15 level thresholds, then +inf, +inf (LDS)
   int p_zero;
   int dbg_row0, dbg_n;
   int32_t* dbg_aqk;
@@ -308,9 +307,9 @@ struct RowState {
 // of the image, one contiguous kilobyte per copy (dma_all), through a buffer resource
 // over the head's images; the lane offset is the only vector operand, the group and
 // wave offsets are scalar.
-template <int D, int KVB, int SM>
+template <int D, int KVB, int SM, bool QS>
 RA_DEV void dma_group(__amdgpu_buffer_rsrc_t r, int g, uint8_t* buf) {
-  using G = Geo<D, KVB, SM>;
+  using G = Geo<D, KVB, SM, QS>;
   constexpr int WB = G::NDMA * 1024;  // bytes per wave
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   dma_all(std::make_integer_sequence<int, G::NDMA>{}, r, buf + w * WB, 16 * (threadIdx.x & 63),
@@ -332,8 +331,7 @@ RA_DEV void qk_tiles(const uint8_t* Kl, int tb, const i32x8 (&qop)[Geo<D, KVB>::
       const i32x2 hi = *(const i32x2*)(row + D / 2 + 8 * c + 8 * ((col >> 3) & 1));
       // six dwords of fp6 values (format 2 = e2m3 for both operands); the last two
       // operand dwords are not read by the instruction
-      const i32x8 kop = __builtin_shufflevector(lo, __builtin_shufflevector(hi, hi, 0, 1, -1, -1), 0, 1, 2, 3, 4,
-                                                5, -1, -1);
+      const i32x8 kop = __builtin_shufflevector(lo, __builtin_shufflevector(hi, hi, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5, -1, -1);
       const f32x16 zero = {0};
       st[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop[kc], kc == 0 ? zero : st[t], 2, 2, 0,
                                                                127, 0, 127);
@@ -530,7 +528,10 @@ RA_DEV void softmax_pv(const Ctx& a, int g, int tb, int step0, const uint8_t* Vl
 #pragma unroll
         for (int tp = 0; tp < PT; ++tp) {
           const int t = pp * PT + tp;
-          pb[tp] = i32x4{0, 0, 0, 0};
+          // pb is not read on this path (the pair's MFMA is skipped), but the path
+          // joins the level path's before the rescale; an empty asm gives pb a value
+          // there without the eight moves that a constant would cost
+          asm volatile("" : "=v"(pb[tp][0]), "=v"(pb[tp][1]), "=v"(pb[tp][2]), "=v"(pb[tp][3]));
           if (ngl[t]) {  // no p of the tile moves l
             S.cnt.exp_skip();
             continue;
@@ -651,10 +652,10 @@ typedef const __attribute__((address_space(4))) float* kscale_ptr;  // read-only
 // The work of key group g on its LDS image cur: the K scales of its 16-key units
 // (scalar loads, so they never wait behind copies in flight), Q K^T, then each
 // online-softmax step's softmax and P V.
-template <int D, int KVB, bool DBG, bool MASK, int SM, class RS>
+template <int D, int KVB, bool DBG, bool MASK, int SM, bool QS, class RS>
 RA_DEV void group_compute(const Ctx& a, int g, uint8_t* const cur, const i32x8 (&qop)[Geo<D, KVB>::KC],
                           float sq, int bh, RS& S, bool dbg_row, int dr) {
-  using G = Geo<D, KVB, SM>;
+  using G = Geo<D, KVB, SM, QS>;
   constexpr bool US = SM == 1;
   const int h = (threadIdx.x >> 5) & 1;
   const kscale_ptr ksh = (kscale_ptr)a.ks + (int64_t)bh * (a.Np >> a.qk_shift);
@@ -693,7 +694,7 @@ RA_DEV void group_compute(const Ctx& a, int g, uint8_t* const cur, const i32x8 (
       for (int t = 0; t < G::TPS; ++t) sa[t] = st[sg][t];
     }
     const float* Sl = (const float*)(cur + G::SOFF);  // per-key K scales (SM 2)
-    if (a.kb) {
+    if constexpr (QS) {
       // Q smoothing: t = fma(a, c, delta_j) in place; with c = 1 from here on the max
       // is max t and y = fma(t, 1, L15 - m) = fl(t + (L15 - m))
       const float* Dl = (const float*)(cur + G::DOFF) + 32 * tb + 16 * h;
@@ -712,7 +713,7 @@ RA_DEV void group_compute(const Ctx& a, int g, uint8_t* const cur, const i32x8 (
       }
     }
     const int step0 = KVB < 32 ? 2 * g : g * G::NSG + sg;
-    softmax_pv<D, KVB, DBG, MASK, SM>(a, g, tb, step0, cur + G::VOFF, (const float*)(cur + G::TOFF), Sl, sq,
+    softmax_pv<D, KVB, DBG, MASK, SM>(a, g, tb, step0, cur + G::VOFF, a.T, Sl, sq,
                                       st[sg], ct[sg], DBG ? sa : st[sg], S, dbg_row, dr);
   }
 }
@@ -722,16 +723,16 @@ RA_DEV void group_compute(const Ctx& a, int g, uint8_t* const cur, const i32x8 (
 // used (free since the last barrier); then the group's work; then a wait until this
 // wave's copy of group g+1 has landed (later copies stay in flight) and one barrier,
 // which also covers the other waves' copies.
-template <int D, int KVB, bool DBG, bool MASK, int SM, int SLOT = -1, class RS>
+template <int D, int KVB, bool DBG, bool MASK, int SM, bool QS, int SLOT = -1, class RS>
 RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngroups, uint8_t* lds,
                        const i32x8 (&qop)[Geo<D, KVB>::KC], float sq, int bh, RS& S, bool dbg_row, int dr) {
-  using G = Geo<D, KVB, SM>;
+  using G = Geo<D, KVB, SM, QS>;
   // ring slot of this group: a compile-time constant when the caller unrolls the
   // group loop by the slot count (SLOT = g % NB), so LDS addresses stay invariant
   const int slot = SLOT >= 0 ? SLOT : g % G::NB;
   if (g + G::NB - 1 < ngroups)
-    dma_group<D, KVB, SM>(rsrc, g + G::NB - 1, lds + ((slot + G::NB - 1) % G::NB) * G::IMG);
-  group_compute<D, KVB, DBG, MASK, SM>(a, g, lds + slot * G::IMG, qop, sq, bh, S, dbg_row, dr);
+    dma_group<D, KVB, SM, QS>(rsrc, g + G::NB - 1, lds + ((slot + G::NB - 1) % G::NB) * G::IMG);
+  group_compute<D, KVB, DBG, MASK, SM, QS>(a, g, lds + slot * G::IMG, qop, sq, bh, S, dbg_row, dr);
   // copies issued after group g+1's: those of groups g+2 .. min(g+NB-1, ngroups-1)
   const int later = min(g + G::NB - 1, ngroups - 1) - (g + 1);
   if (DBG || later <= 0) wait_vm<0>();
@@ -740,9 +741,11 @@ RA_DEV void group_iter(const Ctx& a, __amdgpu_buffer_rsrc_t rsrc, int g, int ngr
   lds_barrier();
 }
 
-template <int D, int KVB, bool DBG, int SM, bool ST = false>
+template <int D, int KVB, bool DBG, int SM, bool QS, bool ST = false>
 RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
-  using G = Geo<D, KVB, SM>;
+  using G = Geo<D, KVB, SM, QS>;
+  // the P level thresholds (then +inf, +inf) for the exact levels
+  __shared__ float Tsh[17];
   constexpr int BM = kBM;  // query rows per workgroup
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
@@ -777,7 +780,8 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   const int64_t c = args.causal;
   auto limit = [&](int64_t i) -> int { return c > 0 ? (int)min((int64_t)Nv, (i / c + 1) * c) : Nv; };
   a.klim = limit(qi);
-  a.kb = args.kbias != nullptr;
+  a.kb = QS;
+  a.T = Tsh;
   const int kmax = limit(min(qt * BM + BM - 1, Nv - 1));
   const int ngroups = (kmax + G::TG - 1) / G::TG;
   const int nfull = min(limit(qt * BM) / G::TG, ngroups);  // groups no row masks
@@ -791,7 +795,8 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
       0x00020000);
 #pragma unroll
   for (int p = 0; p < G::NB - 1; ++p)
-    if (p < ngroups) dma_group<D, KVB, SM>(rsrc, p, lds + p * G::IMG);
+    if (p < ngroups) dma_group<D, KVB, SM, QS>(rsrc, p, lds + p * G::IMG);
+  if (tid < 17) Tsh[tid] = tid < 15 ? args.T[tid] : INFINITY;
 
   // ---- Q operand: packed fp6 e2m3 values of the lane's 32 channels per 64-deep chunk
   i32x8 qop[G::KC];
@@ -823,14 +828,14 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
   int g = 0;
   if (G::NB == 2) {
     for (; g + 2 <= nfull; g += 2) {
-      group_iter<D, KVB, DBG, false, SM, 0>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
-      group_iter<D, KVB, DBG, false, SM, 1>(a, rsrc, g + 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+      group_iter<D, KVB, DBG, false, SM, QS, 0>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+      group_iter<D, KVB, DBG, false, SM, QS, 1>(a, rsrc, g + 1, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
     }
   }
   for (; g < nfull; ++g)
-    group_iter<D, KVB, DBG, false, SM>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+    group_iter<D, KVB, DBG, false, SM, QS>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
   for (; g < ngroups; ++g)
-    group_iter<D, KVB, DBG, true, SM>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
+    group_iter<D, KVB, DBG, true, SM, QS>(a, rsrc, g, ngroups, lds, qop, sq, bh, S, dbg_row, dr);
 
   // ---- epilogue ---------------------------------------------------------------------
   if constexpr (ST) {
@@ -870,38 +875,39 @@ RA_DEV void k2_body(const AttnArgs& args, uint8_t* lds) {
 // The production kernel: two waves per SIMD (<= 256 registers per wave), one for
 // 256-key steps.
 // ST: the instance that also counts the exact skips (args.stats).
-template <int D, int KVB, int SM, bool ST>
+template <int D, int KVB, int SM, bool QS, bool ST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(Geo<D, KVB, SM>::WPE, Geo<D, KVB, SM>::WPE)))
 void k2_attention(const AttnArgs args) {
   extern __shared__ __align__(16) uint8_t lds[];
-  k2_body<D, KVB, false, SM, ST>(args, lds);
+  k2_body<D, KVB, false, SM, QS, ST>(args, lds);
 }
 
 // The debug run (dumps of one head's row range): one wave per SIMD, so that the
 // extra dump state fits in registers.
-template <int D, int KVB, int SM>
+template <int D, int KVB, int SM, bool QS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k2_attention_debug(
     const AttnArgs args) {
   extern __shared__ __align__(16) uint8_t lds[];
-  k2_body<D, KVB, true, SM>(args, lds);
+  k2_body<D, KVB, true, SM, QS>(args, lds);
 }
 
-template <int D, int KVB, int SM>
+template <int D, int KVB, int SM, bool QS>
 hipError_t launch_t(const AttnArgs& a, bool dbg, hipStream_t st) {
-  using G = Geo<D, KVB, SM>;
+  using G = Geo<D, KVB, SM, QS>;
   // The dynamic LDS limit is raised on every call (for the current device; the
   // setting is idempotent), so the library keeps no state between calls.
-  const void* fn = dbg ? (const void*)k2_attention_debug<D, KVB, SM>
-                      : a.stats ? (const void*)k2_attention<D, KVB, SM, true> : (const void*)k2_attention<D, KVB, SM, false>;
+  const void* fn = dbg ? (const void*)k2_attention_debug<D, KVB, SM, QS>
+                      : a.stats ? (const void*)k2_attention<D, KVB, SM, QS, true>
+                                : (const void*)k2_attention<D, KVB, SM, QS, false>;
   const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   if (attr != hipSuccess) return attr;
-  k2_stage<D, KVB, SM><<<dim3((unsigned)(a.Np / G::TG), (unsigned)a.nheads), 256, 0, st>>>(a);
+  k2_stage<D, KVB, SM, QS><<<dim3((unsigned)(a.Np / G::TG), (unsigned)a.nheads), 256, 0, st>>>(a);
   if (dbg) {
     const int first = a.dbg_row0 / kBM, last = (a.dbg_row0 + a.dbg_n - 1) / kBM;
-    k2_attention_debug<D, KVB, SM><<<last - first + 1, 256, G::LDS, st>>>(a);
+    k2_attention_debug<D, KVB, SM, QS><<<last - first + 1, 256, G::LDS, st>>>(a);
   } else {
-    if (a.stats) k2_attention<D, KVB, SM, true><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
-    else k2_attention<D, KVB, SM, false><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
+    if (a.stats) k2_attention<D, KVB, SM, QS, true><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
+    else k2_attention<D, KVB, SM, QS, false><<<8 * a.per_xcd, 256, G::LDS, st>>>(a);
   }
   return hipGetLastError();
 }
@@ -914,15 +920,21 @@ inline int scale_mode(int kv_blk, int qk_blk) {
   return (kv_blk >= 32 && qk_blk >= kv_blk) ? 1 : 0;
 }
 
+template <int D, int KVB, bool QS>
+hipError_t launch_q(const AttnArgs& a, bool dbg, hipStream_t st) {
+  switch (scale_mode(KVB, a.qk_blk)) {
+    case 2: return launch_t<D, KVB, 2, QS>(a, dbg, st);
+    case 1:
+      if constexpr (KVB >= 32 && KVB <= 128) return launch_t<D, KVB, 1, QS>(a, dbg, st);
+      return hipErrorInvalidValue;
+    default: return launch_t<D, KVB, 0, QS>(a, dbg, st);
+  }
+}
+
+// Q smoothing (per-key score terms) selects the image geometry that carries them.
 template <int D, int KVB>
 hipError_t launch_s(const AttnArgs& a, bool dbg, hipStream_t st) {
-  switch (scale_mode(KVB, a.qk_blk)) {
-    case 2: return launch_t<D, KVB, 2>(a, dbg, st);
-    case 1:
-      if constexpr (KVB >= 32 && KVB <= 128) return launch_t<D, KVB, 1>(a, dbg, st);
-      return hipErrorInvalidValue;
-    default: return launch_t<D, KVB, 0>(a, dbg, st);
-  }
+  return a.kbias ? launch_q<D, KVB, true>(a, dbg, st) : launch_q<D, KVB, false>(a, dbg, st);
 }
 
 }  // namespace ra
