@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k3_prep(FbArgs a) {
     pos[1][threadIdx.x] = y;
     pos[2][threadIdx.x] = x;
   }
-  stage_tile<D, DT>(base, n0, Nv, kFbTile, lds);
+  stage_tile<D, DT, kFbTile>(base, n0, Nv, lds);
   __syncthreads();
   static_assert(kFbTile == FbGeo<D>::TG, "a pre-pass tile is one key group");
   static_assert(256 % (D / 2) == 0 && 256 % (kFbTile / 2) == 0, "whole rows per pass");

@@ -63,14 +63,19 @@ RA_DEV void vamax_tile(const QuantArgs& a, int bh, int64_t tile, float* red) {
   float m[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) m[e] = 0.f;
-#pragma unroll 4
-  for (int r = tl; r < kVTile; r += TL) {
-    const int64_t n = n0 + r;
-    if (n < Nb) {
-      float x[8];
-      load_slice<DT, 8>(base, n, D, 8 * cg, x);
+  // batches of kVB tokens per thread, every load of a batch issued before the first
+  // is used; tokens at or past Nb read token Nb - 1 (Nb >= 1) and count as 0
+  constexpr int kVB = 8;
+  static_assert(kVTile % (TL * kVB) == 0, "whole batches");
+  for (int r0 = tl; r0 < kVTile; r0 += TL * kVB) {
+    float x[kVB][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], fabsf(x[e]));
+    for (int u = 0; u < kVB; ++u) load_slice<DT, 8>(base, min(n0 + r0 + u * TL, Nb - 1), D, 8 * cg, x[u]);
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const bool ok = n0 + r0 + u * TL < Nb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], ok ? fabsf(x[u][e]) : 0.f);
     }
   }
 #pragma unroll
@@ -196,7 +201,6 @@ __global__ __launch_bounds__(256) void k1_quant_qk_ws(QuantArgs a) {
   __shared__ float U[ROT == 2 ? 64 * (D + 1) : 1];  // Half exchange rows
   __shared__ uint32_t wred[256];
   __shared__ double dsacc[64];
-  __shared__ float mus[2 * D];
   const Shape s = a.s;
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int64_t Np = a.Np;
@@ -207,31 +211,32 @@ __global__ __launch_bounds__(256) void k1_quant_qk_ws(QuantArgs a) {
   const int64_t n = (int64_t)blockIdx.x * 64 + lane;
   const void* base = (const char*)(isK ? a.k : a.q) + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   const bool valid = n < valid_len(a.nlens, a.lens, bh, s.H, N);
-  // the smoothing mean (and mu_q for the dS chain) staged in LDS: every lane of a
-  // wave reads the same words
+  // the smoothing mean (and mu_q for the dS chain): the words of the wave's channel
+  // slice are the same for every lane, read through the scalar cache (constant
+  // address space: nothing writes them during the launch), so they need neither an
+  // LDS copy nor a wait ahead of the token loads
+  typedef const __attribute__((address_space(4))) float* cfloat_ptr;
   const bool smooth = isK ? a.smooth : a.smooth_q, chain = isK && a.smooth_q;
-  if (smooth && threadIdx.x < D) mus[threadIdx.x] = (isK ? a.kmu : a.qmu)[(int64_t)bh * D + threadIdx.x];
-  if (chain && threadIdx.x < D) mus[D + threadIdx.x] = a.qmu[(int64_t)bh * D + threadIdx.x];
+  const cfloat_ptr mus = (cfloat_ptr)((isK ? a.kmu : a.qmu) + (int64_t)bh * D + c0);
+  const cfloat_ptr mqs = (cfloat_ptr)(a.qmu + (int64_t)bh * D + c0);
   float v[CPT];
   rotated_wave_slice<DT, ROT, D>(base, n, valid, c0, s, a.table, U, lane, v);
-  if (ROT != 2 && (smooth || chain)) __syncthreads();  // (ROT 2 passed a barrier already)
   if (smooth) {
     // tokens that do not exist are smoothed too: their amax contribution is dropped
     // below and their codes are 0 (inv = 0)
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) v[i] = v[i] - mus[c0 + i];
+    for (int i = 0; i < CPT; ++i) v[i] = v[i] - mus[i];
   }
   if (chain) {
     // dS_n = mu_q . K_n: binary64, channels in order (the products are exact), one
     // chain through the four waves' slices in turn; wave 3 writes it (0 for tokens
     // that do not exist)
-    const float* mq = mus + D + c0;
     double acc = 0.0;
     for (int stg = 0; stg < 4; ++stg) {
       if (w == stg) {
         if (stg > 0) acc = dsacc[lane];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) acc = fma((double)mq[i], (double)v[i], acc);
+        for (int i = 0; i < CPT; ++i) acc = fma((double)mqs[i], (double)v[i], acc);
         dsacc[lane] = acc;
       }
       __syncthreads();
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
   const int64_t n0 = (int64_t)blockIdx.x * kTile;
   const void* base = (const char*)a.v + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   const int64_t Nb = valid_len(a.nlens, a.lens, bh, s.H, N);
-  stage_tile<D, DT>(base, n0, Nb, kTile, lds);
+  stage_tile<D, DT, kTile>(base, n0, Nb, lds);
   __syncthreads();
   constexpr int G = 256 / D, TPG = kTile / G;  // groups, tokens per group
   const int c = threadIdx.x % D, g = threadIdx.x / D;

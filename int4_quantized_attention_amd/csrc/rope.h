@@ -9,33 +9,31 @@ namespace ra {
 constexpr int kTile = 128;     // tokens per quantisation workgroup
 constexpr int kMeanTile = 64;  // tokens per ordered binary64 partial sum of K
 
-// Load a tile of `rows` tokens x D elements into LDS (row stride D+2 elements
-// for 16-bit inputs, D+1 for fp32, so that rows fall in different banks).
-template <int D, int DT>
-RA_DEV void stage_tile(const void* x, int64_t row0, int64_t N, int rows, char* lds) {
+// Load a tile of ROWS tokens x D elements into LDS (row stride D+2 elements for
+// 16-bit inputs, D+1 for fp32, so that rows fall in different banks); rows at or past
+// N are zeros.  256 threads: each issues all of its 16-byte loads before it stores any
+// of them (a load-store pair per iteration would wait out one memory latency each).
+// Rows past N read row N-1 (N >= 1), so every load stays inside the tensor and none
+// sits behind a branch; those values are replaced by zeros.
+template <int D, int DT, int ROWS>
+RA_DEV void stage_tile(const void* x, int64_t row0, int64_t N, char* lds) {
+  constexpr int VPR = DT == 0 ? D / 4 : D / 8;  // 16-byte vectors per row
+  static_assert(ROWS * VPR % 256 == 0, "whole passes of 256 threads");
+  constexpr int IT = ROWS * VPR / 256;
   const int tid = threadIdx.x;
-  if (DT == 0) {
-    float* L = (float*)lds;
-    const float4* src = (const float4*)x;
-    const int per_row = D / 4;
-    for (int e = tid; e < rows * per_row; e += blockDim.x) {
-      const int r = e / per_row, c4 = e % per_row;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row0 + r < N) v = src[(row0 + r) * per_row + c4];
-      float* dst = L + r * (D + 1) + c4 * 4;
-      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
-    }
-  } else {
-    uint32_t* L = (uint32_t*)lds;  // 16-bit elements, row stride D+2 = (D+2)/2 dwords
-    const uint4* src = (const uint4*)x;
-    const int per_row = D / 8;
-    for (int e = tid; e < rows * per_row; e += blockDim.x) {
-      const int r = e / per_row, c8 = e % per_row;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row0 + r < N) v = src[(row0 + r) * per_row + c8];
-      uint32_t* dst = L + r * ((D + 2) / 2) + c8 * 4;
-      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
-    }
+  const u32x4* src = (const u32x4*)x;
+  u32x4 v[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = tid + 256 * i, r = e / VPR, c = e % VPR;
+    v[i] = src[min(row0 + r, N - 1) * VPR + c];
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = tid + 256 * i, r = e / VPR, c = e % VPR;
+    const u32x4 w = row0 + r < N ? v[i] : u32x4{0u, 0u, 0u, 0u};
+    uint32_t* dst = (uint32_t*)lds + r * (DT == 0 ? D + 1 : (D + 2) / 2) + c * 4;
+    dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
   }
 }
 
