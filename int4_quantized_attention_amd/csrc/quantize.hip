@@ -143,19 +143,18 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
 }
 
 // Channel means of K (and Q): binary64 sum of the partials in block order, / N, to
-// binary32.  grid (B*H, tensors in the order of k1_kstats' z); thread c < D owns
-// channel c.  The sum is one dependent chain per channel; it runs over chunks of
+// binary32.  One workgroup per (b*H + h, tensor in the order of k1_kstats' z), run by
+// k1_mid; thread c < D owns channel c.  The sum is one dependent chain per channel; it runs over chunks of
 // kMeanChunk partial rows staged in LDS, the next chunk's loads in flight (in
 // registers) while the current one is summed.
 constexpr int kMeanChunk = 32;
+// buf: kMeanChunk * D doubles of LDS.
 template <int D>
-__global__ __launch_bounds__(256) void k1_kmean(QuantArgs a) {
+RA_DEV void kmean_body(const QuantArgs& a, int bh, int z, double* buf) {
   constexpr int PER = kMeanChunk * D / 256;  // partials each thread stages per chunk
-  __shared__ double buf[kMeanChunk * D];
   const int64_t N = (int64_t)a.s.F * a.s.Hs * a.s.Ws;
   const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
-  const int bh = blockIdx.x;
-  const bool isQ = blockIdx.y + (a.smooth ? 0 : 1) == 1;
+  const bool isQ = z + (a.smooth ? 0 : 1) == 1;
   const double* p = (isQ ? a.qpart : a.kpart) + (int64_t)bh * nblk * D;
   const int tid = threadIdx.x;
   double nxt[PER];
@@ -191,24 +190,32 @@ __global__ void k1_zero_u32(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-// Q / K quantisation, wave-sliced (ROT 0-2, qk_blk <= 64): grid (Np/64, B*H, 2 (0 =
-// Q, 1 = K)); lane = token, wave w = channels [w D/4, (w+1) D/4).  A scale block is
+// Q / K quantisation, wave-sliced (ROT 0-2, qk_blk <= 64): a workgroup takes 64
+// tokens of one head; lane = token, wave w = channels [w D/4, (w+1) D/4).  A scale block is
 // qk_blk consecutive lanes of all four waves: its amax is a lane-group maximum in
 // each wave, then the four waves' values through LDS.
+// LDS of one workgroup of the wave-sliced quantiser: the Half exchange rows, the
+// scale-block maxima of the four waves, and the hand-on of the dS chain.
+template <int D, int ROT>
+struct QkwsLds {
+  float U[ROT == 2 ? 64 * (D + 1) : 1];
+  uint32_t wred[256];
+  double dsacc[64];
+};
+
+// One workgroup: tokens 64 blk .. 64 blk + 63 of head bh, Q or K.
 template <int D, int DT, int ROT>
-__global__ __launch_bounds__(256) void k1_quant_qk_ws(QuantArgs a) {
+RA_DEV void quant_qk_ws_body(const QuantArgs& a, int64_t blk, int bh, bool isK, QkwsLds<D, ROT>& L) {
   constexpr int CPT = D / 4;
-  __shared__ float U[ROT == 2 ? 64 * (D + 1) : 1];  // Half exchange rows
-  __shared__ uint32_t wred[256];
-  __shared__ double dsacc[64];
+  float* const U = L.U;
+  uint32_t* const wred = L.wred;
+  double* const dsacc = L.dsacc;
   const Shape s = a.s;
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int64_t Np = a.Np;
-  const int bh = blockIdx.y;
-  const bool isK = blockIdx.z == 1;
   const int lane = threadIdx.x & 63;
   const int c0 = wave_slice_c0<D>(), w = c0 / CPT;
-  const int64_t n = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t n = blk * 64 + lane;
   const void* base = (const char*)(isK ? a.k : a.q) + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   const bool valid = n < valid_len(a.nlens, a.lens, bh, s.H, N);
   // the smoothing mean (and mu_q for the dS chain): the words of the wave's channel
@@ -267,6 +274,13 @@ __global__ __launch_bounds__(256) void k1_quant_qk_ws(QuantArgs a) {
     float* sc = isK ? a.ks : a.qs;
     sc[(int64_t)bh * (Np / s.qk_blk) + n / s.qk_blk] = am == 0.f ? 0.f : am / 7.0f;
   }
+}
+
+// grid (Np/64, B*H, tensors): z = z0 + blockIdx.z, 0 = Q, 1 = K.
+template <int D, int DT, int ROT>
+__global__ __launch_bounds__(256) void k1_quant_qk_ws(QuantArgs a, int z0) {
+  __shared__ QkwsLds<D, ROT> L;
+  quant_qk_ws_body<D, DT, ROT>(a, blockIdx.x, blockIdx.y, z0 + (int)blockIdx.z == 1, L);
 }
 
 // Q / K quantisation, token-sliced (the Full rotation, and qk_blk = 128): grid
@@ -353,24 +367,25 @@ __global__ __launch_bounds__(256) void k1_quant_qk(QuantArgs a) {
 }
 
 // V quantisation into the transposed layout [B,H,D,Np/2] plus per-kv-block
-// column sums.  grid (Np/128, B*H); thread -> (channel c, token group g).
+// column sums: one workgroup per kTile tokens (tile) of head bh, LDS lds of
+// v_tile_bytes<D, DT>(); thread -> (channel c, token group g).
 template <int D, int DT>
-__global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
-  extern __shared__ __align__(16) char lds[];
+constexpr int v_tile_bytes() { return kTile * (DT == 0 ? (D + 1) * 4 : (D + 2) * 2); }
+template <int D, int DT>
+RA_DEV void quant_v_body(const QuantArgs& a, int64_t tile, int bh, char* lds) {
   const Shape s = a.s;
   const int64_t N = (int64_t)s.F * s.Hs * s.Ws;
   const int64_t Np = a.Np;
-  const int bh = blockIdx.y;
-  const int64_t n0 = (int64_t)blockIdx.x * kTile;
+  const int64_t n0 = tile * kTile;
   const void* base = (const char*)a.v + (size_t)bh * N * D * (DT == 0 ? 4 : 2);
   const int64_t Nb = valid_len(a.nlens, a.lens, bh, s.H, N);
-  stage_tile<D, DT, kTile>(base, n0, Nb, lds);
-  __syncthreads();
   constexpr int G = 256 / D, TPG = kTile / G;  // groups, tokens per group
   const int c = threadIdx.x % D, g = threadIdx.x / D;
-  const float amax = __uint_as_float(a.vamax[(int64_t)bh * D + c]);
+  const float amax = __uint_as_float(a.vamax[(int64_t)bh * D + c]);  // in flight with the tile
+  stage_tile<D, DT, kTile>(base, n0, Nb, lds);
+  __syncthreads();
   const float inv = amax == 0.f ? 0.f : 7.0f / amax;
-  if (blockIdx.x == 0 && g == 0) a.vs[(int64_t)bh * D + c] = amax == 0.f ? 0.f : amax / 7.0f;
+  if (tile == 0 && g == 0) a.vs[(int64_t)bh * D + c] = amax == 0.f ? 0.f : amax / 7.0f;
   float vals[TPG];
 #pragma unroll
   for (int i = 0; i < TPG; ++i) vals[i] = lds_elem<D, DT>(lds, g * TPG + i, c);
@@ -438,6 +453,36 @@ __global__ __launch_bounds__(256) void k1_quant_v(QuantArgs a) {
   }
 }
 
+// The launch between the statistics and the K codes: the channel means (one
+// workgroup per head and smoothed tensor, first in dispatch order, so that their
+// dependent chains run beside the streams), the V codes (they need the V amax of
+// the statistics launch) and, when Q is not smoothed (its codes need no statistics),
+// the Q codes.  Per head and 128-token tile the workgroups are: V tile, and with Q
+// two 64-token Q blocks, so that the V stream and the Q arithmetic share the CUs.
+// One dynamic LDS buffer serves whichever part a workgroup runs.  1-D grid.
+template <int D, int DT, int ROT>
+constexpr int mid_lds_bytes() {
+  constexpr int q = (int)sizeof(QkwsLds<D, ROT>), v = v_tile_bytes<D, DT>(), m = kMeanChunk * D * 8;
+  return q > v ? (q > m ? q : m) : (v > m ? v : m);
+}
+template <int D, int DT, int ROT>
+__global__ __launch_bounds__(256) void k1_mid(QuantArgs a, int nmean, int withq) {
+  extern __shared__ __align__(16) char lds[];
+  const int64_t id = blockIdx.x;
+  const int BH = a.s.B * a.s.H;
+  if (id < (int64_t)BH * nmean) {
+    kmean_body<D>(a, (int)(id % BH), (int)(id / BH), (double*)lds);
+    return;
+  }
+  const int per = withq ? 3 : 1;  // workgroups per head and tile
+  const int64_t r = id - (int64_t)BH * nmean, ntile = a.Np / kTile;
+  const int bh = (int)(r / (ntile * per));
+  const int64_t u = r % (ntile * per), tile = u / per;
+  const int j = (int)(u % per);
+  if (j == 0) quant_v_body<D, DT>(a, tile, bh, lds);
+  else if constexpr (ROT <= 2) quant_qk_ws_body<D, DT, ROT>(a, 2 * tile + (j - 1), bh, false, *(QkwsLds<D, ROT>*)lds);
+}
+
 // ---------------------------------------------------------------------------------
 template <int D, int DT, int ROT, int TPT>
 hipError_t launch_qk(const QuantArgs& a, hipStream_t st) {
@@ -450,6 +495,10 @@ hipError_t launch_qk(const QuantArgs& a, hipStream_t st) {
   return hipSuccess;
 }
 
+// Launch order: clear the V amax (and the column sums when a kv block spans several
+// tiles); the statistics (K and Q sums with the V amax, or the V amax alone); k1_mid
+// (the means, the V codes, and the Q codes when Q needs no mean); the remaining Q/K
+// codes.
 template <int D, int DT, int ROT>
 hipError_t launch_rot(const QuantArgs& a, hipStream_t st) {
   const int64_t N = (int64_t)a.s.F * a.s.Hs * a.s.Ws;
@@ -459,17 +508,25 @@ hipError_t launch_rot(const QuantArgs& a, hipStream_t st) {
     // the statistics, with the V amax as the launch's last z
     const int64_t nblk = (N + kMeanTile - 1) / kMeanTile;
     k1_kstats<D, DT, ROT><<<dim3((unsigned)nblk, BH, nz + 1), 256, 0, st>>>(a);
-    k1_kmean<D><<<dim3((unsigned)BH, nz), 256, 0, st>>>(a);
   } else {
     k1_vamax<D, DT><<<dim3((unsigned)((a.Np + kVTile - 1) / kVTile), BH), 256, 0, st>>>(a);
   }
-  // a workgroup covers whole scale blocks: 64 tokens unless qk_blk is 128 (then 128
-  // tokens, two threads each)
+  // the wave-sliced Q/K kernel takes scale blocks of up to 64 tokens; the Full
+  // rotation and qk_blk = 128 use the token-sliced one for both tensors
+  const bool ws = ROT <= 2 && a.s.qk_blk <= 64;
+  const bool withq = ws && !a.smooth_q;
+  constexpr int mid_lds = mid_lds_bytes<D, DT, ROT>();
+  const hipError_t attr = hipFuncSetAttribute((const void*)k1_mid<D, DT, ROT>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, mid_lds);
+  if (attr != hipSuccess) return attr;
+  const int64_t nmid = (int64_t)BH * nz + (int64_t)BH * (a.Np / kTile) * (withq ? 3 : 1);
+  k1_mid<D, DT, ROT><<<(unsigned)nmid, 256, mid_lds, st>>>(a, nz, withq ? 1 : 0);
   if (a.s.qk_blk > 64) return launch_qk<D, DT, ROT, 2>(a, st);
   if constexpr (ROT == 3) {
     return launch_qk<D, DT, ROT, 4>(a, st);
   } else {
-    k1_quant_qk_ws<D, DT, ROT><<<dim3((unsigned)(a.Np / 64), (unsigned)(a.s.B * a.s.H), 2), 256, 0, st>>>(a);
+    k1_quant_qk_ws<D, DT, ROT>
+        <<<dim3((unsigned)(a.Np / 64), (unsigned)BH, withq ? 1 : 2), 256, 0, st>>>(a, withq ? 1 : 0);
     return hipSuccess;
   }
 }
@@ -477,26 +534,19 @@ hipError_t launch_rot(const QuantArgs& a, hipStream_t st) {
 template <int D, int DT>
 hipError_t launch_quantize_t(const QuantArgs& a, hipStream_t st) {
   const int BH = a.s.B * a.s.H;
-  const size_t in_tile = (size_t)kTile * (DT == 0 ? (D + 1) * 4 : (D + 2) * 2);
   const int64_t nvamax = (int64_t)BH * D;
-  if (DT == 0) {
-    // fp32 tiles exceed the default 64 KiB of dynamic LDS; gfx950 has 160 KiB
-    const hipError_t attr = hipFuncSetAttribute((const void*)k1_quant_v<D, DT>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)in_tile);
-    if (attr != hipSuccess) return attr;
-  }
   k1_zero_u32<<<(unsigned)((nvamax + 255) / 256), 256, 0, st>>>(a.vamax, nvamax);  // V amax starts at 0
+  if (a.vcol && a.s.kv_blk > kTile) {
+    // column sums that several V tiles add into (integer atomics) start at 0
+    const int64_t ncol = (int64_t)BH * ((a.s.F * (int64_t)a.s.Hs * a.s.Ws + a.s.kv_blk - 1) / a.s.kv_blk) * D;
+    k1_zero_u32<<<(unsigned)((ncol + 255) / 256), 256, 0, st>>>((uint32_t*)a.vcol, ncol);
+  }
   hipError_t e;
   if (a.rot == 1) e = launch_rot<D, DT, 1>(a, st);
   else if (a.rot == 2) e = launch_rot<D, DT, 2>(a, st);
   else if (a.rot == 3) e = launch_rot<D, DT, 3>(a, st);
   else e = launch_rot<D, DT, 0>(a, st);
   if (e != hipSuccess) return e;
-  if (a.vcol && a.s.kv_blk > kTile) {
-    const int64_t ncol = (int64_t)BH * ((a.s.F * (int64_t)a.s.Hs * a.s.Ws + a.s.kv_blk - 1) / a.s.kv_blk) * D;
-    k1_zero_u32<<<(unsigned)((ncol + 255) / 256), 256, 0, st>>>((uint32_t*)a.vcol, ncol);
-  }
-  k1_quant_v<D, DT><<<dim3((unsigned)(a.Np / kTile), BH), 256, in_tile, st>>>(a);
   return hipGetLastError();
 }
 
