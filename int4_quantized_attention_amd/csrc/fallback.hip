@@ -81,18 +81,32 @@ __global__ __launch_bounds__(256) void k3_prep(FbArgs a) {
   if (which < 2) {
     // a thread owns the channel pair (c, c + 1) of rows r, r + 256/(D/2), ...: one
     // 4-byte store per row
+    // Rows in batches of four: a batch's table loads are all issued before its first
+    // store.  Rows past the sequence's end sit at grid position (0, 0, 0) and hold
+    // zeros in LDS, so they are computed like the others and their values replaced by
+    // zeros.
     _Float16* dst = which == 0 ? a.qr + ((int64_t)bh * Np + n0) * D : nullptr;
     const int c = 2 * (threadIdx.x % (D / 2));
-    for (int r = threadIdx.x / (D / 2); r < kFbTile; r += 256 / (D / 2)) {
-      float v0 = 0.f, v1 = 0.f;
-      if (n0 + r < Nv) {
+    constexpr int RS = 256 / (D / 2), NR = kFbTile / RS, RB = 4;  // row stride, rows per thread, batch
+    static_assert(NR % RB == 0, "whole batches");
+#pragma unroll 1
+    for (int k0 = 0; k0 < NR; k0 += RB) {
+      f16x2 o[RB];
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        const int r = threadIdx.x / (D / 2) + (k0 + k) * RS;
         const int f = pos[0][r], y = pos[1][r], x = pos[2][r];
-        v0 = rope_rot<D, DT>(lds, r, c, s, 0, a.table, f, y, x);
-        v1 = rope_rot<D, DT>(lds, r, c + 1, s, 0, a.table, f, y, x);
+        float v0 = rope_rot<D, DT>(lds, r, c, s, 0, a.table, f, y, x);
+        float v1 = rope_rot<D, DT>(lds, r, c + 1, s, 0, a.table, f, y, x);
+        if (n0 + r >= Nv) v0 = v1 = 0.f;
+        o[k] = f16x2{(_Float16)v0, (_Float16)v1};
       }
-      const f16x2 o = {(_Float16)v0, (_Float16)v1};
-      if (which == 0) *(f16x2*)(dst + (int64_t)r * D + c) = o;
-      else *(f16x2*)(gimg + fb_row_of_key(r) * FbGeo<D>::KROW + c) = o;
+#pragma unroll
+      for (int k = 0; k < RB; ++k) {
+        const int r = threadIdx.x / (D / 2) + (k0 + k) * RS;
+        if (which == 0) *(f16x2*)(dst + (int64_t)r * D + c) = o[k];
+        else *(f16x2*)(gimg + fb_row_of_key(r) * FbGeo<D>::KROW + c) = o[k];
+      }
     }
   } else {
     // V^T: a thread owns the token pair (r, r + 1) of channels c, c + 256/32, ...
