@@ -169,7 +169,8 @@ def main():
                           "achieved": round(k2_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
                           "frac": round(k2_tops / PEAK_INT8_TOPS, 4),
                           "traffic": counted_traffic() if headline else None},
-                         **issued_mfma(ops_q4, k2_ms, stats), **(counted_limiter() if headline else {})),
+                         **issued_mfma(ops_q4, k2_ms, stats),
+                         **(counted_limiter(N * N * H * B, k2_ms) if headline else {})),
         "skips": stats,
         "kernels_ms": dict({"quantize_qk": round(k1_ms, 4), "int4_attention": round(k2_ms, 4)},
                            **({"fp16_fallback_even_heads": round(k3_ms, 4)} if mixed else {})),
@@ -260,10 +261,14 @@ def diffuse_floor(shape, rot, q, k, v, tab, z, out, ops, stream) -> dict:
             "skips": st, **issued_mfma(ops, ms, st)}
 
 
-def counted_limiter() -> dict:
+PEAK_VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9  # CUs x SIMDs x lanes x clock: 39.3e12 lane-ops/s
+
+
+def counted_limiter(elements: int, k2_ms: float) -> dict:
     """What limits k2_attention, from the committed SQ counter summary (VALU active
-    vs MFMA busy share of the launch), or nothing when the attention source has
-    changed since the counters were taken."""
+    vs MFMA busy share of the launch), and the launch against the VALU roofline (its
+    counted VALU lane-ops at one lane-op per lane per clock), or nothing when the
+    attention source has changed since the counters were taken."""
     summ = os.path.join(ROOT, "profiles", "k2_attention_wan720p_sq_counters.md")
     try:
         text = open(summ).read()
@@ -271,12 +276,20 @@ def counted_limiter() -> dict:
     except OSError:
         return {}
     f = dict(l.split(":", 1) for l in text.splitlines()
-             if l.startswith(("valu_active_frac:", "mfma_busy_frac:", "attention_source_sha256_16:")))
+             if l.startswith(("valu_active_frac:", "mfma_busy_frac:", "valu_lane_ops_per_element:",
+                              "attention_source_sha256_16:")))
     if f.get("attention_source_sha256_16", "").strip() != cur or "valu_active_frac" not in f:
         return {}
     valu, mfma = float(f["valu_active_frac"]), float(f["mfma_busy_frac"])
-    return {"limiter": "valu" if valu > mfma else "mfma",
-            "counters": {"valu_active_frac": valu, "mfma_busy_frac": mfma}}
+    out = {"limiter": "valu" if valu > mfma else "mfma",
+           "counters": {"valu_active_frac": valu, "mfma_busy_frac": mfma}}
+    if "valu_lane_ops_per_element" in f:
+        ops = float(f["valu_lane_ops_per_element"]) * elements
+        floor_ms = ops / PEAK_VALU_LANE_OPS * 1e3
+        out["valu_roofline"] = {"lane_ops_per_element": float(f["valu_lane_ops_per_element"]),
+                                "lane_ops_per_launch": ops, "peak_lane_ops_per_s": PEAK_VALU_LANE_OPS,
+                                "floor_ms": round(floor_ms, 3), "frac": round(floor_ms / k2_ms, 4)}
+    return out
 
 
 def io_label(dtype: str) -> str:
