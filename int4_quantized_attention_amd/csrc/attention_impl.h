@@ -27,10 +27,10 @@
 //    O^T = V^T P^T on the same instruction in its fp8 form, with no LDS round trip.
 //    The scores of the next step are issued before the softmax of the current one.
 //  * The P level r = round-half-even(2^y) is taken from the hardware exp2: with
-//    t = 2^y + 128.5 + 4*2^-16 the level is byte 2 of t's bits and the low 16 bits
+//    t = 2^y + 128.5 + 2^-16 the level is byte 2 of t's bits and the low 16 bits
 //    carry the rounding margin.  v_exp_f32 is within 1.5 * 2^-24 relative of 2^y,
-//    so whenever the margin is above 6/2^16 the level equals the exact one; the
-//    (rare) other elements are decided exactly against the 15 thresholds.  The
+//    so whenever the margin is above one unit of 2^-16 the level equals the exact
+//    one; the (rare) other elements are decided exactly against the 15 thresholds.  The
 //    level byte r in [0, 15], read as the fp8 code r * 2^-9 with a B scale of 2^9,
 //    is the operand: sum_j (P~_j + 8) v_j = sum_j r_j v_j folds the zero point into
 //    the product, and every product and sum is an exact integer in fp32.

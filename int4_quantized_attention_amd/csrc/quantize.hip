@@ -143,12 +143,12 @@ __global__ __launch_bounds__(256) void k1_kstats(QuantArgs a) {
 }
 
 // Channel means of K (and Q): binary64 sum of the partials in block order, / N, to
-// binary32.  One workgroup per (b*H + h, tensor in the order of k1_kstats' z), run by
-// k1_mid; thread c < D owns channel c.  The sum is one dependent chain per channel; it runs over chunks of
-// kMeanChunk partial rows staged in LDS, the next chunk's loads in flight (in
-// registers) while the current one is summed.
+// binary32.  One workgroup per (b*H + h, tensor z in the order of k1_kstats' z), run
+// by k1_mid; thread c < D owns channel c.  The sum is one dependent chain per
+// channel; it runs over chunks of kMeanChunk partial rows staged in LDS (buf,
+// kMeanChunk * D doubles), the next chunk's loads in flight (in registers) while the
+// current one is summed.
 constexpr int kMeanChunk = 32;
-// buf: kMeanChunk * D doubles of LDS.
 template <int D>
 RA_DEV void kmean_body(const QuantArgs& a, int bh, int z, double* buf) {
   constexpr int PER = kMeanChunk * D / 256;  // partials each thread stages per chunk
@@ -190,10 +190,6 @@ __global__ void k1_zero_u32(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-// Q / K quantisation, wave-sliced (ROT 0-2, qk_blk <= 64): a workgroup takes 64
-// tokens of one head; lane = token, wave w = channels [w D/4, (w+1) D/4).  A scale block is
-// qk_blk consecutive lanes of all four waves: its amax is a lane-group maximum in
-// each wave, then the four waves' values through LDS.
 // LDS of one workgroup of the wave-sliced quantiser: the Half exchange rows, the
 // scale-block maxima of the four waves, and the hand-on of the dS chain.
 template <int D, int ROT>
@@ -203,7 +199,11 @@ struct QkwsLds {
   double dsacc[64];
 };
 
-// One workgroup: tokens 64 blk .. 64 blk + 63 of head bh, Q or K.
+// Q / K quantisation, wave-sliced (ROT 0-2, qk_blk <= 64): one workgroup takes
+// tokens 64 blk .. 64 blk + 63 of head bh, of Q or of K; lane = token, wave w =
+// channels [w D/4, (w+1) D/4).  A scale block is qk_blk consecutive lanes of all four
+// waves: its amax is a lane-group maximum in each wave, then the four waves' values
+// through LDS.
 template <int D, int DT, int ROT>
 RA_DEV void quant_qk_ws_body(const QuantArgs& a, int64_t blk, int bh, bool isK, QkwsLds<D, ROT>& L) {
   constexpr int CPT = D / 4;
