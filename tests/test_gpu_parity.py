@@ -404,7 +404,7 @@ def _random_config(rng, i):
     return cfg, opts
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(32))
 def test_random_configs_parity(orc, i):
     """Seeded random combinations of shape, head split, block sizes, rotation, K and Q
     smoothing, causal block, variable lengths and P code: codes bit-exact, sampled
