@@ -107,6 +107,53 @@ def test_fallback_input_output_dtypes(orc, in_dt, out_dt):
     assert_close(out.float().cpu().numpy().reshape(-1, 128), ref, *tol)
 
 
+@pytest.mark.parametrize("i", range(12))
+def test_random_fallback_parity(orc, i):
+    """Seeded random fallback cases: D and head split, grid (ragged against the 64-key
+    groups), batch, input dtype, block-causal mask, variable lengths (NaN padding) and
+    a head subset; routed heads against the fallback oracle on sampled rows, rows past
+    each length and heads outside the subset untouched."""
+    rng = np.random.default_rng(2000 + i)
+    D = int(rng.choice([64, 128]))
+    Df, Dh, Dw = (24, 20, 20) if D == 64 else [(44, 42, 42), (16, 56, 56)][int(rng.integers(2))]
+    F, Hs, Ws = int(rng.integers(1, 4)), int(rng.integers(3, 19)), int(rng.integers(3, 29))
+    B, H = int(rng.integers(1, 3)), 3
+    cfg = synth.custom(B, H, F, Hs, Ws, D, Df, Dh, Dw, 64, 64, dtype="float16",
+                       recipe=str(rng.choice(["wan", "peaked"])) if D == 128 else "tiny")
+    N = synth.n_tokens(cfg)
+    cb = [0, 1, Hs * Ws, int(rng.integers(2, 200))][i % 4]
+    lens = [int(rng.integers(1, N + 1)) for _ in range(B)] if i % 3 == 0 else None
+    heads = sorted(int(x) for x in rng.choice(B * H, size=int(rng.integers(1, B * H + 1)), replace=False))
+    in_dt = [torch.float16, torch.bfloat16, torch.float32][i % 3]
+    print("case", i, cfg, cb, lens, heads, in_dt, flush=True)
+    Q, K, V = synth.make_inputs(cfg, seed=i)
+    if lens is not None:
+        for b, n in enumerate(lens):
+            for x in (Q, K, V):
+                x[b, :, n:] = np.nan
+    # the oracle sees exactly the values the library reads
+    Qd, Kd, Vd = (torch.from_numpy(x).to(in_dt) for x in (Q, K, V))
+    Qf, Kf, Vf = (x.float().numpy() for x in (Qd, Kd, Vd))
+    shape = ra.Shape.of(cfg)
+    tab = ra.rotattn_build_rope_table(shape, 0).cuda()
+    ws = torch.empty(ra.rotattn_fp16_fallback_workspace(shape), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, H, N, D), float("nan"), dtype=torch.float32, device="cuda")
+    ra.rotattn_fp16_fallback(shape, Qd.cuda(), Kd.cuda(), Vd.cuda(), tab, out, ws, heads=heads,
+                             causal_block=cb, seq_lens=lens)
+    o = out.cpu().numpy()
+    for bh in range(B * H):
+        ob = o[bh // H, bh % H]
+        if bh not in heads:
+            assert np.isnan(ob).all(), "a head outside the subset was written"
+            continue
+        n = lens[bh // H] if lens is not None else N
+        assert np.isnan(ob[n:]).all(), "rows past the length were written"
+        rows = rows_sample(n, 12, seed=bh)
+        ref = orc.fallback_attention(cfg, orc.rope_table(cfg, 0), Qf, Kf, Vf, rows=bh * N + rows,
+                                     causal_block=cb, seq_lens=lens)
+        assert_close(ob[rows], ref)
+
+
 FULL = [("wan480p", {}), ("wan720p", {}), ("hunyuan720p", {}),
         # the Wan-720p-like layer with per-token Q/K scales and with 256-key steps
         ("wan720p", dict(qk_blk=1)), ("wan720p", dict(kv_blk=256))]
