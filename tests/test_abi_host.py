@@ -165,3 +165,23 @@ def test_rope_table_matches_oracle(L, orc, cfgname, rot):
     ref = orc.rope_table(cfg, rot)
     assert mine.shape == ref.shape
     assert np.array_equal(mine.view(np.uint32), ref.view(np.uint32))
+
+
+def test_plain_c_caller(tmp_path):
+    """The header is a C ABI: a strict C99 program (tests/c_abi_host.c) compiles
+    against it with every warning as an error, links the library, and its host-side
+    calls answer as documented."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = os.path.join(root, "int4_quantized_attention_amd")
+    exe = str(tmp_path / "c_abi_host")
+    cc = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                         "-I" + os.path.join(root, "include"), os.path.join(root, "tests", "c_abi_host.c"),
+                         "-L" + pkg, "-lrotattn", "-Wl,-rpath," + pkg, "-o", exe], capture_output=True, text=True)
+    assert cc.returncode == 0, cc.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, "check %d failed" % run.returncode
+    assert run.stdout.strip() == "c abi ok"
