@@ -465,3 +465,28 @@ def test_empty_head_list_writes_nothing(orc):
     ra.rotattn_fp16_fallback(shape, to_dev(Q), to_dev(K), to_dev(V), tab, out, ws, heads=[])
     torch.cuda.synchronize()
     assert torch.isnan(out).all()
+
+
+def test_plain_c_device_caller(orc, tmp_path):
+    """The device path through the C ABI alone: a C99 program (tests/c_abi_device.c)
+    allocates with the HIP runtime's C API, quantises and runs the attention on the
+    tiny shape, and checks codes, scales and output against the oracle's C entry
+    points."""
+    import os
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg, odir = os.path.join(root, "int4_quantized_attention_amd"), os.path.join(root, "oracle")
+    exe = str(tmp_path / "c_abi_device")
+    cc = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                         "-I" + os.path.join(root, "include"), "-I/opt/rocm/include",
+                         os.path.join(root, "tests", "c_abi_device.c"), "-L" + pkg, "-lrotattn", "-L" + odir,
+                         "-lorc", "-L/opt/rocm/lib", "-lamdhip64", "-lm",
+                         "-Wl,-rpath," + ":".join((pkg, odir, "/opt/rocm/lib")), "-o", exe],
+                        capture_output=True, text=True)
+    assert cc.returncode == 0, cc.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, "check %d failed: %s" % (run.returncode, run.stderr)
+    assert run.stdout.startswith("c device abi ok")
