@@ -50,6 +50,8 @@ def main():
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     ap.add_argument("--no-diffuse", action="store_true",
                     help="skip the second attention timing on the diffuse (skip-free) recipe")
+    ap.add_argument("--torch-sdpa", action="store_true",
+                    help="also time torch's flash scaled-dot-product attention on the same shape (context)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on exactly one GPU (the path shards by head with no "
@@ -199,9 +201,35 @@ def main():
     if headline and not args.no_diffuse:
         result["diffuse"] = diffuse_floor(shape, rot, q, k, v, tab, z, out, ops, stream)
 
+    if args.torch_sdpa and not mixed and not args.causal:
+        result["torch_sdpa"] = torch_sdpa(B, H, N, D, ops, k2_ms)
+
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, rot, causal=args.causal)
     print(json.dumps(result))
+
+
+def torch_sdpa(B, H, N, D, ops, k2_ms) -> dict:
+    """torch's scaled-dot-product attention, flash backend forced (no math-path
+    fallback), on fp16 random tensors of the workload's shape: context for the FP16
+    fallback, not part of the step."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q, k, v = (torch.randn((B, H, N, D), dtype=torch.float16, device="cuda", generator=g) for _ in range(3))
+    with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+        torch.nn.functional.scaled_dot_product_attention(q, k, v)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 2
+        e0.record()
+        for _ in range(reps):
+            torch.nn.functional.scaled_dot_product_attention(q, k, v)
+        e1.record()
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"ms": round(ms, 3), "TFLOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+            "int4_attention_speedup": round(ms / k2_ms, 3), "backend": "flash, fp16, torch " + torch.__version__}
 
 
 def skip_stats(run) -> dict:
